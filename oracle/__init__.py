@@ -1,0 +1,14 @@
+"""fp64 CPU oracle for the Kimi Delta Attention recurrence (test infrastructure).
+
+Only tests/, ``__graft_entry__.smoke()`` and the CPU-baseline leg of bench.py
+may import this package.  The GPU library never imports or calls it.
+"""
+from .oracle import (  # noqa: F401
+    build,
+    load,
+    load_path,
+    fwd,
+    decode,
+    brute_force,
+    max_threads,
+)
