@@ -1,0 +1,114 @@
+// kda_api.hip -- C ABI of the KDA operator: argument checks and dispatch.
+// Declarations and the contract of every entry point are in include/kda.h.
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/kda.h"
+
+namespace kda {
+hipError_t decode_step_launch(const void *q, const void *k, const void *v,
+                              const void *log_alpha, const void *beta, float *S,
+                              void *o, int units, int dk, int dv, bool bf16,
+                              hipStream_t stream);
+hipError_t chunked_fwd_launch(const void *q, const void *k, const void *v, const void *g,
+                              const void *beta, const float *S0, float *S_T, void *o,
+                              const int32_t *cu_seqlens, int num_seqs, int B, int T, int H,
+                              int dk, int dv, bool bf16, void *workspace, hipStream_t stream);
+}  // namespace kda
+
+namespace {
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool dim_ok(int d) { return d == 64 || d == 128; }
+
+// Element counts must stay addressable with 64-bit offsets and the grid must
+// fit a 32-bit block index.
+bool sizes_fit(long long a, long long b, long long c, long long d) {
+    const long long lim = (long long)1 << 46;
+    long long x = a;
+    if (b && x > lim / b) return false;
+    x *= b;
+    if (c && x > lim / c) return false;
+    x *= c;
+    if (d && x > lim / d) return false;
+    return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *kda_status_string(kda_status status)
+{
+    switch (status) {
+    case KDA_OK: return "KDA_OK";
+    case KDA_ERR_INVALID_ARG: return "KDA_ERR_INVALID_ARG";
+    case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED";
+    case KDA_ERR_HIP: return "KDA_ERR_HIP";
+    }
+    return "KDA_ERR_UNKNOWN";
+}
+
+size_t kda_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int num_seqs)
+{
+    (void)B; (void)T; (void)H; (void)dk; (void)dv;
+    // longest-first order of packed sequences
+    if (num_seqs <= 1) return 0;
+    return ((size_t)num_seqs * sizeof(int32_t) + 255) & ~(size_t)255;
+}
+
+kda_status kda_fwd_chunked(const void *q, const void *k, const void *v,
+                           const void *log_alpha, const void *beta,
+                           const float *S0, const int32_t *cu_seqlens, int num_seqs,
+                           int B, int T, int H, int dk, int dv, kda_dtype dtype,
+                           void *o, float *S_T,
+                           void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_INVALID_ARG;
+    if (B < 0 || T < 0 || H <= 0 || dk <= 0 || dv <= 0) return KDA_ERR_INVALID_ARG;
+    if (cu_seqlens && (B != 1 || num_seqs < 0)) return KDA_ERR_INVALID_ARG;
+    const int nseq = cu_seqlens ? num_seqs : B;
+    if (!dim_ok(dk) || !dim_ok(dv)) return KDA_ERR_UNSUPPORTED;
+    if (dtype == KDA_F32 && dk != 64) return KDA_ERR_UNSUPPORTED;
+    if (!sizes_fit(B, T, H, dk > dv ? dk : dv) || !sizes_fit(nseq, H, dk, dv)) return KDA_ERR_INVALID_ARG;
+    if ((long long)nseq * H * 2 >= ((long long)1 << 31)) return KDA_ERR_INVALID_ARG;
+    const long long tokens = (long long)B * T;
+    if (tokens > 0 || nseq > 0) {
+        if (tokens > 0 && (!q || !k || !v || !log_alpha || !beta || !o)) return KDA_ERR_INVALID_ARG;
+        if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(log_alpha) ||
+            !aligned16(beta) || !aligned16(o) || !aligned16(S0) || !aligned16(S_T))
+            return KDA_ERR_INVALID_ARG;
+    }
+    const size_t need = kda_fwd_workspace_bytes(B, T, H, dk, dv, nseq);
+    if (cu_seqlens && need > 0) {
+        if (!workspace || workspace_bytes < need || !aligned16(workspace)) return KDA_ERR_INVALID_ARG;
+    }
+    if (nseq == 0) return KDA_OK;
+    hipError_t e = kda::chunked_fwd_launch(q, k, v, log_alpha, beta, S0, S_T, o, cu_seqlens,
+                                           nseq, B, T, H, dk, dv, dtype == KDA_BF16,
+                                           cu_seqlens ? workspace : nullptr,
+                                           static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status kda_decode_step(const void *q, const void *k, const void *v,
+                           const void *log_alpha, const void *beta,
+                           float *S_cache, int N, int H, int dk, int dv,
+                           kda_dtype dtype, void *o, void *stream)
+{
+    if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_INVALID_ARG;
+    if (N < 0 || H <= 0 || dk <= 0 || dv <= 0) return KDA_ERR_INVALID_ARG;
+    if (!dim_ok(dk) || !dim_ok(dv)) return KDA_ERR_UNSUPPORTED;
+    if (!sizes_fit(N, H, dk, dv)) return KDA_ERR_INVALID_ARG;
+    if ((long long)N * H >= ((long long)1 << 31)) return KDA_ERR_INVALID_ARG;
+    if (N == 0) return KDA_OK;
+    if (!q || !k || !v || !log_alpha || !beta || !S_cache || !o) return KDA_ERR_INVALID_ARG;
+    if (!aligned16(S_cache)) return KDA_ERR_INVALID_ARG;
+    hipError_t e = kda::decode_step_launch(q, k, v, log_alpha, beta, S_cache, o, N * H, dk, dv,
+                                           dtype == KDA_BF16, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,783 @@
+// kda_chunked.hip -- chunkwise KDA forward for gfx950 (MI355X).
+//
+// The pages name a chunkwise algorithm built on the Diagonal-Plus-Low-Rank
+// state transition (akshathtiwari.co.in "Kimi Delta Attention" explainer) that
+// regroups the recurrence into matrix products (daily.dev summary of "You
+// Could Have Come Up with Kimi Delta Attention"); they do not print it, so
+// the form below is derived from the recurrence
+//     S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T,  o_t = S_t^T q_t.
+//
+// Per chunk of C = 64 tokens with entry state S (d_k x d_v), Gamma_r the
+// inclusive cumulative log-decay per key channel inside the chunk:
+//   A      = strict_lower(Diag(beta) K_up K_dn^T)      A_ri = beta_r sum_c k_rc k_ic e^{Gamma_rc - Gamma_ic}
+//   T'     = (I + A)^{-1} Diag(beta)
+//   U      = T' (V - K_up S)                             K_up = K * e^{Gamma}
+//   O      = Q_up S + tril_incl(Q_up K_dn^T) U           Q_up = Q * e^{Gamma}
+//   S_next = Diag(e^{Gamma_last}) S + K_right^T U        K_right = K * e^{Gamma_last - Gamma}
+//
+// Work split: one 256-thread workgroup (4 waves) owns one (sequence, head,
+// value-slice) and walks that sequence's chunks in order.  The fp32 state
+// slice lives in MFMA accumulator registers for the whole sequence: each wave
+// owns 16-column strips of S.  The rows of every accumulator tile are
+// assigned so that an accumulator can be fed straight back as the B operand
+// of the next MFMA in natural k order (see rowmap), so S, V - K_up S and U
+// never round-trip through LDS.
+//
+// Per chunk (all waves):
+//   A1  wave R loads rows 16R..16R+15 of g, scans the log-decay along rows
+//       (DPP), forms lambda = Gamma - Gamma_mid(R) relative to the middle of
+//       its 16-row block, and publishes block sums.
+//   A2  one thread per key channel turns block sums into the few per-chunk
+//       factors (block-to-block decays, e^{Gamma_last}).
+//   A3  wave R scales its k / q rows: k a, q a, k b with a = e^{lambda},
+//       b = e^{-lambda}; K_up, Q_up, K_right^T go to LDS.
+//   A4  wave R forms its row block of A and of the intra-chunk output matrix
+//       P on MFMA: diagonal tile from registers, off-diagonal tiles against
+//       k b (from LDS) times the block-to-block decay.
+//   A5  T = (I + A)^{-1}: 16x16 diagonal blocks by forward substitution,
+//       off-diagonal blocks by fp32 MFMA, then T' = T Diag(beta).
+//   B   per 16-column strip: Y = K_up S, O1 = Q_up S, U = T'(V - Y),
+//       O = O1 + P U, S = Diag(gamma) S + K_right^T U.
+//
+// Exponent range.  All decay factors of the form e^{Gamma_r - Gamma_i} with
+// r >= i are <= 1.  Splitting them at a reference row inside a 16-row block
+// gives one factor above 1; the fast path is taken when every |lambda| in
+// the chunk is <= 96 in log2 units (no factor leaves [2^-96, 2^96]).  A chunk
+// with stronger decay inside a 16-row block takes an exact slower path that
+// forms A and P entry by entry with e^{Gamma_r - Gamma_i} evaluated directly.
+#include "kda_device.h"
+
+namespace kda {
+
+constexpr int CH = 64;   // chunk length (tokens)
+
+struct ChunkParams {
+    const void *q, *k, *v, *g, *beta;
+    const float *S0;
+    float *S_T;
+    void *o;
+    const int32_t *cu_seqlens;   // NULL -> dense
+    const int32_t *order;        // sequence processing order (NULL -> identity)
+    int T;          // tokens per batch row (dense)
+    int H;
+    int DV;         // full value dimension
+    int units;      // num_seqs * H
+    int nslices;    // DV / DVS
+};
+
+// Per-mode operand conventions.  RUN consecutive key channels form one
+// lane's share of one MFMA k-step group:
+//   bf16: v_mfma_f32_16x16x32_bf16, lane (row m, group j) supplies k = 8j..8j+7
+//   f32 : v_mfma_f32_16x16x4f32, four steps; step i, lane group j <-> k = 4j + i
+// A "run" rho covers logical k in [4*RUN*rho, 4*RUN*rho + 4*RUN); lane group
+// j owns logical k = 4*RUN*rho + RUN*j + (0..RUN-1).
+template <bool F32> struct Mode;
+template <> struct Mode<false> {
+    using in_t = bf16_t;
+    using op_t = bf16_t;
+    using frag_t = bf16x8;
+    static constexpr int RUN = 8;
+    static constexpr int PAD = 8;   // elements: 16 bytes
+};
+template <> struct Mode<true> {
+    using in_t = float;
+    using op_t = float;
+    using frag_t = f32x4;
+    static constexpr int RUN = 4;
+    static constexpr int PAD = 4;
+};
+
+// Row (logical index) held by accumulator tile (run rho, half h) at tile row m.
+// With it, the 4 registers of a lane of two (bf16) or one (f32) accumulator
+// tiles are exactly the lane's B-operand k-slots of run rho in natural order.
+template <int RUN>
+__device__ __forceinline__ int rowmap(int rho, int h, int m) {
+    return 4 * RUN * rho + RUN * (m >> 2) + 4 * h + (m & 3);
+}
+
+__device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+template <bool F32>
+__device__ __forceinline__ f32x4 mma_run(f32x4 acc, typename Mode<F32>::frag_t a,
+                                         typename Mode<F32>::frag_t b) {
+    if constexpr (F32) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc = mfma_f32(a[i], b[i], acc);
+        return acc;
+    } else {
+        return mfma_bf16(a, b, acc);
+    }
+}
+
+// B-operand fragment of run rho from accumulator tiles (rowmap layout).
+template <bool F32>
+__device__ __forceinline__ typename Mode<F32>::frag_t acc_frag(const f32x4 *tiles, int rho) {
+    if constexpr (F32) {
+        return tiles[rho];
+    } else {
+        const f32x4 lo = tiles[2 * rho], hi = tiles[2 * rho + 1];
+        bf16x8 f;
+        f[0] = (__bf16)lo[0]; f[1] = (__bf16)lo[1]; f[2] = (__bf16)lo[2]; f[3] = (__bf16)lo[3];
+        f[4] = (__bf16)hi[0]; f[5] = (__bf16)hi[1]; f[6] = (__bf16)hi[2]; f[7] = (__bf16)hi[3];
+        return f;
+    }
+}
+
+template <bool F32>
+__device__ __forceinline__ typename Mode<F32>::frag_t to_frag(const float *x) {
+    typename Mode<F32>::frag_t f;
+    if constexpr (F32) {
+        f[0] = x[0]; f[1] = x[1]; f[2] = x[2]; f[3] = x[3];
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f[e] = (__bf16)x[e];
+    }
+    return f;
+}
+
+// Store RUN fp32 values as operands (16 bytes either way).
+template <bool F32>
+__device__ __forceinline__ void store_run(typename Mode<F32>::op_t *dst, const float *x) {
+    *reinterpret_cast<typename Mode<F32>::frag_t *>(dst) = to_frag<F32>(x);
+}
+
+template <bool F32>
+__device__ __forceinline__ void load_run_f32(const typename Mode<F32>::in_t *src, float *x) {
+    if constexpr (F32) {
+        const float4 t = *reinterpret_cast<const float4 *>(src);
+        x[0] = t.x; x[1] = t.y; x[2] = t.z; x[3] = t.w;
+    } else {
+        const uint4 t = *reinterpret_cast<const uint4 *>(src);
+        const uint32_t w[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            x[2 * e] = __uint_as_float(w[e] << 16);
+            x[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+        }
+    }
+}
+
+__device__ __forceinline__ float dpp_row_shr(float x, int n) {
+    // lanes m < n of each 16-lane row receive 0
+    switch (n) {
+    case 1: return __builtin_amdgcn_update_dpp(0.0f, x, 0x111, 0xf, 0xf, false);
+    case 2: return __builtin_amdgcn_update_dpp(0.0f, x, 0x112, 0xf, 0xf, false);
+    case 4: return __builtin_amdgcn_update_dpp(0.0f, x, 0x114, 0xf, 0xf, false);
+    default: return __builtin_amdgcn_update_dpp(0.0f, x, 0x118, 0xf, 0xf, false);
+    }
+}
+__device__ __forceinline__ float dpp_row_share8(float x) {
+    return __builtin_amdgcn_update_dpp(0.0f, x, 0x158, 0xf, 0xf, false);
+}
+
+// LDS layout (bytes), per instantiation.
+template <int DK, bool F32>
+struct Lds {
+    using op_t = typename Mode<F32>::op_t;
+    static constexpr int PAD = Mode<F32>::PAD;
+    static constexpr int LDK = DK + PAD;          // row stride of [64][DK] operand arrays
+    static constexpr int LCH = CH + PAD;          // row stride of [*][64] operand arrays
+    static constexpr int LF = CH + 4;             // row stride of fp32 [64][64] arrays
+    static constexpr int KU = 0;                                         // K_up  [64][LDK]
+    static constexpr int QU = KU + CH * LDK * (int)sizeof(op_t);         // Q_up  [64][LDK]
+    static constexpr int KRT = QU + CH * LDK * (int)sizeof(op_t);        // K_right^T [DK][LCH]
+    static constexpr int KB = KRT + DK * LCH * (int)sizeof(op_t);        // k b   [64][LDK]
+    static constexpr int AM = KB + CH * LDK * (int)sizeof(op_t);         // A fp32 [64][LF]
+    static constexpr int TF = AM + CH * LF * 4;                          // T fp32 [64][LF]
+    static constexpr int TP = TF + CH * LF * 4;                          // T' op [64][LCH]
+    static constexpr int PM = TP + CH * LCH * (int)sizeof(op_t);         // P op  [64][LCH]
+    static constexpr int FAC = PM + CH * LCH * (int)sizeof(op_t);        // factors fp32 [20][DK]
+    static constexpr int TOT = FAC + 20 * DK * 4;                        // block sums [4][2][DK]
+    static constexpr int BETA = TOT + 8 * DK * 4;                        // beta [64]
+    static constexpr int BYTES = BETA + CH * 4;
+    // slow path: Gamma fp32 [64][DK] over AM..TF (both fp32 [64][LF])
+    static_assert(CH * DK * 4 <= 2 * CH * LF * 4 + CH * LDK * (int)sizeof(op_t), "slow-path Gamma fits");
+};
+// factor rows in Lds::FAC
+constexpr int F_B = 0;      // e^{Gamma_mid(R)}, R = 0..3
+constexpr int F_W = 4;      // e^{Gamma_mid(R) - Gamma_mid(I)}, (1,0),(2,0),(2,1),(3,0),(3,1),(3,2)
+constexpr int F_GAM = 10;   // e^{Gamma_last}
+constexpr int F_Z = 11;     // e^{Gamma_last - Gamma_mid(R)}, R = 0..3
+constexpr int F_P = 15;     // Gamma at the end of block R-1 (log2), R = 0..3; 19: Gamma_last (log2)
+__device__ __forceinline__ int w_index(int R, int I) { return F_W + (R * (R - 1)) / 2 + I; }
+
+template <int DK, int NSTRIP, bool F32>
+__global__ __launch_bounds__(256, 1) void chunked_fwd_kernel(ChunkParams p)
+{
+    using M = Mode<F32>;
+    using in_t = typename M::in_t;
+    using op_t = typename M::op_t;
+    using frag_t = typename M::frag_t;
+    using L = Lds<DK, F32>;
+    constexpr int RUN = M::RUN;
+    constexpr int NCH = DK / 4;          // key channels per lane in the prep phase
+    constexpr int NRUN = NCH / RUN;      // runs over d_k
+    constexpr int TPR = RUN / 4;         // accumulator tiles per run (2 bf16, 1 f32)
+    constexpr int NKT = DK / 16;         // accumulator tiles over d_k (state rows)
+    constexpr int DVS = 64 * NSTRIP;     // value columns per workgroup
+
+    __shared__ __attribute__((aligned(16))) unsigned char smem[L::BYTES];
+    op_t *sKU = reinterpret_cast<op_t *>(smem + L::KU);
+    op_t *sQU = reinterpret_cast<op_t *>(smem + L::QU);
+    op_t *sKRt = reinterpret_cast<op_t *>(smem + L::KRT);
+    op_t *sKB = reinterpret_cast<op_t *>(smem + L::KB);
+    float *sA = reinterpret_cast<float *>(smem + L::AM);
+    float *sTf = reinterpret_cast<float *>(smem + L::TF);
+    op_t *sTp = reinterpret_cast<op_t *>(smem + L::TP);
+    op_t *sP = reinterpret_cast<op_t *>(smem + L::PM);
+    float *sFac = reinterpret_cast<float *>(smem + L::FAC);
+    float *sTot = reinterpret_cast<float *>(smem + L::TOT);
+    float *sBeta = reinterpret_cast<float *>(smem + L::BETA);
+    float *sGam = reinterpret_cast<float *>(smem + L::AM);   // slow path only
+
+    // ---- work unit: XCD-aware (sequence, head, slice) ------------------------
+    // Blocks b and b + 8 run on the same XCD (round-robin dispatch), so the
+    // slices of one (sequence, head) are given ids 8 apart and share that
+    // XCD's L2 for their common k / q / g reads.
+    const int NS = p.nslices;
+    const int bid = blockIdx.x;
+    const int grp = bid / (8 * NS);
+    const int xcd = bid & 7;
+    const int slice = (bid >> 3) % NS;
+    const int sh = grp * 8 + xcd;
+    if (sh >= p.units) return;
+    const int H = p.H, DV = p.DV;
+    const int seq_rank = sh / H, head = sh - (sh / H) * H;
+    const int seq = p.order ? p.order[seq_rank] : seq_rank;
+    long t0, len;
+    if (p.cu_seqlens) {
+        t0 = p.cu_seqlens[seq];
+        len = (long)p.cu_seqlens[seq + 1] - t0;
+    } else {
+        t0 = (long)seq * p.T;
+        len = p.T;
+    }
+    const int col0 = slice * DVS;
+
+    const int tid = threadIdx.x;
+    const int w = tid >> 6, lane = tid & 63, jg = lane >> 4, mr = lane & 15;
+
+    const in_t *gq = static_cast<const in_t *>(p.q);
+    const in_t *gk = static_cast<const in_t *>(p.k);
+    const in_t *gv = static_cast<const in_t *>(p.v);
+    const in_t *gg = static_cast<const in_t *>(p.g);
+    const in_t *gb = static_cast<const in_t *>(p.beta);
+    in_t *go = static_cast<in_t *>(p.o);
+
+    // Upper blocks of T' and P stay zero for the whole sequence.
+    for (int idx = tid; idx < CH * CH; idx += 256) {
+        const int r = idx / CH, c = idx % CH;
+        if ((c >> 4) > (r >> 4)) {
+            store_elem(&sTp[r * L::LCH + c], 0.0f);
+            store_elem(&sP[r * L::LCH + c], 0.0f);
+        }
+    }
+
+    // ---- state: NSTRIP strips x NKT tiles, rowmap rows, column = strip col + mr
+    f32x4 S[NSTRIP][NKT];
+#pragma unroll
+    for (int s = 0; s < NSTRIP; ++s) {
+        const int cb = col0 + 16 * (w + 4 * s);
+#pragma unroll
+        for (int tt = 0; tt < NKT; ++tt) {
+            const int rho = tt / TPR, h = tt % TPR;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = rowmap<RUN>(rho, h, 4 * jg + i);
+                S[s][tt][i] = p.S0 ? p.S0[(((size_t)seq * H + head) * DK + row) * DV + cb + mr] : 0.0f;
+            }
+        }
+    }
+
+    const int R = w;                  // prep row block of this wave
+    const int rloc = 16 * R + mr;     // prep row (token within chunk) of this lane
+
+    for (long c0 = 0; c0 < len; c0 += CH) {
+        const int clen = (int)((len - c0) < CH ? (len - c0) : CH);
+        const bool rvalid = rloc < clen;
+        const size_t th_row = ((size_t)(t0 + c0 + rloc)) * H + head;   // token-head of prep row
+
+        // ================= A1: log-decay scan along rows =====================
+        float lam[NCH];      // Gamma_r - Gamma_mid(R)   (log2), later reused
+        float Lr[NCH];       // local inclusive sum within the 16-row block (log2)
+        bool fast_ok = true;
+#pragma unroll
+        for (int rr = 0; rr < NRUN; ++rr) {
+            const int cbase = 4 * RUN * rr + RUN * jg;
+            float x[RUN];
+            if (rvalid) {
+                load_run_f32<F32>(gg + th_row * DK + cbase, x);
+            } else {
+#pragma unroll
+                for (int e = 0; e < RUN; ++e) x[e] = 0.0f;
+            }
+#pragma unroll
+            for (int e = 0; e < RUN; ++e) {
+                float v = x[e] * kLog2e;
+                v += dpp_row_shr(v, 1);
+                v += dpp_row_shr(v, 2);
+                v += dpp_row_shr(v, 4);
+                v += dpp_row_shr(v, 8);
+                Lr[rr * RUN + e] = v;
+                const float mid = dpp_row_share8(v);
+                const float lm = v - mid;
+                lam[rr * RUN + e] = lm;
+                fast_ok = fast_ok && (fabsf(lm) <= 96.0f);
+                if (mr == 8) sTot[(2 * R + 0) * DK + cbase + e] = v;
+                if (mr == 15) sTot[(2 * R + 1) * DK + cbase + e] = v;
+            }
+        }
+        if (jg == 0) sBeta[rloc] = rvalid ? load_elem(gb + th_row) : 0.0f;
+        const bool slow = __syncthreads_or(!fast_ok);
+
+        // ================= A2: per-channel chunk factors ======================
+        if (tid < DK) {
+            const int c = tid;
+            float Lm[4], Lt[4], Pb[4], Gm[4];
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                Lm[b] = sTot[(2 * b + 0) * DK + c];
+                Lt[b] = sTot[(2 * b + 1) * DK + c];
+            }
+            Pb[0] = 0.0f;
+            Pb[1] = Lt[0];
+            Pb[2] = Pb[1] + Lt[1];
+            Pb[3] = Pb[2] + Lt[2];
+            const float Glast = Pb[3] + Lt[3];
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                Gm[b] = Pb[b] + Lm[b];
+                sFac[(F_B + b) * DK + c] = __builtin_amdgcn_exp2f(Gm[b]);
+                sFac[(F_Z + b) * DK + c] = __builtin_amdgcn_exp2f(Glast - Gm[b]);
+                sFac[(F_P + b) * DK + c] = Pb[b];
+            }
+#pragma unroll
+            for (int b = 1; b < 4; ++b)
+#pragma unroll
+                for (int i = 0; i < b; ++i)
+                    sFac[w_index(b, i) * DK + c] = __builtin_amdgcn_exp2f(Gm[b] - Gm[i]);
+            sFac[F_GAM * DK + c] = __builtin_amdgcn_exp2f(Glast);
+            sFac[(F_P + 4) * DK + c] = Glast;
+        }
+        __syncthreads();
+
+        // ================= A3/A4: operands, A and P ==========================
+        frag_t fka[NRUN], fqa[NRUN], fkb[NRUN];
+        float kreg[NCH], qreg[NCH];
+#pragma unroll
+        for (int rr = 0; rr < NRUN; ++rr) {
+            const int cbase = 4 * RUN * rr + RUN * jg;
+            if (rvalid) {
+                load_run_f32<F32>(gk + th_row * DK + cbase, &kreg[rr * RUN]);
+                load_run_f32<F32>(gq + th_row * DK + cbase, &qreg[rr * RUN]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < RUN; ++e) { kreg[rr * RUN + e] = 0.0f; qreg[rr * RUN + e] = 0.0f; }
+            }
+        }
+
+        if (!slow) {
+#pragma unroll
+            for (int rr = 0; rr < NRUN; ++rr) {
+                const int cbase = 4 * RUN * rr + RUN * jg;
+                float ka[RUN], qa[RUN], kb[RUN], ku[RUN], qu[RUN], kr[RUN];
+#pragma unroll
+                for (int e = 0; e < RUN; ++e) {
+                    const int c = cbase + e;
+                    const float lm = lam[rr * RUN + e];
+                    const float a = __builtin_amdgcn_exp2f(lm);
+                    const float b = __builtin_amdgcn_exp2f(-lm);
+                    ka[e] = kreg[rr * RUN + e] * a;
+                    qa[e] = qreg[rr * RUN + e] * a;
+                    kb[e] = kreg[rr * RUN + e] * b;
+                    const float Bf = sFac[(F_B + R) * DK + c];
+                    ku[e] = ka[e] * Bf;
+                    qu[e] = qa[e] * Bf;
+                    kr[e] = kb[e] * sFac[(F_Z + R) * DK + c];
+                }
+                fka[rr] = to_frag<F32>(ka);
+                fqa[rr] = to_frag<F32>(qa);
+                fkb[rr] = to_frag<F32>(kb);
+                store_run<F32>(&sKU[rloc * L::LDK + cbase], ku);
+                store_run<F32>(&sQU[rloc * L::LDK + cbase], qu);
+                store_run<F32>(&sKB[rloc * L::LDK + cbase], kb);
+#pragma unroll
+                for (int e = 0; e < RUN; ++e) store_elem(&sKRt[(cbase + e) * L::LCH + rloc], kr[e]);
+            }
+            __syncthreads();
+
+            // wave R: tiles (R, I), I = 0..R
+            for (int I = 0; I <= R; ++I) {
+                f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
+                if (I == R) {
+#pragma unroll
+                    for (int rr = 0; rr < NRUN; ++rr) {
+                        accA = mma_run<F32>(accA, fka[rr], fkb[rr]);
+                        accP = mma_run<F32>(accP, fqa[rr], fkb[rr]);
+                    }
+                } else {
+                    const int wrow = w_index(R, I);
+#pragma unroll
+                    for (int rr = 0; rr < NRUN; ++rr) {
+                        const int cbase = 4 * RUN * rr + RUN * jg;
+                        float cv[RUN];
+                        const op_t *src = &sKB[(16 * I + mr) * L::LDK + cbase];
+#pragma unroll
+                        for (int e = 0; e < RUN; ++e)
+                            cv[e] = load_elem(src + e) * sFac[wrow * DK + cbase + e];
+                        const frag_t fc = to_frag<F32>(cv);
+                        accA = mma_run<F32>(accA, fka[rr], fc);
+                        accP = mma_run<F32>(accP, fqa[rr], fc);
+                    }
+                }
+                // C layout: rows 16R + 4jg + i, column 16I + mr
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int row = 16 * R + 4 * jg + i, col = 16 * I + mr;
+                    float a = accA[i] * sBeta[row];
+                    float pv = accP[i];
+                    if (I == R) {
+                        if (col >= row) a = 0.0f;
+                        if (col > row) pv = 0.0f;
+                    }
+                    sA[row * L::LF + col] = a;
+                    store_elem(&sP[row * L::LCH + col], pv);
+                }
+            }
+        } else {
+            // ---- exact path: A and P entry by entry -----------------------------
+            float Gabs[NCH];
+#pragma unroll
+            for (int rr = 0; rr < NRUN; ++rr) {
+                const int cbase = 4 * RUN * rr + RUN * jg;
+                float kk[RUN], qq[RUN];
+#pragma unroll
+                for (int e = 0; e < RUN; ++e) {
+                    const int c = cbase + e;
+                    Gabs[rr * RUN + e] = sFac[(F_P + R) * DK + c] + Lr[rr * RUN + e];
+                    sGam[rloc * DK + c] = Gabs[rr * RUN + e];
+                    kk[e] = kreg[rr * RUN + e];
+                    qq[e] = qreg[rr * RUN + e];
+                }
+                store_run<F32>(&sKU[rloc * L::LDK + cbase], kk);
+                store_run<F32>(&sQU[rloc * L::LDK + cbase], qq);
+            }
+            __syncthreads();
+            constexpr int NPAIR = CH * (CH + 1) / 2;
+            constexpr int PPT = (NPAIR + 255) / 256;
+            float resA[PPT], resP[PPT];
+#pragma unroll
+            for (int n = 0; n < PPT; ++n) {
+                const int pidx = tid + 256 * n;
+                resA[n] = 0.0f;
+                resP[n] = 0.0f;
+                if (pidx < NPAIR) {
+                    int r = (int)((sqrtf(8.0f * pidx + 1.0f) - 1.0f) * 0.5f);
+                    while ((r + 1) * (r + 2) / 2 <= pidx) ++r;
+                    while (r * (r + 1) / 2 > pidx) --r;
+                    const int i = pidx - r * (r + 1) / 2;
+                    float sa = 0.0f, sp = 0.0f;
+                    for (int c = 0; c < DK; ++c) {
+                        const float f = __builtin_amdgcn_exp2f(sGam[r * DK + c] - sGam[i * DK + c]);
+                        const float kic = load_elem(&sKU[i * L::LDK + c]) * f;
+                        sa += load_elem(&sKU[r * L::LDK + c]) * kic;
+                        sp += load_elem(&sQU[r * L::LDK + c]) * kic;
+                    }
+                    resA[n] = (i < r) ? sa * sBeta[r] : 0.0f;
+                    resP[n] = sp;
+                }
+            }
+            __syncthreads();
+#pragma unroll
+            for (int n = 0; n < PPT; ++n) {
+                const int pidx = tid + 256 * n;
+                if (pidx < NPAIR) {
+                    int r = (int)((sqrtf(8.0f * pidx + 1.0f) - 1.0f) * 0.5f);
+                    while ((r + 1) * (r + 2) / 2 <= pidx) ++r;
+                    while (r * (r + 1) / 2 > pidx) --r;
+                    const int i = pidx - r * (r + 1) / 2;
+                    sA[r * L::LF + i] = resA[n];
+                    store_elem(&sP[r * L::LCH + i], resP[n]);
+                }
+            }
+            // zero the strict upper part of the diagonal 16x16 blocks of P
+            for (int idx = tid; idx < CH * 16; idx += 256) {
+                const int r = idx / 16, c = 16 * (r / 16) + (idx % 16);
+                if (c > r) store_elem(&sP[r * L::LCH + c], 0.0f);
+            }
+#pragma unroll
+            for (int rr = 0; rr < NRUN; ++rr) {
+                const int cbase = 4 * RUN * rr + RUN * jg;
+                float ku[RUN], qu[RUN], kr[RUN];
+#pragma unroll
+                for (int e = 0; e < RUN; ++e) {
+                    const int c = cbase + e;
+                    const float Ga = Gabs[rr * RUN + e];
+                    const float up = __builtin_amdgcn_exp2f(Ga);
+                    ku[e] = kreg[rr * RUN + e] * up;
+                    qu[e] = qreg[rr * RUN + e] * up;
+                    kr[e] = kreg[rr * RUN + e] * __builtin_amdgcn_exp2f(sFac[(F_P + 4) * DK + c] - Ga);
+                }
+                store_run<F32>(&sKU[rloc * L::LDK + cbase], ku);
+                store_run<F32>(&sQU[rloc * L::LDK + cbase], qu);
+#pragma unroll
+                for (int e = 0; e < RUN; ++e) store_elem(&sKRt[(cbase + e) * L::LCH + rloc], kr[e]);
+            }
+        }
+        __syncthreads();
+
+        // ================= A5: T = (I + A)^{-1}, T' = T Diag(beta) ===========
+        {
+            // diagonal block R by forward substitution; lane column mr
+            float tcol[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float acc = (r == mr) ? 1.0f : 0.0f;
+                const float *arow = &sA[(16 * R + r) * L::LF + 16 * R];
+#pragma unroll
+                for (int i = 0; i < r; ++i) acc -= arow[i] * tcol[i];
+                tcol[r] = acc;
+            }
+            if (jg == 0) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) sTf[(16 * R + r) * L::LF + 16 * R + mr] = tcol[r];
+            }
+        }
+        __syncthreads();
+        // off-diagonal blocks by distance d = R - I; wave R computes (R, R - d)
+        for (int d = 1; d < 4; ++d) {
+            if (R >= d) {
+                const int I = R - d;
+                f32x4 Mx = {0.f, 0.f, 0.f, 0.f};
+                for (int J = I; J < R; ++J) {
+                    // Mx += A[R,J] T[J,I]
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) {
+                        const float av = sA[(16 * R + mr) * L::LF + 16 * J + 4 * jg + s];
+                        const float bv = sTf[(16 * J + 4 * jg + s) * L::LF + 16 * I + mr];
+                        Mx = mfma_f32(av, bv, Mx);
+                    }
+                }
+                // T[R,I] = -T[R,R] Mx  (Mx accumulator is the B operand: k = 4jg + s)
+                f32x4 Tx = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    const float av = sTf[(16 * R + mr) * L::LF + 16 * R + 4 * jg + s];
+                    Tx = mfma_f32(av, Mx[s], Tx);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    sTf[(16 * R + 4 * jg + i) * L::LF + 16 * I + mr] = -Tx[i];
+            }
+            __syncthreads();
+        }
+        for (int idx = tid; idx < CH * CH; idx += 256) {
+            const int r = idx / CH, c = idx % CH;
+            if ((c >> 4) <= (r >> 4))
+                store_elem(&sTp[r * L::LCH + c], sTf[r * L::LF + c] * sBeta[c]);
+        }
+        __syncthreads();
+
+        // ================= B: state strips ===================================
+#pragma unroll
+        for (int s = 0; s < NSTRIP; ++s) {
+            const int cb = col0 + 16 * (w + 4 * s);
+            frag_t sf[NRUN];
+#pragma unroll
+            for (int rr = 0; rr < NRUN; ++rr) sf[rr] = acc_frag<F32>(S[s], rr);
+
+            // Y = K_up S, O1 = Q_up S over 64 chunk rows: 4 tiles in rowmap order
+            f32x4 Y[4], O[4];
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) {
+                const int row = rowmap<RUN>(tt / TPR, tt % TPR, mr);
+                f32x4 ay = {0.f, 0.f, 0.f, 0.f}, ao = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int rr = 0; rr < NRUN; ++rr) {
+                    const int kc = 4 * RUN * rr + RUN * jg;
+                    const frag_t fa = *reinterpret_cast<const frag_t *>(&sKU[row * L::LDK + kc]);
+                    const frag_t fq = *reinterpret_cast<const frag_t *>(&sQU[row * L::LDK + kc]);
+                    ay = mma_run<F32>(ay, fa, sf[rr]);
+                    ao = mma_run<F32>(ao, fq, sf[rr]);
+                }
+                Y[tt] = ay;
+                O[tt] = ao;
+            }
+            // X = V - Y
+            f32x4 X[4];
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int row = rowmap<RUN>(tt / TPR, tt % TPR, 4 * jg + i);
+                    float vv = 0.0f;
+                    if (row < clen)
+                        vv = load_elem(gv + ((size_t)(t0 + c0 + row) * H + head) * DV + cb + mr);
+                    X[tt][i] = vv - Y[tt][i];
+                }
+            }
+            // U = T' X  (T' lower triangular: run rr needed only for rr <= run of the tile)
+            constexpr int CRUN = CH / (4 * RUN);   // runs over the chunk dimension
+            frag_t xf[CRUN];
+#pragma unroll
+            for (int rr = 0; rr < CRUN; ++rr) xf[rr] = acc_frag<F32>(X, rr);
+            f32x4 U[4];
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) {
+                const int trun = tt / TPR;
+                const int row = rowmap<RUN>(trun, tt % TPR, mr);
+                f32x4 au = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int rr = 0; rr < CRUN; ++rr) {
+                    if (rr <= trun) {
+                        const frag_t fa = *reinterpret_cast<const frag_t *>(&sTp[row * L::LCH + 4 * RUN * rr + RUN * jg]);
+                        au = mma_run<F32>(au, fa, xf[rr]);
+                    }
+                }
+                U[tt] = au;
+            }
+            frag_t uf[CRUN];
+#pragma unroll
+            for (int rr = 0; rr < CRUN; ++rr) uf[rr] = acc_frag<F32>(U, rr);
+            // O = O1 + P U
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) {
+                const int trun = tt / TPR;
+                const int row = rowmap<RUN>(trun, tt % TPR, mr);
+#pragma unroll
+                for (int rr = 0; rr < CRUN; ++rr) {
+                    if (rr <= trun) {
+                        const frag_t fa = *reinterpret_cast<const frag_t *>(&sP[row * L::LCH + 4 * RUN * rr + RUN * jg]);
+                        O[tt] = mma_run<F32>(O[tt], fa, uf[rr]);
+                    }
+                }
+            }
+            // S = Diag(gamma) S + K_right^T U
+#pragma unroll
+            for (int tt = 0; tt < NKT; ++tt) {
+                const int rho = tt / TPR, h = tt % TPR;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int ch = rowmap<RUN>(rho, h, 4 * jg + i);
+                    S[s][tt][i] *= sFac[F_GAM * DK + ch];
+                }
+                const int chrow = rowmap<RUN>(rho, h, mr);
+#pragma unroll
+                for (int rr = 0; rr < CRUN; ++rr) {
+                    const frag_t fa = *reinterpret_cast<const frag_t *>(&sKRt[chrow * L::LCH + 4 * RUN * rr + RUN * jg]);
+                    S[s][tt] = mma_run<F32>(S[s][tt], fa, uf[rr]);
+                }
+            }
+            // store O
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int row = rowmap<RUN>(tt / TPR, tt % TPR, 4 * jg + i);
+                    if (row < clen)
+                        store_elem(go + ((size_t)(t0 + c0 + row) * H + head) * DV + cb + mr, O[tt][i]);
+                }
+            }
+        }
+        __syncthreads();
+    }
+
+    if (p.S_T) {
+#pragma unroll
+        for (int s = 0; s < NSTRIP; ++s) {
+            const int cb = col0 + 16 * (w + 4 * s);
+#pragma unroll
+            for (int tt = 0; tt < NKT; ++tt) {
+                const int rho = tt / TPR, h = tt % TPR;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int row = rowmap<RUN>(rho, h, 4 * jg + i);
+                    p.S_T[(((size_t)seq * H + head) * DK + row) * DV + cb + mr] = S[s][tt][i];
+                }
+            }
+        }
+    }
+}
+
+// Longest-first processing order of packed sequences: order[rank] = seq.
+// One thread per sequence counts the sequences that sort before it
+// (longer, or equally long with a smaller index).
+__global__ void varlen_order_kernel(const int32_t *__restrict__ cu, int n, int32_t *__restrict__ order)
+{
+    const int s = blockIdx.x * blockDim.x + threadIdx.x;
+    if (s >= n) return;
+    const int ls = cu[s + 1] - cu[s];
+    int rank = 0;
+    for (int o = 0; o < n; ++o) {
+        const int lo = cu[o + 1] - cu[o];
+        rank += (lo > ls) || (lo == ls && o < s);
+    }
+    order[rank] = s;
+}
+
+template <int DK, int NSTRIP, bool F32>
+static hipError_t launch_chunked(const ChunkParams &p, hipStream_t stream)
+{
+    const int groups = (p.units + 7) / 8;
+    const dim3 grid(groups * 8 * p.nslices);
+    hipLaunchKernelGGL((chunked_fwd_kernel<DK, NSTRIP, F32>), grid, dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
+
+int cu_count()
+{
+    static int cached = 0;
+    if (cached > 0) return cached;
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached = n;
+    return n;
+}
+
+// Choose the value-slice width: whole d_v per workgroup when there are
+// enough (sequence, head) units to fill the chip twice, else 64 columns.
+int chunked_slice_width(int units, int dv)
+{
+    if (dv == 64) return 64;
+    return (units >= 2 * cu_count()) ? 128 : 64;
+}
+
+hipError_t chunked_fwd_launch(const void *q, const void *k, const void *v, const void *g,
+                              const void *beta, const float *S0, float *S_T, void *o,
+                              const int32_t *cu_seqlens, int num_seqs, int B, int T, int H,
+                              int dk, int dv, bool bf16, void *workspace, hipStream_t stream)
+{
+    ChunkParams p;
+    p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta;
+    p.S0 = S0; p.S_T = S_T; p.o = o;
+    p.cu_seqlens = cu_seqlens;
+    p.order = nullptr;
+    p.T = T; p.H = H; p.DV = dv;
+    const int nseq = cu_seqlens ? num_seqs : B;
+    p.units = nseq * H;
+    if (p.units == 0) return hipSuccess;
+    if (cu_seqlens && nseq > 1 && workspace) {
+        int32_t *order = static_cast<int32_t *>(workspace);
+        hipLaunchKernelGGL(varlen_order_kernel, dim3((nseq + 255) / 256), dim3(256), 0, stream,
+                           cu_seqlens, nseq, order);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        p.order = order;
+    }
+    const int dvs = chunked_slice_width(p.units, dv);
+    p.nslices = dv / dvs;
+    const int nstrip = dvs / 64;
+    if (bf16) {
+        if (dk == 128) return nstrip == 2 ? launch_chunked<128, 2, false>(p, stream) : launch_chunked<128, 1, false>(p, stream);
+        return nstrip == 2 ? launch_chunked<64, 2, false>(p, stream) : launch_chunked<64, 1, false>(p, stream);
+    }
+    return nstrip == 2 ? launch_chunked<64, 2, true>(p, stream) : launch_chunked<64, 1, true>(p, stream);
+}
+
+}  // namespace kda

@@ -1,0 +1,138 @@
+"""C ABI checks that need no GPU: symbols, status strings, argument validation.
+
+Every call here returns before any HIP launch (invalid or empty arguments), so
+it runs on a host without a GPU.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(kda_[a-z_]+)\s*\(",
+                                 text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    from gated_delta_rule_81_amd import kda
+    return kda.lib()
+
+
+def test_header_declares_expected_entry_points():
+    assert declared_functions() == ["kda_decode_step", "kda_fwd_chunked",
+                                    "kda_fwd_workspace_bytes", "kda_status_string"]
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in declared_functions():
+        assert hasattr(L, name), name
+        assert ctypes.cast(getattr(L, name), ctypes.c_void_p).value
+
+
+def test_status_strings(L):
+    from gated_delta_rule_81_amd import kda
+    assert kda.status_string(0) == "KDA_OK"
+    assert kda.status_string(1) == "KDA_ERR_INVALID_ARG"
+    assert kda.status_string(2) == "KDA_ERR_UNSUPPORTED"
+    assert kda.status_string(3) == "KDA_ERR_HIP"
+    assert kda.status_string(99) == "KDA_ERR_UNKNOWN"
+
+
+def test_workspace_bytes(L):
+    from gated_delta_rule_81_amd import kda
+    assert kda.workspace_bytes(1, 100, 32, 128, 128, 1) == 0
+    assert kda.workspace_bytes(1, 100, 32, 128, 128, 64) >= 64 * 4
+    assert kda.workspace_bytes(1, 100, 32, 128, 128, 64) % 256 == 0
+
+
+FAKE = 1 << 20   # a 16-byte aligned non-NULL address; never dereferenced
+
+
+def fwd(L, q=FAKE, k=FAKE, v=FAKE, g=FAKE, b=FAKE, S0=None, cu=None, N=0, B=1, T=64, H=2,
+        dk=128, dv=128, dt=1, o=FAKE, S_T=None, ws=None, wsb=0):
+    return L.kda_fwd_chunked(q, k, v, g, b, S0, cu, N, B, T, H, dk, dv, dt, o, S_T, ws, wsb, None)
+
+
+def dec(L, q=FAKE, k=FAKE, v=FAKE, g=FAKE, b=FAKE, S=FAKE, N=4, H=2, dk=128, dv=128, dt=1, o=FAKE):
+    return L.kda_decode_step(q, k, v, g, b, S, N, H, dk, dv, dt, o, None)
+
+
+@pytest.mark.parametrize("dk,dv", [(32, 128), (128, 96), (256, 128), (128, 256)])
+def test_fwd_unsupported_sizes(L, dk, dv):
+    assert fwd(L, dk=dk, dv=dv) == 2
+
+
+def test_fwd_fp32_needs_dk64(L):
+    assert fwd(L, dk=128, dv=64, dt=0) == 2
+
+
+@pytest.mark.parametrize("kw", [dict(q=None), dict(k=None), dict(v=None), dict(g=None),
+                                dict(b=None), dict(o=None)])
+def test_fwd_null_pointers(L, kw):
+    assert fwd(L, **kw) == 1
+
+
+@pytest.mark.parametrize("kw", [dict(B=-1), dict(T=-1), dict(H=0), dict(dt=7)])
+def test_fwd_bad_sizes(L, kw):
+    assert fwd(L, **kw) == 1
+
+
+@pytest.mark.parametrize("kw", [dict(q=FAKE + 4), dict(o=FAKE + 2), dict(S0=FAKE + 8),
+                                dict(S_T=FAKE + 12)])
+def test_fwd_misaligned(L, kw):
+    assert fwd(L, **kw) == 1
+
+
+def test_fwd_varlen_rules(L):
+    # cu_seqlens needs B == 1
+    assert fwd(L, cu=FAKE, N=4, B=2) == 1
+    # negative number of sequences
+    assert fwd(L, cu=FAKE, N=-1) == 1
+    # more than one packed sequence needs a workspace of the reported size
+    assert fwd(L, cu=FAKE, N=8) == 1
+    assert fwd(L, cu=FAKE, N=8, ws=FAKE, wsb=16) == 1
+    # zero sequences: nothing to do
+    assert fwd(L, cu=FAKE, N=0, T=0) == 0
+
+
+def test_fwd_empty_batch_is_ok(L):
+    assert fwd(L, B=0, T=0) == 0
+    assert fwd(L, q=None, k=None, v=None, g=None, b=None, o=None, B=0, T=0) == 0
+
+
+@pytest.mark.parametrize("kw", [dict(q=None), dict(S=None), dict(o=None)])
+def test_decode_null_pointers(L, kw):
+    assert dec(L, **kw) == 1
+
+
+@pytest.mark.parametrize("kw", [dict(dk=96), dict(dv=32)])
+def test_decode_unsupported(L, kw):
+    assert dec(L, **kw) == 2
+
+
+@pytest.mark.parametrize("kw", [dict(N=-1), dict(H=0), dict(dt=5), dict(S=FAKE + 4)])
+def test_decode_invalid(L, kw):
+    assert dec(L, **kw) == 1
+
+
+def test_decode_empty_is_ok(L):
+    assert dec(L, N=0) == 0
+
+
+def test_binding_rejects_cpu_and_mismatched_tensors():
+    import torch
+    from gated_delta_rule_81_amd import kda
+    q = torch.zeros(1, 4, 2, 64)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        kda.fwd_chunked(q, q.clone(), q.clone(), q.clone(), torch.zeros(1, 4, 2), None)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        kda.decode_step(q[0], q[0].clone(), q[0].clone(), q[0].clone(), torch.zeros(4, 2),
+                        torch.zeros(4, 2, 64, 64))
