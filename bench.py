@@ -1,0 +1,304 @@
+#!/usr/bin/env python3
+"""Benchmark of the MI355X KDA operator (one GPU).
+
+A step is one chunked forward (kda_fwd_chunked: log-decay scan, intra-chunk
+WY blocks, inverse, state propagation and outputs, all in one kernel) over
+the B=4, H=32, T=8192, d_k=d_v=128 bf16 workload with fp32 state, inputs
+already resident in HBM.  Reported value: tokens/s (B*T per step time).
+
+Also reported on the same JSON line:
+  roofline      the chunked kernel's algorithmic HBM bytes per launch over its
+                average launch time (HIP events on the launch stream), against
+                8 TB/s; the useful-flop MFMA fraction against 2.5 PFLOP/s bf16;
+                traffic from the committed rocprofv3 counter summary when it was
+                taken on the current kernel source, else null
+  decode        kda_decode_step over N=512, H=32, d=128 (1 GiB fp32 cache),
+                1000 chained steps with fresh inputs pre-generated on the GPU
+  copy_ceiling  a plain device copy of 1 GiB (practical HBM ceiling)
+  cpu_baseline  the fp64 oracle on a bounded sample of the same workload,
+                timed on this host's cores
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "KDA fwd tokens/s @H=32,d=128,T=8K bf16 (MFMA %); decode HBM GB/s"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_DENSE_PEAK_TFLOPS = 2500.0
+CHUNK = 64
+PROFILES = os.path.join(ROOT, "profiles")
+_CSRC = os.path.join(ROOT, "gated_delta_rule_81_amd", "csrc")
+# sources each profiled kernel is built from (a counter summary is valid only
+# for the source it was taken on)
+KERNEL_SOURCES = {
+    "chunked_fwd_kernel": [os.path.join(_CSRC, f) for f in ("kda_chunked.hip", "kda_device.h")],
+    "decode_step_kernel": [os.path.join(_CSRC, f) for f in ("kda_decode.hip", "kda_device.h")],
+}
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def source_hash(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def fwd_algorithmic_bytes(B, T, H, dk, dv, N, elem=2):
+    """Bytes the chunked forward must move at least once: every input read
+    once, o written once, S0 read and S_T written once."""
+    tok = B * T * H
+    return (tok * (2 * dk + dv + dk + 1) * elem      # q, k, v, log_alpha, beta
+            + tok * dv * elem                       # o
+            + 2 * N * H * dk * dv * 4)              # S0 in, S_T out (fp32)
+
+
+def fwd_useful_flops(B, T, H, dk, dv, C=CHUNK):
+    """Useful flops per token-head of the chunked form: the three C x dk x dv
+    products (W S, Q S, K^T U), the triangular intra-chunk products counted
+    at half, and the C^3/3 inverse per chunk."""
+    per = 6 * dk * dv + C * (3 * dk + 2 * dv) + C * C / 3.0
+    return B * T * H * per
+
+
+def decode_algorithmic_bytes(N, H, dk, dv, elem=2):
+    units = N * H
+    return units * (2 * dk * dv * 4                  # state read + write
+                    + (2 * dk + dv + dk + 1) * elem  # q, k, v, log_alpha, beta
+                    + dv * elem)                     # o
+
+
+def kernel_sources_hash(kernel: str) -> str:
+    cur = "".join(source_hash(p) for p in KERNEL_SOURCES[kernel])
+    return hashlib.sha256(cur.encode()).hexdigest()[:16]
+
+
+def read_traffic(summary: str, kernel: str):
+    """HBM bytes per launch from a committed rocprofv3 counter summary.
+
+    The summary records the hash of the kernel source it was taken on; when
+    the kernel has changed since, the figure no longer applies (None)."""
+    path = os.path.join(PROFILES, summary)
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_hash = re.search(r"source_sha256_16:\s*([0-9a-f]+)", text)
+    m_bytes = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_hash or not m_bytes or m_hash.group(1) != kernel_sources_hash(kernel):
+        return None
+    return float(m_bytes.group(1))
+
+
+def time_loop(torch, fn, steps, warmup):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / 1000.0   # seconds
+
+
+def bench_forward(torch, kda, synth, steps, warmup):
+    w = synth.FWD_H32_T8K
+    log(f"[bench] generating {w.name} on the GPU")
+    x = synth.fwd_inputs(w, device="cuda")
+    B, T, H, dk, dv, N = x["B"], x["T"], x["H"], x["dk"], x["dv"], x["N"]
+    o = torch.empty((B, T, H, dv), dtype=w.dtype, device="cuda")
+    S_T = torch.empty((N, H, dk, dv), dtype=torch.float32, device="cuda")
+
+    def step():
+        kda.fwd_chunked(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["S0"], None,
+                        o=o, S_T=S_T)
+
+    log(f"[bench] chunked forward: {warmup} warmup + {steps} timed steps")
+    secs = time_loop(torch, step, steps, warmup)
+    t_step = secs / steps
+    nbytes = fwd_algorithmic_bytes(B, T, H, dk, dv, N)
+    flops = fwd_useful_flops(B, T, H, dk, dv)
+    return dict(w=w, x=x, t_step=t_step, bytes=nbytes, flops=flops,
+                tokens_per_s=B * T / t_step)
+
+
+def bench_decode(torch, kda, synth, steps=None):
+    w = synth.DECODE_512
+    n = w.steps if steps is None else steps
+    log(f"[bench] decode: pre-generating {n} steps of inputs for {w.name}")
+    S = synth.decode_state(w, device="cuda")
+    ins = [synth.decode_step_inputs(w, s, device="cuda") for s in range(n)]
+    o = torch.empty((w.N, w.H, w.dv), dtype=w.dtype, device="cuda")
+    # warm up on a copy so the timed chain starts from the seeded cache
+    S_warm = S.clone()
+    for s in range(3):
+        x = ins[s]
+        kda.decode_step(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], S_warm, o=o)
+    del S_warm
+    torch.cuda.synchronize()
+    it = iter(range(n))
+
+    def step():
+        x = ins[next(it)]
+        kda.decode_step(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], S, o=o)
+
+    log(f"[bench] decode: {n} chained steps")
+    secs = time_loop(torch, step, n, 0)
+    t_step = secs / n
+    nbytes = decode_algorithmic_bytes(w.N, w.H, w.dk, w.dv)
+    del ins
+    return dict(w=w, t_step=t_step, bytes=nbytes, steps=n)
+
+
+def bench_copy(torch, nbytes=1 << 30, reps=20):
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    secs = time_loop(torch, lambda: dst.copy_(src), reps, 3)
+    return 2 * nbytes / (secs / reps) / 1e9
+
+
+def cpu_baseline(torch, x, target_s=10.0, max_units=128):
+    """Time the fp64 oracle on (b, h) units of the same workload on this host."""
+    import numpy as np
+    import oracle
+    oracle.load()
+    threads = oracle.default_threads()
+    B, T, H = x["B"], x["T"], x["H"]
+    max_units = min(max_units, B * H)
+
+    def units_inputs(n):
+        idx = [(u // H, u % H) for u in range(n)]
+        pack = {}
+        for key in ("q", "k", "v", "log_alpha", "beta"):
+            parts = [x[key][b:b + 1, :, h:h + 1].to("cpu", torch.float32).numpy().astype(np.float64)
+                     for b, h in idx]
+            pack[key] = np.concatenate(parts, axis=1)
+        S0 = np.concatenate([x["S0"][b:b + 1, h:h + 1].cpu().numpy().astype(np.float64)
+                             for b, h in idx], axis=0)
+        cu = np.arange(n + 1, dtype=np.int64) * T
+        return pack, S0, cu
+
+    n = min(threads, max_units)
+    while True:
+        pack, S0, cu = units_inputs(n)
+        t0 = time.perf_counter()
+        oracle.fwd(pack["q"], pack["k"], pack["v"], pack["log_alpha"], pack["beta"], S0, cu,
+                   nthreads=threads)
+        el = time.perf_counter() - t0
+        if el >= target_s or n >= max_units:
+            break
+        n = min(max_units, max(n + 1, int(n * target_s / max(el, 1e-3) * 1.1)))
+    token_heads_per_s = n * T / el
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {
+        "value": token_heads_per_s / H,
+        "unit": "tokens/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"{n} of {B * H} (b,h) units x {T} tokens of the same workload "
+                   f"(fp64 token loop, OpenMP over units), {el:.1f} s wall; tokens/s = "
+                   f"token-heads/s / H; host CPU: {cpu_model}"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode leg")
+    ap.add_argument("--decode-steps", type=int, default=None)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (the operator is measured on one GPU's "
+              f"share); --gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU (HIP device) and the built libkda.so", file=sys.stderr)
+        sys.exit(2)
+    from gated_delta_rule_81_amd import kda, synth
+    kda.lib()   # fails loudly when the library is missing
+
+    fw = bench_forward(torch, kda, synth, args.steps, args.warmup)
+    achieved = fw["bytes"] / fw["t_step"] / 1e9
+    traffic = read_traffic("chunked_fwd_kernel_B4_H32_T8192_d128.pmc.md", "chunked_fwd_kernel")
+    roofline = {
+        "bound": "hbm",
+        "achieved": round(achieved, 1),
+        "peak": HBM_PEAK_GBS,
+        "unit": "GB/s",
+        "frac": round(achieved / HBM_PEAK_GBS, 4),
+        "traffic": traffic,
+        "kernel": "chunked_fwd_kernel",
+        "algorithmic_bytes_per_launch": fw["bytes"],
+        "avg_launch_us": round(fw["t_step"] * 1e6, 2),
+        "mfma_useful_tflops": round(fw["flops"] / fw["t_step"] / 1e12, 1),
+        "mfma_useful_frac": round(fw["flops"] / fw["t_step"] / 1e12 / BF16_DENSE_PEAK_TFLOPS, 4),
+        "source_sha256_16": kernel_sources_hash("chunked_fwd_kernel"),
+    }
+    out = {
+        "metric": METRIC,
+        "value": round(fw["tokens_per_s"], 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(fw["t_step"] * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; q,k L2-normalised, gates -softplus(N(-2,1)), S0 ~ N(0,0.02^2))",
+        "config": {"workload": fw["w"].name, "B": 4, "T": 8192, "H": 32, "dk": 128, "dv": 128,
+                   "chunk": CHUNK, "state": "fp32", "parallelism": "single GPU"},
+        "roofline": roofline,
+    }
+    if not args.no_decode:
+        dc = bench_decode(torch, kda, synth, args.decode_steps)
+        gbs = dc["bytes"] / dc["t_step"] / 1e9
+        out["decode"] = {
+            "workload": dc["w"].name,
+            "steps": dc["steps"],
+            "us_per_step": round(dc["t_step"] * 1e6, 2),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "traffic": read_traffic("decode_step_kernel_N512_H32_d128.pmc.md",
+                                                 "decode_step_kernel"),
+                         "algorithmic_bytes_per_launch": dc["bytes"],
+                         "source_sha256_16": kernel_sources_hash("decode_step_kernel")},
+        }
+    out["copy_ceiling_GBps"] = round(bench_copy(torch), 1)
+    if not args.no_cpu:
+        log("[bench] oracle CPU baseline")
+        out["cpu_baseline"] = cpu_baseline(torch, fw["x"])
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -146,13 +146,13 @@ __device__ __forceinline__ void store_run(typename Mode<F32>::op_t *dst, const f
     *reinterpret_cast<typename Mode<F32>::frag_t *>(dst) = to_frag<F32>(x);
 }
 
+// Convert 16 raw bytes of inputs (8 bf16 or 4 fp32) to fp32.
 template <bool F32>
-__device__ __forceinline__ void load_run_f32(const typename Mode<F32>::in_t *src, float *x) {
+__device__ __forceinline__ void raw_to_f32(const uint4 t, float *x) {
     if constexpr (F32) {
-        const float4 t = *reinterpret_cast<const float4 *>(src);
-        x[0] = t.x; x[1] = t.y; x[2] = t.z; x[3] = t.w;
+        x[0] = __uint_as_float(t.x); x[1] = __uint_as_float(t.y);
+        x[2] = __uint_as_float(t.z); x[3] = __uint_as_float(t.w);
     } else {
-        const uint4 t = *reinterpret_cast<const uint4 *>(src);
         const uint32_t w[4] = {t.x, t.y, t.z, t.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -192,8 +192,8 @@ struct Lds {
     static constexpr int TP = TF + CH * LF * 4;                          // T' op [64][LCH]
     static constexpr int PM = TP + CH * LCH * (int)sizeof(op_t);         // P op  [64][LCH]
     static constexpr int FAC = PM + CH * LCH * (int)sizeof(op_t);        // factors fp32 [20][DK]
-    static constexpr int TOT = FAC + 20 * DK * 4;                        // block sums [4][2][DK]
-    static constexpr int BETA = TOT + 8 * DK * 4;                        // beta [64]
+    static constexpr int TOT = FAC + 20 * DK * 4;                        // block sums [4][2][DK] + dummy
+    static constexpr int BETA = TOT + (8 * DK + 256 + DK) * 4;          // beta [64]
     static constexpr int BYTES = BETA + CH * 4;
     // slow path: Gamma fp32 [64][DK] over AM..TF (both fp32 [64][LF])
     static_assert(CH * DK * 4 <= 2 * CH * LF * 4 + CH * LDK * (int)sizeof(op_t), "slow-path Gamma fits");
@@ -278,61 +278,120 @@ __global__ __launch_bounds__(256, 1) void chunked_fwd_kernel(ChunkParams p)
         }
     }
 
+    const int R = w;                  // prep row block of this wave
+    const int rloc = 16 * R + mr;     // prep row (token within chunk) of this lane
+    const uint32_t tokstride_k = (uint32_t)H * DK;   // elements between tokens (q, k, g)
+    const uint32_t tokstride_v = (uint32_t)H * DV;   // elements between tokens (v, o)
+
+    // ---- prefetch registers: raw bits of one chunk's inputs -----------------
+    // g / k / q rows of this lane's prep row (RUN channels per run), beta of
+    // that row, and v at the rows / columns this lane's accumulator tiles hold.
+    // Rows past the chunk's end are read at the last valid row (always in
+    // bounds) and masked where they are used, so no load sits behind a branch.
+    uint4 rawg[NRUN], rawk[NRUN], rawq[NRUN];
+    uint32_t rawb;
+    uint32_t rawv[NSTRIP][16];
+
+    auto load_prep = [&](long cs, int cl) {
+        const uint32_t rr_ = (uint32_t)(rloc < cl ? rloc : cl - 1);
+        const size_t tb = ((size_t)(t0 + cs) * H + head);
+        const in_t *bg = gg + tb * DK, *bk = gk + tb * DK, *bq = gq + tb * DK;
+        const uint32_t ro = rr_ * tokstride_k + RUN * jg;
+#pragma unroll
+        for (int rr = 0; rr < NRUN; ++rr) {
+            rawg[rr] = *reinterpret_cast<const uint4 *>(bg + ro + 4 * RUN * rr);
+            rawk[rr] = *reinterpret_cast<const uint4 *>(bk + ro + 4 * RUN * rr);
+            rawq[rr] = *reinterpret_cast<const uint4 *>(bq + ro + 4 * RUN * rr);
+        }
+        // kept raw: converting here would make the wait counter (in order)
+        // drain every load issued before this one
+        if constexpr (F32)
+            rawb = __float_as_uint(gb[tb + (size_t)rr_ * H]);
+        else
+            rawb = (uint32_t)gb[tb + (size_t)rr_ * H].x;
+    };
+    auto load_v = [&](long cs, int cl) {
+        const in_t *bv = gv + ((size_t)(t0 + cs) * H + head) * DV + col0;
+#pragma unroll
+        for (int s = 0; s < NSTRIP; ++s) {
+            const uint32_t co = 16 * (w + 4 * s) + mr;
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int row = rowmap<RUN>(tt / TPR, tt % TPR, 4 * jg + i);
+                    const uint32_t crow = (uint32_t)(row < cl ? row : cl - 1);
+                    if constexpr (F32)
+                        rawv[s][4 * tt + i] = __float_as_uint(bv[crow * tokstride_v + co]);
+                    else
+                        rawv[s][4 * tt + i] = (uint32_t)bv[crow * tokstride_v + co].x;
+                }
+        }
+    };
+    if (len > 0) {
+        const int cl0 = (int)(len < CH ? len : CH);
+        load_prep(0, cl0);
+        load_v(0, cl0);
+    }
+
     // ---- state: NSTRIP strips x NKT tiles, rowmap rows, column = strip col + mr
     f32x4 S[NSTRIP][NKT];
+    {
 #pragma unroll
-    for (int s = 0; s < NSTRIP; ++s) {
-        const int cb = col0 + 16 * (w + 4 * s);
+        for (int s = 0; s < NSTRIP; ++s)
 #pragma unroll
-        for (int tt = 0; tt < NKT; ++tt) {
-            const int rho = tt / TPR, h = tt % TPR;
+            for (int tt = 0; tt < NKT; ++tt) S[s][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (p.S0) {
+            const float *s0 = p.S0 + ((size_t)seq * H + head) * DK * DV + col0;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = rowmap<RUN>(rho, h, 4 * jg + i);
-                S[s][tt][i] = p.S0 ? p.S0[(((size_t)seq * H + head) * DK + row) * DV + cb + mr] : 0.0f;
+            for (int s = 0; s < NSTRIP; ++s) {
+                const uint32_t co = 16 * (w + 4 * s) + mr;
+#pragma unroll
+                for (int tt = 0; tt < NKT; ++tt) {
+                    const int rho = tt / TPR, h = tt % TPR;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const uint32_t row = rowmap<RUN>(rho, h, 4 * jg + i);
+                        S[s][tt][i] = s0[row * DV + co];
+                    }
+                }
             }
         }
     }
 
-    const int R = w;                  // prep row block of this wave
-    const int rloc = 16 * R + mr;     // prep row (token within chunk) of this lane
-
     for (long c0 = 0; c0 < len; c0 += CH) {
         const int clen = (int)((len - c0) < CH ? (len - c0) : CH);
         const bool rvalid = rloc < clen;
-        const size_t th_row = ((size_t)(t0 + c0 + rloc)) * H + head;   // token-head of prep row
+        const bool has_next = c0 + CH < len;
+        const int clen_next = has_next ? (int)((len - c0 - CH) < CH ? (len - c0 - CH) : CH) : 0;
 
         // ================= A1: log-decay scan along rows =====================
-        float lam[NCH];      // Gamma_r - Gamma_mid(R)   (log2), later reused
-        float Lr[NCH];       // local inclusive sum within the 16-row block (log2)
+        float lam[NCH];      // Gamma_r - Gamma_mid(R)   (log2)
         bool fast_ok = true;
+        // rows 8 (block middle) and 15 (block end) publish their running sums;
+        // every other lane writes to its own dummy slot, so there is no branch
+        const int tot_base = (mr == 8) ? (2 * R + 0) * DK : (mr == 15) ? (2 * R + 1) * DK
+                                                                         : 8 * DK + 64 * w + lane - RUN * jg;
 #pragma unroll
         for (int rr = 0; rr < NRUN; ++rr) {
             const int cbase = 4 * RUN * rr + RUN * jg;
             float x[RUN];
-            if (rvalid) {
-                load_run_f32<F32>(gg + th_row * DK + cbase, x);
-            } else {
-#pragma unroll
-                for (int e = 0; e < RUN; ++e) x[e] = 0.0f;
-            }
+            raw_to_f32<F32>(rawg[rr], x);
 #pragma unroll
             for (int e = 0; e < RUN; ++e) {
-                float v = x[e] * kLog2e;
+                float v = rvalid ? x[e] * kLog2e : 0.0f;
                 v += dpp_row_shr(v, 1);
                 v += dpp_row_shr(v, 2);
                 v += dpp_row_shr(v, 4);
                 v += dpp_row_shr(v, 8);
-                Lr[rr * RUN + e] = v;
                 const float mid = dpp_row_share8(v);
                 const float lm = v - mid;
                 lam[rr * RUN + e] = lm;
                 fast_ok = fast_ok && (fabsf(lm) <= 96.0f);
-                if (mr == 8) sTot[(2 * R + 0) * DK + cbase + e] = v;
-                if (mr == 15) sTot[(2 * R + 1) * DK + cbase + e] = v;
+                sTot[tot_base + ((mr == 8 || mr == 15) ? cbase + e : RUN * jg)] = v;
             }
         }
-        if (jg == 0) sBeta[rloc] = rvalid ? load_elem(gb + th_row) : 0.0f;
+        if (jg == 0) sBeta[rloc] = rvalid ? __uint_as_float(F32 ? rawb : rawb << 16) : 0.0f;
         const bool slow = __syncthreads_or(!fast_ok);
 
         // ================= A2: per-channel chunk factors ======================
@@ -352,7 +411,8 @@ __global__ __launch_bounds__(256, 1) void chunked_fwd_kernel(ChunkParams p)
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
                 Gm[b] = Pb[b] + Lm[b];
-                sFac[(F_B + b) * DK + c] = __builtin_amdgcn_exp2f(Gm[b]);
+                // K_up is stored negated so that V + (-K_up) S accumulates directly
+                sFac[(F_B + b) * DK + c] = -__builtin_amdgcn_exp2f(Gm[b]);
                 sFac[(F_Z + b) * DK + c] = __builtin_amdgcn_exp2f(Glast - Gm[b]);
                 sFac[(F_P + b) * DK + c] = Pb[b];
             }
@@ -367,37 +427,28 @@ __global__ __launch_bounds__(256, 1) void chunked_fwd_kernel(ChunkParams p)
         __syncthreads();
 
         // ================= A3/A4: operands, A and P ==========================
-        frag_t fka[NRUN], fqa[NRUN], fkb[NRUN];
-        float kreg[NCH], qreg[NCH];
-#pragma unroll
-        for (int rr = 0; rr < NRUN; ++rr) {
-            const int cbase = 4 * RUN * rr + RUN * jg;
-            if (rvalid) {
-                load_run_f32<F32>(gk + th_row * DK + cbase, &kreg[rr * RUN]);
-                load_run_f32<F32>(gq + th_row * DK + cbase, &qreg[rr * RUN]);
-            } else {
-#pragma unroll
-                for (int e = 0; e < RUN; ++e) { kreg[rr * RUN + e] = 0.0f; qreg[rr * RUN + e] = 0.0f; }
-            }
-        }
-
         if (!slow) {
+            frag_t fka[NRUN], fqa[NRUN], fkb[NRUN];
 #pragma unroll
             for (int rr = 0; rr < NRUN; ++rr) {
                 const int cbase = 4 * RUN * rr + RUN * jg;
+                float kk[RUN], qq[RUN];
+                raw_to_f32<F32>(rawk[rr], kk);
+                raw_to_f32<F32>(rawq[rr], qq);
                 float ka[RUN], qa[RUN], kb[RUN], ku[RUN], qu[RUN], kr[RUN];
 #pragma unroll
                 for (int e = 0; e < RUN; ++e) {
                     const int c = cbase + e;
                     const float lm = lam[rr * RUN + e];
+                    const float kv = rvalid ? kk[e] : 0.0f, qv = rvalid ? qq[e] : 0.0f;
                     const float a = __builtin_amdgcn_exp2f(lm);
                     const float b = __builtin_amdgcn_exp2f(-lm);
-                    ka[e] = kreg[rr * RUN + e] * a;
-                    qa[e] = qreg[rr * RUN + e] * a;
-                    kb[e] = kreg[rr * RUN + e] * b;
+                    ka[e] = kv * a;
+                    qa[e] = qv * a;
+                    kb[e] = kv * b;
                     const float Bf = sFac[(F_B + R) * DK + c];
                     ku[e] = ka[e] * Bf;
-                    qu[e] = qa[e] * Bf;
+                    qu[e] = -qa[e] * Bf;
                     kr[e] = kb[e] * sFac[(F_Z + R) * DK + c];
                 }
                 fka[rr] = to_frag<F32>(ka);
@@ -409,6 +460,7 @@ __global__ __launch_bounds__(256, 1) void chunked_fwd_kernel(ChunkParams p)
 #pragma unroll
                 for (int e = 0; e < RUN; ++e) store_elem(&sKRt[(cbase + e) * L::LCH + rloc], kr[e]);
             }
+            if (has_next) load_prep(c0 + CH, clen_next);
             __syncthreads();
 
             // wave R: tiles (R, I), I = 0..R
@@ -456,13 +508,15 @@ __global__ __launch_bounds__(256, 1) void chunked_fwd_kernel(ChunkParams p)
             for (int rr = 0; rr < NRUN; ++rr) {
                 const int cbase = 4 * RUN * rr + RUN * jg;
                 float kk[RUN], qq[RUN];
+                raw_to_f32<F32>(rawk[rr], kk);
+                raw_to_f32<F32>(rawq[rr], qq);
 #pragma unroll
                 for (int e = 0; e < RUN; ++e) {
                     const int c = cbase + e;
-                    Gabs[rr * RUN + e] = sFac[(F_P + R) * DK + c] + Lr[rr * RUN + e];
+                    // absolute log2 decay: block prefix + (lambda + value at the block middle)
+                    Gabs[rr * RUN + e] = sFac[(F_P + R) * DK + c] + lam[rr * RUN + e] + sTot[(2 * R) * DK + c];
                     sGam[rloc * DK + c] = Gabs[rr * RUN + e];
-                    kk[e] = kreg[rr * RUN + e];
-                    qq[e] = qreg[rr * RUN + e];
+                    if (!rvalid) { kk[e] = 0.0f; qq[e] = 0.0f; }
                 }
                 store_run<F32>(&sKU[rloc * L::LDK + cbase], kk);
                 store_run<F32>(&sQU[rloc * L::LDK + cbase], qq);
@@ -513,21 +567,25 @@ __global__ __launch_bounds__(256, 1) void chunked_fwd_kernel(ChunkParams p)
 #pragma unroll
             for (int rr = 0; rr < NRUN; ++rr) {
                 const int cbase = 4 * RUN * rr + RUN * jg;
-                float ku[RUN], qu[RUN], kr[RUN];
+                float kk[RUN], qq[RUN], ku[RUN], qu[RUN], kr[RUN];
+                raw_to_f32<F32>(rawk[rr], kk);
+                raw_to_f32<F32>(rawq[rr], qq);
 #pragma unroll
                 for (int e = 0; e < RUN; ++e) {
                     const int c = cbase + e;
+                    const float kv = rvalid ? kk[e] : 0.0f, qv = rvalid ? qq[e] : 0.0f;
                     const float Ga = Gabs[rr * RUN + e];
                     const float up = __builtin_amdgcn_exp2f(Ga);
-                    ku[e] = kreg[rr * RUN + e] * up;
-                    qu[e] = qreg[rr * RUN + e] * up;
-                    kr[e] = kreg[rr * RUN + e] * __builtin_amdgcn_exp2f(sFac[(F_P + 4) * DK + c] - Ga);
+                    ku[e] = -kv * up;
+                    qu[e] = qv * up;
+                    kr[e] = kv * __builtin_amdgcn_exp2f(sFac[(F_P + 4) * DK + c] - Ga);
                 }
                 store_run<F32>(&sKU[rloc * L::LDK + cbase], ku);
                 store_run<F32>(&sQU[rloc * L::LDK + cbase], qu);
 #pragma unroll
                 for (int e = 0; e < RUN; ++e) store_elem(&sKRt[(cbase + e) * L::LCH + rloc], kr[e]);
             }
+            if (has_next) load_prep(c0 + CH, clen_next);
         }
         __syncthreads();
 
@@ -584,41 +642,37 @@ __global__ __launch_bounds__(256, 1) void chunked_fwd_kernel(ChunkParams p)
         __syncthreads();
 
         // ================= B: state strips ===================================
+        in_t *obase = go + ((size_t)(t0 + c0) * H + head) * DV + col0;
 #pragma unroll
         for (int s = 0; s < NSTRIP; ++s) {
-            const int cb = col0 + 16 * (w + 4 * s);
+            const uint32_t co = 16 * (w + 4 * s) + mr;
             frag_t sf[NRUN];
 #pragma unroll
             for (int rr = 0; rr < NRUN; ++rr) sf[rr] = acc_frag<F32>(S[s], rr);
 
-            // Y = K_up S, O1 = Q_up S over 64 chunk rows: 4 tiles in rowmap order
-            f32x4 Y[4], O[4];
-#pragma unroll
-            for (int tt = 0; tt < 4; ++tt) {
-                const int row = rowmap<RUN>(tt / TPR, tt % TPR, mr);
-                f32x4 ay = {0.f, 0.f, 0.f, 0.f}, ao = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int rr = 0; rr < NRUN; ++rr) {
-                    const int kc = 4 * RUN * rr + RUN * jg;
-                    const frag_t fa = *reinterpret_cast<const frag_t *>(&sKU[row * L::LDK + kc]);
-                    const frag_t fq = *reinterpret_cast<const frag_t *>(&sQU[row * L::LDK + kc]);
-                    ay = mma_run<F32>(ay, fa, sf[rr]);
-                    ao = mma_run<F32>(ao, fq, sf[rr]);
-                }
-                Y[tt] = ay;
-                O[tt] = ao;
-            }
-            // X = V - Y
-            f32x4 X[4];
+            // X = V - K_up S (sKU holds -K_up), O1 = Q_up S: 4 tiles in rowmap order
+            f32x4 X[4], O[4];
 #pragma unroll
             for (int tt = 0; tt < 4; ++tt) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int row = rowmap<RUN>(tt / TPR, tt % TPR, 4 * jg + i);
-                    float vv = 0.0f;
-                    if (row < clen)
-                        vv = load_elem(gv + ((size_t)(t0 + c0 + row) * H + head) * DV + cb + mr);
-                    X[tt][i] = vv - Y[tt][i];
+                    const float vv = F32 ? __uint_as_float(rawv[s][4 * tt + i])
+                                         : __uint_as_float(rawv[s][4 * tt + i] << 16);
+                    X[tt][i] = row < clen ? vv : 0.0f;
+                    O[tt][i] = 0.0f;
+                }
+            }
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) {
+                const int row = rowmap<RUN>(tt / TPR, tt % TPR, mr);
+#pragma unroll
+                for (int rr = 0; rr < NRUN; ++rr) {
+                    const int kc = 4 * RUN * rr + RUN * jg;
+                    const frag_t fa = *reinterpret_cast<const frag_t *>(&sKU[row * L::LDK + kc]);
+                    const frag_t fq = *reinterpret_cast<const frag_t *>(&sQU[row * L::LDK + kc]);
+                    X[tt] = mma_run<F32>(X[tt], fa, sf[rr]);
+                    O[tt] = mma_run<F32>(O[tt], fq, sf[rr]);
                 }
             }
             // U = T' X  (T' lower triangular: run rr needed only for rr <= run of the tile)
@@ -661,11 +715,11 @@ __global__ __launch_bounds__(256, 1) void chunked_fwd_kernel(ChunkParams p)
 #pragma unroll
             for (int tt = 0; tt < NKT; ++tt) {
                 const int rho = tt / TPR, h = tt % TPR;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int ch = rowmap<RUN>(rho, h, 4 * jg + i);
-                    S[s][tt][i] *= sFac[F_GAM * DK + ch];
-                }
+                const float4 gm = *reinterpret_cast<const float4 *>(&sFac[F_GAM * DK + rowmap<RUN>(rho, h, 4 * jg)]);
+                S[s][tt][0] *= gm.x;
+                S[s][tt][1] *= gm.y;
+                S[s][tt][2] *= gm.z;
+                S[s][tt][3] *= gm.w;
                 const int chrow = rowmap<RUN>(rho, h, mr);
 #pragma unroll
                 for (int rr = 0; rr < CRUN; ++rr) {
@@ -673,31 +727,41 @@ __global__ __launch_bounds__(256, 1) void chunked_fwd_kernel(ChunkParams p)
                     S[s][tt] = mma_run<F32>(S[s][tt], fa, uf[rr]);
                 }
             }
-            // store O
+            // store O (rows past the chunk end are not written)
+            if (clen == CH) {
 #pragma unroll
-            for (int tt = 0; tt < 4; ++tt) {
+                for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int row = rowmap<RUN>(tt / TPR, tt % TPR, 4 * jg + i);
-                    if (row < clen)
-                        store_elem(go + ((size_t)(t0 + c0 + row) * H + head) * DV + cb + mr, O[tt][i]);
-                }
+                    for (int i = 0; i < 4; ++i) {
+                        const uint32_t row = rowmap<RUN>(tt / TPR, tt % TPR, 4 * jg + i);
+                        store_elem(obase + row * tokstride_v + co, O[tt][i]);
+                    }
+            } else {
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const uint32_t row = rowmap<RUN>(tt / TPR, tt % TPR, 4 * jg + i);
+                        if ((int)row < clen) store_elem(obase + row * tokstride_v + co, O[tt][i]);
+                    }
             }
         }
+        if (has_next) load_v(c0 + CH, clen_next);
         __syncthreads();
     }
 
     if (p.S_T) {
+        float *st = p.S_T + ((size_t)seq * H + head) * DK * DV + col0;
 #pragma unroll
         for (int s = 0; s < NSTRIP; ++s) {
-            const int cb = col0 + 16 * (w + 4 * s);
+            const uint32_t co = 16 * (w + 4 * s) + mr;
 #pragma unroll
             for (int tt = 0; tt < NKT; ++tt) {
                 const int rho = tt / TPR, h = tt % TPR;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int row = rowmap<RUN>(rho, h, 4 * jg + i);
-                    p.S_T[(((size_t)seq * H + head) * DK + row) * DV + cb + mr] = S[s][tt][i];
+                    const uint32_t row = rowmap<RUN>(rho, h, 4 * jg + i);
+                    st[row * DV + co] = S[s][tt][i];
                 }
             }
         }

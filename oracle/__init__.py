@@ -11,4 +11,5 @@ from .oracle import (  # noqa: F401
     decode,
     brute_force,
     max_threads,
+    default_threads,
 )

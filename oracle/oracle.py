@@ -80,6 +80,14 @@ def max_threads() -> int:
     return int(load().kda_oracle_max_threads())
 
 
+def default_threads() -> int:
+    """OMP_NUM_THREADS when set (the host's CPU share), else the affinity mask size."""
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        return int(env)
+    return max(1, len(os.sched_getaffinity(0)))
+
+
 def _f64(x) -> np.ndarray:
     return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
 
@@ -116,7 +124,7 @@ def fwd(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None,
     o = np.zeros((B, T, H, dv), dtype=np.float64)
     S_T = np.zeros((N, H, dk, dv), dtype=np.float64)
     lib = lib if lib is not None else load()
-    nt = nthreads if nthreads else max(1, len(os.sched_getaffinity(0)))
+    nt = nthreads if nthreads else default_threads()
     rc = lib.kda_oracle_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
                             _ptr(S0), cu.ctypes.data_as(_i64p) if cu is not None
                             else ctypes.cast(None, _i64p), N, B, T, H, dk, dv,
@@ -138,7 +146,7 @@ def decode(q, k, v, log_alpha, beta, S, nthreads: Optional[int] = None, lib=None
     S_new = np.array(S, dtype=np.float64, copy=True, order="C")
     assert S_new.shape == (N, H, dk, dv)
     o = np.zeros((N, H, dv), dtype=np.float64)
-    nt = nthreads if nthreads else max(1, len(os.sched_getaffinity(0)))
+    nt = nthreads if nthreads else default_threads()
     lib = lib if lib is not None else load()
     rc = lib.kda_oracle_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
                                   _ptr(S_new), N, H, dk, dv, _ptr(o), nt)
