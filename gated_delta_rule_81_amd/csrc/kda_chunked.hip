@@ -260,7 +260,10 @@ __global__ __launch_bounds__(256, 1) void chunked_fwd_kernel(ChunkParams p)
     const int col0 = slice * DVS;
 
     const int tid = threadIdx.x;
-    const int w = tid >> 6, lane = tid & 63, jg = lane >> 4, mr = lane & 15;
+    // the wave index is uniform across a wave; say so, so that everything
+    // derived from it (chunk ids, row bounds) lives in scalar registers
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, jg = lane >> 4, mr = lane & 15;
 
     const in_t *gq = static_cast<const in_t *>(p.q);
     const in_t *gk = static_cast<const in_t *>(p.k);
@@ -812,6 +815,11 @@ int chunked_slice_width(int units, int dv)
     return (units >= 2 * cu_count()) ? 128 : 64;
 }
 
+hipError_t chunked_ws_launch(const void *q, const void *k, const void *v, const void *g,
+                             const void *beta, const float *S0, float *S_T, void *o,
+                             const int32_t *cu_seqlens, const int32_t *order, int nseq, int T,
+                             int H, int dk, int dv, int slice_width, hipStream_t stream);
+
 hipError_t chunked_fwd_launch(const void *q, const void *k, const void *v, const void *g,
                               const void *beta, const float *S0, float *S_T, void *o,
                               const int32_t *cu_seqlens, int num_seqs, int B, int T, int H,
@@ -835,12 +843,12 @@ hipError_t chunked_fwd_launch(const void *q, const void *k, const void *v, const
         p.order = order;
     }
     const int dvs = chunked_slice_width(p.units, dv);
+    if (bf16)   // producer / consumer kernel with 32-token chunks
+        return chunked_ws_launch(q, k, v, g, beta, S0, S_T, o, cu_seqlens, p.order, nseq, T, H,
+                                 dk, dv, dvs, stream);
     p.nslices = dv / dvs;
     const int nstrip = dvs / 64;
-    if (bf16) {
-        if (dk == 128) return nstrip == 2 ? launch_chunked<128, 2, false>(p, stream) : launch_chunked<128, 1, false>(p, stream);
-        return nstrip == 2 ? launch_chunked<64, 2, false>(p, stream) : launch_chunked<64, 1, false>(p, stream);
-    }
+    // fp32 inputs (d_k = 64): fp32 MFMA, 64-token chunks
     return nstrip == 2 ? launch_chunked<64, 2, true>(p, stream) : launch_chunked<64, 1, true>(p, stream);
 }
 

@@ -1,0 +1,745 @@
+// kda_chunked_ws.hip -- chunkwise KDA forward for bf16 inputs on gfx950,
+// producer / consumer waves.
+//
+// Same chunk algebra as the fp32 kernel (kda_chunked.hip), derived from the
+// recurrence S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T,
+// o_t = S_t^T q_t.  Here the chunk is C = 32 tokens and decay factors are
+// referenced to the chunk start: with E_r = e^{Gamma_r} (<= 1, Gamma the
+// inclusive cumulative log-decay per key channel) and R_r = e^{Gamma_last - Gamma_r}
+// (<= 1),
+//   K_up = K * E,  Q_up = Q * E,  K_right = K * R,  K_dn = K_right / gamma,
+//   A = strict_lower(Diag(beta) K_up K_dn^T),  P = tril_incl(Q_up K_dn^T),
+//   T' = (I + A)^{-1} Diag(beta),
+//   U = T' (V - K_up S),  O = Q_up S + P U,  S <- Diag(gamma) S + K_right^T U.
+// K_dn carries factors up to 1/gamma; a chunk whose decay on some channel
+// exceeds 2^100 (or whose keys exceed 2^16 in magnitude) forms A and P
+// entry by entry with e^{Gamma_r - Gamma_i} evaluated directly instead.
+//
+// Work split (one 512-thread workgroup per (sequence, head, value slice)):
+//   waves 0-3  consumers: each owns 16-column strips of the fp32 state, kept
+//              in MFMA accumulators for the whole sequence, and applies the
+//              chunk update from operands a producer left in LDS.
+//   waves 4-7  producers: wave p prepares chunks p, p+4, p+8, ... entirely by
+//              itself (lane = key channel(s), all 32 rows): cumulative decay
+//              products, scaled operands, A and P on MFMA, the 32x32 inverse.
+// Producer and consumer waves of a SIMD overlap: VALU-heavy preparation runs
+// while the MFMA-heavy state update of an earlier chunk runs.  Handoff is a
+// ring of 4 LDS slots, slot p belonging to producer p, with per-slot flags
+// (full: chunk id + 1 written by the producer; freed: consumer completions).
+// Every wait is bounded; a wait that runs out marks the workgroup dead and
+// all waves leave, so a protocol error gives wrong numbers, never a hang.
+//
+// LDS rows are made of 16-byte chunks stored at position chunk ^ key(row),
+// so that the 16 rows one fragment read touches fall in distinct banks
+// without row padding (padding would leave no room for four slots).
+#include "kda_device.h"
+
+namespace kda {
+
+struct WsParams {
+    const void *q, *k, *v, *g, *beta;
+    const float *S0;
+    float *S_T;
+    void *o;
+    const int32_t *cu_seqlens;
+    const int32_t *order;
+    int T, H, DV, units, nslices;
+};
+
+namespace ws {
+
+constexpr int C = 32;          // chunk length
+constexpr int NSLOT = 4;       // LDS ring depth (one slot per producer)
+constexpr int NPROD = 4;
+constexpr int SPIN_LIMIT = 1 << 20;
+constexpr int LA = 36;         // fp32 row stride of the private [32][32] matrices
+
+template <int DK>
+struct Lds {
+    // one ring slot
+    static constexpr int KU = 0;                          // -K_up     [32][DK] bf16
+    static constexpr int QU = KU + C * DK * 2;            // Q_up      [32][DK]
+    static constexpr int KRT = QU + C * DK * 2;           // K_right^T [DK][32]
+    static constexpr int TP = KRT + DK * C * 2;           // T'        [32][32]
+    static constexpr int PM = TP + C * C * 2;             // P         [32][32]
+    static constexpr int GM = PM + C * C * 2;             // gamma     [DK] fp32
+    static constexpr int SLOT = GM + DK * 4;
+    // producer-private region: K_dn [32][DK] bf16 while A and P are formed,
+    // then A^T and T fp32 [32][LA]; the exact path first uses it to stage
+    // 32 channels at a time (log2 Gamma fp32 [32][32], k and q bf16 [32][32])
+    static constexpr int P_KD = 0;
+    static constexpr int P_AT = 0;
+    static constexpr int P_T = C * LA * 4;
+    static constexpr int P_USED = (C * DK * 2 > 2 * C * LA * 4) ? C * DK * 2 : 2 * C * LA * 4;
+    static constexpr int P_BETA = P_USED > 8192 ? P_USED : 8192;
+    static constexpr int PRIV = P_BETA + C * 4;
+    static constexpr int PRIV_BASE = NSLOT * SLOT;
+    static constexpr int SYNC = PRIV_BASE + NPROD * PRIV;   // full[4], freed[4], dead
+    static constexpr int BYTES = SYNC + 64;
+    static_assert(SLOT % 16 == 0 && PRIV % 16 == 0, "alignment");
+    static_assert(BYTES <= 160 * 1024, "LDS budget");
+};
+
+// Swizzle key of row r of a [32][DK] array.  Consumer fragment reads touch
+// rows 8a + 4h + b (a, b = 0..3, h fixed), producer reads rows 16R + m
+// (m = 0..15, R fixed); for both sets the pair (bank half of the row for
+// d_k = 64, chunk ^ key) takes 16 distinct values.
+template <int DK>
+__device__ __forceinline__ int keyK(int r) {
+    if constexpr (DK == 128) return ((((r >> 3) & 3) << 2) | (r & 3)) ^ (((r >> 2) & 1) << 3);
+    else return ((((r >> 3) & 3) << 1) | ((r >> 1) & 1)) ^ (((r >> 2) & 1) << 2);
+}
+// [*][32] arrays: 4 rows share the 64 banks; rows 8a + 4h + b get distinct
+// (b, chunk ^ a) pairs
+__device__ __forceinline__ int key4(int r) { return (r >> 3) & 3; }
+
+// element index of (r, c) in a swizzled [32][DK] array
+template <int DK>
+__device__ __forceinline__ int idxK(int r, int c) {
+    return r * DK + (((c >> 3) ^ keyK<DK>(r)) << 3) + (c & 7);
+}
+// element index of (r, c) in a swizzled [*][32] array
+__device__ __forceinline__ int idx4(int r, int c) {
+    return r * C + (((c >> 3) ^ key4(r)) << 3) + (c & 7);
+}
+
+__device__ __forceinline__ int ld_acquire(const int *p) {
+    return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// Wait until *p >= target (or, with eq, *p == target).  Returns false when
+// the workgroup is dead or the wait ran out (which kills the workgroup).
+__device__ __forceinline__ bool wait_flag(const int *p, int target, bool eq, int *dead) {
+    for (int it = 0; it < SPIN_LIMIT; ++it) {
+        const int v = ld_acquire(p);
+        if (eq ? (v == target) : (v >= target)) return true;
+        if (__hip_atomic_load(dead, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) return false;
+        __builtin_amdgcn_s_sleep(1);
+    }
+    __hip_atomic_store(dead, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    return false;
+}
+
+__device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// Chunk row held by consumer accumulator tile h (0, 1) at tile row m: the
+// 4 registers of a lane of tiles 0 and 1 are then its B-operand k-slots
+// 8j..8j+7 of the next MFMA in natural order.
+__device__ __forceinline__ int crow(int h, int m) { return 8 * (m >> 2) + 4 * h + (m & 3); }
+// Key channel held by state tile (run rho, half h) at tile row m.
+__device__ __forceinline__ int srow(int rho, int h, int m) { return 32 * rho + 8 * (m >> 2) + 4 * h + (m & 3); }
+
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// fp32 -> bf16 (round to nearest even), two values per v_cvt_pk_bf16_f32
+__device__ __forceinline__ bf16x8 pack8(const f32x4 lo, const f32x4 hi) {
+    const f32x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_convertvector(v, bf16x8);
+}
+
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+    const f32x2 v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+__device__ __forceinline__ float bf_lo(uint32_t x) { return __uint_as_float(x << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
+
+// Row r and column i of pair number pidx of the lower triangle (i <= r),
+// pairs numbered row by row.
+__device__ __forceinline__ void tri_pair(int pidx, int &r, int &i) {
+    int rr = (int)((sqrtf(8.0f * pidx + 1.0f) - 1.0f) * 0.5f);
+    if ((rr + 1) * (rr + 2) / 2 <= pidx) ++rr;
+    if (rr * (rr + 1) / 2 > pidx) --rr;
+    r = rr;
+    i = pidx - rr * (rr + 1) / 2;
+}
+
+}  // namespace ws
+
+// Exact A and P for one 32-token chunk, entry by entry: A_ri = beta_r sum_c
+// k_rc k_ic 2^(G_rc - G_ic) (i < r), P_ri = sum_c q_rc k_ic 2^(G_rc - G_ic)
+// (i <= r), G the inclusive cumulative decay in log2 units.  Channels are
+// staged 32 at a time in the producer's private LDS region; lane l owns
+// pairs l, l+64, ... of the 528 lower pairs.  Writes A^T (fp32, private) and
+// P (bf16, slot).  Kept out of line: it runs only for chunks with extreme
+// decay, and its registers stay out of the hot path's budget.
+template <int DK>
+__device__ __attribute__((noinline)) void exact_ap(int lane, int cl, uint32_t tokk,
+                                                   const bf16_t *bg, const bf16_t *bk,
+                                                   const bf16_t *bq, unsigned char *priv,
+                                                   float *pAt, bf16_t *sP, const float *pBeta)
+{
+    using namespace ws;
+    constexpr int CPL = DK / 64;
+    constexpr int NPAIR = C * (C + 1) / 2;
+    constexpr int PPL = (NPAIR + 63) / 64;
+    constexpr int QCH = 32;                 // channels per stage
+    constexpr int LPQ = QCH / CPL;          // lanes staging one stage's channels
+    float resA[PPL], resP[PPL];
+#pragma unroll
+    for (int u = 0; u < PPL; ++u) { resA[u] = 0.0f; resP[u] = 0.0f; }
+    float *stG = reinterpret_cast<float *>(priv);                     // [32][32] fp32
+    bf16_t *stK = reinterpret_cast<bf16_t *>(priv + C * 32 * 4);       // [32][32]
+    bf16_t *stQ = reinterpret_cast<bf16_t *>(priv + C * 32 * 4 + C * 32 * 2);
+    for (int qd = 0; qd < DK / QCH; ++qd) {
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+        if (lane / LPQ == qd) {
+            float G[CPL];
+#pragma unroll
+            for (int e = 0; e < CPL; ++e) G[e] = 0.0f;
+            for (int r = 0; r < C; ++r) {
+                const uint32_t rr_ = (uint32_t)(r < cl ? r : cl - 1);
+                const uint16_t m16 = r < cl ? 0xffffu : 0u;
+#pragma unroll
+                for (int e = 0; e < CPL; ++e) {
+                    const int cq = CPL * (lane - qd * LPQ) + e;
+                    const int c = QCH * qd + cq;
+                    const uint32_t g1 = (uint32_t)(bg[rr_ * tokk + c].x & m16);
+                    bf16_t k1, q1;
+                    k1.x = bk[rr_ * tokk + c].x & m16;
+                    q1.x = bq[rr_ * tokk + c].x & m16;
+                    G[e] += bf_lo(g1) * kLog2e;
+                    stG[r * 32 + cq] = G[e];
+                    stK[r * 32 + cq] = k1;
+                    stQ[r * 32 + cq] = q1;
+                }
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+#pragma unroll
+        for (int u = 0; u < PPL; ++u) {
+            const int pidx = lane + 64 * u;
+            if (pidx < NPAIR) {
+                int r, i;
+                tri_pair(pidx, r, i);
+                float sa = resA[u], sp = resP[u];
+                for (int c = 0; c < 32; ++c) {
+                    const float f = __builtin_amdgcn_exp2f(stG[r * 32 + c] - stG[i * 32 + c]);
+                    const float kic = to_f32(stK[i * 32 + c]) * f;
+                    sa += to_f32(stK[r * 32 + c]) * kic;
+                    sp += to_f32(stQ[r * 32 + c]) * kic;
+                }
+                resA[u] = sa;
+                resP[u] = sp;
+            }
+        }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+#pragma unroll
+    for (int u = 0; u < PPL; ++u) {
+        const int pidx = lane + 64 * u;
+        if (pidx < NPAIR) {
+            int r, i;
+            tri_pair(pidx, r, i);
+            pAt[i * LA + r] = (i < r) ? resA[u] * pBeta[r] : 0.0f;
+            sP[idx4(r, i)] = to_bf16(resP[u]);
+        }
+    }
+    // strict upper part of P
+    for (int idx = lane; idx < C * C; idx += 64) {
+        const int r = idx / C, i = idx % C;
+        if (i > r) sP[idx4(r, i)] = to_bf16(0.0f);
+    }
+}
+
+template <int DK, int NSTRIP>
+__global__ __launch_bounds__(512, 1) void chunked_ws_kernel(WsParams p)
+{
+    using namespace ws;
+    using L = Lds<DK>;
+    constexpr int CPL = DK / 64;        // key channels per producer lane
+    constexpr int NRUN = DK / 32;       // 32-channel MFMA runs over d_k
+    constexpr int NKT = DK / 16;        // state tiles over d_k
+    constexpr int DVS = 64 * NSTRIP;
+
+    __shared__ __attribute__((aligned(16))) unsigned char smem[L::BYTES];
+    int *s_full = reinterpret_cast<int *>(smem + L::SYNC);
+    int *s_freed = s_full + NSLOT;
+    int *s_dead = s_full + 2 * NSLOT;
+
+    // ---- work unit: XCD-aware (sequence, head, slice) ------------------------
+    // Blocks b and b + 8 run on the same XCD (round-robin dispatch), so the
+    // slices of one (sequence, head) are given ids 8 apart and share that
+    // XCD's L2 for their common k / q / g reads.
+    const int NS = p.nslices;
+    const int bid = blockIdx.x;
+    const int grp = bid / (8 * NS);
+    const int xcd = bid & 7;
+    const int slice = (bid >> 3) % NS;
+    const int sh = grp * 8 + xcd;
+    if (sh >= p.units) return;
+    const int H = p.H, DV = p.DV;
+    const int seq_rank = sh / H, head = sh - (sh / H) * H;
+    const int seq = p.order ? p.order[seq_rank] : seq_rank;
+    long t0, len;
+    if (p.cu_seqlens) {
+        t0 = p.cu_seqlens[seq];
+        len = (long)p.cu_seqlens[seq + 1] - t0;
+    } else {
+        t0 = (long)seq * p.T;
+        len = p.T;
+    }
+    const int nchunks = (int)((len + C - 1) / C);
+    const int col0 = slice * DVS;
+
+    const int tid = threadIdx.x;
+    // the wave index is uniform across a wave; say so, so that everything
+    // derived from it (chunk ids, row bounds) lives in scalar registers
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, jg = lane >> 4, mr = lane & 15;
+
+    const bf16_t *gq = static_cast<const bf16_t *>(p.q);
+    const bf16_t *gk = static_cast<const bf16_t *>(p.k);
+    const bf16_t *gv = static_cast<const bf16_t *>(p.v);
+    const bf16_t *gg = static_cast<const bf16_t *>(p.g);
+    const bf16_t *gb = static_cast<const bf16_t *>(p.beta);
+    bf16_t *go = static_cast<bf16_t *>(p.o);
+
+    if (tid < 2 * NSLOT + 1) s_full[tid] = 0;
+    __syncthreads();
+
+    if (w < 4) {
+        // =========================== consumer ==================================
+        const uint32_t tokv = (uint32_t)H * DV;
+        f32x4 S[NSTRIP][NKT];
+#pragma unroll
+        for (int s = 0; s < NSTRIP; ++s)
+#pragma unroll
+            for (int tt = 0; tt < NKT; ++tt) S[s][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (p.S0) {
+            const float *s0 = p.S0 + ((size_t)seq * H + head) * DK * DV + col0;
+#pragma unroll
+            for (int s = 0; s < NSTRIP; ++s) {
+                const uint32_t co = 16 * (w + 4 * s) + mr;
+#pragma unroll
+                for (int tt = 0; tt < NKT; ++tt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        S[s][tt][i] = s0[(uint32_t)srow(tt >> 1, tt & 1, 4 * jg + i) * DV + co];
+            }
+        }
+        // v prefetch (raw bf16 bits) of the rows / columns this lane's tiles hold
+        uint32_t rawv[NSTRIP][8];
+        auto load_v = [&](int n) {
+            const long cs = (long)n * C;
+            const int cl = (int)((len - cs) < C ? (len - cs) : C);
+            const bf16_t *bv = gv + ((size_t)(t0 + cs) * H + head) * DV + col0;
+#pragma unroll
+            for (int s = 0; s < NSTRIP; ++s) {
+                const uint32_t co = 16 * (w + 4 * s) + mr;
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int row = crow(h, 4 * jg + i);
+                        const uint32_t r = (uint32_t)(row < cl ? row : cl - 1);
+                        rawv[s][4 * h + i] = (uint32_t)bv[r * tokv + co].x;
+                    }
+            }
+        };
+        if (nchunks > 0) load_v(0);
+
+        for (int n = 0; n < nchunks; ++n) {
+            const int slot = n % NSLOT;
+            const long cs = (long)n * C;
+            const int cl = (int)((len - cs) < C ? (len - cs) : C);
+            if (!wait_flag(&s_full[slot], n + 1, true, s_dead)) break;
+            const unsigned char *sb = smem + slot * L::SLOT;
+            const bf16_t *sKU = reinterpret_cast<const bf16_t *>(sb + L::KU);
+            const bf16_t *sQU = reinterpret_cast<const bf16_t *>(sb + L::QU);
+            const bf16_t *sKRt = reinterpret_cast<const bf16_t *>(sb + L::KRT);
+            const bf16_t *sTp = reinterpret_cast<const bf16_t *>(sb + L::TP);
+            const bf16_t *sP = reinterpret_cast<const bf16_t *>(sb + L::PM);
+            const float *sG = reinterpret_cast<const float *>(sb + L::GM);
+            bf16_t *obase = go + ((size_t)(t0 + cs) * H + head) * DV + col0;
+
+#pragma unroll
+            for (int s = 0; s < NSTRIP; ++s) {
+                const uint32_t co = 16 * (w + 4 * s) + mr;
+                bf16x8 sf[NRUN];
+#pragma unroll
+                for (int rr = 0; rr < NRUN; ++rr) sf[rr] = pack8(S[s][2 * rr], S[s][2 * rr + 1]);
+                // X = V - K_up S (the slot holds -K_up), O = Q_up S
+                f32x4 X[2], O[2];
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int row = crow(h, 4 * jg + i);
+                        X[h][i] = row < cl ? bf_lo(rawv[s][4 * h + i]) : 0.0f;
+                        O[h][i] = 0.0f;
+                    }
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int row = crow(h, mr);
+                    const int kr = keyK<DK>(row);
+#pragma unroll
+                    for (int rr = 0; rr < NRUN; ++rr) {
+                        const int off = row * DK + (((4 * rr + jg) ^ kr) << 3);
+                        const bf16x8 fa = *reinterpret_cast<const bf16x8 *>(&sKU[off]);
+                        const bf16x8 fq = *reinterpret_cast<const bf16x8 *>(&sQU[off]);
+                        X[h] = mfma_bf16(fa, sf[rr], X[h]);
+                        O[h] = mfma_bf16(fq, sf[rr], O[h]);
+                    }
+                }
+                // U = T' X
+                const bf16x8 xf = pack8(X[0], X[1]);
+                f32x4 U[2];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int row = crow(h, mr);
+                    const bf16x8 fa = *reinterpret_cast<const bf16x8 *>(&sTp[row * C + ((jg ^ key4(row)) << 3)]);
+                    U[h] = mfma_bf16(fa, xf, f32x4{0.f, 0.f, 0.f, 0.f});
+                }
+                const bf16x8 uf = pack8(U[0], U[1]);
+                // O += P U
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int row = crow(h, mr);
+                    const bf16x8 fa = *reinterpret_cast<const bf16x8 *>(&sP[row * C + ((jg ^ key4(row)) << 3)]);
+                    O[h] = mfma_bf16(fa, uf, O[h]);
+                }
+                // S = Diag(gamma) S + K_right^T U
+#pragma unroll
+                for (int tt = 0; tt < NKT; ++tt) {
+                    const int rho = tt >> 1, h = tt & 1;
+                    const float4 gm = *reinterpret_cast<const float4 *>(&sG[srow(rho, h, 4 * jg)]);
+                    S[s][tt][0] *= gm.x;
+                    S[s][tt][1] *= gm.y;
+                    S[s][tt][2] *= gm.z;
+                    S[s][tt][3] *= gm.w;
+                    const int ch = srow(rho, h, mr);
+                    const bf16x8 fa = *reinterpret_cast<const bf16x8 *>(&sKRt[ch * C + ((jg ^ key4(ch)) << 3)]);
+                    S[s][tt] = mfma_bf16(fa, uf, S[s][tt]);
+                }
+                // store O
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int row = crow(h, 4 * jg + i);
+                        if (row < cl) obase[(uint32_t)row * tokv + co] = to_bf16(O[h][i]);
+                    }
+            }
+            // all reads of the slot are done once their values were consumed
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+            if (lane == 0)
+                __hip_atomic_fetch_add(&s_freed[slot], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            if (n + 1 < nchunks) load_v(n + 1);
+        }
+
+        if (p.S_T) {
+            float *st = p.S_T + ((size_t)seq * H + head) * DK * DV + col0;
+#pragma unroll
+            for (int s = 0; s < NSTRIP; ++s) {
+                const uint32_t co = 16 * (w + 4 * s) + mr;
+#pragma unroll
+                for (int tt = 0; tt < NKT; ++tt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        st[(uint32_t)srow(tt >> 1, tt & 1, 4 * jg + i) * DV + co] = S[s][tt][i];
+            }
+        }
+        return;
+    }
+
+    // =============================== producer ==================================
+    const int pw = w - 4;
+    unsigned char *priv = smem + L::PRIV_BASE + pw * L::PRIV;
+    bf16_t *pKD = reinterpret_cast<bf16_t *>(priv + L::P_KD);
+    float *pAt = reinterpret_cast<float *>(priv + L::P_AT);
+    float *pT = reinterpret_cast<float *>(priv + L::P_T);
+    float *pBeta = reinterpret_cast<float *>(priv + L::P_BETA);
+    const uint32_t tokk = (uint32_t)H * DK;
+    // LDS element offset of this lane's channel(s) in row r of a [32][DK] array
+    auto kofs = [&](int r) { return idxK<DK>(r, CPL * lane); };
+
+    for (int n = pw; n < nchunks; n += NPROD) {
+        const int slot = pw;                   // n % NSLOT
+        const long cs = (long)n * C;
+        const int cl = (int)((len - cs) < C ? (len - cs) : C);
+        const size_t tb = (size_t)(t0 + cs) * H + head;
+        const bf16_t *bg = gg + tb * DK, *bk = gk + tb * DK, *bq = gq + tb * DK;
+
+        // ---- loads: all 32 rows of g, k, q for this lane's CPL channels and
+        // beta of row `lane`, in one batch.  Rows past the chunk end read the
+        // last valid row (always in bounds) and are masked where used.
+        uint32_t gx[C], kx[C], qx[C];
+#pragma unroll
+        for (int r = 0; r < C; ++r) {
+            const uint32_t rr_ = (uint32_t)(r < cl ? r : cl - 1);
+            if constexpr (CPL == 2) {
+                gx[r] = *reinterpret_cast<const uint32_t *>(bg + rr_ * tokk + 2 * lane);
+                kx[r] = *reinterpret_cast<const uint32_t *>(bk + rr_ * tokk + 2 * lane);
+                qx[r] = *reinterpret_cast<const uint32_t *>(bq + rr_ * tokk + 2 * lane);
+            } else {
+                gx[r] = (uint32_t)bg[rr_ * tokk + lane].x;
+                kx[r] = (uint32_t)bk[rr_ * tokk + lane].x;
+                qx[r] = (uint32_t)bq[rr_ * tokk + lane].x;
+            }
+        }
+        uint32_t bx;
+        {
+            const int rb = lane & (C - 1);
+            const uint32_t rr_ = (uint32_t)(rb < cl ? rb : cl - 1);
+            bx = (uint32_t)gb[tb + (size_t)rr_ * H].x;
+        }
+        // wait for the slot: the consumers are done with chunk n - NSLOT
+        if (n >= NSLOT) {
+            if (!wait_flag(&s_freed[slot], 4 * (n / NSLOT), false, s_dead)) break;
+        }
+        if (lane < C) pBeta[lane] = lane < cl ? __uint_as_float(bx << 16) : 0.0f;
+        unsigned char *sb = smem + slot * L::SLOT;
+        bf16_t *sKU = reinterpret_cast<bf16_t *>(sb + L::KU);
+        bf16_t *sQU = reinterpret_cast<bf16_t *>(sb + L::QU);
+        bf16_t *sKRt = reinterpret_cast<bf16_t *>(sb + L::KRT);
+        bf16_t *sTp = reinterpret_cast<bf16_t *>(sb + L::TP);
+        bf16_t *sP = reinterpret_cast<bf16_t *>(sb + L::PM);
+        float *sG = reinterpret_cast<float *>(sb + L::GM);
+
+        // ---- decay products per key channel ------------------------------------
+        // forward: E_r = prod_{j<=r} alpha_j -> -K_up, Q_up rows;
+        // reverse: R_r = prod_{j>r} alpha_j  -> K_right^T rows, K_dn rows.
+        if (cl < C) {
+            // partial last chunk: rows past the end get g = 0 (alpha = 1), k = q = 0
+#pragma unroll
+            for (int r = 0; r < C; ++r) {
+                const uint32_t m = r < cl ? 0xffffffffu : 0u;
+                gx[r] &= m;
+                kx[r] &= m;
+                qx[r] &= m;
+            }
+        }
+        float al[CPL][C];
+#pragma unroll
+        for (int r = 0; r < C; ++r) {
+            al[0][r] = __builtin_amdgcn_exp2f(bf_lo(gx[r]) * kLog2e);
+            if constexpr (CPL == 2) al[1][r] = __builtin_amdgcn_exp2f(bf_hi(gx[r]) * kLog2e);
+        }
+        float E[CPL], kmax = 0.0f;
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) E[e] = 1.0f;
+#pragma unroll
+        for (int r = 0; r < C; ++r) {
+            float kv[CPL], qv[CPL], ku[CPL], qu[CPL];
+            kv[0] = bf_lo(kx[r]); qv[0] = bf_lo(qx[r]);
+            if constexpr (CPL == 2) { kv[1] = bf_hi(kx[r]); qv[1] = bf_hi(qx[r]); }
+#pragma unroll
+            for (int e = 0; e < CPL; ++e) {
+                E[e] *= al[e][r];
+                ku[e] = -kv[e] * E[e];
+                qu[e] = qv[e] * E[e];
+                kmax = fmaxf(kmax, fabsf(kv[e]));
+            }
+            if constexpr (CPL == 2) {
+                *reinterpret_cast<uint32_t *>(&sKU[kofs(r)]) = pack2(ku[0], ku[1]);
+                *reinterpret_cast<uint32_t *>(&sQU[kofs(r)]) = pack2(qu[0], qu[1]);
+            } else {
+                sKU[kofs(r)] = to_bf16(ku[0]);
+                sQU[kofs(r)] = to_bf16(qu[0]);
+            }
+        }
+        // K_dn stays below 2^116 when gamma >= 2^-100 and |k| <= 2^16
+        bool ok = kmax <= 65536.0f;
+        float invg[CPL], run[CPL], krv[CPL][2];
+        uint32_t krp[CPL][C / 2];
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) {
+            sG[CPL * lane + e] = E[e];
+            ok = ok && (E[e] >= 7.888609052210118e-31f);
+            invg[e] = 1.0f / E[e];
+            run[e] = 1.0f;
+        }
+#pragma unroll
+        for (int r = C - 1; r >= 0; --r) {
+            float kv[CPL], kd[CPL];
+            kv[0] = bf_lo(kx[r]);
+            if constexpr (CPL == 2) kv[1] = bf_hi(kx[r]);
+#pragma unroll
+            for (int e = 0; e < CPL; ++e) {
+                const float kr = kv[e] * run[e];
+                run[e] *= al[e][r];
+                kd[e] = kr * invg[e];
+                krv[e][r & 1] = kr;
+            }
+            if ((r & 1) == 0) {
+#pragma unroll
+                for (int e = 0; e < CPL; ++e) krp[e][r >> 1] = pack2(krv[e][0], krv[e][1]);
+            }
+            if constexpr (CPL == 2)
+                *reinterpret_cast<uint32_t *>(&pKD[kofs(r)]) = pack2(kd[0], kd[1]);
+            else
+                pKD[kofs(r)] = to_bf16(kd[0]);
+        }
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) {
+            const int ch = CPL * lane + e;
+#pragma unroll
+            for (int v4 = 0; v4 < C / 8; ++v4)
+                *reinterpret_cast<uint4 *>(&sKRt[ch * C + ((v4 ^ key4(ch)) << 3)]) =
+                    make_uint4(krp[e][4 * v4], krp[e][4 * v4 + 1], krp[e][4 * v4 + 2], krp[e][4 * v4 + 3]);
+        }
+        const bool fast = __builtin_amdgcn_ballot_w64(!ok) == 0;
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+
+        // ---- A and P -----------------------------------------------------------
+        // A^T fp32 into the private region (over K_dn, once it has been read),
+        // P bf16 into the slot
+        if (fast) {
+            f32x4 accA[3], accP[3];
+            // tiles (R, I) = (0,0), (1,0), (1,1)
+#pragma unroll
+            for (int t = 0; t < 3; ++t) {
+                const int R = (t == 0) ? 0 : 1, I = (t == 2) ? 1 : 0;
+                const int ra = 16 * R + mr, rb = 16 * I + mr;
+                f32x4 a = {0.f, 0.f, 0.f, 0.f}, q = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int rr = 0; rr < NRUN; ++rr) {
+                    const int ka = ra * DK + (((4 * rr + jg) ^ keyK<DK>(ra)) << 3);
+                    const int kb = rb * DK + (((4 * rr + jg) ^ keyK<DK>(rb)) << 3);
+                    const bf16x8 fk = *reinterpret_cast<const bf16x8 *>(&sKU[ka]);
+                    const bf16x8 fq = *reinterpret_cast<const bf16x8 *>(&sQU[ka]);
+                    const bf16x8 fd = *reinterpret_cast<const bf16x8 *>(&pKD[kb]);
+                    a = mfma_bf16(fk, fd, a);
+                    q = mfma_bf16(fq, fd, q);
+                }
+                accA[t] = a;
+                accP[t] = q;
+            }
+            __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+            // accumulator layout: lane holds rows 16R + 4jg + i of column 16I + mr
+            const float4 b4_0 = *reinterpret_cast<const float4 *>(&pBeta[4 * jg]);
+            const float4 b4_1 = *reinterpret_cast<const float4 *>(&pBeta[16 + 4 * jg]);
+#pragma unroll
+            for (int t = 0; t < 3; ++t) {
+                const int R = (t == 0) ? 0 : 1, I = (t == 2) ? 1 : 0;
+                const float4 b4 = R ? b4_1 : b4_0;
+                const float bb[4] = {b4.x, b4.y, b4.z, b4.w};
+                float a4[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int row = 16 * R + 4 * jg + i, col = 16 * I + mr;
+                    // the slot's K_up is negated: A = -beta (K_up' K_dn^T)
+                    a4[i] = (col < row) ? -accA[t][i] * bb[i] : 0.0f;
+                    const float pv = (col <= row) ? accP[t][i] : 0.0f;
+                    sP[idx4(row, col)] = to_bf16(pv);
+                }
+                *reinterpret_cast<float4 *>(&pAt[(16 * I + mr) * LA + 16 * R + 4 * jg]) =
+                    make_float4(a4[0], a4[1], a4[2], a4[3]);
+            }
+            // upper block (0,1) of P is zero
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sP[idx4(4 * jg + i, 16 + mr)] = to_bf16(0.0f);
+        } else {
+            // exact path for chunks whose decay leaves the range of K_dn
+            exact_ap<DK>(lane, cl, tokk, bg, bk, bq, priv, pAt, sP, pBeta);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+
+        // ---- T = (I + A)^{-1}; T' = T Diag(beta) into the slot ----------------
+        {
+            // diagonal blocks: lanes with jg & 1 == b solve block b for column
+            // mr, right-looking: once t_i is final every later row subtracts
+            // A[r][i] t_i, column i of A being row i of A^T (one broadcast read)
+            const int blk = jg & 1;
+            // the identity column is rebuilt each chunk (16 selects) rather
+            // than kept live across the loop in 16 registers
+            int col = mr;
+            asm volatile("" : "+v"(col));
+            float acc[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[r] = (r == col) ? 1.0f : 0.0f;
+#pragma unroll
+            for (int i = 0; i < 15; ++i) {
+                const float *arow = &pAt[(16 * blk + i) * LA + 16 * blk];
+                const float4 a0 = *reinterpret_cast<const float4 *>(arow);
+                const float4 a1 = *reinterpret_cast<const float4 *>(arow + 4);
+                const float4 a2 = *reinterpret_cast<const float4 *>(arow + 8);
+                const float4 a3 = *reinterpret_cast<const float4 *>(arow + 12);
+                const float av[16] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w,
+                                      a2.x, a2.y, a2.z, a2.w, a3.x, a3.y, a3.z, a3.w};
+                const float ti = acc[i];
+#pragma unroll
+                for (int r = i + 1; r < 16; ++r) acc[r] -= av[r] * ti;
+            }
+            if (jg < 2) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) pT[(16 * blk + r) * LA + 16 * blk + mr] = acc[r];
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+        {
+            // T[1,0] = -T[1,1] (A[1,0] T[0,0]) on fp32 MFMA (k = 4 jg + s per step)
+            f32x4 Mx = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                Mx = mfma_f32(pAt[(4 * jg + s) * LA + 16 + mr], pT[(4 * jg + s) * LA + mr], Mx);
+            const float4 t11 = *reinterpret_cast<const float4 *>(&pT[(16 + mr) * LA + 16 + 4 * jg]);
+            f32x4 Tx = {0.f, 0.f, 0.f, 0.f};
+            Tx = mfma_f32(t11.x, Mx[0], Tx);
+            Tx = mfma_f32(t11.y, Mx[1], Tx);
+            Tx = mfma_f32(t11.z, Mx[2], Tx);
+            Tx = mfma_f32(t11.w, Mx[3], Tx);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) pT[(16 + 4 * jg + i) * LA + mr] = -Tx[i];
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+        {
+            // T' row r = lane / 2, columns 16 (lane & 1) .. +15
+            const int r = lane >> 1, cb = (lane & 1) * 16;
+            const bool lower = (cb >> 4) <= (r >> 4);
+            uint32_t pk[8];
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const float4 tv = *reinterpret_cast<const float4 *>(&pT[r * LA + cb + 4 * q4]);
+                const float4 bv = *reinterpret_cast<const float4 *>(&pBeta[cb + 4 * q4]);
+                pk[2 * q4] = pack2(lower ? tv.x * bv.x : 0.0f, lower ? tv.y * bv.y : 0.0f);
+                pk[2 * q4 + 1] = pack2(lower ? tv.z * bv.z : 0.0f, lower ? tv.w * bv.w : 0.0f);
+            }
+            *reinterpret_cast<uint4 *>(&sTp[r * C + (((cb >> 3) ^ key4(r)) << 3)]) =
+                make_uint4(pk[0], pk[1], pk[2], pk[3]);
+            *reinterpret_cast<uint4 *>(&sTp[r * C + ((((cb >> 3) + 1) ^ key4(r)) << 3)]) =
+                make_uint4(pk[4], pk[5], pk[6], pk[7]);
+        }
+
+        // ---- publish -------------------------------------------------------------
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        if (lane == 0) __hip_atomic_store(&s_full[slot], n + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+}
+
+template <int DK, int NSTRIP>
+static hipError_t launch_ws(const WsParams &p, hipStream_t stream)
+{
+    const int groups = (p.units + 7) / 8;
+    const dim3 grid(groups * 8 * p.nslices);
+    hipLaunchKernelGGL((chunked_ws_kernel<DK, NSTRIP>), grid, dim3(512), 0, stream, p);
+    return hipGetLastError();
+}
+
+hipError_t chunked_ws_launch(const void *q, const void *k, const void *v, const void *g,
+                             const void *beta, const float *S0, float *S_T, void *o,
+                             const int32_t *cu_seqlens, const int32_t *order, int nseq, int T,
+                             int H, int dk, int dv, int slice_width, hipStream_t stream)
+{
+    WsParams p;
+    p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta;
+    p.S0 = S0; p.S_T = S_T; p.o = o;
+    p.cu_seqlens = cu_seqlens;
+    p.order = order;
+    p.T = T; p.H = H; p.DV = dv;
+    p.units = nseq * H;
+    p.nslices = dv / slice_width;
+    const int nstrip = slice_width / 64;
+    if (dk == 128) return nstrip == 2 ? launch_ws<128, 2>(p, stream) : launch_ws<128, 1>(p, stream);
+    return nstrip == 2 ? launch_ws<64, 2>(p, stream) : launch_ws<64, 1>(p, stream);
+}
+
+}  // namespace kda
