@@ -32,6 +32,8 @@
 // LDS rows are made of 16-byte chunks stored at position chunk ^ key(row),
 // so that the 16 rows one fragment read touches fall in distinct banks
 // without row padding (padding would leave no room for four slots).
+#include <type_traits>
+
 #include "kda_device.h"
 
 namespace kda {
@@ -102,6 +104,15 @@ __device__ __forceinline__ int idxK(int r, int c) {
 __device__ __forceinline__ int idx4(int r, int c) {
     return r * C + (((c >> 3) ^ key4(r)) << 3) + (c & 7);
 }
+// K_right^T [DK][32]: groups of 4 rows (256 bytes, all banks) form one row
+// of 16 chunks, chunk (4 (ch & 3) + j) stored at position ^ keyT(ch).  The
+// producer writes chunk j = row group of channels 8g + e (fixed e) and the
+// consumer reads rows 32 rho + 8a + 4h + b; both sets of 16 lanes then hit
+// 16 distinct positions.
+__device__ __forceinline__ int keyT(int ch) { return ((ch >> 3) ^ (((ch >> 2) & 1) << 3)) & 15; }
+__device__ __forceinline__ int idxT(int ch, int j) {
+    return (ch >> 2) * (4 * C) + (((((ch & 3) << 2) | j) ^ keyT(ch)) << 3);
+}
 
 __device__ __forceinline__ int ld_acquire(const int *p) {
     return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -135,6 +146,7 @@ __device__ __forceinline__ int crow(int h, int m) { return 8 * (m >> 2) + 4 * h 
 __device__ __forceinline__ int srow(int rho, int h, int m) { return 32 * rho + 8 * (m >> 2) + 4 * h + (m & 3); }
 
 typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 // fp32 -> bf16 (round to nearest even), two values per v_cvt_pk_bf16_f32
@@ -254,7 +266,7 @@ __global__ __launch_bounds__(512, 1) void chunked_ws_kernel(WsParams p)
 {
     using namespace ws;
     using L = Lds<DK>;
-    constexpr int CPL = DK / 64;        // key channels per producer lane
+    constexpr int NCL = DK / 16;        // key channels per producer lane
     constexpr int NRUN = DK / 32;       // 32-channel MFMA runs over d_k
     constexpr int NKT = DK / 16;        // state tiles over d_k
     constexpr int DVS = 64 * NSTRIP;
@@ -325,6 +337,7 @@ __global__ __launch_bounds__(512, 1) void chunked_ws_kernel(WsParams p)
                         S[s][tt][i] = s0[(uint32_t)srow(tt >> 1, tt & 1, 4 * jg + i) * DV + co];
             }
         }
+        __builtin_amdgcn_s_waitcnt(0x0F70);
         // v prefetch (raw bf16 bits) of the rows / columns this lane's tiles hold
         uint32_t rawv[NSTRIP][8];
         auto load_v = [&](int n) {
@@ -350,7 +363,9 @@ __global__ __launch_bounds__(512, 1) void chunked_ws_kernel(WsParams p)
             const int slot = n % NSLOT;
             const long cs = (long)n * C;
             const int cl = (int)((len - cs) < C ? (len - cs) : C);
-            if (!wait_flag(&s_full[slot], n + 1, true, s_dead)) break;
+            // a dead workgroup (a bounded wait ran out) leaves at once; its
+            // outputs are not meaningful, and the state is not written back
+            if (!wait_flag(&s_full[slot], n + 1, true, s_dead)) return;
             const unsigned char *sb = smem + slot * L::SLOT;
             const bf16_t *sKU = reinterpret_cast<const bf16_t *>(sb + L::KU);
             const bf16_t *sQU = reinterpret_cast<const bf16_t *>(sb + L::QU);
@@ -359,6 +374,18 @@ __global__ __launch_bounds__(512, 1) void chunked_ws_kernel(WsParams p)
             const bf16_t *sP = reinterpret_cast<const bf16_t *>(sb + L::PM);
             const float *sG = reinterpret_cast<const float *>(sb + L::GM);
             bf16_t *obase = go + ((size_t)(t0 + cs) * H + head) * DV + col0;
+
+            // v of this chunk out of the prefetch registers, which then take
+            // the next chunk's loads at once (a whole chunk of latency slack)
+            float xv[NSTRIP][8];
+#pragma unroll
+            for (int s = 0; s < NSTRIP; ++s)
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        xv[s][4 * h + i] = crow(h, 4 * jg + i) < cl ? bf_lo(rawv[s][4 * h + i]) : 0.0f;
+            if (n + 1 < nchunks) load_v(n + 1);
 
 #pragma unroll
             for (int s = 0; s < NSTRIP; ++s) {
@@ -372,8 +399,7 @@ __global__ __launch_bounds__(512, 1) void chunked_ws_kernel(WsParams p)
                 for (int h = 0; h < 2; ++h)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const int row = crow(h, 4 * jg + i);
-                        X[h][i] = row < cl ? bf_lo(rawv[s][4 * h + i]) : 0.0f;
+                        X[h][i] = xv[s][4 * h + i];
                         O[h][i] = 0.0f;
                     }
 #pragma unroll
@@ -416,7 +442,7 @@ __global__ __launch_bounds__(512, 1) void chunked_ws_kernel(WsParams p)
                     S[s][tt][2] *= gm.z;
                     S[s][tt][3] *= gm.w;
                     const int ch = srow(rho, h, mr);
-                    const bf16x8 fa = *reinterpret_cast<const bf16x8 *>(&sKRt[ch * C + ((jg ^ key4(ch)) << 3)]);
+                    const bf16x8 fa = *reinterpret_cast<const bf16x8 *>(&sKRt[idxT(ch, jg)]);
                     S[s][tt] = mfma_bf16(fa, uf, S[s][tt]);
                 }
                 // store O
@@ -432,7 +458,6 @@ __global__ __launch_bounds__(512, 1) void chunked_ws_kernel(WsParams p)
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
             if (lane == 0)
                 __hip_atomic_fetch_add(&s_freed[slot], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-            if (n + 1 < nchunks) load_v(n + 1);
         }
 
         if (p.S_T) {
@@ -458,31 +483,51 @@ __global__ __launch_bounds__(512, 1) void chunked_ws_kernel(WsParams p)
     float *pT = reinterpret_cast<float *>(priv + L::P_T);
     float *pBeta = reinterpret_cast<float *>(priv + L::P_BETA);
     const uint32_t tokk = (uint32_t)H * DK;
-    // LDS element offset of this lane's channel(s) in row r of a [32][DK] array
-    auto kofs = [&](int r) { return idxK<DK>(r, CPL * lane); };
 
     for (int n = pw; n < nchunks; n += NPROD) {
+        // Lane-derived LDS offsets are recomputed per chunk (a few cheap ops)
+        // instead of being hoisted out of the loop and kept live, which would
+        // take registers the chunk's working set needs.
+        int lane_o = tid & 63;
+        asm volatile("" : "+v"(lane_o));
+        const int lane = lane_o, jg = lane_o >> 4, mr = lane_o & 15;
         const int slot = pw;                   // n % NSLOT
         const long cs = (long)n * C;
         const int cl = (int)((len - cs) < C ? (len - cs) : C);
         const size_t tb = (size_t)(t0 + cs) * H + head;
         const bf16_t *bg = gg + tb * DK, *bk = gk + tb * DK, *bq = gq + tb * DK;
 
-        // ---- loads: all 32 rows of g, k, q for this lane's CPL channels and
-        // beta of row `lane`, in one batch.  Rows past the chunk end read the
-        // last valid row (always in bounds) and are masked where used.
-        uint32_t gx[C], kx[C], qx[C];
+        // ---- loads ---------------------------------------------------------------
+        // Lane (cg, rg) = (lane & 15, lane >> 4) holds channels NCL*cg .. +NCL-1
+        // of rows 8*rg .. 8*rg+7: one 16-byte (d_k = 128) or 8-byte (d_k = 64)
+        // load per row and tensor.  Rows past the chunk end read the last
+        // valid row (always in bounds) and are masked below.
+        const int cg = lane & 15, rg = lane >> 4;
+        const int c0 = NCL * cg, r0 = 8 * rg;
+        uint32_t gx[8][NCL / 2], kx[8][NCL / 2], qx[8][NCL / 2];
+        // byte offsets from the chunk's first row (32-bit: a chunk spans
+        // 32 rows); rows past the end read row 0 instead
+        const uint32_t base_off = ((uint32_t)r0 * tokk + (uint32_t)c0) * 2u;
 #pragma unroll
-        for (int r = 0; r < C; ++r) {
-            const uint32_t rr_ = (uint32_t)(r < cl ? r : cl - 1);
-            if constexpr (CPL == 2) {
-                gx[r] = *reinterpret_cast<const uint32_t *>(bg + rr_ * tokk + 2 * lane);
-                kx[r] = *reinterpret_cast<const uint32_t *>(bk + rr_ * tokk + 2 * lane);
-                qx[r] = *reinterpret_cast<const uint32_t *>(bq + rr_ * tokk + 2 * lane);
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t off = (r0 + i < cl) ? base_off + (uint32_t)i * tokk * 2u : (uint32_t)c0 * 2u;
+            const char *pg = reinterpret_cast<const char *>(bg) + off;
+            const char *pk = reinterpret_cast<const char *>(bk) + off;
+            const char *pq = reinterpret_cast<const char *>(bq) + off;
+            if constexpr (NCL == 8) {
+                const uint4 g4 = *reinterpret_cast<const uint4 *>(pg);
+                const uint4 k4 = *reinterpret_cast<const uint4 *>(pk);
+                const uint4 q4 = *reinterpret_cast<const uint4 *>(pq);
+                gx[i][0] = g4.x; gx[i][1] = g4.y; gx[i][2] = g4.z; gx[i][3] = g4.w;
+                kx[i][0] = k4.x; kx[i][1] = k4.y; kx[i][2] = k4.z; kx[i][3] = k4.w;
+                qx[i][0] = q4.x; qx[i][1] = q4.y; qx[i][2] = q4.z; qx[i][3] = q4.w;
             } else {
-                gx[r] = (uint32_t)bg[rr_ * tokk + lane].x;
-                kx[r] = (uint32_t)bk[rr_ * tokk + lane].x;
-                qx[r] = (uint32_t)bq[rr_ * tokk + lane].x;
+                const uint2 g2 = *reinterpret_cast<const uint2 *>(pg);
+                const uint2 k2 = *reinterpret_cast<const uint2 *>(pk);
+                const uint2 q2 = *reinterpret_cast<const uint2 *>(pq);
+                gx[i][0] = g2.x; gx[i][1] = g2.y;
+                kx[i][0] = k2.x; kx[i][1] = k2.y;
+                qx[i][0] = q2.x; qx[i][1] = q2.y;
             }
         }
         uint32_t bx;
@@ -491,6 +536,77 @@ __global__ __launch_bounds__(512, 1) void chunked_ws_kernel(WsParams p)
             const uint32_t rr_ = (uint32_t)(rb < cl ? rb : cl - 1);
             bx = (uint32_t)gb[tb + (size_t)rr_ * H].x;
         }
+
+        // ---- decay per key channel ---------------------------------------------
+        // alpha, and the products of alpha over this lane's 8 rows (tot);
+        // then, across the four row groups, the products over the groups
+        // before (pre) and after (post) this one, so that
+        //   E_r = pre * prod_{j <= r, j in group} alpha_j,
+        //   R_r = post * prod_{j > r, j in group} alpha_j,
+        //   gamma = pre * tot * post.
+        if (r0 + 8 > cl) {
+            // rows past the chunk end: g = 0 (alpha = 1), k = q = 0
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const uint32_t m = (r0 + i) < cl ? 0xffffffffu : 0u;
+#pragma unroll
+                for (int d = 0; d < NCL / 2; ++d) {
+                    gx[i][d] &= m;
+                    kx[i][d] &= m;
+                    qx[i][d] &= m;
+                }
+            }
+        }
+        float al[8][NCL], tot[NCL];
+        // largest |k| bit pattern per bf16 half (monotonic in |k|)
+        uint32_t kbits = 0;
+#pragma unroll
+        for (int e = 0; e < NCL; ++e) tot[e] = 1.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int d = 0; d < NCL / 2; ++d) {
+                al[i][2 * d] = __builtin_amdgcn_exp2f(bf_lo(gx[i][d]) * kLog2e);
+                al[i][2 * d + 1] = __builtin_amdgcn_exp2f(bf_hi(gx[i][d]) * kLog2e);
+                tot[2 * d] *= al[i][2 * d];
+                tot[2 * d + 1] *= al[i][2 * d + 1];
+                kbits = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(
+                    __builtin_bit_cast(u16x2, kbits), __builtin_bit_cast(u16x2, kx[i][d] & 0x7fff7fffu)));
+            }
+        // exclusive prefix / suffix products over the row groups (lanes 16
+        // apart), by three lane shifts each
+        float pre[NCL], post[NCL], gam[NCL];
+        {
+            const int up16 = (lane - 16) << 2, up32 = (lane - 32) << 2;
+            const int dn16 = (lane + 16) << 2, dn32 = (lane + 32) << 2;
+            auto shf = [](float x, int addr) {
+                return __int_as_float(__builtin_amdgcn_ds_bpermute(addr, __float_as_int(x)));
+            };
+#pragma unroll
+            for (int e = 0; e < NCL; ++e) {
+                // every lane takes part in each shift (all lanes active), and
+                // lanes without a group on that side select 1 afterwards
+                float t;
+                t = shf(tot[e], up16);
+                const float a = rg >= 1 ? t : 1.0f;
+                t = shf(a, up16);
+                const float b = a * (rg >= 1 ? t : 1.0f);
+                t = shf(b, up32);
+                pre[e] = b * (rg >= 2 ? t : 1.0f);
+                t = shf(tot[e], dn16);
+                const float a2 = rg <= 2 ? t : 1.0f;
+                t = shf(a2, dn16);
+                const float b2 = a2 * (rg <= 2 ? t : 1.0f);
+                t = shf(b2, dn32);
+                post[e] = b2 * (rg <= 1 ? t : 1.0f);
+                gam[e] = pre[e] * tot[e] * post[e];
+            }
+        }
+        // K_dn stays below 2^116 when gamma >= 2^-100 and |k| <= 2^16
+        bool ok = (kbits & 0xffffu) <= 0x4780u && (kbits >> 16) <= 0x4780u;   // 0x4780: 2^16
+#pragma unroll
+        for (int e = 0; e < NCL; ++e) ok = ok && (gam[e] >= 7.888609052210118e-31f);
+
         // wait for the slot: the consumers are done with chunk n - NSLOT
         if (n >= NSLOT) {
             if (!wait_flag(&s_freed[slot], 4 * (n / NSLOT), false, s_dead)) break;
@@ -503,88 +619,69 @@ __global__ __launch_bounds__(512, 1) void chunked_ws_kernel(WsParams p)
         bf16_t *sTp = reinterpret_cast<bf16_t *>(sb + L::TP);
         bf16_t *sP = reinterpret_cast<bf16_t *>(sb + L::PM);
         float *sG = reinterpret_cast<float *>(sb + L::GM);
+        if (rg == 0) {
+#pragma unroll
+            for (int e = 0; e < NCL; e += 4)
+                *reinterpret_cast<float4 *>(&sG[c0 + e]) = make_float4(gam[e], gam[e + 1], gam[e + 2], gam[e + 3]);
+        }
 
-        // ---- decay products per key channel ------------------------------------
-        // forward: E_r = prod_{j<=r} alpha_j -> -K_up, Q_up rows;
-        // reverse: R_r = prod_{j>r} alpha_j  -> K_right^T rows, K_dn rows.
-        if (cl < C) {
-            // partial last chunk: rows past the end get g = 0 (alpha = 1), k = q = 0
+        // forward: -K_up, Q_up rows
+        {
+            float E[NCL];
 #pragma unroll
-            for (int r = 0; r < C; ++r) {
-                const uint32_t m = r < cl ? 0xffffffffu : 0u;
-                gx[r] &= m;
-                kx[r] &= m;
-                qx[r] &= m;
+            for (int e = 0; e < NCL; ++e) E[e] = pre[e];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                uint32_t ku[NCL / 2], qu[NCL / 2];
+#pragma unroll
+                for (int d = 0; d < NCL / 2; ++d) {
+                    E[2 * d] *= al[i][2 * d];
+                    E[2 * d + 1] *= al[i][2 * d + 1];
+                    ku[d] = pack2(-bf_lo(kx[i][d]) * E[2 * d], -bf_hi(kx[i][d]) * E[2 * d + 1]);
+                    qu[d] = pack2(bf_lo(qx[i][d]) * E[2 * d], bf_hi(qx[i][d]) * E[2 * d + 1]);
+                }
+                const int o = idxK<DK>(r0 + i, c0);
+                if constexpr (NCL == 8) {
+                    *reinterpret_cast<uint4 *>(&sKU[o]) = make_uint4(ku[0], ku[1], ku[2], ku[3]);
+                    *reinterpret_cast<uint4 *>(&sQU[o]) = make_uint4(qu[0], qu[1], qu[2], qu[3]);
+                } else {
+                    *reinterpret_cast<uint2 *>(&sKU[o]) = make_uint2(ku[0], ku[1]);
+                    *reinterpret_cast<uint2 *>(&sQU[o]) = make_uint2(qu[0], qu[1]);
+                }
             }
         }
-        float al[CPL][C];
+        // reverse: K_right (rows of K_right^T, 8 tokens per channel) and K_dn rows
+        {
+            float R[NCL], invg[NCL], kr[8][NCL];
 #pragma unroll
-        for (int r = 0; r < C; ++r) {
-            al[0][r] = __builtin_amdgcn_exp2f(bf_lo(gx[r]) * kLog2e);
-            if constexpr (CPL == 2) al[1][r] = __builtin_amdgcn_exp2f(bf_hi(gx[r]) * kLog2e);
-        }
-        float E[CPL], kmax = 0.0f;
-#pragma unroll
-        for (int e = 0; e < CPL; ++e) E[e] = 1.0f;
-#pragma unroll
-        for (int r = 0; r < C; ++r) {
-            float kv[CPL], qv[CPL], ku[CPL], qu[CPL];
-            kv[0] = bf_lo(kx[r]); qv[0] = bf_lo(qx[r]);
-            if constexpr (CPL == 2) { kv[1] = bf_hi(kx[r]); qv[1] = bf_hi(qx[r]); }
-#pragma unroll
-            for (int e = 0; e < CPL; ++e) {
-                E[e] *= al[e][r];
-                ku[e] = -kv[e] * E[e];
-                qu[e] = qv[e] * E[e];
-                kmax = fmaxf(kmax, fabsf(kv[e]));
+            for (int e = 0; e < NCL; ++e) {
+                R[e] = post[e];
+                invg[e] = __builtin_amdgcn_rcpf(gam[e]);
             }
-            if constexpr (CPL == 2) {
-                *reinterpret_cast<uint32_t *>(&sKU[kofs(r)]) = pack2(ku[0], ku[1]);
-                *reinterpret_cast<uint32_t *>(&sQU[kofs(r)]) = pack2(qu[0], qu[1]);
-            } else {
-                sKU[kofs(r)] = to_bf16(ku[0]);
-                sQU[kofs(r)] = to_bf16(qu[0]);
+#pragma unroll
+            for (int i = 7; i >= 0; --i) {
+                uint32_t kd[NCL / 2];
+#pragma unroll
+                for (int d = 0; d < NCL / 2; ++d) {
+                    kr[i][2 * d] = bf_lo(kx[i][d]) * R[2 * d];
+                    kr[i][2 * d + 1] = bf_hi(kx[i][d]) * R[2 * d + 1];
+                    R[2 * d] *= al[i][2 * d];
+                    R[2 * d + 1] *= al[i][2 * d + 1];
+                    kd[d] = pack2(kr[i][2 * d] * invg[2 * d], kr[i][2 * d + 1] * invg[2 * d + 1]);
+                }
+                const int o = idxK<DK>(r0 + i, c0);
+                if constexpr (NCL == 8)
+                    *reinterpret_cast<uint4 *>(&pKD[o]) = make_uint4(kd[0], kd[1], kd[2], kd[3]);
+                else
+                    *reinterpret_cast<uint2 *>(&pKD[o]) = make_uint2(kd[0], kd[1]);
             }
-        }
-        // K_dn stays below 2^116 when gamma >= 2^-100 and |k| <= 2^16
-        bool ok = kmax <= 65536.0f;
-        float invg[CPL], run[CPL], krv[CPL][2];
-        uint32_t krp[CPL][C / 2];
 #pragma unroll
-        for (int e = 0; e < CPL; ++e) {
-            sG[CPL * lane + e] = E[e];
-            ok = ok && (E[e] >= 7.888609052210118e-31f);
-            invg[e] = 1.0f / E[e];
-            run[e] = 1.0f;
-        }
-#pragma unroll
-        for (int r = C - 1; r >= 0; --r) {
-            float kv[CPL], kd[CPL];
-            kv[0] = bf_lo(kx[r]);
-            if constexpr (CPL == 2) kv[1] = bf_hi(kx[r]);
-#pragma unroll
-            for (int e = 0; e < CPL; ++e) {
-                const float kr = kv[e] * run[e];
-                run[e] *= al[e][r];
-                kd[e] = kr * invg[e];
-                krv[e][r & 1] = kr;
+            for (int e = 0; e < NCL; ++e) {
+                const int ch = c0 + e;
+                *reinterpret_cast<uint4 *>(&sKRt[idxT(ch, rg)]) =
+                    make_uint4(pack2(kr[0][e], kr[1][e]), pack2(kr[2][e], kr[3][e]),
+                               pack2(kr[4][e], kr[5][e]), pack2(kr[6][e], kr[7][e]));
             }
-            if ((r & 1) == 0) {
-#pragma unroll
-                for (int e = 0; e < CPL; ++e) krp[e][r >> 1] = pack2(krv[e][0], krv[e][1]);
-            }
-            if constexpr (CPL == 2)
-                *reinterpret_cast<uint32_t *>(&pKD[kofs(r)]) = pack2(kd[0], kd[1]);
-            else
-                pKD[kofs(r)] = to_bf16(kd[0]);
-        }
-#pragma unroll
-        for (int e = 0; e < CPL; ++e) {
-            const int ch = CPL * lane + e;
-#pragma unroll
-            for (int v4 = 0; v4 < C / 8; ++v4)
-                *reinterpret_cast<uint4 *>(&sKRt[ch * C + ((v4 ^ key4(ch)) << 3)]) =
-                    make_uint4(krp[e][4 * v4], krp[e][4 * v4 + 1], krp[e][4 * v4 + 2], krp[e][4 * v4 + 3]);
         }
         const bool fast = __builtin_amdgcn_ballot_w64(!ok) == 0;
         __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
@@ -608,13 +705,15 @@ __global__ __launch_bounds__(512, 1) void chunked_ws_kernel(WsParams p)
                     const bf16x8 fq = *reinterpret_cast<const bf16x8 *>(&sQU[ka]);
                     const bf16x8 fd = *reinterpret_cast<const bf16x8 *>(&pKD[kb]);
                     a = mfma_bf16(fk, fd, a);
-                    q = mfma_bf16(fq, fd, q);
+                    // P^T tile: lane ends up with P[16R + mr][16I + 4jg + i]
+                    q = mfma_bf16(fd, fq, q);
                 }
                 accA[t] = a;
                 accP[t] = q;
             }
             __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-            // accumulator layout: lane holds rows 16R + 4jg + i of column 16I + mr
+            // accA: lane holds A' rows 16R + 4jg + i of column 16I + mr;
+            // accP: P row 16R + mr, columns 16I + 4jg + i
             const float4 b4_0 = *reinterpret_cast<const float4 *>(&pBeta[4 * jg]);
             const float4 b4_1 = *reinterpret_cast<const float4 *>(&pBeta[16 + 4 * jg]);
 #pragma unroll
@@ -622,21 +721,20 @@ __global__ __launch_bounds__(512, 1) void chunked_ws_kernel(WsParams p)
                 const int R = (t == 0) ? 0 : 1, I = (t == 2) ? 1 : 0;
                 const float4 b4 = R ? b4_1 : b4_0;
                 const float bb[4] = {b4.x, b4.y, b4.z, b4.w};
-                float a4[4];
+                float a4[4], p4[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int row = 16 * R + 4 * jg + i, col = 16 * I + mr;
                     // the slot's K_up is negated: A = -beta (K_up' K_dn^T)
-                    a4[i] = (col < row) ? -accA[t][i] * bb[i] : 0.0f;
-                    const float pv = (col <= row) ? accP[t][i] : 0.0f;
-                    sP[idx4(row, col)] = to_bf16(pv);
+                    a4[i] = (16 * I + mr < 16 * R + 4 * jg + i) ? -accA[t][i] * bb[i] : 0.0f;
+                    p4[i] = (16 * I + 4 * jg + i <= 16 * R + mr) ? accP[t][i] : 0.0f;
                 }
                 *reinterpret_cast<float4 *>(&pAt[(16 * I + mr) * LA + 16 * R + 4 * jg]) =
                     make_float4(a4[0], a4[1], a4[2], a4[3]);
+                *reinterpret_cast<uint2 *>(&sP[idx4(16 * R + mr, 16 * I + 4 * jg)]) =
+                    make_uint2(pack2(p4[0], p4[1]), pack2(p4[2], p4[3]));
             }
             // upper block (0,1) of P is zero
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sP[idx4(4 * jg + i, 16 + mr)] = to_bf16(0.0f);
+            *reinterpret_cast<uint2 *>(&sP[idx4(mr, 16 + 4 * jg)]) = make_uint2(0u, 0u);
         } else {
             // exact path for chunks whose decay leaves the range of K_dn
             exact_ap<DK>(lane, cl, tokk, bg, bk, bq, priv, pAt, sP, pBeta);
@@ -649,6 +747,7 @@ __global__ __launch_bounds__(512, 1) void chunked_ws_kernel(WsParams p)
             // mr, right-looking: once t_i is final every later row subtracts
             // A[r][i] t_i, column i of A being row i of A^T (one broadcast read)
             const int blk = jg & 1;
+            const float *ab = &pAt[(16 * blk) * LA + 16 * blk];
             // the identity column is rebuilt each chunk (16 selects) rather
             // than kept live across the loop in 16 registers
             int col = mr;
@@ -656,19 +755,34 @@ __global__ __launch_bounds__(512, 1) void chunked_ws_kernel(WsParams p)
             float acc[16];
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[r] = (r == col) ? 1.0f : 0.0f;
+            // rows i0 .. i0 + 4 of A^T: their needed groups read first, then
+            // the five elimination steps
+            auto steps = [&](auto i0c) {
+                constexpr int i0 = decltype(i0c)::value;
+                // keeps the compiler from hoisting every batch's reads to the
+                // top, which would need all 36 float4 at once
+                asm volatile("" ::: "memory");
+                float4 arow[5][4];
 #pragma unroll
-            for (int i = 0; i < 15; ++i) {
-                const float *arow = &pAt[(16 * blk + i) * LA + 16 * blk];
-                const float4 a0 = *reinterpret_cast<const float4 *>(arow);
-                const float4 a1 = *reinterpret_cast<const float4 *>(arow + 4);
-                const float4 a2 = *reinterpret_cast<const float4 *>(arow + 8);
-                const float4 a3 = *reinterpret_cast<const float4 *>(arow + 12);
-                const float av[16] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w,
-                                      a2.x, a2.y, a2.z, a2.w, a3.x, a3.y, a3.z, a3.w};
-                const float ti = acc[i];
+                for (int ii = 0; ii < 5; ++ii)
 #pragma unroll
-                for (int r = i + 1; r < 16; ++r) acc[r] -= av[r] * ti;
-            }
+                    for (int g4 = (i0 + ii + 1) >> 2; g4 < 4; ++g4)
+                        arow[ii][g4] = *reinterpret_cast<const float4 *>(ab + (i0 + ii) * LA + 4 * g4);
+#pragma unroll
+                for (int ii = 0; ii < 5; ++ii) {
+                    const int i = i0 + ii;
+                    const float ti = acc[i];
+#pragma unroll
+                    for (int r = i + 1; r < 16; ++r) {
+                        const float4 a4 = arow[ii][r >> 2];
+                        const float a = (r & 3) == 0 ? a4.x : (r & 3) == 1 ? a4.y : (r & 3) == 2 ? a4.z : a4.w;
+                        acc[r] -= a * ti;
+                    }
+                }
+            };
+            steps(std::integral_constant<int, 0>{});
+            steps(std::integral_constant<int, 5>{});
+            steps(std::integral_constant<int, 10>{});
             if (jg < 2) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) pT[(16 * blk + r) * LA + 16 * blk + mr] = acc[r];
