@@ -12,110 +12,121 @@
 //   o  = S^T q = p + (k . q) u
 //
 // The step is bound by HBM: each 64 KB state (d = 128) is read once and
-// written once, everything else is ~1.3 KB per (n, h).  One 256-thread
-// workgroup owns one (n, h) state.  Thread t holds a 4-column group (16-byte
-// loads/stores, a wave reads two full 512-byte rows per instruction) for
-// d_k / 8 rows spread with stride 8, so the whole state sits in registers
-// between the read and the write.  Column sums over rows are reduced through
-// LDS; all loads of the state are issued before any arithmetic.
+// written once, everything else is ~1.3 KB per (n, h).  A 1024-thread
+// workgroup walks (n, h) units with a stride of the grid (a few workgroups
+// per CU); thread t holds a 4-column group (16-byte accesses; a wave covers
+// two whole 512-byte rows) of d_k / 32 rows, so a unit's state sits in
+// registers between its read and its write, and the next unit's state is
+// already being read while the current one is reduced and written.  Column
+// sums over rows go through LDS.  State traffic uses non-temporal loads and
+// stores: every byte is touched once per step, so caching it only costs.
 #include "kda_device.h"
 
 namespace kda {
 
+constexpr int DEC_THREADS = 1024;
+
 template <int DK, int DV, typename T>
-__global__ __launch_bounds__(256) void decode_step_kernel(
+__global__ __launch_bounds__(DEC_THREADS) void decode_step_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const T *__restrict__ log_alpha, const T *__restrict__ beta,
-    float *__restrict__ S_cache, T *__restrict__ o)
+    float *__restrict__ S_cache, T *__restrict__ o, int units)
 {
-    constexpr int NT = 256;
-    constexpr int CG = DV / 4;     // float4 column groups per row
+    constexpr int NT = DEC_THREADS;
+    constexpr int CG = DV / 4;     // 16-byte column groups per row
     constexpr int RG = NT / CG;    // row groups
     constexpr int RPT = DK / RG;   // rows per thread
-    static_assert(NT % CG == 0 && DK % RG == 0, "decode tiling");
+    static_assert(NT % CG == 0 && DK % RG == 0 && RPT >= 1, "decode tiling");
+    typedef float f4v __attribute__((ext_vector_type(4)));
 
-    const int unit = blockIdx.x;   // flattened (n, h)
     const int t = threadIdx.x;
     const int cg = t % CG, rg = t / CG;
 
     __shared__ float s_a[DK], s_k[DK], s_q[DK];
-    __shared__ float s_red[2][RG][DV];
-    __shared__ float s_u[DV];
+    __shared__ __attribute__((aligned(16))) float s_red[2][RG][DV];
+    __shared__ __attribute__((aligned(16))) float s_u[DV];
     __shared__ float s_kq;
 
-    float *Su = S_cache + (size_t)unit * DK * DV;
-    float4 st[RPT];
+    f4v cur[RPT], nxt[RPT];
+    auto load_state = [&](int unit, f4v (&r)[RPT]) {
+        const f4v *Su = reinterpret_cast<const f4v *>(S_cache + (size_t)unit * DK * DV);
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-        const int row = rg + i * RG;
-        st[i] = *reinterpret_cast<const float4 *>(Su + (size_t)row * DV + 4 * cg);
-    }
+        for (int i = 0; i < RPT; ++i) r[i] = __builtin_nontemporal_load(Su + (rg + i * RG) * CG + cg);
+    };
 
-    if (t < DK) {
-        const size_t idx = (size_t)unit * DK + t;
-        s_a[t] = expf(load_elem(log_alpha + idx));
-        s_k[t] = load_elem(k + idx);
-        s_q[t] = load_elem(q + idx);
-    }
-    __syncthreads();
+    int unit = blockIdx.x;
+    if (unit < units) load_state(unit, cur);
+    for (; unit < units; unit += gridDim.x) {
+        const int next = unit + gridDim.x;
+        if (next < units) load_state(next, nxt);
 
-    if (t < 64) {   // k . q by the first wave
-        float acc = 0.f;
-        for (int r = t; r < DK; r += 64) acc += s_k[r] * s_q[r];
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-        if (t == 0) s_kq = acc;
-    }
-
-    float e0 = 0.f, e1 = 0.f, e2 = 0.f, e3 = 0.f;
-    float p0 = 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-        const int row = rg + i * RG;
-        const float a = s_a[row], kr = s_k[row], qr = s_q[row];
-        float4 s = st[i];
-        s.x *= a; s.y *= a; s.z *= a; s.w *= a;
-        st[i] = s;
-        e0 += s.x * kr; e1 += s.y * kr; e2 += s.z * kr; e3 += s.w * kr;
-        p0 += s.x * qr; p1 += s.y * qr; p2 += s.z * qr; p3 += s.w * qr;
-    }
-    *reinterpret_cast<float4 *>(&s_red[0][rg][4 * cg]) = make_float4(e0, e1, e2, e3);
-    *reinterpret_cast<float4 *>(&s_red[1][rg][4 * cg]) = make_float4(p0, p1, p2, p3);
-    __syncthreads();
-
-    if (t < DV) {
-        float e = 0.f, p = 0.f;
-#pragma unroll
-        for (int r = 0; r < RG; ++r) {
-            e += s_red[0][r][t];
-            p += s_red[1][r][t];
+        if (t < DK) {
+            const size_t idx = (size_t)unit * DK + t;
+            s_a[t] = expf(load_elem(log_alpha + idx));
+            s_k[t] = load_elem(k + idx);
+            s_q[t] = load_elem(q + idx);
         }
-        const size_t vidx = (size_t)unit * DV + t;
-        const float u = load_elem(beta + unit) * (load_elem(v + vidx) - e);
-        s_u[t] = u;
-        store_elem(o + vidx, p + s_kq * u);
-    }
-    __syncthreads();
+        __syncthreads();
 
-    const float4 u4 = *reinterpret_cast<const float4 *>(&s_u[4 * cg]);
+        if (t < 64) {   // k . q by the first wave
+            float acc = 0.f;
+            for (int r = t; r < DK; r += 64) acc += s_k[r] * s_q[r];
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-        const int row = rg + i * RG;
-        const float kr = s_k[row];
-        float4 s = st[i];
-        s.x += kr * u4.x; s.y += kr * u4.y; s.z += kr * u4.z; s.w += kr * u4.w;
-        *reinterpret_cast<float4 *>(Su + (size_t)row * DV + 4 * cg) = s;
+            for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+            if (t == 0) s_kq = acc;
+        }
+
+        f4v e = {0.f, 0.f, 0.f, 0.f}, pq = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            const int row = rg + i * RG;
+            cur[i] *= s_a[row];
+            e += cur[i] * s_k[row];
+            pq += cur[i] * s_q[row];
+        }
+        *reinterpret_cast<f4v *>(&s_red[0][rg][4 * cg]) = e;
+        *reinterpret_cast<f4v *>(&s_red[1][rg][4 * cg]) = pq;
+        __syncthreads();
+
+        if (t < DV) {
+            float es = 0.f, ps = 0.f;
+#pragma unroll 8
+            for (int r = 0; r < RG; ++r) {
+                es += s_red[0][r][t];
+                ps += s_red[1][r][t];
+            }
+            const size_t vidx = (size_t)unit * DV + t;
+            const float u = load_elem(beta + unit) * (load_elem(v + vidx) - es);
+            s_u[t] = u;
+            store_elem(o + vidx, ps + s_kq * u);
+        }
+        __syncthreads();
+
+        const f4v u4 = *reinterpret_cast<const f4v *>(&s_u[4 * cg]);
+        f4v *Sw = reinterpret_cast<f4v *>(S_cache + (size_t)unit * DK * DV);
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            const int row = rg + i * RG;
+            __builtin_nontemporal_store(cur[i] + s_k[row] * u4, Sw + row * CG + cg);
+        }
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) cur[i] = nxt[i];
+        __syncthreads();   // the LDS vectors are rewritten for the next unit
     }
 }
+
+int cu_count();
 
 template <int DK, int DV, typename T>
 static hipError_t launch_decode(const void *q, const void *k, const void *v,
                                 const void *log_alpha, const void *beta, float *S,
                                 void *o, int units, hipStream_t stream)
 {
-    hipLaunchKernelGGL((decode_step_kernel<DK, DV, T>), dim3(units), dim3(256), 0, stream,
+    // four workgroups per CU, each walking units with the grid stride
+    const int grid = units < 4 * cu_count() ? units : 4 * cu_count();
+    hipLaunchKernelGGL((decode_step_kernel<DK, DV, T>), dim3(grid), dim3(DEC_THREADS), 0, stream,
                        (const T *)q, (const T *)k, (const T *)v, (const T *)log_alpha,
-                       (const T *)beta, S, (T *)o);
+                       (const T *)beta, S, (T *)o, units);
     return hipGetLastError();
 }
 
