@@ -161,6 +161,20 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
 }
 
 __device__ __forceinline__ float bf_lo(uint32_t x) { return __uint_as_float(x << 16); }
+
+// Raw buffer resource over `base` (uniform): untyped 32-bit format, no
+// stride, bounds = 2^31 - 16 bytes.  Accesses at offset OOB_OFF read as zero
+// and drop stores, which lets masked rows go without branches.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *base) {
+    // the address is the same in every lane; saying so keeps the resource in
+    // scalar registers (otherwise each access becomes a loop over lanes)
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    void *u = reinterpret_cast<void *>(((uint64_t)hi << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(u, 0, 0x7ffffff0, 0x00020000);
+}
+constexpr uint32_t OOB_OFF = 0x80000000u;
 __device__ __forceinline__ float bf_hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
 
 // Row r and column i of pair number pidx of the lower triangle (i <= r),
@@ -340,24 +354,35 @@ __global__ __launch_bounds__(512, 1) void chunked_ws_kernel(WsParams p)
         __builtin_amdgcn_s_waitcnt(0x0F70);
         // v prefetch (raw bf16 bits) of the rows / columns this lane's tiles hold
         uint32_t rawv[NSTRIP][8];
+        // byte offset of (chunk row 8 jg, this lane's column) from a chunk's
+        // first v element; rows past the end read row 0 instead
+        const uint32_t vlane = (uint32_t)(8 * jg) * tokv * 2u + (uint32_t)(16 * w + mr) * 2u;
+        // Every load and store of v and o is issued on every chunk (rows past
+        // the end go out of the buffer's bounds: zero / dropped), so the
+        // number of memory operations in flight is fixed and the wait for
+        // the v prefetch never has to include the o stores.
         auto load_v = [&](int n) {
             const long cs = (long)n * C;
             const int cl = (int)((len - cs) < C ? (len - cs) : C);
-            const bf16_t *bv = gv + ((size_t)(t0 + cs) * H + head) * DV + col0;
+            const __amdgpu_buffer_rsrc_t rv = buf_rsrc(gv + ((size_t)(t0 + cs) * H + head) * DV + col0);
 #pragma unroll
-            for (int s = 0; s < NSTRIP; ++s) {
-                const uint32_t co = 16 * (w + 4 * s) + mr;
+            for (int s = 0; s < NSTRIP; ++s)
 #pragma unroll
                 for (int h = 0; h < 2; ++h)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int row = crow(h, 4 * jg + i);
-                        const uint32_t r = (uint32_t)(row < cl ? row : cl - 1);
-                        rawv[s][4 * h + i] = (uint32_t)bv[r * tokv + co].x;
+                        // the aligned 4-byte word holding this column (and its
+                        // neighbour): the register is the load's own result
+                        const uint32_t off = row < cl ? ((vlane + (uint32_t)(4 * h + i) * tokv * 2u + 128u * s) & ~3u)
+                                                      : OOB_OFF;
+                        rawv[s][4 * h + i] = __builtin_amdgcn_raw_buffer_load_b32(rv, off, 0, 0);
                     }
-            }
         };
         if (nchunks > 0) load_v(0);
+        // the first chunk's v has landed before the loop, as it has at the end of
+        // every iteration, so the loop head needs no wait on memory
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
 
         for (int n = 0; n < nchunks; ++n) {
             const int slot = n % NSLOT;
@@ -373,26 +398,84 @@ __global__ __launch_bounds__(512, 1) void chunked_ws_kernel(WsParams p)
             const bf16_t *sTp = reinterpret_cast<const bf16_t *>(sb + L::TP);
             const bf16_t *sP = reinterpret_cast<const bf16_t *>(sb + L::PM);
             const float *sG = reinterpret_cast<const float *>(sb + L::GM);
-            bf16_t *obase = go + ((size_t)(t0 + cs) * H + head) * DV + col0;
+            const __amdgpu_buffer_rsrc_t ro = buf_rsrc(go + ((size_t)(t0 + cs) * H + head) * DV + col0);
 
             // v of this chunk out of the prefetch registers, which then take
-            // the next chunk's loads at once (a whole chunk of latency slack)
+            // the next chunk's loads at once (a whole chunk of latency slack).
+            // Only the v loads must have landed, not the o stores issued after
+            // them: vmcnt counts both, in order, so wait down to the 8 * NSTRIP
+            // stores (without this the compiler waits for everything here)
+            if constexpr (NSTRIP == 1) __builtin_amdgcn_s_waitcnt(0x0F78);   // vmcnt(8)
+            else __builtin_amdgcn_s_waitcnt(0x4F70);                        // vmcnt(16)
             float xv[NSTRIP][8];
+            const uint32_t vsh = (mr & 1) ? 0u : 16u;   // odd columns are the high half
 #pragma unroll
             for (int s = 0; s < NSTRIP; ++s)
 #pragma unroll
                 for (int h = 0; h < 2; ++h)
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        xv[s][4 * h + i] = crow(h, 4 * jg + i) < cl ? bf_lo(rawv[s][4 * h + i]) : 0.0f;
-            if (n + 1 < nchunks) load_v(n + 1);
+                        xv[s][4 * h + i] = __uint_as_float((rawv[s][4 * h + i] << vsh) & 0xffff0000u);
+            // unconditional (the last chunk reloads itself): a conditional
+            // load leaves the registers with two definitions, which the compiler
+            // resolves with copies that wait for every outstanding access
+            load_v(n + 1 < nchunks ? n + 1 : n);
+
+            // every operand fragment of the chunk, read at once (one LDS
+            // round trip instead of one per MFMA stage); with two strips per
+            // wave they are read per strip, as holding them for both strips
+            // would exceed the register file
+            bf16x8 fku[2][NRUN], fqu[2][NRUN], ftp[2], fpm[2], fkr[NKT];
+            float4 fgm[NKT];
+            auto read_frags = [&]() {
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int row = crow(h, mr);
+                    const int kr = keyK<DK>(row);
+#pragma unroll
+                    for (int rr = 0; rr < NRUN; ++rr) {
+                        const int off = row * DK + (((4 * rr + jg) ^ kr) << 3);
+                        fku[h][rr] = *reinterpret_cast<const bf16x8 *>(&sKU[off]);
+                        fqu[h][rr] = *reinterpret_cast<const bf16x8 *>(&sQU[off]);
+                    }
+                    ftp[h] = *reinterpret_cast<const bf16x8 *>(&sTp[row * C + ((jg ^ key4(row)) << 3)]);
+                    fpm[h] = *reinterpret_cast<const bf16x8 *>(&sP[row * C + ((jg ^ key4(row)) << 3)]);
+                }
+            };
+            auto read_kr = [&]() {
+#pragma unroll
+                for (int tt = 0; tt < NKT; ++tt) {
+                    const int rho = tt >> 1, h = tt & 1;
+                    fgm[tt] = *reinterpret_cast<const float4 *>(&sG[srow(rho, h, 4 * jg)]);
+                    fkr[tt] = *reinterpret_cast<const bf16x8 *>(&sKRt[idxT(srow(rho, h, mr), jg)]);
+                }
+            };
+            if constexpr (NSTRIP == 1) {
+                read_frags();
+                read_kr();
+            }
 
 #pragma unroll
             for (int s = 0; s < NSTRIP; ++s) {
-                const uint32_t co = 16 * (w + 4 * s) + mr;
+                if constexpr (NSTRIP > 1) {
+                    // a compiler barrier, so the second strip's reads are not
+                    // merged with the first's (which would keep both live)
+                    asm volatile("" ::: "memory");
+                }
                 bf16x8 sf[NRUN];
 #pragma unroll
                 for (int rr = 0; rr < NRUN; ++rr) sf[rr] = pack8(S[s][2 * rr], S[s][2 * rr + 1]);
+                if constexpr (NSTRIP > 1) read_frags();
+                // the decay of the old state does not wait for the chain below
+                if constexpr (NSTRIP == 1) {
+#pragma unroll
+                    for (int tt = 0; tt < NKT; ++tt) {
+                        S[s][tt][0] *= fgm[tt].x;
+                        S[s][tt][1] *= fgm[tt].y;
+                        S[s][tt][2] *= fgm[tt].z;
+                        S[s][tt][3] *= fgm[tt].w;
+                    }
+                }
                 // X = V - K_up S (the slot holds -K_up), O = Q_up S
                 f32x4 X[2], O[2];
 #pragma unroll
@@ -403,55 +486,45 @@ __global__ __launch_bounds__(512, 1) void chunked_ws_kernel(WsParams p)
                         O[h][i] = 0.0f;
                     }
 #pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const int row = crow(h, mr);
-                    const int kr = keyK<DK>(row);
+                for (int rr = 0; rr < NRUN; ++rr)
 #pragma unroll
-                    for (int rr = 0; rr < NRUN; ++rr) {
-                        const int off = row * DK + (((4 * rr + jg) ^ kr) << 3);
-                        const bf16x8 fa = *reinterpret_cast<const bf16x8 *>(&sKU[off]);
-                        const bf16x8 fq = *reinterpret_cast<const bf16x8 *>(&sQU[off]);
-                        X[h] = mfma_bf16(fa, sf[rr], X[h]);
-                        O[h] = mfma_bf16(fq, sf[rr], O[h]);
+                    for (int h = 0; h < 2; ++h) {
+                        X[h] = mfma_bf16(fku[h][rr], sf[rr], X[h]);
+                        O[h] = mfma_bf16(fqu[h][rr], sf[rr], O[h]);
                     }
-                }
                 // U = T' X
                 const bf16x8 xf = pack8(X[0], X[1]);
                 f32x4 U[2];
 #pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const int row = crow(h, mr);
-                    const bf16x8 fa = *reinterpret_cast<const bf16x8 *>(&sTp[row * C + ((jg ^ key4(row)) << 3)]);
-                    U[h] = mfma_bf16(fa, xf, f32x4{0.f, 0.f, 0.f, 0.f});
-                }
+                for (int h = 0; h < 2; ++h) U[h] = mfma_bf16(ftp[h], xf, f32x4{0.f, 0.f, 0.f, 0.f});
                 const bf16x8 uf = pack8(U[0], U[1]);
-                // O += P U
+                // S = Diag(gamma) S + K_right^T U;  O += P U
+                if constexpr (NSTRIP > 1) {
 #pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const int row = crow(h, mr);
-                    const bf16x8 fa = *reinterpret_cast<const bf16x8 *>(&sP[row * C + ((jg ^ key4(row)) << 3)]);
-                    O[h] = mfma_bf16(fa, uf, O[h]);
-                }
-                // S = Diag(gamma) S + K_right^T U
+                    for (int tt = 0; tt < NKT; ++tt) {
+                        const int rho = tt >> 1, h = tt & 1;
+                        const float4 gm = *reinterpret_cast<const float4 *>(&sG[srow(rho, h, 4 * jg)]);
+                        S[s][tt][0] *= gm.x;
+                        S[s][tt][1] *= gm.y;
+                        S[s][tt][2] *= gm.z;
+                        S[s][tt][3] *= gm.w;
+                        const bf16x8 fa = *reinterpret_cast<const bf16x8 *>(&sKRt[idxT(srow(rho, h, mr), jg)]);
+                        S[s][tt] = mfma_bf16(fa, uf, S[s][tt]);
+                    }
+                } else {
 #pragma unroll
-                for (int tt = 0; tt < NKT; ++tt) {
-                    const int rho = tt >> 1, h = tt & 1;
-                    const float4 gm = *reinterpret_cast<const float4 *>(&sG[srow(rho, h, 4 * jg)]);
-                    S[s][tt][0] *= gm.x;
-                    S[s][tt][1] *= gm.y;
-                    S[s][tt][2] *= gm.z;
-                    S[s][tt][3] *= gm.w;
-                    const int ch = srow(rho, h, mr);
-                    const bf16x8 fa = *reinterpret_cast<const bf16x8 *>(&sKRt[idxT(ch, jg)]);
-                    S[s][tt] = mfma_bf16(fa, uf, S[s][tt]);
+                    for (int tt = 0; tt < NKT; ++tt) S[s][tt] = mfma_bf16(fkr[tt], uf, S[s][tt]);
                 }
+#pragma unroll
+                for (int h = 0; h < 2; ++h) O[h] = mfma_bf16(fpm[h], uf, O[h]);
                 // store O
 #pragma unroll
                 for (int h = 0; h < 2; ++h)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int row = crow(h, 4 * jg + i);
-                        if (row < cl) obase[(uint32_t)row * tokv + co] = to_bf16(O[h][i]);
+                        const uint32_t off = row < cl ? vlane + (uint32_t)(4 * h + i) * tokv * 2u + 128u * s : OOB_OFF;
+                        __builtin_amdgcn_raw_buffer_store_b16(to_bf16(O[h][i]).x, ro, off, 0, 0);
                     }
             }
             // all reads of the slot are done once their values were consumed
@@ -484,6 +557,42 @@ __global__ __launch_bounds__(512, 1) void chunked_ws_kernel(WsParams p)
     float *pBeta = reinterpret_cast<float *>(priv + L::P_BETA);
     const uint32_t tokk = (uint32_t)H * DK;
 
+    // Raw g and k of one chunk, lane (cg, rg) = (lane & 15, lane >> 4)
+    // holding channels NCL*cg .. +NCL-1 of rows 8*rg .. 8*rg+7 (one 16- or
+    // 8-byte load per row and tensor), and beta of row `lane`.  Rows past the
+    // chunk end read row 0 (always in bounds) and are masked where used.
+    // A producer requests its next chunk's g and k while it still finishes
+    // the current one, which hides their latency.
+    uint32_t gx[8][NCL / 2], kx[8][NCL / 2], bx;
+    auto load_gk = [&](int n) {
+        const int lane = tid & 63, cg = lane & 15, rg = lane >> 4;
+        const int c0 = NCL * cg, r0 = 8 * rg;
+        const long cs = (long)n * C;
+        const int cl = (int)((len - cs) < C ? (len - cs) : C);
+        const size_t tb = (size_t)(t0 + cs) * H + head;
+        const char *bg = reinterpret_cast<const char *>(gg + tb * DK);
+        const char *bk = reinterpret_cast<const char *>(gk + tb * DK);
+        const uint32_t base_off = ((uint32_t)r0 * tokk + (uint32_t)c0) * 2u;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t off = (r0 + i < cl) ? base_off + (uint32_t)i * tokk * 2u : (uint32_t)c0 * 2u;
+            if constexpr (NCL == 8) {
+                const uint4 g4 = *reinterpret_cast<const uint4 *>(bg + off);
+                const uint4 k4 = *reinterpret_cast<const uint4 *>(bk + off);
+                gx[i][0] = g4.x; gx[i][1] = g4.y; gx[i][2] = g4.z; gx[i][3] = g4.w;
+                kx[i][0] = k4.x; kx[i][1] = k4.y; kx[i][2] = k4.z; kx[i][3] = k4.w;
+            } else {
+                const uint2 g2 = *reinterpret_cast<const uint2 *>(bg + off);
+                const uint2 k2 = *reinterpret_cast<const uint2 *>(bk + off);
+                gx[i][0] = g2.x; gx[i][1] = g2.y;
+                kx[i][0] = k2.x; kx[i][1] = k2.y;
+            }
+        }
+        const int rb = lane & (C - 1);
+        bx = (uint32_t)gb[tb + (size_t)(rb < cl ? rb : cl - 1) * H].x;
+    };
+    if (pw < nchunks) load_gk(pw);
+
     for (int n = pw; n < nchunks; n += NPROD) {
         // Lane-derived LDS offsets are recomputed per chunk (a few cheap ops)
         // instead of being hoisted out of the loop and kept live, which would
@@ -498,43 +607,25 @@ __global__ __launch_bounds__(512, 1) void chunked_ws_kernel(WsParams p)
         const bf16_t *bg = gg + tb * DK, *bk = gk + tb * DK, *bq = gq + tb * DK;
 
         // ---- loads ---------------------------------------------------------------
-        // Lane (cg, rg) = (lane & 15, lane >> 4) holds channels NCL*cg .. +NCL-1
-        // of rows 8*rg .. 8*rg+7: one 16-byte (d_k = 128) or 8-byte (d_k = 64)
-        // load per row and tensor.  Rows past the chunk end read the last
-        // valid row (always in bounds) and are masked below.
+        // g and k of this chunk were requested at the end of the producer's
+        // previous chunk; q (first needed after the decay products) now.
         const int cg = lane & 15, rg = lane >> 4;
         const int c0 = NCL * cg, r0 = 8 * rg;
-        uint32_t gx[8][NCL / 2], kx[8][NCL / 2], qx[8][NCL / 2];
-        // byte offsets from the chunk's first row (32-bit: a chunk spans
-        // 32 rows); rows past the end read row 0 instead
-        const uint32_t base_off = ((uint32_t)r0 * tokk + (uint32_t)c0) * 2u;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const uint32_t off = (r0 + i < cl) ? base_off + (uint32_t)i * tokk * 2u : (uint32_t)c0 * 2u;
-            const char *pg = reinterpret_cast<const char *>(bg) + off;
-            const char *pk = reinterpret_cast<const char *>(bk) + off;
-            const char *pq = reinterpret_cast<const char *>(bq) + off;
-            if constexpr (NCL == 8) {
-                const uint4 g4 = *reinterpret_cast<const uint4 *>(pg);
-                const uint4 k4 = *reinterpret_cast<const uint4 *>(pk);
-                const uint4 q4 = *reinterpret_cast<const uint4 *>(pq);
-                gx[i][0] = g4.x; gx[i][1] = g4.y; gx[i][2] = g4.z; gx[i][3] = g4.w;
-                kx[i][0] = k4.x; kx[i][1] = k4.y; kx[i][2] = k4.z; kx[i][3] = k4.w;
-                qx[i][0] = q4.x; qx[i][1] = q4.y; qx[i][2] = q4.z; qx[i][3] = q4.w;
-            } else {
-                const uint2 g2 = *reinterpret_cast<const uint2 *>(pg);
-                const uint2 k2 = *reinterpret_cast<const uint2 *>(pk);
-                const uint2 q2 = *reinterpret_cast<const uint2 *>(pq);
-                gx[i][0] = g2.x; gx[i][1] = g2.y;
-                kx[i][0] = k2.x; kx[i][1] = k2.y;
-                qx[i][0] = q2.x; qx[i][1] = q2.y;
-            }
-        }
-        uint32_t bx;
+        uint32_t qx[8][NCL / 2];
         {
-            const int rb = lane & (C - 1);
-            const uint32_t rr_ = (uint32_t)(rb < cl ? rb : cl - 1);
-            bx = (uint32_t)gb[tb + (size_t)rr_ * H].x;
+            const uint32_t base_off = ((uint32_t)r0 * tokk + (uint32_t)c0) * 2u;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const uint32_t off = (r0 + i < cl) ? base_off + (uint32_t)i * tokk * 2u : (uint32_t)c0 * 2u;
+                const char *pq = reinterpret_cast<const char *>(bq) + off;
+                if constexpr (NCL == 8) {
+                    const uint4 q4 = *reinterpret_cast<const uint4 *>(pq);
+                    qx[i][0] = q4.x; qx[i][1] = q4.y; qx[i][2] = q4.z; qx[i][3] = q4.w;
+                } else {
+                    const uint2 q2 = *reinterpret_cast<const uint2 *>(pq);
+                    qx[i][0] = q2.x; qx[i][1] = q2.y;
+                }
+            }
         }
 
         // ---- decay per key channel ---------------------------------------------
@@ -740,6 +831,9 @@ __global__ __launch_bounds__(512, 1) void chunked_ws_kernel(WsParams p)
             exact_ap<DK>(lane, cl, tokk, bg, bk, bq, priv, pAt, sP, pBeta);
         }
         __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+
+        // next chunk's g and k (not live across the out-of-line exact path)
+        if (n + NPROD < nchunks) load_gk(n + NPROD);
 
         // ---- T = (I + A)^{-1}; T' = T Diag(beta) into the slot ----------------
         {
