@@ -13,6 +13,9 @@ Also reported on the same JSON line:
                 8 TB/s; the useful-flop MFMA fraction against 2.5 PFLOP/s bf16;
                 traffic from the committed rocprofv3 counter summary when it was
                 taken on the current kernel source, else null
+  workloads     the same forward on the B=1, H=16, T=4096 workload and on 64
+                packed sequences of 512..16384 tokens (H=32, d=128): time per
+                call, tokens/s and the fraction of 8 TB/s of algorithmic bytes
   decode        kda_decode_step over N=512, H=32, d=128 (1 GiB fp32 cache),
                 1000 chained steps with fresh inputs pre-generated on the GPU
   copy_ceiling  a plain device copy of 1 GiB (practical HBM ceiling)
@@ -136,6 +139,36 @@ def bench_forward(torch, kda, synth, steps, warmup):
     flops = fwd_useful_flops(B, T, H, dk, dv)
     return dict(w=w, x=x, t_step=t_step, bytes=nbytes, flops=flops,
                 tokens_per_s=B * T / t_step)
+
+
+def bench_other_workloads(torch, kda, synth, steps=10, warmup=3):
+    """The forward on the H16 and packed-varlen workloads (reported beside
+    the headline line, not in `value`)."""
+    out = {}
+    for w in (synth.FWD_H16_T4K, synth.VARLEN_64):
+        log(f"[bench] generating {w.name} on the GPU")
+        x = synth.fwd_inputs(w, device="cuda")
+        B, T, H, dk, dv, N = x["B"], x["T"], x["H"], x["dk"], x["dv"], x["N"]
+        o = torch.empty((B, T, H, dv), dtype=w.dtype, device="cuda")
+        S_T = torch.empty((N, H, dk, dv), dtype=torch.float32, device="cuda")
+        ws = None
+        nws = kda.workspace_bytes(B, T, H, dk, dv, N) if x["cu_seqlens"] is not None else 0
+        if nws:
+            ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
+
+        def step():
+            kda.fwd_chunked(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["S0"],
+                            x["cu_seqlens"], o=o, S_T=S_T, workspace=ws)
+
+        secs = time_loop(torch, step, steps, warmup) / steps
+        tokens = B * T
+        nbytes = (tokens * H * ((2 * dk + dv + dk + 1) * 2 + dv * 2) + 2 * N * H * dk * dv * 4)
+        out[w.name] = {"us_per_call": round(secs * 1e6, 1), "tokens": tokens,
+                       "tokens_per_s": round(tokens / secs, 1),
+                       "hbm_frac": round(nbytes / secs / 1e9 / HBM_PEAK_GBS, 4)}
+        del x, o, S_T, ws
+        torch.cuda.empty_cache()
+    return out
 
 
 def bench_decode(torch, kda, synth, steps=None):
@@ -280,6 +313,7 @@ def main():
                    "chunk": CHUNK, "state": "fp32", "parallelism": "single GPU"},
         "roofline": roofline,
     }
+    out["workloads"] = bench_other_workloads(torch, kda, synth)
     if not args.no_decode:
         dc = bench_decode(torch, kda, synth, args.decode_steps)
         gbs = dc["bytes"] / dc["t_step"] / 1e9
