@@ -8,11 +8,12 @@
 
 namespace kda {
 hipError_t decode_step_launch(const void *q, const void *k, const void *v,
-                              const void *log_alpha, const void *beta, float *S,
-                              void *o, int units, int dk, int dv, bool bf16,
-                              hipStream_t stream);
+                              const void *log_alpha, const void *beta, int gate, float *S,
+                              const int32_t *state_idx, int pool, void *o, int N, int H,
+                              int dk, int dv, bool bf16, hipStream_t stream);
 hipError_t chunked_fwd_launch(const void *q, const void *k, const void *v, const void *g,
-                              const void *beta, const float *S0, float *S_T, void *o,
+                              const void *beta, int gate, const float *S0, float *S_T,
+                              const int32_t *state_idx, int pool, void *o,
                               const int32_t *cu_seqlens, int num_seqs, int B, int T, int H,
                               int dk, int dv, bool bf16, void *workspace, hipStream_t stream);
 }  // namespace kda
@@ -22,6 +23,10 @@ namespace {
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 bool dim_ok(int d) { return d == 64 || d == 128; }
+
+bool gate_ok(kda_gate g) { return g == KDA_GATE_CHANNEL || g == KDA_GATE_HEAD || g == KDA_GATE_NONE; }
+
+bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
 // Element counts must stay addressable with 64-bit offsets and the grid must
 // fit a 32-bit block index.
@@ -59,14 +64,15 @@ size_t kda_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int num_seqs
     return ((size_t)num_seqs * sizeof(int32_t) + 255) & ~(size_t)255;
 }
 
-kda_status kda_fwd_chunked(const void *q, const void *k, const void *v,
-                           const void *log_alpha, const void *beta,
-                           const float *S0, const int32_t *cu_seqlens, int num_seqs,
-                           int B, int T, int H, int dk, int dv, kda_dtype dtype,
-                           void *o, float *S_T,
-                           void *workspace, size_t workspace_bytes, void *stream)
+kda_status kda_fwd_chunked_ex(const void *q, const void *k, const void *v,
+                              const void *log_alpha, const void *beta, kda_gate gate,
+                              const float *S0, float *S_T, const int32_t *state_idx, int pool_size,
+                              const int32_t *cu_seqlens, int num_seqs,
+                              int B, int T, int H, int dk, int dv, kda_dtype dtype,
+                              void *o, void *workspace, size_t workspace_bytes, void *stream)
 {
     if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_INVALID_ARG;
+    if (!gate_ok(gate)) return KDA_ERR_INVALID_ARG;
     if (B < 0 || T < 0 || H <= 0 || dk <= 0 || dv <= 0) return KDA_ERR_INVALID_ARG;
     if (cu_seqlens && (B != 1 || num_seqs < 0)) return KDA_ERR_INVALID_ARG;
     const int nseq = cu_seqlens ? num_seqs : B;
@@ -74,10 +80,16 @@ kda_status kda_fwd_chunked(const void *q, const void *k, const void *v,
     if (dtype == KDA_F32 && dk != 64) return KDA_ERR_UNSUPPORTED;
     if (!sizes_fit(B, T, H, dk > dv ? dk : dv) || !sizes_fit(nseq, H, dk, dv)) return KDA_ERR_INVALID_ARG;
     if ((long long)nseq * H * 2 >= ((long long)1 << 31)) return KDA_ERR_INVALID_ARG;
+    if (state_idx) {
+        if (pool_size < 0 || !aligned4(state_idx) || !sizes_fit(pool_size, H, dk, dv))
+            return KDA_ERR_INVALID_ARG;
+    }
     const long long tokens = (long long)B * T;
+    const void *g = gate == KDA_GATE_NONE ? nullptr : log_alpha;
     if (tokens > 0 || nseq > 0) {
-        if (tokens > 0 && (!q || !k || !v || !log_alpha || !beta || !o)) return KDA_ERR_INVALID_ARG;
-        if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(log_alpha) ||
+        if (tokens > 0 && (!q || !k || !v || !beta || !o)) return KDA_ERR_INVALID_ARG;
+        if (tokens > 0 && gate != KDA_GATE_NONE && !log_alpha) return KDA_ERR_INVALID_ARG;
+        if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(g) ||
             !aligned16(beta) || !aligned16(o) || !aligned16(S0) || !aligned16(S_T))
             return KDA_ERR_INVALID_ARG;
     }
@@ -86,9 +98,45 @@ kda_status kda_fwd_chunked(const void *q, const void *k, const void *v,
         if (!workspace || workspace_bytes < need || !aligned16(workspace)) return KDA_ERR_INVALID_ARG;
     }
     if (nseq == 0) return KDA_OK;
-    hipError_t e = kda::chunked_fwd_launch(q, k, v, log_alpha, beta, S0, S_T, o, cu_seqlens,
-                                           nseq, B, T, H, dk, dv, dtype == KDA_BF16,
-                                           cu_seqlens ? workspace : nullptr,
+    hipError_t e = kda::chunked_fwd_launch(q, k, v, g, beta, (int)gate, S0, S_T, state_idx,
+                                           pool_size, o, cu_seqlens, nseq, B, T, H, dk, dv,
+                                           dtype == KDA_BF16, cu_seqlens ? workspace : nullptr,
+                                           static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status kda_fwd_chunked(const void *q, const void *k, const void *v,
+                           const void *log_alpha, const void *beta,
+                           const float *S0, const int32_t *cu_seqlens, int num_seqs,
+                           int B, int T, int H, int dk, int dv, kda_dtype dtype,
+                           void *o, float *S_T,
+                           void *workspace, size_t workspace_bytes, void *stream)
+{
+    return kda_fwd_chunked_ex(q, k, v, log_alpha, beta, KDA_GATE_CHANNEL, S0, S_T, nullptr, 0,
+                              cu_seqlens, num_seqs, B, T, H, dk, dv, dtype, o, workspace,
+                              workspace_bytes, stream);
+}
+
+kda_status kda_decode_step_ex(const void *q, const void *k, const void *v,
+                              const void *log_alpha, const void *beta, kda_gate gate,
+                              float *S_pool, const int32_t *state_idx, int pool_size,
+                              int N, int H, int dk, int dv, kda_dtype dtype, void *o, void *stream)
+{
+    if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_INVALID_ARG;
+    if (!gate_ok(gate)) return KDA_ERR_INVALID_ARG;
+    if (N < 0 || H <= 0 || dk <= 0 || dv <= 0) return KDA_ERR_INVALID_ARG;
+    if (!dim_ok(dk) || !dim_ok(dv)) return KDA_ERR_UNSUPPORTED;
+    if (!sizes_fit(N, H, dk, dv)) return KDA_ERR_INVALID_ARG;
+    if ((long long)N * H >= ((long long)1 << 31)) return KDA_ERR_INVALID_ARG;
+    if (state_idx && (pool_size < 0 || !aligned4(state_idx) || !sizes_fit(pool_size, H, dk, dv)))
+        return KDA_ERR_INVALID_ARG;
+    if (N == 0) return KDA_OK;
+    if (!q || !k || !v || !beta || !S_pool || !o) return KDA_ERR_INVALID_ARG;
+    if (gate != KDA_GATE_NONE && !log_alpha) return KDA_ERR_INVALID_ARG;
+    if (!aligned16(S_pool)) return KDA_ERR_INVALID_ARG;
+    hipError_t e = kda::decode_step_launch(q, k, v, gate == KDA_GATE_NONE ? nullptr : log_alpha,
+                                           beta, (int)gate, S_pool, state_idx, pool_size, o, N, H,
+                                           dk, dv, dtype == KDA_BF16,
                                            static_cast<hipStream_t>(stream));
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
@@ -98,17 +146,8 @@ kda_status kda_decode_step(const void *q, const void *k, const void *v,
                            float *S_cache, int N, int H, int dk, int dv,
                            kda_dtype dtype, void *o, void *stream)
 {
-    if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_INVALID_ARG;
-    if (N < 0 || H <= 0 || dk <= 0 || dv <= 0) return KDA_ERR_INVALID_ARG;
-    if (!dim_ok(dk) || !dim_ok(dv)) return KDA_ERR_UNSUPPORTED;
-    if (!sizes_fit(N, H, dk, dv)) return KDA_ERR_INVALID_ARG;
-    if ((long long)N * H >= ((long long)1 << 31)) return KDA_ERR_INVALID_ARG;
-    if (N == 0) return KDA_OK;
-    if (!q || !k || !v || !log_alpha || !beta || !S_cache || !o) return KDA_ERR_INVALID_ARG;
-    if (!aligned16(S_cache)) return KDA_ERR_INVALID_ARG;
-    hipError_t e = kda::decode_step_launch(q, k, v, log_alpha, beta, S_cache, o, N * H, dk, dv,
-                                           dtype == KDA_BF16, static_cast<hipStream_t>(stream));
-    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+    return kda_decode_step_ex(q, k, v, log_alpha, beta, KDA_GATE_CHANNEL, S_cache, nullptr, 0,
+                              N, H, dk, dv, dtype, o, stream);
 }
 
 }  // extern "C"

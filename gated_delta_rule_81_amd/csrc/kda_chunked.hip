@@ -58,6 +58,9 @@ struct ChunkParams {
     void *o;
     const int32_t *cu_seqlens;   // NULL -> dense
     const int32_t *order;        // sequence processing order (NULL -> identity)
+    const int32_t *state_idx;    // slot map of S0 / S_T rows (NULL -> row = sequence)
+    int pool;       // rows of S0 / S_T when state_idx is set
+    int gate;       // GATE_CHANNEL / GATE_HEAD / GATE_NONE
     int T;          // tokens per batch row (dense)
     int H;
     int DV;         // full value dimension
@@ -249,6 +252,7 @@ __global__ __launch_bounds__(256, 1) void chunked_fwd_kernel(ChunkParams p)
     const int H = p.H, DV = p.DV;
     const int seq_rank = sh / H, head = sh - (sh / H) * H;
     const int seq = p.order ? p.order[seq_rank] : seq_rank;
+    const long strow = state_row(p.state_idx, p.pool, seq);
     long t0, len;
     if (p.cu_seqlens) {
         t0 = p.cu_seqlens[seq];
@@ -300,9 +304,17 @@ __global__ __launch_bounds__(256, 1) void chunked_fwd_kernel(ChunkParams p)
         const size_t tb = ((size_t)(t0 + cs) * H + head);
         const in_t *bg = gg + tb * DK, *bk = gk + tb * DK, *bq = gq + tb * DK;
         const uint32_t ro = rr_ * tokstride_k + RUN * jg;
+        // a per-head gate is broadcast over the lane's channels (the scans
+        // below then see equal values on every channel); no gate reads as 0
+        uint32_t gbits = 0u;
+        if (p.gate == GATE_HEAD) {
+            if constexpr (F32) gbits = __float_as_uint(gg[tb + (size_t)rr_ * H]);
+            else gbits = (uint32_t)gg[tb + (size_t)rr_ * H].x * 0x00010001u;
+        }
 #pragma unroll
         for (int rr = 0; rr < NRUN; ++rr) {
-            rawg[rr] = *reinterpret_cast<const uint4 *>(bg + ro + 4 * RUN * rr);
+            if (p.gate == GATE_CHANNEL) rawg[rr] = *reinterpret_cast<const uint4 *>(bg + ro + 4 * RUN * rr);
+            else rawg[rr] = make_uint4(gbits, gbits, gbits, gbits);
             rawk[rr] = *reinterpret_cast<const uint4 *>(bk + ro + 4 * RUN * rr);
             rawq[rr] = *reinterpret_cast<const uint4 *>(bq + ro + 4 * RUN * rr);
         }
@@ -344,8 +356,8 @@ __global__ __launch_bounds__(256, 1) void chunked_fwd_kernel(ChunkParams p)
         for (int s = 0; s < NSTRIP; ++s)
 #pragma unroll
             for (int tt = 0; tt < NKT; ++tt) S[s][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (p.S0) {
-            const float *s0 = p.S0 + ((size_t)seq * H + head) * DK * DV + col0;
+        if (p.S0 && strow >= 0) {
+            const float *s0 = p.S0 + ((size_t)strow * H + head) * DK * DV + col0;
 #pragma unroll
             for (int s = 0; s < NSTRIP; ++s) {
                 const uint32_t co = 16 * (w + 4 * s) + mr;
@@ -753,8 +765,8 @@ __global__ __launch_bounds__(256, 1) void chunked_fwd_kernel(ChunkParams p)
         __syncthreads();
     }
 
-    if (p.S_T) {
-        float *st = p.S_T + ((size_t)seq * H + head) * DK * DV + col0;
+    if (p.S_T && strow >= 0) {
+        float *st = p.S_T + ((size_t)strow * H + head) * DK * DV + col0;
 #pragma unroll
         for (int s = 0; s < NSTRIP; ++s) {
             const uint32_t co = 16 * (w + 4 * s) + mr;
@@ -816,12 +828,14 @@ int chunked_slice_width(int units, int dv)
 }
 
 hipError_t chunked_ws_launch(const void *q, const void *k, const void *v, const void *g,
-                             const void *beta, const float *S0, float *S_T, void *o,
+                             const void *beta, int gate, const float *S0, float *S_T,
+                             const int32_t *state_idx, int pool, void *o,
                              const int32_t *cu_seqlens, const int32_t *order, int nseq, int T,
                              int H, int dk, int dv, int slice_width, hipStream_t stream);
 
 hipError_t chunked_fwd_launch(const void *q, const void *k, const void *v, const void *g,
-                              const void *beta, const float *S0, float *S_T, void *o,
+                              const void *beta, int gate, const float *S0, float *S_T,
+                              const int32_t *state_idx, int pool, void *o,
                               const int32_t *cu_seqlens, int num_seqs, int B, int T, int H,
                               int dk, int dv, bool bf16, void *workspace, hipStream_t stream)
 {
@@ -830,6 +844,9 @@ hipError_t chunked_fwd_launch(const void *q, const void *k, const void *v, const
     p.S0 = S0; p.S_T = S_T; p.o = o;
     p.cu_seqlens = cu_seqlens;
     p.order = nullptr;
+    p.state_idx = state_idx;
+    p.pool = pool;
+    p.gate = gate;
     p.T = T; p.H = H; p.DV = dv;
     const int nseq = cu_seqlens ? num_seqs : B;
     p.units = nseq * H;
@@ -844,8 +861,8 @@ hipError_t chunked_fwd_launch(const void *q, const void *k, const void *v, const
     }
     const int dvs = chunked_slice_width(p.units, dv);
     if (bf16)   // producer / consumer kernel with 32-token chunks
-        return chunked_ws_launch(q, k, v, g, beta, S0, S_T, o, cu_seqlens, p.order, nseq, T, H,
-                                 dk, dv, dvs, stream);
+        return chunked_ws_launch(q, k, v, g, beta, gate, S0, S_T, state_idx, pool, o, cu_seqlens,
+                                 p.order, nseq, T, H, dk, dv, dvs, stream);
     p.nslices = dv / dvs;
     const int nstrip = dvs / 64;
     // fp32 inputs (d_k = 64): fp32 MFMA, 64-token chunks

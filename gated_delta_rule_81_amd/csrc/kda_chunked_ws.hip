@@ -45,7 +45,8 @@ struct WsParams {
     void *o;
     const int32_t *cu_seqlens;
     const int32_t *order;
-    int T, H, DV, units, nslices;
+    const int32_t *state_idx;   // slot map of S0 / S_T rows (NULL: row = sequence)
+    int T, H, DV, units, nslices, pool;
 };
 
 namespace ws {
@@ -191,13 +192,16 @@ __device__ __forceinline__ void tri_pair(int pidx, int &r, int &i) {
 
 // Exact A and P for one 32-token chunk, entry by entry: A_ri = beta_r sum_c
 // k_rc k_ic 2^(G_rc - G_ic) (i < r), P_ri = sum_c q_rc k_ic 2^(G_rc - G_ic)
-// (i <= r), G the inclusive cumulative decay in log2 units.  Channels are
+// (i <= r), G the inclusive cumulative decay in log2 units.  The gate of
+// (row r, channel c) is bg[r * gstride + c * gch]: gch = 0 for a gate shared
+// by the channels of a head.  Channels are
 // staged 32 at a time in the producer's private LDS region; lane l owns
 // pairs l, l+64, ... of the 528 lower pairs.  Writes A^T (fp32, private) and
 // P (bf16, slot).  Kept out of line: it runs only for chunks with extreme
 // decay, and its registers stay out of the hot path's budget.
 template <int DK>
 __device__ __attribute__((noinline)) void exact_ap(int lane, int cl, uint32_t tokk,
+                                                   uint32_t gstride, uint32_t gch,
                                                    const bf16_t *bg, const bf16_t *bk,
                                                    const bf16_t *bq, unsigned char *priv,
                                                    float *pAt, bf16_t *sP, const float *pBeta)
@@ -227,7 +231,7 @@ __device__ __attribute__((noinline)) void exact_ap(int lane, int cl, uint32_t to
                 for (int e = 0; e < CPL; ++e) {
                     const int cq = CPL * (lane - qd * LPQ) + e;
                     const int c = QCH * qd + cq;
-                    const uint32_t g1 = (uint32_t)(bg[rr_ * tokk + c].x & m16);
+                    const uint32_t g1 = (uint32_t)(bg[rr_ * gstride + c * gch].x & m16);
                     bf16_t k1, q1;
                     k1.x = bk[rr_ * tokk + c].x & m16;
                     q1.x = bq[rr_ * tokk + c].x & m16;
@@ -275,7 +279,7 @@ __device__ __attribute__((noinline)) void exact_ap(int lane, int cl, uint32_t to
     }
 }
 
-template <int DK, int NSTRIP>
+template <int DK, int NSTRIP, int GATE>
 __global__ __launch_bounds__(512, 1) void chunked_ws_kernel(WsParams p)
 {
     using namespace ws;
@@ -314,6 +318,7 @@ __global__ __launch_bounds__(512, 1) void chunked_ws_kernel(WsParams p)
     }
     const int nchunks = (int)((len + C - 1) / C);
     const int col0 = slice * DVS;
+    const long strow = state_row(p.state_idx, p.pool, seq);
 
     const int tid = threadIdx.x;
     // the wave index is uniform across a wave; say so, so that everything
@@ -339,8 +344,8 @@ __global__ __launch_bounds__(512, 1) void chunked_ws_kernel(WsParams p)
         for (int s = 0; s < NSTRIP; ++s)
 #pragma unroll
             for (int tt = 0; tt < NKT; ++tt) S[s][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (p.S0) {
-            const float *s0 = p.S0 + ((size_t)seq * H + head) * DK * DV + col0;
+        if (p.S0 && strow >= 0) {
+            const float *s0 = p.S0 + ((size_t)strow * H + head) * DK * DV + col0;
 #pragma unroll
             for (int s = 0; s < NSTRIP; ++s) {
                 const uint32_t co = 16 * (w + 4 * s) + mr;
@@ -533,8 +538,8 @@ __global__ __launch_bounds__(512, 1) void chunked_ws_kernel(WsParams p)
                 __hip_atomic_fetch_add(&s_freed[slot], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         }
 
-        if (p.S_T) {
-            float *st = p.S_T + ((size_t)seq * H + head) * DK * DV + col0;
+        if (p.S_T && strow >= 0) {
+            float *st = p.S_T + ((size_t)strow * H + head) * DK * DV + col0;
 #pragma unroll
             for (int s = 0; s < NSTRIP; ++s) {
                 const uint32_t co = 16 * (w + 4 * s) + mr;
@@ -562,8 +567,9 @@ __global__ __launch_bounds__(512, 1) void chunked_ws_kernel(WsParams p)
     // 8-byte load per row and tensor), and beta of row `lane`.  Rows past the
     // chunk end read row 0 (always in bounds) and are masked where used.
     // A producer requests its next chunk's g and k while it still finishes
-    // the current one, which hides their latency.
-    uint32_t gx[8][NCL / 2], kx[8][NCL / 2], bx;
+    // the current one, which hides their latency.  A per-head gate (gh) is
+    // one value per row, laid out like beta; without a gate nothing is read.
+    uint32_t gx[8][NCL / 2], gh[8], kx[8][NCL / 2], bx;
     auto load_gk = [&](int n) {
         const int lane = tid & 63, cg = lane & 15, rg = lane >> 4;
         const int c0 = NCL * cg, r0 = 8 * rg;
@@ -577,16 +583,22 @@ __global__ __launch_bounds__(512, 1) void chunked_ws_kernel(WsParams p)
         for (int i = 0; i < 8; ++i) {
             const uint32_t off = (r0 + i < cl) ? base_off + (uint32_t)i * tokk * 2u : (uint32_t)c0 * 2u;
             if constexpr (NCL == 8) {
-                const uint4 g4 = *reinterpret_cast<const uint4 *>(bg + off);
+                if constexpr (GATE == GATE_CHANNEL) {
+                    const uint4 g4 = *reinterpret_cast<const uint4 *>(bg + off);
+                    gx[i][0] = g4.x; gx[i][1] = g4.y; gx[i][2] = g4.z; gx[i][3] = g4.w;
+                }
                 const uint4 k4 = *reinterpret_cast<const uint4 *>(bk + off);
-                gx[i][0] = g4.x; gx[i][1] = g4.y; gx[i][2] = g4.z; gx[i][3] = g4.w;
                 kx[i][0] = k4.x; kx[i][1] = k4.y; kx[i][2] = k4.z; kx[i][3] = k4.w;
             } else {
-                const uint2 g2 = *reinterpret_cast<const uint2 *>(bg + off);
+                if constexpr (GATE == GATE_CHANNEL) {
+                    const uint2 g2 = *reinterpret_cast<const uint2 *>(bg + off);
+                    gx[i][0] = g2.x; gx[i][1] = g2.y;
+                }
                 const uint2 k2 = *reinterpret_cast<const uint2 *>(bk + off);
-                gx[i][0] = g2.x; gx[i][1] = g2.y;
                 kx[i][0] = k2.x; kx[i][1] = k2.y;
             }
+            if constexpr (GATE == GATE_HEAD)
+                gh[i] = (uint32_t)gg[tb + (size_t)(r0 + i < cl ? r0 + i : 0) * H].x;
         }
         const int rb = lane & (C - 1);
         bx = (uint32_t)gb[tb + (size_t)(rb < cl ? rb : cl - 1) * H].x;
@@ -628,13 +640,7 @@ __global__ __launch_bounds__(512, 1) void chunked_ws_kernel(WsParams p)
             }
         }
 
-        // ---- decay per key channel ---------------------------------------------
-        // alpha, and the products of alpha over this lane's 8 rows (tot);
-        // then, across the four row groups, the products over the groups
-        // before (pre) and after (post) this one, so that
-        //   E_r = pre * prod_{j <= r, j in group} alpha_j,
-        //   R_r = post * prod_{j > r, j in group} alpha_j,
-        //   gamma = pre * tot * post.
+        // ---- decay ---------------------------------------------------------------
         if (r0 + 8 > cl) {
             // rows past the chunk end: g = 0 (alpha = 1), k = q = 0
 #pragma unroll
@@ -642,61 +648,93 @@ __global__ __launch_bounds__(512, 1) void chunked_ws_kernel(WsParams p)
                 const uint32_t m = (r0 + i) < cl ? 0xffffffffu : 0u;
 #pragma unroll
                 for (int d = 0; d < NCL / 2; ++d) {
-                    gx[i][d] &= m;
+                    if constexpr (GATE == GATE_CHANNEL) gx[i][d] &= m;
                     kx[i][d] &= m;
                     qx[i][d] &= m;
                 }
+                if constexpr (GATE == GATE_HEAD) gh[i] &= m;
             }
         }
-        float al[8][NCL], tot[NCL];
+        // Decay factors.  Per key channel: alpha of each (row, channel) and the
+        // products over this lane's 8 rows (tot); for a per-head gate the same
+        // per row (alh, toth); none without a gate (alpha = 1).
+        float al[8][NCL], tot[NCL], alh[8], toth = 1.0f;
         // largest |k| bit pattern per bf16 half (monotonic in |k|)
         uint32_t kbits = 0;
+        if constexpr (GATE != GATE_NONE) {
 #pragma unroll
-        for (int e = 0; e < NCL; ++e) tot[e] = 1.0f;
+            for (int e = 0; e < NCL; ++e) tot[e] = 1.0f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
+            for (int i = 0; i < 8; ++i) {
+                if constexpr (GATE == GATE_HEAD) {
+                    alh[i] = __builtin_amdgcn_exp2f(bf_lo(gh[i]) * kLog2e);
+                    toth *= alh[i];
+                }
 #pragma unroll
-            for (int d = 0; d < NCL / 2; ++d) {
-                al[i][2 * d] = __builtin_amdgcn_exp2f(bf_lo(gx[i][d]) * kLog2e);
-                al[i][2 * d + 1] = __builtin_amdgcn_exp2f(bf_hi(gx[i][d]) * kLog2e);
-                tot[2 * d] *= al[i][2 * d];
-                tot[2 * d + 1] *= al[i][2 * d + 1];
-                kbits = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(
-                    __builtin_bit_cast(u16x2, kbits), __builtin_bit_cast(u16x2, kx[i][d] & 0x7fff7fffu)));
+                for (int d = 0; d < NCL / 2; ++d) {
+                    if constexpr (GATE == GATE_CHANNEL) {
+                        al[i][2 * d] = __builtin_amdgcn_exp2f(bf_lo(gx[i][d]) * kLog2e);
+                        al[i][2 * d + 1] = __builtin_amdgcn_exp2f(bf_hi(gx[i][d]) * kLog2e);
+                        tot[2 * d] *= al[i][2 * d];
+                        tot[2 * d + 1] *= al[i][2 * d + 1];
+                    }
+                    kbits = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(
+                        __builtin_bit_cast(u16x2, kbits), __builtin_bit_cast(u16x2, kx[i][d] & 0x7fff7fffu)));
+                }
             }
+        }
         // exclusive prefix / suffix products over the row groups (lanes 16
-        // apart), by three lane shifts each
-        float pre[NCL], post[NCL], gam[NCL];
-        {
+        // apart), by three lane shifts each, so that
+        //   E_r = pre * prod_{j <= r, j in group} alpha_j,
+        //   R_r = post * prod_{j > r, j in group} alpha_j,
+        //   gamma = pre * tot * post.
+        float pre[NCL], post[NCL], gam[NCL], preh = 1.0f, posth = 1.0f, gamh = 1.0f;
+        if constexpr (GATE != GATE_NONE) {
             const int up16 = (lane - 16) << 2, up32 = (lane - 32) << 2;
             const int dn16 = (lane + 16) << 2, dn32 = (lane + 32) << 2;
             auto shf = [](float x, int addr) {
                 return __int_as_float(__builtin_amdgcn_ds_bpermute(addr, __float_as_int(x)));
             };
-#pragma unroll
-            for (int e = 0; e < NCL; ++e) {
-                // every lane takes part in each shift (all lanes active), and
-                // lanes without a group on that side select 1 afterwards
+            // every lane takes part in each shift (all lanes active), and
+            // lanes without a group on that side select 1 afterwards
+            auto scan = [&](float tv, float &pr, float &po) {
                 float t;
-                t = shf(tot[e], up16);
+                t = shf(tv, up16);
                 const float a = rg >= 1 ? t : 1.0f;
                 t = shf(a, up16);
                 const float b = a * (rg >= 1 ? t : 1.0f);
                 t = shf(b, up32);
-                pre[e] = b * (rg >= 2 ? t : 1.0f);
-                t = shf(tot[e], dn16);
+                pr = b * (rg >= 2 ? t : 1.0f);
+                t = shf(tv, dn16);
                 const float a2 = rg <= 2 ? t : 1.0f;
                 t = shf(a2, dn16);
                 const float b2 = a2 * (rg <= 2 ? t : 1.0f);
                 t = shf(b2, dn32);
-                post[e] = b2 * (rg <= 1 ? t : 1.0f);
-                gam[e] = pre[e] * tot[e] * post[e];
+                po = b2 * (rg <= 1 ? t : 1.0f);
+            };
+            if constexpr (GATE == GATE_CHANNEL) {
+#pragma unroll
+                for (int e = 0; e < NCL; ++e) {
+                    scan(tot[e], pre[e], post[e]);
+                    gam[e] = pre[e] * tot[e] * post[e];
+                }
+            } else {
+                scan(toth, preh, posth);
+                gamh = preh * toth * posth;
             }
         }
-        // K_dn stays below 2^116 when gamma >= 2^-100 and |k| <= 2^16
-        bool ok = (kbits & 0xffffu) <= 0x4780u && (kbits >> 16) <= 0x4780u;   // 0x4780: 2^16
+        // K_dn stays below 2^116 when gamma >= 2^-100 and |k| <= 2^16; with
+        // no gate K_dn = K and the fast path always holds
+        bool ok = true;
+        if constexpr (GATE != GATE_NONE) {
+            ok = (kbits & 0xffffu) <= 0x4780u && (kbits >> 16) <= 0x4780u;   // 0x4780: 2^16
+            if constexpr (GATE == GATE_CHANNEL) {
 #pragma unroll
-        for (int e = 0; e < NCL; ++e) ok = ok && (gam[e] >= 7.888609052210118e-31f);
+                for (int e = 0; e < NCL; ++e) ok = ok && (gam[e] >= 7.888609052210118e-31f);
+            } else {
+                ok = ok && (gamh >= 7.888609052210118e-31f);
+            }
+        }
 
         // wait for the slot: the consumers are done with chunk n - NSLOT
         if (n >= NSLOT) {
@@ -712,24 +750,38 @@ __global__ __launch_bounds__(512, 1) void chunked_ws_kernel(WsParams p)
         float *sG = reinterpret_cast<float *>(sb + L::GM);
         if (rg == 0) {
 #pragma unroll
-            for (int e = 0; e < NCL; e += 4)
-                *reinterpret_cast<float4 *>(&sG[c0 + e]) = make_float4(gam[e], gam[e + 1], gam[e + 2], gam[e + 3]);
+            for (int e = 0; e < NCL; e += 4) {
+                float4 g4;
+                if constexpr (GATE == GATE_CHANNEL) g4 = make_float4(gam[e], gam[e + 1], gam[e + 2], gam[e + 3]);
+                else g4 = make_float4(gamh, gamh, gamh, gamh);   // 1 without a gate
+                *reinterpret_cast<float4 *>(&sG[c0 + e]) = g4;
+            }
         }
 
         // forward: -K_up, Q_up rows
         {
-            float E[NCL];
+            float E[NCL], Eh = preh;
 #pragma unroll
             for (int e = 0; e < NCL; ++e) E[e] = pre[e];
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 uint32_t ku[NCL / 2], qu[NCL / 2];
+                if constexpr (GATE == GATE_HEAD) Eh *= alh[i];
 #pragma unroll
                 for (int d = 0; d < NCL / 2; ++d) {
-                    E[2 * d] *= al[i][2 * d];
-                    E[2 * d + 1] *= al[i][2 * d + 1];
-                    ku[d] = pack2(-bf_lo(kx[i][d]) * E[2 * d], -bf_hi(kx[i][d]) * E[2 * d + 1]);
-                    qu[d] = pack2(bf_lo(qx[i][d]) * E[2 * d], bf_hi(qx[i][d]) * E[2 * d + 1]);
+                    if constexpr (GATE == GATE_CHANNEL) {
+                        E[2 * d] *= al[i][2 * d];
+                        E[2 * d + 1] *= al[i][2 * d + 1];
+                        ku[d] = pack2(-bf_lo(kx[i][d]) * E[2 * d], -bf_hi(kx[i][d]) * E[2 * d + 1]);
+                        qu[d] = pack2(bf_lo(qx[i][d]) * E[2 * d], bf_hi(qx[i][d]) * E[2 * d + 1]);
+                    } else if constexpr (GATE == GATE_HEAD) {
+                        ku[d] = pack2(-bf_lo(kx[i][d]) * Eh, -bf_hi(kx[i][d]) * Eh);
+                        qu[d] = pack2(bf_lo(qx[i][d]) * Eh, bf_hi(qx[i][d]) * Eh);
+                    } else {
+                        // E = 1: the inputs themselves, K negated by its sign bits
+                        ku[d] = kx[i][d] ^ 0x80008000u;
+                        qu[d] = qx[i][d];
+                    }
                 }
                 const int o = idxK<DK>(r0 + i, c0);
                 if constexpr (NCL == 8) {
@@ -742,24 +794,32 @@ __global__ __launch_bounds__(512, 1) void chunked_ws_kernel(WsParams p)
             }
         }
         // reverse: K_right (rows of K_right^T, 8 tokens per channel) and K_dn rows
-        {
-            float R[NCL], invg[NCL], kr[8][NCL];
+        if constexpr (GATE != GATE_NONE) {
+            float R[NCL], invg[NCL], kr[8][NCL], Rh = posth;
+            const float invgh = __builtin_amdgcn_rcpf(gamh);
 #pragma unroll
             for (int e = 0; e < NCL; ++e) {
                 R[e] = post[e];
-                invg[e] = __builtin_amdgcn_rcpf(gam[e]);
+                if constexpr (GATE == GATE_CHANNEL) invg[e] = __builtin_amdgcn_rcpf(gam[e]);
             }
 #pragma unroll
             for (int i = 7; i >= 0; --i) {
                 uint32_t kd[NCL / 2];
 #pragma unroll
                 for (int d = 0; d < NCL / 2; ++d) {
-                    kr[i][2 * d] = bf_lo(kx[i][d]) * R[2 * d];
-                    kr[i][2 * d + 1] = bf_hi(kx[i][d]) * R[2 * d + 1];
-                    R[2 * d] *= al[i][2 * d];
-                    R[2 * d + 1] *= al[i][2 * d + 1];
-                    kd[d] = pack2(kr[i][2 * d] * invg[2 * d], kr[i][2 * d + 1] * invg[2 * d + 1]);
+                    if constexpr (GATE == GATE_CHANNEL) {
+                        kr[i][2 * d] = bf_lo(kx[i][d]) * R[2 * d];
+                        kr[i][2 * d + 1] = bf_hi(kx[i][d]) * R[2 * d + 1];
+                        R[2 * d] *= al[i][2 * d];
+                        R[2 * d + 1] *= al[i][2 * d + 1];
+                        kd[d] = pack2(kr[i][2 * d] * invg[2 * d], kr[i][2 * d + 1] * invg[2 * d + 1]);
+                    } else {
+                        kr[i][2 * d] = bf_lo(kx[i][d]) * Rh;
+                        kr[i][2 * d + 1] = bf_hi(kx[i][d]) * Rh;
+                        kd[d] = pack2(kr[i][2 * d] * invgh, kr[i][2 * d + 1] * invgh);
+                    }
                 }
+                if constexpr (GATE == GATE_HEAD) Rh *= alh[i];
                 const int o = idxK<DK>(r0 + i, c0);
                 if constexpr (NCL == 8)
                     *reinterpret_cast<uint4 *>(&pKD[o]) = make_uint4(kd[0], kd[1], kd[2], kd[3]);
@@ -772,6 +832,28 @@ __global__ __launch_bounds__(512, 1) void chunked_ws_kernel(WsParams p)
                 *reinterpret_cast<uint4 *>(&sKRt[idxT(ch, rg)]) =
                     make_uint4(pack2(kr[0][e], kr[1][e]), pack2(kr[2][e], kr[3][e]),
                                pack2(kr[4][e], kr[5][e]), pack2(kr[6][e], kr[7][e]));
+            }
+        } else {
+            // R = gamma = 1: K_dn rows are K's rows, and K_right^T takes the
+            // bf16 halves of pairs of rows
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int o = idxK<DK>(r0 + i, c0);
+                if constexpr (NCL == 8)
+                    *reinterpret_cast<uint4 *>(&pKD[o]) = make_uint4(kx[i][0], kx[i][1], kx[i][2], kx[i][3]);
+                else
+                    *reinterpret_cast<uint2 *>(&pKD[o]) = make_uint2(kx[i][0], kx[i][1]);
+            }
+#pragma unroll
+            for (int e = 0; e < NCL; ++e) {
+                const int d = e >> 1;
+                // channel e of rows a (low half) and b (high half)
+                auto pr = [&](int a, int b) {
+                    return (e & 1) ? ((kx[a][d] >> 16) | (kx[b][d] & 0xffff0000u))
+                                   : ((kx[a][d] & 0xffffu) | (kx[b][d] << 16));
+                };
+                *reinterpret_cast<uint4 *>(&sKRt[idxT(c0 + e, rg)]) =
+                    make_uint4(pr(0, 1), pr(2, 3), pr(4, 5), pr(6, 7));
             }
         }
         const bool fast = __builtin_amdgcn_ballot_w64(!ok) == 0;
@@ -828,7 +910,10 @@ __global__ __launch_bounds__(512, 1) void chunked_ws_kernel(WsParams p)
             *reinterpret_cast<uint2 *>(&sP[idx4(mr, 16 + 4 * jg)]) = make_uint2(0u, 0u);
         } else {
             // exact path for chunks whose decay leaves the range of K_dn
-            exact_ap<DK>(lane, cl, tokk, bg, bk, bq, priv, pAt, sP, pBeta);
+            if constexpr (GATE == GATE_CHANNEL)
+                exact_ap<DK>(lane, cl, tokk, tokk, 1u, bg, bk, bq, priv, pAt, sP, pBeta);
+            else if constexpr (GATE == GATE_HEAD)
+                exact_ap<DK>(lane, cl, tokk, (uint32_t)H, 0u, gg + tb, bk, bq, priv, pAt, sP, pBeta);
         }
         __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
 
@@ -923,17 +1008,26 @@ __global__ __launch_bounds__(512, 1) void chunked_ws_kernel(WsParams p)
     }
 }
 
-template <int DK, int NSTRIP>
+template <int DK, int NSTRIP, int GATE>
 static hipError_t launch_ws(const WsParams &p, hipStream_t stream)
 {
     const int groups = (p.units + 7) / 8;
     const dim3 grid(groups * 8 * p.nslices);
-    hipLaunchKernelGGL((chunked_ws_kernel<DK, NSTRIP>), grid, dim3(512), 0, stream, p);
+    hipLaunchKernelGGL((chunked_ws_kernel<DK, NSTRIP, GATE>), grid, dim3(512), 0, stream, p);
     return hipGetLastError();
 }
 
+template <int DK, int NSTRIP>
+static hipError_t launch_ws_gate(const WsParams &p, int gate, hipStream_t stream)
+{
+    if (gate == GATE_HEAD) return launch_ws<DK, NSTRIP, GATE_HEAD>(p, stream);
+    if (gate == GATE_NONE) return launch_ws<DK, NSTRIP, GATE_NONE>(p, stream);
+    return launch_ws<DK, NSTRIP, GATE_CHANNEL>(p, stream);
+}
+
 hipError_t chunked_ws_launch(const void *q, const void *k, const void *v, const void *g,
-                             const void *beta, const float *S0, float *S_T, void *o,
+                             const void *beta, int gate, const float *S0, float *S_T,
+                             const int32_t *state_idx, int pool, void *o,
                              const int32_t *cu_seqlens, const int32_t *order, int nseq, int T,
                              int H, int dk, int dv, int slice_width, hipStream_t stream)
 {
@@ -942,12 +1036,15 @@ hipError_t chunked_ws_launch(const void *q, const void *k, const void *v, const 
     p.S0 = S0; p.S_T = S_T; p.o = o;
     p.cu_seqlens = cu_seqlens;
     p.order = order;
+    p.state_idx = state_idx;
+    p.pool = pool;
     p.T = T; p.H = H; p.DV = dv;
     p.units = nseq * H;
     p.nslices = dv / slice_width;
     const int nstrip = slice_width / 64;
-    if (dk == 128) return nstrip == 2 ? launch_ws<128, 2>(p, stream) : launch_ws<128, 1>(p, stream);
-    return nstrip == 2 ? launch_ws<64, 2>(p, stream) : launch_ws<64, 1>(p, stream);
+    if (dk == 128)
+        return nstrip == 2 ? launch_ws_gate<128, 2>(p, gate, stream) : launch_ws_gate<128, 1>(p, gate, stream);
+    return nstrip == 2 ? launch_ws_gate<64, 2>(p, gate, stream) : launch_ws_gate<64, 1>(p, gate, stream);
 }
 
 }  // namespace kda

@@ -20,6 +20,11 @@
 // already being read while the current one is reduced and written.  Column
 // sums over rows go through LDS.  State traffic uses non-temporal loads and
 // stores: every byte is touched once per step, so caching it only costs.
+//
+// The gate is one value per key channel (alpha above), one per (n, h) shared
+// by the channels, or absent (alpha = 1).  With a slot map the state of
+// sequence n is row state_idx[n] of a pool; a slot outside the pool starts
+// from zeros and is not written.
 #include "kda_device.h"
 
 namespace kda {
@@ -30,7 +35,8 @@ template <int DK, int DV, typename T>
 __global__ __launch_bounds__(DEC_THREADS) void decode_step_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const T *__restrict__ log_alpha, const T *__restrict__ beta,
-    float *__restrict__ S_cache, T *__restrict__ o, int units)
+    float *__restrict__ S_cache, T *__restrict__ o, int units, int H, int gate,
+    const int32_t *__restrict__ state_idx, int pool)
 {
     constexpr int NT = DEC_THREADS;
     constexpr int CG = DV / 4;     // 16-byte column groups per row
@@ -47,9 +53,21 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_step_kernel(
     __shared__ __attribute__((aligned(16))) float s_u[DV];
     __shared__ float s_kq;
 
+    // state row of a unit (n, h): n's slot, or -1 for no state
+    auto unit_row = [&](int unit) -> long {
+        const int n = unit / H;
+        const long r = state_row(state_idx, pool, n);
+        return r < 0 ? -1L : r * H + (unit - n * H);
+    };
     f4v cur[RPT], nxt[RPT];
     auto load_state = [&](int unit, f4v (&r)[RPT]) {
-        const f4v *Su = reinterpret_cast<const f4v *>(S_cache + (size_t)unit * DK * DV);
+        const long row = unit_row(unit);
+        if (row < 0) {
+#pragma unroll
+            for (int i = 0; i < RPT; ++i) r[i] = f4v{0.f, 0.f, 0.f, 0.f};
+            return;
+        }
+        const f4v *Su = reinterpret_cast<const f4v *>(S_cache + (size_t)row * DK * DV);
 #pragma unroll
         for (int i = 0; i < RPT; ++i) r[i] = __builtin_nontemporal_load(Su + (rg + i * RG) * CG + cg);
     };
@@ -62,7 +80,9 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_step_kernel(
 
         if (t < DK) {
             const size_t idx = (size_t)unit * DK + t;
-            s_a[t] = expf(load_elem(log_alpha + idx));
+            s_a[t] = gate == GATE_CHANNEL ? expf(load_elem(log_alpha + idx))
+                   : gate == GATE_HEAD    ? expf(load_elem(log_alpha + unit))
+                                          : 1.0f;
             s_k[t] = load_elem(k + idx);
             s_q[t] = load_elem(q + idx);
         }
@@ -103,11 +123,14 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_step_kernel(
         __syncthreads();
 
         const f4v u4 = *reinterpret_cast<const f4v *>(&s_u[4 * cg]);
-        f4v *Sw = reinterpret_cast<f4v *>(S_cache + (size_t)unit * DK * DV);
+        const long srow_ = unit_row(unit);
+        if (srow_ >= 0) {
+            f4v *Sw = reinterpret_cast<f4v *>(S_cache + (size_t)srow_ * DK * DV);
 #pragma unroll
-        for (int i = 0; i < RPT; ++i) {
-            const int row = rg + i * RG;
-            __builtin_nontemporal_store(cur[i] + s_k[row] * u4, Sw + row * CG + cg);
+            for (int i = 0; i < RPT; ++i) {
+                const int row = rg + i * RG;
+                __builtin_nontemporal_store(cur[i] + s_k[row] * u4, Sw + row * CG + cg);
+            }
         }
 #pragma unroll
         for (int i = 0; i < RPT; ++i) cur[i] = nxt[i];
@@ -120,36 +143,46 @@ int cu_count();
 template <int DK, int DV, typename T>
 static hipError_t launch_decode(const void *q, const void *k, const void *v,
                                 const void *log_alpha, const void *beta, float *S,
-                                void *o, int units, hipStream_t stream)
+                                void *o, int units, int H, int gate, const int32_t *state_idx,
+                                int pool, hipStream_t stream)
 {
     // four workgroups per CU, each walking units with the grid stride
     const int grid = units < 4 * cu_count() ? units : 4 * cu_count();
     hipLaunchKernelGGL((decode_step_kernel<DK, DV, T>), dim3(grid), dim3(DEC_THREADS), 0, stream,
                        (const T *)q, (const T *)k, (const T *)v, (const T *)log_alpha,
-                       (const T *)beta, S, (T *)o, units);
+                       (const T *)beta, S, (T *)o, units, H, gate, state_idx, pool);
     return hipGetLastError();
 }
 
 template <typename T>
 static hipError_t dispatch_decode_t(const void *q, const void *k, const void *v,
                                     const void *log_alpha, const void *beta, float *S,
-                                    void *o, int units, int dk, int dv, hipStream_t stream)
+                                    void *o, int units, int H, int gate,
+                                    const int32_t *state_idx, int pool, int dk, int dv,
+                                    hipStream_t stream)
 {
-    if (dk == 128 && dv == 128) return launch_decode<128, 128, T>(q, k, v, log_alpha, beta, S, o, units, stream);
-    if (dk == 128 && dv == 64) return launch_decode<128, 64, T>(q, k, v, log_alpha, beta, S, o, units, stream);
-    if (dk == 64 && dv == 128) return launch_decode<64, 128, T>(q, k, v, log_alpha, beta, S, o, units, stream);
-    return launch_decode<64, 64, T>(q, k, v, log_alpha, beta, S, o, units, stream);
+#define KDA_DEC(DK_, DV_) \
+    launch_decode<DK_, DV_, T>(q, k, v, log_alpha, beta, S, o, units, H, gate, state_idx, pool, stream)
+    if (dk == 128 && dv == 128) return KDA_DEC(128, 128);
+    if (dk == 128 && dv == 64) return KDA_DEC(128, 64);
+    if (dk == 64 && dv == 128) return KDA_DEC(64, 128);
+    return KDA_DEC(64, 64);
+#undef KDA_DEC
 }
 
 // Host-side launcher used by the C ABI (sizes already validated).
 hipError_t decode_step_launch(const void *q, const void *k, const void *v,
-                              const void *log_alpha, const void *beta, float *S,
-                              void *o, int units, int dk, int dv, bool bf16,
-                              hipStream_t stream)
+                              const void *log_alpha, const void *beta, int gate, float *S,
+                              const int32_t *state_idx, int pool, void *o, int N, int H,
+                              int dk, int dv, bool bf16, hipStream_t stream)
 {
+    const int units = N * H;
     if (units == 0) return hipSuccess;
-    if (bf16) return dispatch_decode_t<bf16_t>(q, k, v, log_alpha, beta, S, o, units, dk, dv, stream);
-    return dispatch_decode_t<float>(q, k, v, log_alpha, beta, S, o, units, dk, dv, stream);
+    if (bf16)
+        return dispatch_decode_t<bf16_t>(q, k, v, log_alpha, beta, S, o, units, H, gate, state_idx,
+                                         pool, dk, dv, stream);
+    return dispatch_decode_t<float>(q, k, v, log_alpha, beta, S, o, units, H, gate, state_idx, pool,
+                                    dk, dv, stream);
 }
 
 }  // namespace kda

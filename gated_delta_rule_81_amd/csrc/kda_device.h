@@ -35,4 +35,18 @@ __device__ __forceinline__ float load_elem(const bf16_t *p) { return to_f32(*p);
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// Layout of the forget gate log_alpha (values match kda_gate in kda.h):
+// one value per key channel, one per (token, head) shared by every key
+// channel, or none (alpha = 1).
+enum : int { GATE_CHANNEL = 0, GATE_HEAD = 1, GATE_NONE = 2 };
+
+// Row of the state arrays that a sequence (or decode slot) reads and writes:
+// the sequence index itself, or state_idx[seq] when a slot map is given;
+// -1 (start from zeros, write nothing) for an index outside [0, pool).
+__device__ __forceinline__ long state_row(const int32_t *state_idx, int pool, int seq) {
+    if (!state_idx) return seq;
+    const int r = state_idx[seq];
+    return (r >= 0 && r < pool) ? (long)r : -1L;
+}
+
 }  // namespace kda

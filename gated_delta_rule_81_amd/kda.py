@@ -18,6 +18,8 @@ LIB_PATH = os.path.join(_HERE, "libkda.so")
 
 KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_HIP = 0, 1, 2, 3
 KDA_F32, KDA_BF16 = 0, 1
+KDA_GATE_CHANNEL, KDA_GATE_HEAD, KDA_GATE_NONE = 0, 1, 2
+_GATES = {"channel": KDA_GATE_CHANNEL, "head": KDA_GATE_HEAD, "none": KDA_GATE_NONE}
 
 _vp = ctypes.c_void_p
 _lib = None
@@ -50,6 +52,15 @@ def lib() -> ctypes.CDLL:
     L.kda_decode_step.restype = ctypes.c_int
     L.kda_decode_step.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, ctypes.c_int,
                                   ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp, _vp]
+    L.kda_fwd_chunked_ex.restype = ctypes.c_int
+    L.kda_fwd_chunked_ex.argtypes = [_vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp,
+                                     ctypes.c_int, _vp, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                     ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp,
+                                     _vp, ctypes.c_size_t, _vp]
+    L.kda_decode_step_ex.restype = ctypes.c_int
+    L.kda_decode_step_ex.argtypes = [_vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp, _vp,
+                                     ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                     ctypes.c_int, ctypes.c_int, _vp, _vp]
     _lib = L
     return L
 
@@ -89,78 +100,145 @@ def workspace_bytes(B: int, T: int, H: int, dk: int, dv: int, num_seqs: int) -> 
     return int(lib().kda_fwd_workspace_bytes(B, T, H, dk, dv, num_seqs))
 
 
+def _gate_code(gate: str) -> int:
+    if gate not in _GATES:
+        raise ValueError(f"gate must be one of {sorted(_GATES)}, got {gate!r}")
+    return _GATES[gate]
+
+
+def _check_gate(log_alpha, gate: str, shape_k, dev, dt):
+    """log_alpha's expected shape: per key channel, per (token, head), or unused."""
+    code = _gate_code(gate)
+    if code == KDA_GATE_NONE:
+        return code
+    if log_alpha is None:
+        raise ValueError(f"log_alpha is required for gate={gate!r}")
+    _check(log_alpha, "log_alpha", dev, dt)
+    want = tuple(shape_k) if code == KDA_GATE_CHANNEL else tuple(shape_k[:-1])
+    if tuple(log_alpha.shape) != want:
+        raise ValueError(f"log_alpha must have shape {want} for gate={gate!r}")
+    return code
+
+
 def fwd_chunked(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, *,
                 output_final_state: bool = True, o=None, S_T=None,
-                workspace=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
-    """Chunkwise KDA forward (kda_fwd_chunked).
+                workspace=None, gate: str = "channel", state_idx=None,
+                pool_size: Optional[int] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Chunkwise KDA forward (kda_fwd_chunked / kda_fwd_chunked_ex).
 
-    q, k, log_alpha: (B, T, H, dk); v: (B, T, H, dv); beta: (B, T, H), all of
-    one dtype (bf16 or fp32) on one GPU.  S0: (N, H, dk, dv) fp32 or None.
-    cu_seqlens: int32 (N+1,) on the same GPU (requires B == 1) or None.
+    q, k: (B, T, H, dk); v: (B, T, H, dv); beta: (B, T, H), all of one dtype
+    (bf16 or fp32) on one GPU.  log_alpha: (B, T, H, dk) for gate="channel",
+    (B, T, H) for gate="head", ignored (may be None) for gate="none".
+    S0: (N, H, dk, dv) fp32 or None.  cu_seqlens: int32 (N+1,) on the same GPU
+    (requires B == 1) or None.  With state_idx (int32 (N,), on the GPU), S0 and
+    S_T are pools of pool_size rows (default: S0's or S_T's first dimension)
+    and sequence s reads and writes row state_idx[s]; S_T is then never
+    allocated here (pass S_T=S0 to continue a pool in place).
     Returns (o, S_T); S_T is None when output_final_state is False.
     """
+    _gate_code(gate)
     dev = q.device
     dt = q.dtype
-    for name, t in (("q", q), ("k", k), ("v", v), ("log_alpha", log_alpha), ("beta", beta)):
+    for name, t in (("q", q), ("k", k), ("v", v), ("beta", beta)):
         _check(t, name, dev, dt)
     B, T, H, dk = q.shape
     dv = v.shape[-1]
-    if k.shape != q.shape or log_alpha.shape != q.shape or v.shape != (B, T, H, dv) \
-            or beta.shape != (B, T, H):
+    gcode = _check_gate(log_alpha, gate, q.shape, dev, dt)
+    if k.shape != q.shape or v.shape != (B, T, H, dv) or beta.shape != (B, T, H):
         raise ValueError("inconsistent input shapes")
     if cu_seqlens is not None:
         _check(cu_seqlens, "cu_seqlens", dev, torch.int32)
         N = cu_seqlens.shape[0] - 1
     else:
         N = B
+    if state_idx is not None:
+        _check(state_idx, "state_idx", dev, torch.int32)
+        if state_idx.shape != (N,):
+            raise ValueError(f"state_idx must have shape {(N,)}")
+        if pool_size is None:
+            ref = S0 if S0 is not None else S_T
+            pool_size = ref.shape[0] if ref is not None else 0
+        rows = pool_size
+    else:
+        rows = N
     if S0 is not None:
         _check(S0, "S0", dev, torch.float32)
-        if S0.shape != (N, H, dk, dv):
-            raise ValueError(f"S0 must have shape {(N, H, dk, dv)}")
+        if S0.shape != (rows, H, dk, dv):
+            raise ValueError(f"S0 must have shape {(rows, H, dk, dv)}")
     if o is None:
         o = torch.empty((B, T, H, dv), dtype=dt, device=dev)
     else:
         _check(o, "o", dev, dt)
-    if output_final_state and S_T is None:
+    if output_final_state and S_T is None and state_idx is None:
         S_T = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
     if S_T is not None:
         _check(S_T, "S_T", dev, torch.float32)
+        if S_T.shape != (rows, H, dk, dv):
+            raise ValueError(f"S_T must have shape {(rows, H, dk, dv)}")
     need = workspace_bytes(B, T, H, dk, dv, N) if cu_seqlens is not None else 0
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    st = lib().kda_fwd_chunked(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
-                               _ptr(S0), _ptr(cu_seqlens), N, B, T, H, dk, dv,
-                               _dtype_code(q), _ptr(o), _ptr(S_T), _ptr(workspace), ws_bytes,
-                               _stream(dev))
+    ga = None if gcode == KDA_GATE_NONE else log_alpha
+    if gcode == KDA_GATE_CHANNEL and state_idx is None:
+        st = lib().kda_fwd_chunked(_ptr(q), _ptr(k), _ptr(v), _ptr(ga), _ptr(beta),
+                                   _ptr(S0), _ptr(cu_seqlens), N, B, T, H, dk, dv,
+                                   _dtype_code(q), _ptr(o), _ptr(S_T), _ptr(workspace), ws_bytes,
+                                   _stream(dev))
+        where = "kda_fwd_chunked"
+    else:
+        st = lib().kda_fwd_chunked_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(ga), _ptr(beta), gcode,
+                                      _ptr(S0), _ptr(S_T), _ptr(state_idx), int(rows),
+                                      _ptr(cu_seqlens), N, B, T, H, dk, dv, _dtype_code(q),
+                                      _ptr(o), _ptr(workspace), ws_bytes, _stream(dev))
+        where = "kda_fwd_chunked_ex"
     if st != KDA_OK:
-        raise KdaError(st, "kda_fwd_chunked")
+        raise KdaError(st, where)
     return o, S_T
 
 
-def decode_step(q, k, v, log_alpha, beta, S_cache, *, o=None) -> torch.Tensor:
-    """One-token KDA update of S_cache in place (kda_decode_step); returns o.
+def decode_step(q, k, v, log_alpha, beta, S_cache, *, o=None, gate: str = "channel",
+                state_idx=None) -> torch.Tensor:
+    """One-token KDA update of S_cache in place (kda_decode_step / _ex); returns o.
 
-    q, k, log_alpha: (N, H, dk); v: (N, H, dv); beta: (N, H) of one dtype;
-    S_cache: (N, H, dk, dv) fp32.
+    q, k: (N, H, dk); v: (N, H, dv); beta: (N, H) of one dtype; log_alpha:
+    (N, H, dk) for gate="channel", (N, H) for gate="head", ignored for
+    gate="none".  S_cache: (N, H, dk, dv) fp32, or with state_idx (int32 (N,)
+    on the GPU) a pool (P, H, dk, dv) whose row state_idx[n] sequence n updates.
     """
+    _gate_code(gate)
     dev = q.device
     dt = q.dtype
-    for name, t in (("q", q), ("k", k), ("v", v), ("log_alpha", log_alpha), ("beta", beta)):
+    for name, t in (("q", q), ("k", k), ("v", v), ("beta", beta)):
         _check(t, name, dev, dt)
     _check(S_cache, "S_cache", dev, torch.float32)
     N, H, dk = q.shape
     dv = v.shape[-1]
-    if k.shape != q.shape or log_alpha.shape != q.shape or v.shape != (N, H, dv) \
-            or beta.shape != (N, H) or S_cache.shape != (N, H, dk, dv):
+    gcode = _check_gate(log_alpha, gate, q.shape, dev, dt)
+    rows = N
+    if state_idx is not None:
+        _check(state_idx, "state_idx", dev, torch.int32)
+        if state_idx.shape != (N,):
+            raise ValueError(f"state_idx must have shape {(N,)}")
+        rows = S_cache.shape[0]
+    if k.shape != q.shape or v.shape != (N, H, dv) or beta.shape != (N, H) \
+            or S_cache.shape != (rows, H, dk, dv):
         raise ValueError("inconsistent input shapes")
     if o is None:
         o = torch.empty((N, H, dv), dtype=dt, device=dev)
     else:
         _check(o, "o", dev, dt)
-    st = lib().kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
-                               _ptr(S_cache), N, H, dk, dv, _dtype_code(q), _ptr(o),
-                               _stream(dev))
+    ga = None if gcode == KDA_GATE_NONE else log_alpha
+    if gcode == KDA_GATE_CHANNEL and state_idx is None:
+        st = lib().kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(ga), _ptr(beta),
+                                   _ptr(S_cache), N, H, dk, dv, _dtype_code(q), _ptr(o),
+                                   _stream(dev))
+        where = "kda_decode_step"
+    else:
+        st = lib().kda_decode_step_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(ga), _ptr(beta), gcode,
+                                      _ptr(S_cache), _ptr(state_idx), int(rows), N, H, dk, dv,
+                                      _dtype_code(q), _ptr(o), _stream(dev))
+        where = "kda_decode_step_ex"
     if st != KDA_OK:
-        raise KdaError(st, "kda_decode_step")
+        raise KdaError(st, where)
     return o

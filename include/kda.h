@@ -19,7 +19,8 @@
  * Two entry points: a chunkwise forward over whole sequences (the chunkwise
  * form named in the daily.dev summary; training and prefill) and a one-token
  * decode step that rewrites a state cache in place (the recurrent form; the
- * per-token work is constant, "The fourth layer remembers").
+ * per-token work is constant, "The fourth layer remembers").  Their *_ex
+ * forms add the per-head and absent gates and slot-indexed state pools.
  *
  * Conventions shared by every entry point
  *   - All pointers are DEVICE pointers (HIP global memory) unless stated.
@@ -61,6 +62,24 @@ typedef enum {
     KDA_BF16 = 1
 } kda_dtype;
 
+/* Layout of the forget gate log_alpha (used by the *_ex entry points).
+ *   KDA_GATE_CHANNEL  one value per key channel: the operator above.
+ *   KDA_GATE_HEAD     one value per token and head, shared by all key channels
+ *                     (log_alpha has beta's shape): the scalar-gated delta rule
+ *                     that KDA generalises, Gated DeltaNet ("The fourth layer
+ *                     remembers", the paragraph on the forget gate: one decay per
+ *                     head per token there, one per key channel in KDA).
+ *   KDA_GATE_NONE     no gate, alpha = 1 (log_alpha is not read and may be NULL):
+ *                     the plain delta rule, DeltaNet (akshathtiwari.co.in "Kimi
+ *                     Delta Attention" explainer, delta-rule paragraph).
+ * Each is exactly the channel-gated operator with log_alpha broadcast over the
+ * key channels, or zero. */
+typedef enum {
+    KDA_GATE_CHANNEL = 0,
+    KDA_GATE_HEAD = 1,
+    KDA_GATE_NONE = 2
+} kda_gate;
+
 /* Human-readable name of a status code (static storage, never NULL). */
 const char *kda_status_string(kda_status status);
 
@@ -100,6 +119,39 @@ kda_status kda_fwd_chunked(const void *q, const void *k, const void *v,
                            void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * kda_fwd_chunked_ex -- kda_fwd_chunked with a gate layout and slot-indexed states.
+ *
+ * Serving keeps one fixed-size state per live sequence (constant memory per
+ * sequence and constant work per decoded token, "The fourth layer remembers")
+ * in a pool whose rows are handed out to requests; this entry point continues
+ * sequences straight from and into such a pool (chunked prefill, or a few
+ * tokens per sequence as multi-token decode).
+ *
+ *   gate            : layout of log_alpha (kda_gate): (B, T, H, dk) for
+ *                     KDA_GATE_CHANNEL, (B, T, H) for KDA_GATE_HEAD, unused for
+ *                     KDA_GATE_NONE.
+ *   S0, S_T         : as in kda_fwd_chunked when state_idx is NULL.  Otherwise
+ *                     pools of shape (pool_size, H, dk, dv) fp32 (each may be
+ *                     NULL; S0 == S_T continues the pool in place).
+ *   state_idx       : NULL, or (N,) int32 device array: sequence s starts from
+ *                     row state_idx[s] of S0 and writes its final state to row
+ *                     state_idx[s] of S_T.  An index outside [0, pool_size)
+ *                     means no state: the sequence starts from zeros and its
+ *                     final state is not written (padding slots).  Valid
+ *                     indices must be distinct when S_T is given.
+ *   pool_size       : rows of the pools (used only with state_idx).
+ * Every other argument, the supported sizes and the errors are those of
+ * kda_fwd_chunked, which equals this call with KDA_GATE_CHANNEL and no
+ * state_idx.
+ */
+kda_status kda_fwd_chunked_ex(const void *q, const void *k, const void *v,
+                              const void *log_alpha, const void *beta, kda_gate gate,
+                              const float *S0, float *S_T, const int32_t *state_idx, int pool_size,
+                              const int32_t *cu_seqlens, int num_seqs,
+                              int B, int T, int H, int dk, int dv, kda_dtype dtype,
+                              void *o, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * kda_decode_step -- one token for each of N independent sequences.
  *
  *   q, k, log_alpha : (N, H, dk)         dtype
@@ -114,6 +166,24 @@ kda_status kda_decode_step(const void *q, const void *k, const void *v,
                            const void *log_alpha, const void *beta,
                            float *S_cache, int N, int H, int dk, int dv,
                            kda_dtype dtype, void *o, void *stream);
+
+/*
+ * kda_decode_step_ex -- kda_decode_step with a gate layout and a state pool.
+ *
+ *   gate            : layout of log_alpha: (N, H, dk), (N, H) or unused (kda_gate).
+ *   S_pool          : fp32 states, read and rewritten in place: (N, H, dk, dv)
+ *                     when state_idx is NULL, else (pool_size, H, dk, dv).
+ *   state_idx       : NULL, or (N,) int32 device array: sequence n updates row
+ *                     state_idx[n] of S_pool.  An index outside [0, pool_size)
+ *                     means no state: o is computed from a zero state and
+ *                     nothing is written.  Valid indices must be distinct.
+ * Every other argument is that of kda_decode_step, which equals this call
+ * with KDA_GATE_CHANNEL and no state_idx.
+ */
+kda_status kda_decode_step_ex(const void *q, const void *k, const void *v,
+                              const void *log_alpha, const void *beta, kda_gate gate,
+                              float *S_pool, const int32_t *state_idx, int pool_size,
+                              int N, int H, int dk, int dv, kda_dtype dtype, void *o, void *stream);
 
 #ifdef __cplusplus
 }

@@ -10,6 +10,11 @@ from .oracle import (  # noqa: F401
     fwd,
     decode,
     brute_force,
+    channel_gate,
+    pool_rows,
+    fwd_pooled,
+    decode_pooled,
+    GATES,
     max_threads,
     default_threads,
 )

@@ -12,6 +12,11 @@ Two independent routes to the same result live here:
   diagonal gate, daily.dev summary of "You Could Have Come Up with Kimi Delta
   Attention").  It shares no code with the C loop.
 
+``channel_gate`` restates the two narrower gate layouts (one decay per head,
+or none) as the per-channel gate they stand for, and ``fwd_pooled`` /
+``decode_pooled`` read and write states as rows of a pool through a slot map;
+both only rearrange inputs and outputs around ``fwd`` / ``decode``.
+
 Every function here is pinned by tests/test_oracle_pins.py (values the pages
 print, closed forms, special cases that reduce to published recurrences, brute
 force), and tests/test_oracle_mutants.py checks that planted mistakes in the C
@@ -98,14 +103,44 @@ def _ptr(a: Optional[np.ndarray]):
     return a.ctypes.data_as(_dp)
 
 
+GATES = ("channel", "head", "none")
+
+
+def channel_gate(log_alpha, gate: str, shape_k) -> np.ndarray:
+    """The per-key-channel log-gate that a gate layout stands for.
+
+    "channel": log_alpha itself, shape (..., dk).
+    "head": one value per (token, head), shape (...,), the same on every key
+    channel -- the single decay per head and token of Gated DeltaNet, which
+    KDA turns into one per key channel ("The fourth layer remembers",
+    paragraph on the forget gate): repeated over dk.
+    "none": alpha = 1, the plain delta rule of DeltaNet (akshathtiwari.co.in
+    "Kimi Delta Attention" explainer, delta-rule paragraph): zeros.
+    """
+    shape_k = tuple(shape_k)
+    if gate == "channel":
+        g = _f64(log_alpha)
+        assert g.shape == shape_k
+        return g
+    if gate == "head":
+        g = _f64(log_alpha)
+        assert g.shape == shape_k[:-1]
+        return np.ascontiguousarray(np.repeat(g[..., None], shape_k[-1], axis=-1))
+    if gate == "none":
+        return np.zeros(shape_k)
+    raise ValueError(f"unknown gate layout {gate!r}")
+
+
 def fwd(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None,
-        nthreads: Optional[int] = None, lib=None) -> Tuple[np.ndarray, np.ndarray]:
+        nthreads: Optional[int] = None, lib=None, gate: str = "channel") -> Tuple[np.ndarray, np.ndarray]:
     """Literal recurrence over whole sequences.
 
-    q, k, log_alpha: (B, T, H, dk); v: (B, T, H, dv); beta: (B, T, H);
+    q, k: (B, T, H, dk); v: (B, T, H, dv); beta: (B, T, H); log_alpha in the
+    layout ``gate`` names (see channel_gate);
     S0: (N, H, dk, dv) or None (zeros); cu_seqlens: (N+1,) ints or None.
     Returns (o (B, T, H, dv), S_T (N, H, dk, dv)) as float64.
     """
+    log_alpha = channel_gate(log_alpha, gate, np.shape(q))
     q, k, v, log_alpha, beta = map(_f64, (q, k, v, log_alpha, beta))
     B, T, H, dk = q.shape
     dv = v.shape[-1]
@@ -134,12 +169,15 @@ def fwd(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None,
     return o, S_T
 
 
-def decode(q, k, v, log_alpha, beta, S, nthreads: Optional[int] = None, lib=None):
+def decode(q, k, v, log_alpha, beta, S, nthreads: Optional[int] = None, lib=None,
+           gate: str = "channel"):
     """One token for each of N independent states.
 
-    q, k, log_alpha: (N, H, dk); v: (N, H, dv); beta: (N, H); S: (N, H, dk, dv).
+    q, k: (N, H, dk); v: (N, H, dv); beta: (N, H); S: (N, H, dk, dv);
+    log_alpha in the layout ``gate`` names (see channel_gate).
     Returns (o (N, H, dv), S_new (N, H, dk, dv)); the input S is not modified.
     """
+    log_alpha = channel_gate(log_alpha, gate, np.shape(q))
     q, k, v, log_alpha, beta = map(_f64, (q, k, v, log_alpha, beta))
     N, H, dk = q.shape
     dv = v.shape[-1]
@@ -153,6 +191,67 @@ def decode(q, k, v, log_alpha, beta, S, nthreads: Optional[int] = None, lib=None
     if rc != 0:
         raise ValueError(f"kda_oracle_decode rejected its arguments (rc={rc})")
     return o, S_new
+
+
+def pool_rows(state_idx, pool_size: int) -> np.ndarray:
+    """Pool row of each sequence, or -1 (no state) for an index outside [0, pool_size)."""
+    idx = np.asarray(state_idx, dtype=np.int64)
+    return np.where((idx >= 0) & (idx < pool_size), idx, -1)
+
+
+def fwd_pooled(q, k, v, log_alpha, beta, S0_pool, state_idx, cu_seqlens=None, gate="channel",
+               S_T_pool=None, pool_size: Optional[int] = None, nthreads: Optional[int] = None,
+               lib=None):
+    """Sequences continued from and into rows of state pools (slot-indexed states).
+
+    Sequence s starts from row state_idx[s] of S0_pool (zeros when S0_pool is
+    None or the index is outside the pool) and its final state replaces row
+    state_idx[s] of a copy of S_T_pool; other rows are kept.  Pools have shape
+    (P, H, dk, dv); P = pool_size, else the pools' first dimension.
+    Returns (o, new S_T pool or None).
+    """
+    B, T, H, dk = np.shape(q)
+    dv = np.shape(v)[-1]
+    if pool_size is None:
+        ref = S0_pool if S0_pool is not None else S_T_pool
+        pool_size = 0 if ref is None else np.shape(ref)[0]
+    rows = pool_rows(state_idx, pool_size)
+    N = rows.shape[0]
+    S0 = np.zeros((N, H, dk, dv))
+    if S0_pool is not None:
+        pool0 = _f64(S0_pool)
+        for s in range(N):
+            if rows[s] >= 0:
+                S0[s] = pool0[rows[s]]
+    o, S_T = fwd(q, k, v, log_alpha, beta, S0, cu_seqlens, nthreads=nthreads, lib=lib, gate=gate)
+    if S_T_pool is None:
+        return o, None
+    new = np.array(S_T_pool, dtype=np.float64, copy=True)
+    for s in range(N):
+        if rows[s] >= 0:
+            new[rows[s]] = S_T[s]
+    return o, new
+
+
+def decode_pooled(q, k, v, log_alpha, beta, pool, state_idx, gate="channel",
+                  nthreads: Optional[int] = None, lib=None):
+    """One token per sequence on rows of a state pool; returns (o, new pool).
+
+    Sequence n updates row state_idx[n]; for an index outside the pool it
+    starts from a zero state and writes nothing.
+    """
+    pool = np.array(pool, dtype=np.float64, copy=True)
+    rows = pool_rows(state_idx, pool.shape[0])
+    N = rows.shape[0]
+    S = np.zeros((N,) + pool.shape[1:])
+    for n in range(N):
+        if rows[n] >= 0:
+            S[n] = pool[rows[n]]
+    o, S_new = decode(q, k, v, log_alpha, beta, S, nthreads=nthreads, lib=lib, gate=gate)
+    for n in range(N):
+        if rows[n] >= 0:
+            pool[rows[n]] = S_new[n]
+    return o, pool
 
 
 def brute_force(q, k, v, log_alpha, beta, S0=None):

@@ -27,8 +27,9 @@ def L():
 
 
 def test_header_declares_expected_entry_points():
-    assert declared_functions() == ["kda_decode_step", "kda_fwd_chunked",
-                                    "kda_fwd_workspace_bytes", "kda_status_string"]
+    assert declared_functions() == ["kda_decode_step", "kda_decode_step_ex", "kda_fwd_chunked",
+                                    "kda_fwd_chunked_ex", "kda_fwd_workspace_bytes",
+                                    "kda_status_string"]
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -125,6 +126,56 @@ def test_decode_invalid(L, kw):
 
 def test_decode_empty_is_ok(L):
     assert dec(L, N=0) == 0
+
+
+def fwd_ex(L, q=FAKE, k=FAKE, v=FAKE, g=FAKE, b=FAKE, gate=0, S0=None, S_T=None, idx=None, P=0,
+           cu=None, N=0, B=1, T=64, H=2, dk=128, dv=128, dt=1, o=FAKE, ws=None, wsb=0):
+    return L.kda_fwd_chunked_ex(q, k, v, g, b, gate, S0, S_T, idx, P, cu, N, B, T, H, dk, dv, dt,
+                                o, ws, wsb, None)
+
+
+def dec_ex(L, q=FAKE, k=FAKE, v=FAKE, g=FAKE, b=FAKE, gate=0, S=FAKE, idx=None, P=0, N=4, H=2,
+           dk=128, dv=128, dt=1, o=FAKE):
+    return L.kda_decode_step_ex(q, k, v, g, b, gate, S, idx, P, N, H, dk, dv, dt, o, None)
+
+
+@pytest.mark.parametrize("gate", [-1, 3, 100])
+def test_ex_rejects_unknown_gate(L, gate):
+    assert fwd_ex(L, gate=gate) == 1
+    assert dec_ex(L, gate=gate) == 1
+
+
+def test_ex_gate_needs_log_alpha_unless_none(L):
+    assert fwd_ex(L, g=None, gate=0) == 1
+    assert fwd_ex(L, g=None, gate=1) == 1
+    assert dec_ex(L, g=None, gate=0) == 1
+    assert dec_ex(L, g=None, gate=1) == 1
+    # without a gate log_alpha is not read: NULL and even misaligned pass the checks
+    assert fwd_ex(L, g=None, gate=2, B=0, T=0) == 0
+    assert fwd_ex(L, g=FAKE + 2, gate=2, B=0, T=0) == 0
+    assert dec_ex(L, g=None, gate=2, N=0) == 0
+
+
+def test_ex_slot_map_rules(L):
+    assert fwd_ex(L, idx=FAKE, P=-1) == 1
+    assert fwd_ex(L, idx=FAKE + 2, P=4) == 1            # int32 array misaligned
+    assert dec_ex(L, idx=FAKE, P=-1) == 1
+    assert dec_ex(L, idx=FAKE + 1, P=4) == 1
+    # the ordinary checks still apply
+    assert fwd_ex(L, dk=96) == 2
+    assert dec_ex(L, dv=32) == 2
+    assert fwd_ex(L, cu=FAKE, N=8, idx=FAKE, P=8) == 1  # varlen workspace missing
+    assert fwd_ex(L, B=0, T=0, idx=FAKE, P=0) == 0
+
+
+def test_binding_rejects_bad_gate_shapes():
+    import torch
+    from gated_delta_rule_81_amd import kda
+    q = torch.zeros(1, 4, 2, 64)
+    with pytest.raises(ValueError, match="gate must be one of"):
+        kda.fwd_chunked(q, q, q, q, torch.zeros(1, 4, 2), gate="token")
+    with pytest.raises(ValueError, match="GPU tensor"):
+        kda.fwd_chunked(q, q, q, None, torch.zeros(1, 4, 2), gate="none")
 
 
 def test_binding_rejects_cpu_and_mismatched_tensors():
