@@ -13,11 +13,13 @@ Also reported on the same JSON line:
                 8 TB/s; the useful-flop MFMA fraction against 2.5 PFLOP/s bf16;
                 traffic from the committed rocprofv3 counter summary when it was
                 taken on the current kernel source, else null
-  workloads     the same forward on the B=1, H=16, T=4096 workload and on 64
-                packed sequences of 512..16384 tokens (H=32, d=128): time per
+  workloads     the same forward on the B=1, H=16, T=4096 workload, on 64
+                packed sequences of 512..16384 tokens (H=32, d=128), and on the
+                headline shape with a per-head gate and with no gate: time per
                 call, tokens/s and the fraction of 8 TB/s of algorithmic bytes
   decode        kda_decode_step over N=512, H=32, d=128 (1 GiB fp32 cache),
-                1000 chained steps with fresh inputs pre-generated on the GPU
+                1000 chained steps with fresh inputs pre-generated on the GPU;
+                also the same step on states at scattered rows of a pool
   copy_ceiling  a plain device copy of 1 GiB (practical HBM ceiling)
   cpu_baseline  the fp64 oracle on a bounded sample of the same workload,
                 timed on this host's cores
@@ -141,14 +143,29 @@ def bench_forward(torch, kda, synth, steps, warmup):
                 tokens_per_s=B * T / t_step)
 
 
+def _fwd_bytes(tokens, H, dk, dv, N, gate_elems, elem=2):
+    """Algorithmic bytes of one forward call: q, k, v, beta, the gate (dk,
+    1 or 0 values per token-head), o, and the fp32 states in and out."""
+    return (tokens * H * ((2 * dk + dv + gate_elems + 1) * elem + dv * elem)
+            + 2 * N * H * dk * dv * 4)
+
+
 def bench_other_workloads(torch, kda, synth, steps=10, warmup=3):
-    """The forward on the H16 and packed-varlen workloads (reported beside
-    the headline line, not in `value`)."""
+    """The forward on the H16 and packed-varlen workloads, and the headline
+    shape with a per-head gate and with no gate (reported beside the
+    headline line, not in `value`)."""
     out = {}
-    for w in (synth.FWD_H16_T4K, synth.VARLEN_64):
-        log(f"[bench] generating {w.name} on the GPU")
+    cases = [(synth.FWD_H16_T4K, "channel", ""), (synth.VARLEN_64, "channel", ""),
+             (synth.FWD_H32_T8K, "head", "_gate_head"), (synth.FWD_H32_T8K, "none", "_gate_none")]
+    for w, gate, suffix in cases:
+        log(f"[bench] generating {w.name} on the GPU (gate={gate})")
         x = synth.fwd_inputs(w, device="cuda")
         B, T, H, dk, dv, N = x["B"], x["T"], x["H"], x["dk"], x["dv"], x["N"]
+        g = x["log_alpha"]
+        if gate == "head":
+            g = g[..., 0].contiguous()     # one value per (token, head)
+        elif gate == "none":
+            g = None
         o = torch.empty((B, T, H, dv), dtype=w.dtype, device="cuda")
         S_T = torch.empty((N, H, dk, dv), dtype=torch.float32, device="cuda")
         ws = None
@@ -157,18 +174,46 @@ def bench_other_workloads(torch, kda, synth, steps=10, warmup=3):
             ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
 
         def step():
-            kda.fwd_chunked(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["S0"],
-                            x["cu_seqlens"], o=o, S_T=S_T, workspace=ws)
+            kda.fwd_chunked(x["q"], x["k"], x["v"], g, x["beta"], x["S0"],
+                            x["cu_seqlens"], o=o, S_T=S_T, workspace=ws, gate=gate)
 
         secs = time_loop(torch, step, steps, warmup) / steps
         tokens = B * T
-        nbytes = (tokens * H * ((2 * dk + dv + dk + 1) * 2 + dv * 2) + 2 * N * H * dk * dv * 4)
-        out[w.name] = {"us_per_call": round(secs * 1e6, 1), "tokens": tokens,
-                       "tokens_per_s": round(tokens / secs, 1),
-                       "hbm_frac": round(nbytes / secs / 1e9 / HBM_PEAK_GBS, 4)}
-        del x, o, S_T, ws
+        nbytes = _fwd_bytes(tokens, H, dk, dv, N, {"channel": dk, "head": 1, "none": 0}[gate])
+        out[w.name + suffix] = {"us_per_call": round(secs * 1e6, 1), "tokens": tokens,
+                                "tokens_per_s": round(tokens / secs, 1),
+                                "hbm_frac": round(nbytes / secs / 1e9 / HBM_PEAK_GBS, 4)}
+        del x, g, o, S_T, ws
         torch.cuda.empty_cache()
     return out
+
+
+def bench_pooled_decode(torch, kda, synth, steps=200):
+    """Decode with a slot map: the N=512, H=32 states live at scattered rows
+    of a 1024-row pool (2 GiB); same bytes per step as the dense decode."""
+    w = synth.DECODE_512
+    P = 2 * w.N
+    log(f"[bench] pooled decode: {steps} steps, {w.N} of {P} pool rows")
+    pool = synth.decode_state(w, device="cuda").repeat(2, 1, 1, 1)
+    gen = torch.Generator(device="cpu").manual_seed(99)
+    idx = torch.randperm(P, generator=gen)[: w.N].to(torch.int32).to("cuda")
+    ins = [synth.decode_step_inputs(w, s, device="cuda") for s in range(steps)]
+    o = torch.empty((w.N, w.H, w.dv), dtype=w.dtype, device="cuda")
+    it = iter(range(steps + 3))
+
+    def step():
+        x = ins[next(it) % steps]
+        kda.decode_step(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], pool, o=o,
+                        state_idx=idx)
+
+    secs = time_loop(torch, step, steps, 3) / steps
+    nbytes = decode_algorithmic_bytes(w.N, w.H, w.dk, w.dv)
+    del ins, pool
+    torch.cuda.empty_cache()
+    return {"workload": w.name.replace("_1000steps", f"_pool{P}_{steps}steps"),
+            "us_per_step": round(secs * 1e6, 2),
+            "GBps": round(nbytes / secs / 1e9, 1),
+            "hbm_frac": round(nbytes / secs / 1e9 / HBM_PEAK_GBS, 4)}
 
 
 def bench_decode(torch, kda, synth, steps=None):
@@ -328,6 +373,7 @@ def main():
                          "algorithmic_bytes_per_launch": dc["bytes"],
                          "source_sha256_16": kernel_sources_hash("decode_step_kernel")},
         }
+        out["decode_pool"] = bench_pooled_decode(torch, kda, synth)
     out["copy_ceiling_GBps"] = round(bench_copy(torch), 1)
     if not args.no_cpu:
         log("[bench] oracle CPU baseline")

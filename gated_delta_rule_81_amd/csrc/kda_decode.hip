@@ -30,6 +30,9 @@
 namespace kda {
 
 constexpr int DEC_THREADS = 1024;
+// cache-policy operand of the buffer loads: non-temporal (each state byte is
+// touched once per step)
+constexpr int kNonTemporal = 2;
 
 template <int DK, int DV, typename T>
 __global__ __launch_bounds__(DEC_THREADS) void decode_step_kernel(
@@ -59,32 +62,71 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_step_kernel(
         const long r = state_row(state_idx, pool, n);
         return r < 0 ? -1L : r * H + (unit - n * H);
     };
-    f4v cur[RPT], nxt[RPT];
+    // A unit's state is read through a buffer resource over its 64 KB block;
+    // a unit without a state gets a resource of zero bytes, whose loads read
+    // zeros.  The loads are then unconditional, so the next unit's prefetch
+    // stays in flight (a branch around them would make the compiler wait
+    // for them where the two paths join).
     auto load_state = [&](int unit, f4v (&r)[RPT]) {
         const long row = unit_row(unit);
-        if (row < 0) {
+        const float *base = row < 0 ? S_cache : S_cache + (size_t)row * DK * DV;
+        const uint64_t a = reinterpret_cast<uint64_t>(base);
+        const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+        const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            reinterpret_cast<void *>(((uint64_t)hi << 32) | lo), 0, row < 0 ? 0 : DK * DV * 4, 0x00020000);
 #pragma unroll
-            for (int i = 0; i < RPT; ++i) r[i] = f4v{0.f, 0.f, 0.f, 0.f};
-            return;
-        }
-        const f4v *Su = reinterpret_cast<const f4v *>(S_cache + (size_t)row * DK * DV);
-#pragma unroll
-        for (int i = 0; i < RPT; ++i) r[i] = __builtin_nontemporal_load(Su + (rg + i * RG) * CG + cg);
+        for (int i = 0; i < RPT; ++i)
+            r[i] = __builtin_bit_cast(f4v, __builtin_amdgcn_raw_buffer_load_b128(
+                rs, (uint32_t)(((rg + i * RG) * CG + cg) * 16), 0, kNonTemporal));
     };
 
-    int unit = blockIdx.x;
-    if (unit < units) load_state(unit, cur);
-    for (; unit < units; unit += gridDim.x) {
-        const int next = unit + gridDim.x;
-        if (next < units) load_state(next, nxt);
+    // gate, k and q (threads t < DK), v (t < DV) and beta of a unit,
+    // requested together with the unit's state one unit ahead and kept as
+    // raw bits until used: the wait counter is in order, so a load issued
+    // after the prefetch and used in the same step would wait for the
+    // prefetch too, and a conversion right after a load would wait for it.
+    // One unconditional load each: without a gate the k address stands in,
+    // its value unused.
+    auto raw = [](const T *ptr) -> uint32_t {
+        if constexpr (sizeof(T) == 2) return (uint32_t)reinterpret_cast<const bf16_t *>(ptr)->x;
+        else return __float_as_uint(*reinterpret_cast<const float *>(ptr));
+    };
+    auto val = [](uint32_t r) -> float { return __uint_as_float(sizeof(T) == 2 ? r << 16 : r); };
+    // (every thread loads, threads past DK a duplicate of element 0, so that
+    // no branch surrounds the loads)
+    struct Small { uint32_t g, k, q, v, b; };
+    auto load_small = [&](int u, Small &r) {
+        const size_t idx = (size_t)u * DK + (t < DK ? t : 0);
+        const T *gp = gate == GATE_CHANNEL ? log_alpha + idx
+                    : gate == GATE_HEAD    ? log_alpha + u
+                                           : k + idx;
+        r.g = raw(gp);
+        r.k = raw(k + idx);
+        r.q = raw(q + idx);
+        r.v = raw(v + (size_t)u * DV + (t < DV ? t : 0));
+        r.b = raw(beta + u);
+    };
 
+    // One unit: its state `cur` and small vectors (gc, kc, qc) were requested
+    // one unit earlier; the next unit's go into `nxt` / (gn, kn, qn) now.
+    auto step = [&](int unit, f4v (&cur)[RPT], const Small &sc, f4v (&nxt)[RPT], Small &sn) {
+        // every wave waits here for this unit's loads (an empty asm that
+        // reads them), so the compiler knows them, and the state loaded
+        // before them, to be complete below; otherwise it sinks the wait into
+        // the branches that use them and later waits for the prefetch too
+        asm volatile("" ::"v"(sc.g), "v"(sc.k), "v"(sc.q), "v"(sc.v), "v"(sc.b));
+        const float a_ = gate == GATE_NONE ? 1.0f : expf(val(sc.g));
+        const float k_ = val(sc.k), q_ = val(sc.q), v_ = val(sc.v), b_ = val(sc.b);
         if (t < DK) {
-            const size_t idx = (size_t)unit * DK + t;
-            s_a[t] = gate == GATE_CHANNEL ? expf(load_elem(log_alpha + idx))
-                   : gate == GATE_HEAD    ? expf(load_elem(log_alpha + unit))
-                                          : 1.0f;
-            s_k[t] = load_elem(k + idx);
-            s_q[t] = load_elem(q + idx);
+            s_a[t] = a_;
+            s_k[t] = k_;
+            s_q[t] = q_;
+        }
+        const int next = unit + gridDim.x;
+        if (next < units) {
+            load_state(next, nxt);
+            load_small(next, sn);
         }
         __syncthreads();
 
@@ -116,7 +158,7 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_step_kernel(
                 ps += s_red[1][r][t];
             }
             const size_t vidx = (size_t)unit * DV + t;
-            const float u = load_elem(beta + unit) * (load_elem(v + vidx) - es);
+            const float u = b_ * (v_ - es);
             s_u[t] = u;
             store_elem(o + vidx, ps + s_kq * u);
         }
@@ -132,9 +174,25 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_step_kernel(
                 __builtin_nontemporal_store(cur[i] + s_k[row] * u4, Sw + row * CG + cg);
             }
         }
-#pragma unroll
-        for (int i = 0; i < RPT; ++i) cur[i] = nxt[i];
         __syncthreads();   // the LDS vectors are rewritten for the next unit
+    };
+
+    // Two register sets take turns (unrolled by two), so a prefetched state
+    // is never copied, which would wait for its loads right away.
+    f4v sa[RPT], sb[RPT];
+    Small ma = {0u, 0u, 0u, 0u, 0u}, mb = {0u, 0u, 0u, 0u, 0u};
+    int unit = blockIdx.x;
+    if (unit < units) {
+        load_state(unit, sa);
+        load_small(unit, ma);
+    }
+    // the first unit's loads have landed before the loop, as the next unit's
+    // have (except for the stores issued after them) at the end of every step
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    for (; unit < units; unit += 2 * gridDim.x) {
+        step(unit, sa, ma, sb, mb);
+        if (unit + (int)gridDim.x >= units) break;
+        step(unit + gridDim.x, sb, mb, sa, ma);
     }
 }
 
