@@ -917,9 +917,6 @@ __global__ __launch_bounds__(512, 1) void chunked_ws_kernel(WsParams p)
         }
         __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
 
-        // next chunk's g and k (not live across the out-of-line exact path)
-        if (n + NPROD < nchunks) load_gk(n + NPROD);
-
         // ---- T = (I + A)^{-1}; T' = T Diag(beta) into the slot ----------------
         {
             // diagonal blocks: lanes with jg & 1 == b solve block b for column
@@ -1001,6 +998,10 @@ __global__ __launch_bounds__(512, 1) void chunked_ws_kernel(WsParams p)
             *reinterpret_cast<uint4 *>(&sTp[r * C + ((((cb >> 3) + 1) ^ key4(r)) << 3)]) =
                 make_uint4(pk[4], pk[5], pk[6], pk[7]);
         }
+
+        // next chunk's g and k (requested once the inverse no longer needs
+        // registers; not live across the out-of-line exact path)
+        if (n + NPROD < nchunks) load_gk(n + NPROD);
 
         // ---- publish -------------------------------------------------------------
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
