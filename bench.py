@@ -19,7 +19,9 @@ Also reported on the same JSON line:
                 call, tokens/s and the fraction of 8 TB/s of algorithmic bytes
   decode        kda_decode_step over N=512, H=32, d=128 (1 GiB fp32 cache),
                 1000 chained steps with fresh inputs pre-generated on the GPU;
-                also the same step on states at scattered rows of a pool
+                also the same step on states at scattered rows of a pool, and
+                four tokens per sequence per call from such a pool (decode
+                kernel and chunked forward)
   copy_ceiling  a plain device copy of 1 GiB (practical HBM ceiling)
   cpu_baseline  the fp64 oracle on a bounded sample of the same workload,
                 timed on this host's cores
@@ -186,6 +188,50 @@ def bench_other_workloads(torch, kda, synth, steps=10, warmup=3):
         del x, g, o, S_T, ws
         torch.cuda.empty_cache()
     return out
+
+
+def bench_multi_token_decode(torch, kda, synth, L=4, steps=20):
+    """Multi-token decode on a state pool: each of the N=512 sequences (H=32,
+    d=128) advances by L tokens per call, its state read from and written back
+    to a scattered row of a 1024-row pool; through the decode kernel (L tokens
+    per call) and through the chunked forward (L-token sequences)."""
+    w = synth.DECODE_512
+    N, H, dk, dv, P = w.N, w.H, w.dk, w.dv, 2 * w.N
+    log(f"[bench] multi-token decode: {N} sequences x {L} tokens from a {P}-row pool")
+    x = synth.random_fwd(1, 0, H, dk, dv, dtype=w.dtype, seed=98, gate_mu=-2.0, s0_std=0.0,
+                         lengths=[L] * N, device="cuda")
+    pool = synth.decode_state(w, device="cuda").repeat(2, 1, 1, 1)
+    gen = torch.Generator(device="cpu").manual_seed(97)
+    idx = torch.randperm(P, generator=gen)[:N].to(torch.int32).to("cuda")
+    o = torch.empty((1, N * L, H, dv), dtype=w.dtype, device="cuda")
+    ws = torch.empty(kda.workspace_bytes(1, N * L, H, dk, dv, N), dtype=torch.uint8, device="cuda")
+
+    def step():
+        kda.fwd_chunked(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], pool, x["cu_seqlens"],
+                        o=o, S_T=pool, workspace=ws, state_idx=idx)
+
+    secs = time_loop(torch, step, steps, 3) / steps
+    nbytes = _fwd_bytes(N * L, H, dk, dv, N, dk)
+    # the same L tokens per sequence through the decode kernel in one call
+    xd = {key: x[key].reshape((N, L) + x[key].shape[2:]).contiguous()
+          for key in ("q", "k", "v", "log_alpha", "beta")}
+    od = torch.empty((N, L, H, dv), dtype=w.dtype, device="cuda")
+
+    def dstep():
+        kda.decode_step(xd["q"], xd["k"], xd["v"], xd["log_alpha"], xd["beta"], pool, o=od,
+                        state_idx=idx)
+
+    dsecs = time_loop(torch, dstep, steps, 3) / steps
+    del x, xd, pool, o, od, ws
+    torch.cuda.empty_cache()
+    return {"workload": f"kda_decode_pool_bf16_N{N}x{L}tok_H{H}_d{dk}_pool{P}",
+            "tokens": N * L,
+            "decode_kernel": {"us_per_call": round(dsecs * 1e6, 1),
+                              "tokens_per_s": round(N * L / dsecs, 1),
+                              "hbm_frac": round(nbytes / dsecs / 1e9 / HBM_PEAK_GBS, 4)},
+            "chunked_kernel": {"us_per_call": round(secs * 1e6, 1),
+                               "tokens_per_s": round(N * L / secs, 1),
+                               "hbm_frac": round(nbytes / secs / 1e9 / HBM_PEAK_GBS, 4)}}
 
 
 def bench_pooled_decode(torch, kda, synth, steps=200):
@@ -374,6 +420,7 @@ def main():
                          "source_sha256_16": kernel_sources_hash("decode_step_kernel")},
         }
         out["decode_pool"] = bench_pooled_decode(torch, kda, synth)
+        out["multi_token_decode"] = bench_multi_token_decode(torch, kda, synth)
     out["copy_ceiling_GBps"] = round(bench_copy(torch), 1)
     if not args.no_cpu:
         log("[bench] oracle CPU baseline")

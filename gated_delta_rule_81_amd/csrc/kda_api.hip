@@ -9,7 +9,7 @@
 namespace kda {
 hipError_t decode_step_launch(const void *q, const void *k, const void *v,
                               const void *log_alpha, const void *beta, int gate, float *S,
-                              const int32_t *state_idx, int pool, void *o, int N, int H,
+                              const int32_t *state_idx, int pool, void *o, int N, int L, int H,
                               int dk, int dv, bool bf16, hipStream_t stream);
 hipError_t chunked_fwd_launch(const void *q, const void *k, const void *v, const void *g,
                               const void *beta, int gate, const float *S0, float *S_T,
@@ -120,22 +120,23 @@ kda_status kda_fwd_chunked(const void *q, const void *k, const void *v,
 kda_status kda_decode_step_ex(const void *q, const void *k, const void *v,
                               const void *log_alpha, const void *beta, kda_gate gate,
                               float *S_pool, const int32_t *state_idx, int pool_size,
-                              int N, int H, int dk, int dv, kda_dtype dtype, void *o, void *stream)
+                              int N, int L, int H, int dk, int dv, kda_dtype dtype, void *o,
+                              void *stream)
 {
     if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_INVALID_ARG;
     if (!gate_ok(gate)) return KDA_ERR_INVALID_ARG;
-    if (N < 0 || H <= 0 || dk <= 0 || dv <= 0) return KDA_ERR_INVALID_ARG;
+    if (N < 0 || L < 0 || H <= 0 || dk <= 0 || dv <= 0) return KDA_ERR_INVALID_ARG;
     if (!dim_ok(dk) || !dim_ok(dv)) return KDA_ERR_UNSUPPORTED;
-    if (!sizes_fit(N, H, dk, dv)) return KDA_ERR_INVALID_ARG;
+    if (!sizes_fit(N, H, dk, dv) || !sizes_fit(N, L, H, dk > dv ? dk : dv)) return KDA_ERR_INVALID_ARG;
     if ((long long)N * H >= ((long long)1 << 31)) return KDA_ERR_INVALID_ARG;
     if (state_idx && (pool_size < 0 || !aligned4(state_idx) || !sizes_fit(pool_size, H, dk, dv)))
         return KDA_ERR_INVALID_ARG;
-    if (N == 0) return KDA_OK;
+    if (N == 0 || L == 0) return KDA_OK;
     if (!q || !k || !v || !beta || !S_pool || !o) return KDA_ERR_INVALID_ARG;
     if (gate != KDA_GATE_NONE && !log_alpha) return KDA_ERR_INVALID_ARG;
     if (!aligned16(S_pool)) return KDA_ERR_INVALID_ARG;
     hipError_t e = kda::decode_step_launch(q, k, v, gate == KDA_GATE_NONE ? nullptr : log_alpha,
-                                           beta, (int)gate, S_pool, state_idx, pool_size, o, N, H,
+                                           beta, (int)gate, S_pool, state_idx, pool_size, o, N, L, H,
                                            dk, dv, dtype == KDA_BF16,
                                            static_cast<hipStream_t>(stream));
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
@@ -147,7 +148,7 @@ kda_status kda_decode_step(const void *q, const void *k, const void *v,
                            kda_dtype dtype, void *o, void *stream)
 {
     return kda_decode_step_ex(q, k, v, log_alpha, beta, KDA_GATE_CHANNEL, S_cache, nullptr, 0,
-                              N, H, dk, dv, dtype, o, stream);
+                              N, 1, H, dk, dv, dtype, o, stream);
 }
 
 }  // extern "C"

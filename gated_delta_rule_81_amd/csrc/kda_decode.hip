@@ -21,8 +21,10 @@
 // sums over rows go through LDS.  State traffic uses non-temporal loads and
 // stores: every byte is touched once per step, so caching it only costs.
 //
-// The gate is one value per key channel (alpha above), one per (n, h) shared
-// by the channels, or absent (alpha = 1).  With a slot map the state of
+// With L > 1 each sequence takes L consecutive tokens in one call (inputs
+// (N, L, H, .)): the state stays in registers across them and is read and
+// written once.  The gate is one value per key channel (alpha above), one
+// per token and head shared by the channels, or absent (alpha = 1).  With a slot map the state of
 // sequence n is row state_idx[n] of a pool; a slot outside the pool starts
 // from zeros and is not written.
 #include "kda_device.h"
@@ -34,13 +36,15 @@ constexpr int DEC_THREADS = 1024;
 // touched once per step)
 constexpr int kNonTemporal = 2;
 
-template <int DK, int DV, typename T>
+template <int DK, int DV, typename T, bool MULTI>
 __global__ __launch_bounds__(DEC_THREADS) void decode_step_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const T *__restrict__ log_alpha, const T *__restrict__ beta,
-    float *__restrict__ S_cache, T *__restrict__ o, int units, int H, int gate,
+    float *__restrict__ S_cache, T *__restrict__ o, int units, int H, int L_, int gate,
     const int32_t *__restrict__ state_idx, int pool)
 {
+    // tokens per sequence: a compile-time 1 for the one-token instantiation
+    const int L = MULTI ? L_ : 1;
     constexpr int NT = DEC_THREADS;
     constexpr int CG = DV / 4;     // 16-byte column groups per row
     constexpr int RG = NT / CG;    // row groups
@@ -56,9 +60,12 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_step_kernel(
     __shared__ __attribute__((aligned(16))) float s_u[DV];
     __shared__ float s_kq;
 
-    // state row of a unit (n, h): n's slot, or -1 for no state
+    // state row of a unit (n, h): n's slot, or -1 for no state.  The unit is
+    // the same in every lane; saying so keeps the slot-map read a scalar load
+    // (a vector load would be counted with the state prefetch, and waiting
+    // for it would wait for the prefetch too).
     auto unit_row = [&](int unit) -> long {
-        const int n = unit / H;
+        const int n = __builtin_amdgcn_readfirstlane(unit / H);
         const long r = state_row(state_idx, pool, n);
         return r < 0 ? -1L : r * H + (unit - n * H);
     };
@@ -95,38 +102,51 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_step_kernel(
     auto val = [](uint32_t r) -> float { return __uint_as_float(sizeof(T) == 2 ? r << 16 : r); };
     // (every thread loads, threads past DK a duplicate of element 0, so that
     // no branch surrounds the loads)
+    // token tk (0 .. L-1) of unit u = (n, h) is row (n L + tk) H + h of the
+    // (N, L, H, .) inputs
+    auto tok_row = [&](int u, int tk) -> size_t {
+        const int n = u / H;
+        return ((size_t)n * L + tk) * H + (u - n * H);
+    };
     struct Small { uint32_t g, k, q, v, b; };
-    auto load_small = [&](int u, Small &r) {
-        const size_t idx = (size_t)u * DK + (t < DK ? t : 0);
+    auto load_small = [&](int u, int tk, Small &r) {
+        const size_t row = tok_row(u, tk);
+        const size_t idx = row * DK + (t < DK ? t : 0);
         const T *gp = gate == GATE_CHANNEL ? log_alpha + idx
-                    : gate == GATE_HEAD    ? log_alpha + u
+                    : gate == GATE_HEAD    ? log_alpha + row
                                            : k + idx;
         r.g = raw(gp);
         r.k = raw(k + idx);
         r.q = raw(q + idx);
-        r.v = raw(v + (size_t)u * DV + (t < DV ? t : 0));
-        r.b = raw(beta + u);
+        r.v = raw(v + row * DV + (t < DV ? t : 0));
+        r.b = raw(beta + row);
     };
 
-    // One unit: its state `cur` and small vectors (gc, kc, qc) were requested
-    // one unit earlier; the next unit's go into `nxt` / (gn, kn, qn) now.
-    auto step = [&](int unit, f4v (&cur)[RPT], const Small &sc, f4v (&nxt)[RPT], Small &sn) {
-        // every wave waits here for this unit's loads (an empty asm that
+    // Token tk of a unit: its small vectors `cs` were requested one token
+    // earlier; the next token's go into `ns`, or after the unit's last token
+    // the next unit's state and first token into `nxt` / `sn`.  The state
+    // stays in registers across the unit's L tokens and is written back once.
+    auto token = [&](int unit, long urow, int tk, f4v (&cur)[RPT], const Small &cs, Small &ns,
+                     f4v (&nxt)[RPT], Small &sn) {
+        // every wave waits here for this token's loads (an empty asm that
         // reads them), so the compiler knows them, and the state loaded
         // before them, to be complete below; otherwise it sinks the wait into
         // the branches that use them and later waits for the prefetch too
-        asm volatile("" ::"v"(sc.g), "v"(sc.k), "v"(sc.q), "v"(sc.v), "v"(sc.b));
-        const float a_ = gate == GATE_NONE ? 1.0f : expf(val(sc.g));
-        const float k_ = val(sc.k), q_ = val(sc.q), v_ = val(sc.v), b_ = val(sc.b);
+        asm volatile("" ::"v"(cs.g), "v"(cs.k), "v"(cs.q), "v"(cs.v), "v"(cs.b));
+        const float a_ = gate == GATE_NONE ? 1.0f : expf(val(cs.g));
+        const float k_ = val(cs.k), q_ = val(cs.q), v_ = val(cs.v), b_ = val(cs.b);
         if (t < DK) {
             s_a[t] = a_;
             s_k[t] = k_;
             s_q[t] = q_;
         }
+        const bool last = tk + 1 == L;
         const int next = unit + gridDim.x;
-        if (next < units) {
+        if (!last) {
+            load_small(unit, tk + 1, ns);
+        } else if (next < units) {
             load_state(next, nxt);
-            load_small(next, sn);
+            load_small(next, 0, sn);
         }
         __syncthreads();
 
@@ -157,24 +177,39 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_step_kernel(
                 es += s_red[0][r][t];
                 ps += s_red[1][r][t];
             }
-            const size_t vidx = (size_t)unit * DV + t;
             const float u = b_ * (v_ - es);
             s_u[t] = u;
-            store_elem(o + vidx, ps + s_kq * u);
+            store_elem(o + tok_row(unit, tk) * DV + t, ps + s_kq * u);
         }
         __syncthreads();
 
         const f4v u4 = *reinterpret_cast<const f4v *>(&s_u[4 * cg]);
-        const long srow_ = unit_row(unit);
-        if (srow_ >= 0) {
-            f4v *Sw = reinterpret_cast<f4v *>(S_cache + (size_t)srow_ * DK * DV);
 #pragma unroll
-            for (int i = 0; i < RPT; ++i) {
-                const int row = rg + i * RG;
-                __builtin_nontemporal_store(cur[i] + s_k[row] * u4, Sw + row * CG + cg);
+        for (int i = 0; i < RPT; ++i) cur[i] += s_k[rg + i * RG] * u4;
+        if (last) {
+            if (urow >= 0) {
+                f4v *Sw = reinterpret_cast<f4v *>(S_cache + (size_t)urow * DK * DV);
+#pragma unroll
+                for (int i = 0; i < RPT; ++i)
+                    __builtin_nontemporal_store(cur[i], Sw + (rg + i * RG) * CG + cg);
             }
         }
-        __syncthreads();   // the LDS vectors are rewritten for the next unit
+        __syncthreads();   // the LDS vectors are rewritten for the next token
+    };
+    // One unit: its state and first token were requested one unit earlier.
+    // Tokens alternate between `sc` and a second buffer (unrolled by two), so
+    // no prefetched value is ever copied (a copy waits for its load).
+    auto step = [&](int unit, f4v (&cur)[RPT], Small &sc, f4v (&nxt)[RPT], Small &sn) {
+        const long urow = unit_row(unit);
+        if constexpr (!MULTI) {
+            token(unit, urow, 0, cur, sc, sc, nxt, sn);
+        } else {
+            Small tb = {0u, 0u, 0u, 0u, 0u};
+            for (int tk = 0; tk < L; tk += 2) {
+                token(unit, urow, tk, cur, sc, tb, nxt, sn);
+                if (tk + 1 < L) token(unit, urow, tk + 1, cur, tb, sc, nxt, sn);
+            }
+        }
     };
 
     // Two register sets take turns (unrolled by two), so a prefetched state
@@ -184,7 +219,7 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_step_kernel(
     int unit = blockIdx.x;
     if (unit < units) {
         load_state(unit, sa);
-        load_small(unit, ma);
+        load_small(unit, 0, ma);
     }
     // the first unit's loads have landed before the loop, as the next unit's
     // have (except for the stores issued after them) at the end of every step
@@ -201,26 +236,31 @@ int cu_count();
 template <int DK, int DV, typename T>
 static hipError_t launch_decode(const void *q, const void *k, const void *v,
                                 const void *log_alpha, const void *beta, float *S,
-                                void *o, int units, int H, int gate, const int32_t *state_idx,
-                                int pool, hipStream_t stream)
+                                void *o, int units, int H, int L, int gate,
+                                const int32_t *state_idx, int pool, hipStream_t stream)
 {
     // four workgroups per CU, each walking units with the grid stride
     const int grid = units < 4 * cu_count() ? units : 4 * cu_count();
-    hipLaunchKernelGGL((decode_step_kernel<DK, DV, T>), dim3(grid), dim3(DEC_THREADS), 0, stream,
-                       (const T *)q, (const T *)k, (const T *)v, (const T *)log_alpha,
-                       (const T *)beta, S, (T *)o, units, H, gate, state_idx, pool);
+    if (L == 1)
+        hipLaunchKernelGGL((decode_step_kernel<DK, DV, T, false>), dim3(grid), dim3(DEC_THREADS), 0,
+                           stream, (const T *)q, (const T *)k, (const T *)v, (const T *)log_alpha,
+                           (const T *)beta, S, (T *)o, units, H, L, gate, state_idx, pool);
+    else
+        hipLaunchKernelGGL((decode_step_kernel<DK, DV, T, true>), dim3(grid), dim3(DEC_THREADS), 0,
+                           stream, (const T *)q, (const T *)k, (const T *)v, (const T *)log_alpha,
+                           (const T *)beta, S, (T *)o, units, H, L, gate, state_idx, pool);
     return hipGetLastError();
 }
 
 template <typename T>
 static hipError_t dispatch_decode_t(const void *q, const void *k, const void *v,
                                     const void *log_alpha, const void *beta, float *S,
-                                    void *o, int units, int H, int gate,
+                                    void *o, int units, int H, int L, int gate,
                                     const int32_t *state_idx, int pool, int dk, int dv,
                                     hipStream_t stream)
 {
 #define KDA_DEC(DK_, DV_) \
-    launch_decode<DK_, DV_, T>(q, k, v, log_alpha, beta, S, o, units, H, gate, state_idx, pool, stream)
+    launch_decode<DK_, DV_, T>(q, k, v, log_alpha, beta, S, o, units, H, L, gate, state_idx, pool, stream)
     if (dk == 128 && dv == 128) return KDA_DEC(128, 128);
     if (dk == 128 && dv == 64) return KDA_DEC(128, 64);
     if (dk == 64 && dv == 128) return KDA_DEC(64, 128);
@@ -231,16 +271,16 @@ static hipError_t dispatch_decode_t(const void *q, const void *k, const void *v,
 // Host-side launcher used by the C ABI (sizes already validated).
 hipError_t decode_step_launch(const void *q, const void *k, const void *v,
                               const void *log_alpha, const void *beta, int gate, float *S,
-                              const int32_t *state_idx, int pool, void *o, int N, int H,
+                              const int32_t *state_idx, int pool, void *o, int N, int L, int H,
                               int dk, int dv, bool bf16, hipStream_t stream)
 {
     const int units = N * H;
-    if (units == 0) return hipSuccess;
+    if (units == 0 || L == 0) return hipSuccess;
     if (bf16)
-        return dispatch_decode_t<bf16_t>(q, k, v, log_alpha, beta, S, o, units, H, gate, state_idx,
-                                         pool, dk, dv, stream);
-    return dispatch_decode_t<float>(q, k, v, log_alpha, beta, S, o, units, H, gate, state_idx, pool,
-                                    dk, dv, stream);
+        return dispatch_decode_t<bf16_t>(q, k, v, log_alpha, beta, S, o, units, H, L, gate,
+                                         state_idx, pool, dk, dv, stream);
+    return dispatch_decode_t<float>(q, k, v, log_alpha, beta, S, o, units, H, L, gate, state_idx,
+                                    pool, dk, dv, stream);
 }
 
 }  // namespace kda

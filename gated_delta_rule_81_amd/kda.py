@@ -60,7 +60,7 @@ def lib() -> ctypes.CDLL:
     L.kda_decode_step_ex.restype = ctypes.c_int
     L.kda_decode_step_ex.argtypes = [_vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp, _vp,
                                      ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                                     ctypes.c_int, ctypes.c_int, _vp, _vp]
+                                     ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp, _vp]
     _lib = L
     return L
 
@@ -199,12 +199,14 @@ def fwd_chunked(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, *,
 
 def decode_step(q, k, v, log_alpha, beta, S_cache, *, o=None, gate: str = "channel",
                 state_idx=None) -> torch.Tensor:
-    """One-token KDA update of S_cache in place (kda_decode_step / _ex); returns o.
+    """KDA decode of S_cache in place (kda_decode_step / _ex); returns o.
 
-    q, k: (N, H, dk); v: (N, H, dv); beta: (N, H) of one dtype; log_alpha:
-    (N, H, dk) for gate="channel", (N, H) for gate="head", ignored for
-    gate="none".  S_cache: (N, H, dk, dv) fp32, or with state_idx (int32 (N,)
-    on the GPU) a pool (P, H, dk, dv) whose row state_idx[n] sequence n updates.
+    One token per sequence: q, k: (N, H, dk); v: (N, H, dv); beta: (N, H);
+    or L consecutive tokens per sequence: q, k: (N, L, H, dk); v: (N, L, H, dv);
+    beta: (N, L, H), all of one dtype.  log_alpha has q's shape for
+    gate="channel", beta's for gate="head", and is ignored for gate="none".
+    S_cache: (N, H, dk, dv) fp32, or with state_idx (int32 (N,) on the GPU) a
+    pool (P, H, dk, dv) whose row state_idx[n] sequence n updates.
     """
     _gate_code(gate)
     dev = q.device
@@ -212,31 +214,35 @@ def decode_step(q, k, v, log_alpha, beta, S_cache, *, o=None, gate: str = "chann
     for name, t in (("q", q), ("k", k), ("v", v), ("beta", beta)):
         _check(t, name, dev, dt)
     _check(S_cache, "S_cache", dev, torch.float32)
-    N, H, dk = q.shape
+    if q.dim() == 4:
+        N, L, H, dk = q.shape
+    else:
+        (N, H, dk), L = q.shape, 1
     dv = v.shape[-1]
     gcode = _check_gate(log_alpha, gate, q.shape, dev, dt)
+    tok = (N, L, H) if q.dim() == 4 else (N, H)
     rows = N
     if state_idx is not None:
         _check(state_idx, "state_idx", dev, torch.int32)
         if state_idx.shape != (N,):
             raise ValueError(f"state_idx must have shape {(N,)}")
         rows = S_cache.shape[0]
-    if k.shape != q.shape or v.shape != (N, H, dv) or beta.shape != (N, H) \
+    if k.shape != q.shape or v.shape != tok + (dv,) or beta.shape != tok \
             or S_cache.shape != (rows, H, dk, dv):
         raise ValueError("inconsistent input shapes")
     if o is None:
-        o = torch.empty((N, H, dv), dtype=dt, device=dev)
+        o = torch.empty(tok + (dv,), dtype=dt, device=dev)
     else:
         _check(o, "o", dev, dt)
     ga = None if gcode == KDA_GATE_NONE else log_alpha
-    if gcode == KDA_GATE_CHANNEL and state_idx is None:
+    if gcode == KDA_GATE_CHANNEL and state_idx is None and L == 1:
         st = lib().kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(ga), _ptr(beta),
                                    _ptr(S_cache), N, H, dk, dv, _dtype_code(q), _ptr(o),
                                    _stream(dev))
         where = "kda_decode_step"
     else:
         st = lib().kda_decode_step_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(ga), _ptr(beta), gcode,
-                                      _ptr(S_cache), _ptr(state_idx), int(rows), N, H, dk, dv,
+                                      _ptr(S_cache), _ptr(state_idx), int(rows), N, L, H, dk, dv,
                                       _dtype_code(q), _ptr(o), _stream(dev))
         where = "kda_decode_step_ex"
     if st != KDA_OK:

@@ -168,9 +168,18 @@ kda_status kda_decode_step(const void *q, const void *k, const void *v,
                            kda_dtype dtype, void *o, void *stream);
 
 /*
- * kda_decode_step_ex -- kda_decode_step with a gate layout and a state pool.
+ * kda_decode_step_ex -- kda_decode_step with a gate layout, a state pool and
+ * L consecutive tokens per sequence.
  *
- *   gate            : layout of log_alpha: (N, H, dk), (N, H) or unused (kda_gate).
+ *   L               : tokens per sequence in this call (L >= 0; 0 does nothing).
+ *                     The recurrence runs over them in order (the recurrent
+ *                     form, constant work per token: "The fourth layer
+ *                     remembers"); each state is read and written once per call.
+ *   q, k            : (N, L, H, dk)      dtype
+ *   v               : (N, L, H, dv)      dtype
+ *   log_alpha       : (N, L, H, dk), (N, L, H) or unused, per `gate` (kda_gate)
+ *   beta            : (N, L, H)          dtype
+ *   o               : (N, L, H, dv)      dtype, written
  *   S_pool          : fp32 states, read and rewritten in place: (N, H, dk, dv)
  *                     when state_idx is NULL, else (pool_size, H, dk, dv).
  *   state_idx       : NULL, or (N,) int32 device array: sequence n updates row
@@ -178,12 +187,13 @@ kda_status kda_decode_step(const void *q, const void *k, const void *v,
  *                     means no state: o is computed from a zero state and
  *                     nothing is written.  Valid indices must be distinct.
  * Every other argument is that of kda_decode_step, which equals this call
- * with KDA_GATE_CHANNEL and no state_idx.
+ * with KDA_GATE_CHANNEL, no state_idx and L = 1.
  */
 kda_status kda_decode_step_ex(const void *q, const void *k, const void *v,
                               const void *log_alpha, const void *beta, kda_gate gate,
                               float *S_pool, const int32_t *state_idx, int pool_size,
-                              int N, int H, int dk, int dv, kda_dtype dtype, void *o, void *stream);
+                              int N, int L, int H, int dk, int dv, kda_dtype dtype, void *o,
+                              void *stream);
 
 #ifdef __cplusplus
 }

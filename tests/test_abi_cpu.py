@@ -134,9 +134,9 @@ def fwd_ex(L, q=FAKE, k=FAKE, v=FAKE, g=FAKE, b=FAKE, gate=0, S0=None, S_T=None,
                                 o, ws, wsb, None)
 
 
-def dec_ex(L, q=FAKE, k=FAKE, v=FAKE, g=FAKE, b=FAKE, gate=0, S=FAKE, idx=None, P=0, N=4, H=2,
+def dec_ex(L, q=FAKE, k=FAKE, v=FAKE, g=FAKE, b=FAKE, gate=0, S=FAKE, idx=None, P=0, N=4, T=1, H=2,
            dk=128, dv=128, dt=1, o=FAKE):
-    return L.kda_decode_step_ex(q, k, v, g, b, gate, S, idx, P, N, H, dk, dv, dt, o, None)
+    return L.kda_decode_step_ex(q, k, v, g, b, gate, S, idx, P, N, T, H, dk, dv, dt, o, None)
 
 
 @pytest.mark.parametrize("gate", [-1, 3, 100])
@@ -166,6 +166,13 @@ def test_ex_slot_map_rules(L):
     assert dec_ex(L, dv=32) == 2
     assert fwd_ex(L, cu=FAKE, N=8, idx=FAKE, P=8) == 1  # varlen workspace missing
     assert fwd_ex(L, B=0, T=0, idx=FAKE, P=0) == 0
+
+
+def test_decode_ex_tokens_per_sequence(L):
+    assert dec_ex(L, T=-1) == 1
+    assert dec_ex(L, T=0) == 0                          # nothing to do
+    assert dec_ex(L, T=0, q=None, S=None) == 0
+    assert dec_ex(L, T=3, q=None) == 1
 
 
 def test_binding_rejects_bad_gate_shapes():

@@ -242,3 +242,60 @@ def test_multi_token_decode_matches_steps(gate):
     assert rel_err(f64(o_dec), f64(o_chunk)) <= TOL[torch.bfloat16]
     assert rel_err(f64(pool_b), f64(pool_a)) <= TOL[torch.bfloat16]
     assert torch.equal(pool_a[4].cpu(), pool[4].cpu()) and torch.equal(pool_b[4].cpu(), pool[4].cpu())
+
+
+@pytest.mark.parametrize("L", [2, 5])
+@pytest.mark.parametrize("gate", ["channel", "head", "none"])
+@pytest.mark.parametrize("dt,dk,dv", [(torch.bfloat16, 128, 128), (torch.float32, 64, 128)])
+def test_decode_several_tokens_per_sequence(L, gate, dt, dk, dv):
+    """L tokens per sequence in one decode call (state kept in registers
+    across them), on a pool with padding and out-of-pool slots."""
+    import oracle
+    from gated_delta_rule_81_amd import kda
+    N, H, P = 6, 3, 8
+    idx = [7, 0, -1, 3, 9, 5]
+    _say(f"case: decode L={L} gate={gate} {dt} dk{dk} dv{dv} idx {idx}")
+    x = _inputs(N, L, H, dk, dv, dt, seed=70 + L, gate=gate, s0_std=0.0)
+    gen = torch.Generator().manual_seed(71)
+    pool = 0.2 * torch.randn(P, H, dk, dv, generator=gen)
+    xg = {k_: (v_.to(DEV) if isinstance(v_, torch.Tensor) else v_) for k_, v_ in x.items()}
+    pg = pool.to(DEV)
+    o = kda.decode_step(xg["q"], xg["k"], xg["v"], xg["log_alpha"], xg["beta"], pg, gate=gate,
+                        state_idx=torch.tensor(idx, dtype=torch.int32, device=DEV))
+    torch.cuda.synchronize()
+    assert o.shape == (N, L, H, dv)
+    # the (N, L, H, .) inputs are N dense sequences of L tokens
+    o_ref, pool_ref = oracle.fwd_pooled(f64(x["q"]), f64(x["k"]), f64(x["v"]),
+                                        _f64o(x["log_alpha"]), f64(x["beta"]), f64(pool), idx,
+                                        None, gate=gate, S_T_pool=f64(pool))
+    eo, es = rel_err(f64(o), o_ref), rel_err(f64(pg), pool_ref)
+    _say(f"  rel err o={eo:.3e} pool={es:.3e}")
+    assert eo <= TOL[dt] and es <= TOL[dt]
+    for r in (1, 2, 4, 6):
+        assert torch.equal(pg[r].cpu(), pool[r])
+
+
+def test_decode_tokens_match_chunked_and_single_steps():
+    """Four tokens per sequence: one decode call with L = 4, the pooled chunked
+    forward, and four single-token decode steps agree."""
+    from gated_delta_rule_81_amd import kda
+    N, H, dk, dv, P, L = 5, 2, 128, 128, 6, 4
+    idx = torch.tensor([5, 1, 0, 3, 2], dtype=torch.int32, device=DEV)
+    _say(f"case: decode L={L} vs chunked vs steps")
+    x = _inputs(N, L, H, dk, dv, torch.bfloat16, seed=81, gate="channel", s0_std=0.0)
+    g = {k_: (v_.to(DEV) if isinstance(v_, torch.Tensor) else v_) for k_, v_ in x.items()}
+    pool = (0.2 * torch.randn(P, H, dk, dv, generator=torch.Generator().manual_seed(82))).to(DEV)
+    pa, pb, pc = pool.clone(), pool.clone(), pool.clone()
+    o_l = kda.decode_step(g["q"], g["k"], g["v"], g["log_alpha"], g["beta"], pa, state_idx=idx)
+    flat = {k_: g[k_].reshape((1, N * L) + g[k_].shape[2:]).contiguous() for k_ in ("q", "k", "v", "log_alpha", "beta")}
+    cu = torch.arange(0, N * L + 1, L, dtype=torch.int32, device=DEV)
+    o_c, _ = kda.fwd_chunked(flat["q"], flat["k"], flat["v"], flat["log_alpha"], flat["beta"], pb,
+                             cu, S_T=pb, state_idx=idx)
+    steps = [kda.decode_step(*(g[k_][:, t].contiguous() for k_ in ("q", "k", "v", "log_alpha", "beta")),
+                             pc, state_idx=idx) for t in range(L)]
+    torch.cuda.synchronize()
+    o_s = torch.stack(steps, dim=1)
+    tol = TOL[torch.bfloat16]
+    assert rel_err(f64(o_l), f64(o_s)) <= tol and rel_err(f64(pa), f64(pc)) <= tol
+    assert rel_err(f64(o_l.reshape(1, N * L, H, dv)), f64(o_c)) <= tol
+    assert rel_err(f64(pa), f64(pb)) <= tol
