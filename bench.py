@@ -154,12 +154,16 @@ def _fwd_bytes(tokens, H, dk, dv, N, gate_elems, elem=2):
 
 def bench_other_workloads(torch, kda, synth, steps=10, warmup=3):
     """The forward on the H16 and packed-varlen workloads, and the headline
-    shape with a per-head gate and with no gate (reported beside the
-    headline line, not in `value`)."""
+    shape with a per-head gate, with no gate, and with the input preparation
+    fused in (q and k L2-normalised in the kernel, the gate taken as
+    -softplus of its input; the headline inputs serve as the raw inputs)
+    (reported beside the headline line, not in `value`)."""
     out = {}
-    cases = [(synth.FWD_H16_T4K, "channel", ""), (synth.VARLEN_64, "channel", ""),
-             (synth.FWD_H32_T8K, "head", "_gate_head"), (synth.FWD_H32_T8K, "none", "_gate_none")]
-    for w, gate, suffix in cases:
+    prep = kda.KDA_FLAG_L2NORM_QK | kda.KDA_FLAG_GATE_SOFTPLUS
+    cases = [(synth.FWD_H16_T4K, "channel", "", 0), (synth.VARLEN_64, "channel", "", 0),
+             (synth.FWD_H32_T8K, "head", "_gate_head", 0), (synth.FWD_H32_T8K, "none", "_gate_none", 0),
+             (synth.FWD_H32_T8K, "channel", "_prep_l2norm_softplus", prep)]
+    for w, gate, suffix, flags in cases:
         log(f"[bench] generating {w.name} on the GPU (gate={gate})")
         x = synth.fwd_inputs(w, device="cuda")
         B, T, H, dk, dv, N = x["B"], x["T"], x["H"], x["dk"], x["dv"], x["N"]
@@ -177,7 +181,7 @@ def bench_other_workloads(torch, kda, synth, steps=10, warmup=3):
 
         def step():
             kda.fwd_chunked(x["q"], x["k"], x["v"], g, x["beta"], x["S0"],
-                            x["cu_seqlens"], o=o, S_T=S_T, workspace=ws, gate=gate)
+                            x["cu_seqlens"], o=o, S_T=S_T, workspace=ws, gate=gate, flags=flags)
 
         secs = time_loop(torch, step, steps, warmup) / steps
         tokens = B * T

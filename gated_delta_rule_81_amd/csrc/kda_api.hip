@@ -8,11 +8,11 @@
 
 namespace kda {
 hipError_t decode_step_launch(const void *q, const void *k, const void *v,
-                              const void *log_alpha, const void *beta, int gate, float *S,
+                              const void *log_alpha, const void *beta, int gate, int prep, float *S,
                               const int32_t *state_idx, int pool, void *o, int N, int L, int H,
                               int dk, int dv, bool bf16, hipStream_t stream);
 hipError_t chunked_fwd_launch(const void *q, const void *k, const void *v, const void *g,
-                              const void *beta, int gate, const float *S0, float *S_T,
+                              const void *beta, int gate, int prep, const float *S0, float *S_T,
                               const int32_t *state_idx, int pool, void *o,
                               const int32_t *cu_seqlens, int num_seqs, int B, int T, int H,
                               int dk, int dv, bool bf16, void *workspace, hipStream_t stream);
@@ -25,6 +25,8 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 bool dim_ok(int d) { return d == 64 || d == 128; }
 
 bool gate_ok(kda_gate g) { return g == KDA_GATE_CHANNEL || g == KDA_GATE_HEAD || g == KDA_GATE_NONE; }
+
+bool flags_ok(unsigned f) { return (f & ~(unsigned)(KDA_FLAG_L2NORM_QK | KDA_FLAG_GATE_SOFTPLUS)) == 0; }
 
 bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
@@ -66,13 +68,14 @@ size_t kda_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int num_seqs
 
 kda_status kda_fwd_chunked_ex(const void *q, const void *k, const void *v,
                               const void *log_alpha, const void *beta, kda_gate gate,
+                              unsigned flags,
                               const float *S0, float *S_T, const int32_t *state_idx, int pool_size,
                               const int32_t *cu_seqlens, int num_seqs,
                               int B, int T, int H, int dk, int dv, kda_dtype dtype,
                               void *o, void *workspace, size_t workspace_bytes, void *stream)
 {
     if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_INVALID_ARG;
-    if (!gate_ok(gate)) return KDA_ERR_INVALID_ARG;
+    if (!gate_ok(gate) || !flags_ok(flags)) return KDA_ERR_INVALID_ARG;
     if (B < 0 || T < 0 || H <= 0 || dk <= 0 || dv <= 0) return KDA_ERR_INVALID_ARG;
     if (cu_seqlens && (B != 1 || num_seqs < 0)) return KDA_ERR_INVALID_ARG;
     const int nseq = cu_seqlens ? num_seqs : B;
@@ -98,7 +101,7 @@ kda_status kda_fwd_chunked_ex(const void *q, const void *k, const void *v,
         if (!workspace || workspace_bytes < need || !aligned16(workspace)) return KDA_ERR_INVALID_ARG;
     }
     if (nseq == 0) return KDA_OK;
-    hipError_t e = kda::chunked_fwd_launch(q, k, v, g, beta, (int)gate, S0, S_T, state_idx,
+    hipError_t e = kda::chunked_fwd_launch(q, k, v, g, beta, (int)gate, (int)flags, S0, S_T, state_idx,
                                            pool_size, o, cu_seqlens, nseq, B, T, H, dk, dv,
                                            dtype == KDA_BF16, cu_seqlens ? workspace : nullptr,
                                            static_cast<hipStream_t>(stream));
@@ -112,19 +115,20 @@ kda_status kda_fwd_chunked(const void *q, const void *k, const void *v,
                            void *o, float *S_T,
                            void *workspace, size_t workspace_bytes, void *stream)
 {
-    return kda_fwd_chunked_ex(q, k, v, log_alpha, beta, KDA_GATE_CHANNEL, S0, S_T, nullptr, 0,
+    return kda_fwd_chunked_ex(q, k, v, log_alpha, beta, KDA_GATE_CHANNEL, 0u, S0, S_T, nullptr, 0,
                               cu_seqlens, num_seqs, B, T, H, dk, dv, dtype, o, workspace,
                               workspace_bytes, stream);
 }
 
 kda_status kda_decode_step_ex(const void *q, const void *k, const void *v,
                               const void *log_alpha, const void *beta, kda_gate gate,
+                              unsigned flags,
                               float *S_pool, const int32_t *state_idx, int pool_size,
                               int N, int L, int H, int dk, int dv, kda_dtype dtype, void *o,
                               void *stream)
 {
     if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_INVALID_ARG;
-    if (!gate_ok(gate)) return KDA_ERR_INVALID_ARG;
+    if (!gate_ok(gate) || !flags_ok(flags)) return KDA_ERR_INVALID_ARG;
     if (N < 0 || L < 0 || H <= 0 || dk <= 0 || dv <= 0) return KDA_ERR_INVALID_ARG;
     if (!dim_ok(dk) || !dim_ok(dv)) return KDA_ERR_UNSUPPORTED;
     if (!sizes_fit(N, H, dk, dv) || !sizes_fit(N, L, H, dk > dv ? dk : dv)) return KDA_ERR_INVALID_ARG;
@@ -136,7 +140,7 @@ kda_status kda_decode_step_ex(const void *q, const void *k, const void *v,
     if (gate != KDA_GATE_NONE && !log_alpha) return KDA_ERR_INVALID_ARG;
     if (!aligned16(S_pool)) return KDA_ERR_INVALID_ARG;
     hipError_t e = kda::decode_step_launch(q, k, v, gate == KDA_GATE_NONE ? nullptr : log_alpha,
-                                           beta, (int)gate, S_pool, state_idx, pool_size, o, N, L, H,
+                                           beta, (int)gate, (int)flags, S_pool, state_idx, pool_size, o, N, L, H,
                                            dk, dv, dtype == KDA_BF16,
                                            static_cast<hipStream_t>(stream));
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
@@ -147,7 +151,7 @@ kda_status kda_decode_step(const void *q, const void *k, const void *v,
                            float *S_cache, int N, int H, int dk, int dv,
                            kda_dtype dtype, void *o, void *stream)
 {
-    return kda_decode_step_ex(q, k, v, log_alpha, beta, KDA_GATE_CHANNEL, S_cache, nullptr, 0,
+    return kda_decode_step_ex(q, k, v, log_alpha, beta, KDA_GATE_CHANNEL, 0u, S_cache, nullptr, 0,
                               N, 1, H, dk, dv, dtype, o, stream);
 }
 

@@ -61,6 +61,7 @@ struct ChunkParams {
     const int32_t *state_idx;    // slot map of S0 / S_T rows (NULL -> row = sequence)
     int pool;       // rows of S0 / S_T when state_idx is set
     int gate;       // GATE_CHANNEL / GATE_HEAD / GATE_NONE
+    int prep;       // PREP_L2NORM | PREP_SOFTPLUS
     int T;          // tokens per batch row (dense)
     int H;
     int DV;         // full value dimension
@@ -377,6 +378,38 @@ __global__ __launch_bounds__(256, 1) void chunked_fwd_kernel(ChunkParams p)
     for (long c0 = 0; c0 < len; c0 += CH) {
         const int clen = (int)((len - c0) < CH ? (len - c0) : CH);
         const bool rvalid = rloc < clen;
+        // L2 normalisation of this lane's k and q row, whose channels are
+        // spread over the four lanes 16 apart (factors 1 when not asked for)
+        float ikn = 1.0f, iqn = 1.0f;
+        if (p.prep & PREP_L2NORM) {
+            float sk = 0.f, sq = 0.f;
+#pragma unroll
+            for (int rr = 0; rr < NRUN; ++rr) {
+                float kk[RUN], qq[RUN];
+                raw_to_f32<F32>(rawk[rr], kk);
+                raw_to_f32<F32>(rawq[rr], qq);
+#pragma unroll
+                for (int e = 0; e < RUN; ++e) {
+                    sk += kk[e] * kk[e];
+                    sq += qq[e] * qq[e];
+                }
+            }
+            sk += __shfl_xor(sk, 16);
+            sk += __shfl_xor(sk, 32);
+            sq += __shfl_xor(sq, 16);
+            sq += __shfl_xor(sq, 32);
+            ikn = inv_norm(sk);
+            iqn = inv_norm(sq);
+        }
+        auto load_kq = [&](int rr, float *kk, float *qq) {
+            raw_to_f32<F32>(rawk[rr], kk);
+            raw_to_f32<F32>(rawq[rr], qq);
+#pragma unroll
+            for (int e = 0; e < RUN; ++e) {
+                kk[e] *= ikn;
+                qq[e] *= iqn;
+            }
+        };
         const bool has_next = c0 + CH < len;
         const int clen_next = has_next ? (int)((len - c0 - CH) < CH ? (len - c0 - CH) : CH) : 0;
 
@@ -394,7 +427,9 @@ __global__ __launch_bounds__(256, 1) void chunked_fwd_kernel(ChunkParams p)
             raw_to_f32<F32>(rawg[rr], x);
 #pragma unroll
             for (int e = 0; e < RUN; ++e) {
-                float v = rvalid ? x[e] * kLog2e : 0.0f;
+                float v = !rvalid ? 0.0f
+                        : (p.prep & PREP_SOFTPLUS) && p.gate != GATE_NONE ? log2_alpha_softplus(x[e])
+                                                                          : x[e] * kLog2e;
                 v += dpp_row_shr(v, 1);
                 v += dpp_row_shr(v, 2);
                 v += dpp_row_shr(v, 4);
@@ -448,8 +483,7 @@ __global__ __launch_bounds__(256, 1) void chunked_fwd_kernel(ChunkParams p)
             for (int rr = 0; rr < NRUN; ++rr) {
                 const int cbase = 4 * RUN * rr + RUN * jg;
                 float kk[RUN], qq[RUN];
-                raw_to_f32<F32>(rawk[rr], kk);
-                raw_to_f32<F32>(rawq[rr], qq);
+                load_kq(rr, kk, qq);
                 float ka[RUN], qa[RUN], kb[RUN], ku[RUN], qu[RUN], kr[RUN];
 #pragma unroll
                 for (int e = 0; e < RUN; ++e) {
@@ -523,8 +557,7 @@ __global__ __launch_bounds__(256, 1) void chunked_fwd_kernel(ChunkParams p)
             for (int rr = 0; rr < NRUN; ++rr) {
                 const int cbase = 4 * RUN * rr + RUN * jg;
                 float kk[RUN], qq[RUN];
-                raw_to_f32<F32>(rawk[rr], kk);
-                raw_to_f32<F32>(rawq[rr], qq);
+                load_kq(rr, kk, qq);
 #pragma unroll
                 for (int e = 0; e < RUN; ++e) {
                     const int c = cbase + e;
@@ -583,8 +616,7 @@ __global__ __launch_bounds__(256, 1) void chunked_fwd_kernel(ChunkParams p)
             for (int rr = 0; rr < NRUN; ++rr) {
                 const int cbase = 4 * RUN * rr + RUN * jg;
                 float kk[RUN], qq[RUN], ku[RUN], qu[RUN], kr[RUN];
-                raw_to_f32<F32>(rawk[rr], kk);
-                raw_to_f32<F32>(rawq[rr], qq);
+                load_kq(rr, kk, qq);
 #pragma unroll
                 for (int e = 0; e < RUN; ++e) {
                     const int c = cbase + e;
@@ -828,13 +860,13 @@ int chunked_slice_width(int units, int dv)
 }
 
 hipError_t chunked_ws_launch(const void *q, const void *k, const void *v, const void *g,
-                             const void *beta, int gate, const float *S0, float *S_T,
+                             const void *beta, int gate, int prep, const float *S0, float *S_T,
                              const int32_t *state_idx, int pool, void *o,
                              const int32_t *cu_seqlens, const int32_t *order, int nseq, int T,
                              int H, int dk, int dv, int slice_width, hipStream_t stream);
 
 hipError_t chunked_fwd_launch(const void *q, const void *k, const void *v, const void *g,
-                              const void *beta, int gate, const float *S0, float *S_T,
+                              const void *beta, int gate, int prep, const float *S0, float *S_T,
                               const int32_t *state_idx, int pool, void *o,
                               const int32_t *cu_seqlens, int num_seqs, int B, int T, int H,
                               int dk, int dv, bool bf16, void *workspace, hipStream_t stream)
@@ -847,6 +879,7 @@ hipError_t chunked_fwd_launch(const void *q, const void *k, const void *v, const
     p.state_idx = state_idx;
     p.pool = pool;
     p.gate = gate;
+    p.prep = prep;
     p.T = T; p.H = H; p.DV = dv;
     const int nseq = cu_seqlens ? num_seqs : B;
     p.units = nseq * H;
@@ -861,7 +894,7 @@ hipError_t chunked_fwd_launch(const void *q, const void *k, const void *v, const
     }
     const int dvs = chunked_slice_width(p.units, dv);
     if (bf16)   // producer / consumer kernel with 32-token chunks
-        return chunked_ws_launch(q, k, v, g, beta, gate, S0, S_T, state_idx, pool, o, cu_seqlens,
+        return chunked_ws_launch(q, k, v, g, beta, gate, prep, S0, S_T, state_idx, pool, o, cu_seqlens,
                                  p.order, nseq, T, H, dk, dv, dvs, stream);
     p.nslices = dv / dvs;
     const int nstrip = dvs / 64;

@@ -75,7 +75,8 @@ struct Lds {
     static constexpr int P_T = C * LA * 4;
     static constexpr int P_USED = (C * DK * 2 > 2 * C * LA * 4) ? C * DK * 2 : 2 * C * LA * 4;
     static constexpr int P_BETA = P_USED > 8192 ? P_USED : 8192;
-    static constexpr int PRIV = P_BETA + C * 4;
+    static constexpr int P_NORM = P_BETA + C * 4;             // 1/|k_r|, 1/|q_r| fp32 [2][32]
+    static constexpr int PRIV = P_NORM + 2 * C * 4;
     static constexpr int PRIV_BASE = NSLOT * SLOT;
     static constexpr int SYNC = PRIV_BASE + NPROD * PRIV;   // full[4], freed[4], dead
     static constexpr int BYTES = SYNC + 64;
@@ -178,6 +179,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *base) {
 constexpr uint32_t OOB_OFF = 0x80000000u;
 __device__ __forceinline__ float bf_hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
 
+// Sum over the 16 lanes of a row (lanes 16j .. 16j + 15), in every lane of it:
+// pair swaps within quads, then the mirrors of 8 and 16 lanes.
+__device__ __forceinline__ float row16_sum(float v) {
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));
+    return v;
+}
+
 // Row r and column i of pair number pidx of the lower triangle (i <= r),
 // pairs numbered row by row.
 __device__ __forceinline__ void tri_pair(int pidx, int &r, int &i) {
@@ -194,17 +205,19 @@ __device__ __forceinline__ void tri_pair(int pidx, int &r, int &i) {
 // k_rc k_ic 2^(G_rc - G_ic) (i < r), P_ri = sum_c q_rc k_ic 2^(G_rc - G_ic)
 // (i <= r), G the inclusive cumulative decay in log2 units.  The gate of
 // (row r, channel c) is bg[r * gstride + c * gch]: gch = 0 for a gate shared
-// by the channels of a head.  Channels are
+// by the channels of a head.  With PREP_SOFTPLUS the gate is the softplus
+// input; with PREP_L2NORM k and q rows are scaled by pNorm (1/|k_r|, 1/|q_r|).  Channels are
 // staged 32 at a time in the producer's private LDS region; lane l owns
 // pairs l, l+64, ... of the 528 lower pairs.  Writes A^T (fp32, private) and
 // P (bf16, slot).  Kept out of line: it runs only for chunks with extreme
 // decay, and its registers stay out of the hot path's budget.
 template <int DK>
 __device__ __attribute__((noinline)) void exact_ap(int lane, int cl, uint32_t tokk,
-                                                   uint32_t gstride, uint32_t gch,
+                                                   uint32_t gstride, uint32_t gch, int prep,
                                                    const bf16_t *bg, const bf16_t *bk,
                                                    const bf16_t *bq, unsigned char *priv,
-                                                   float *pAt, bf16_t *sP, const float *pBeta)
+                                                   float *pAt, bf16_t *sP, const float *pBeta,
+                                                   const float *pNorm)
 {
     using namespace ws;
     constexpr int CPL = DK / 64;
@@ -232,13 +245,19 @@ __device__ __attribute__((noinline)) void exact_ap(int lane, int cl, uint32_t to
                     const int cq = CPL * (lane - qd * LPQ) + e;
                     const int c = QCH * qd + cq;
                     const uint32_t g1 = (uint32_t)(bg[rr_ * gstride + c * gch].x & m16);
-                    bf16_t k1, q1;
-                    k1.x = bk[rr_ * tokk + c].x & m16;
-                    q1.x = bq[rr_ * tokk + c].x & m16;
-                    G[e] += bf_lo(g1) * kLog2e;
+                    float kf = bf_lo((uint32_t)(bk[rr_ * tokk + c].x & m16));
+                    float qf = bf_lo((uint32_t)(bq[rr_ * tokk + c].x & m16));
+                    if (prep & PREP_L2NORM) {
+                        kf *= pNorm[r];
+                        qf *= pNorm[C + r];
+                    }
+                    // rows past the end: alpha = 1
+                    G[e] += r >= cl ? 0.0f
+                          : (prep & PREP_SOFTPLUS) ? log2_alpha_softplus(bf_lo(g1))
+                                                   : bf_lo(g1) * kLog2e;
                     stG[r * 32 + cq] = G[e];
-                    stK[r * 32 + cq] = k1;
-                    stQ[r * 32 + cq] = q1;
+                    stK[r * 32 + cq] = to_bf16(kf);
+                    stQ[r * 32 + cq] = to_bf16(qf);
                 }
             }
         }
@@ -279,7 +298,7 @@ __device__ __attribute__((noinline)) void exact_ap(int lane, int cl, uint32_t to
     }
 }
 
-template <int DK, int NSTRIP, int GATE>
+template <int DK, int NSTRIP, int GATE, int PREP>
 __global__ __launch_bounds__(512, 1) void chunked_ws_kernel(WsParams p)
 {
     using namespace ws;
@@ -560,6 +579,7 @@ __global__ __launch_bounds__(512, 1) void chunked_ws_kernel(WsParams p)
     float *pAt = reinterpret_cast<float *>(priv + L::P_AT);
     float *pT = reinterpret_cast<float *>(priv + L::P_T);
     float *pBeta = reinterpret_cast<float *>(priv + L::P_BETA);
+    float *pNorm = reinterpret_cast<float *>(priv + L::P_NORM);
     const uint32_t tokk = (uint32_t)H * DK;
 
     // Raw g and k of one chunk, lane (cg, rg) = (lane & 15, lane >> 4)
@@ -571,7 +591,11 @@ __global__ __launch_bounds__(512, 1) void chunked_ws_kernel(WsParams p)
     // one value per row, laid out like beta; without a gate nothing is read.
     uint32_t gx[8][NCL / 2], gh[8], kx[8][NCL / 2], bx;
     auto load_gk = [&](int n) {
-        const int lane = tid & 63, cg = lane & 15, rg = lane >> 4;
+        // the row offsets below are recomputed per chunk from an opaque copy
+        // of the lane id instead of being hoisted out of the loop
+        int lane_o = tid & 63;
+        asm volatile("" : "+v"(lane_o));
+        const int lane = lane_o, cg = lane & 15, rg = lane >> 4;
         const int c0 = NCL * cg, r0 = 8 * rg;
         const long cs = (long)n * C;
         const int cl = (int)((len - cs) < C ? (len - cs) : C);
@@ -642,19 +666,49 @@ __global__ __launch_bounds__(512, 1) void chunked_ws_kernel(WsParams p)
 
         // ---- decay ---------------------------------------------------------------
         if (r0 + 8 > cl) {
-            // rows past the chunk end: g = 0 (alpha = 1), k = q = 0
+            // rows past the chunk end: alpha = 1 (g = 0, or a softplus input
+            // of -inf), k = q = 0
+            constexpr uint32_t g0 = (PREP & PREP_SOFTPLUS) ? 0xff80ff80u : 0u;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const uint32_t m = (r0 + i) < cl ? 0xffffffffu : 0u;
 #pragma unroll
                 for (int d = 0; d < NCL / 2; ++d) {
-                    if constexpr (GATE == GATE_CHANNEL) gx[i][d] &= m;
+                    if constexpr (GATE == GATE_CHANNEL) gx[i][d] = (gx[i][d] & m) | (g0 & ~m);
                     kx[i][d] &= m;
                     qx[i][d] &= m;
                 }
-                if constexpr (GATE == GATE_HEAD) gh[i] &= m;
+                if constexpr (GATE == GATE_HEAD) gh[i] = (gh[i] & m) | (g0 & 0xffffu & ~m);
             }
         }
+        // L2 normalisation of k and q rows: sums of squares over this lane's
+        // channels, then over the 16 lanes that hold the row, one row at a
+        // time where the forward pass below first needs it.  The factors also
+        // go to this wave's LDS area, from which the reverse pass and the
+        // exact path read them back row by row, so that none stays live in a
+        // register through the decay work.
+        auto row_norm = [&](const uint32_t (&x)[NCL / 2]) -> float {
+            float ss = 0.0f;
+#pragma unroll
+            for (int d = 0; d < NCL / 2; ++d) {
+                const float a = bf_lo(x[d]), b = bf_hi(x[d]);
+                ss += a * a + b * b;
+            }
+            return inv_norm(row16_sum(ss));
+        };
+        // norm factor of row r0 + i of k (q: at C + r0 + i); 1 without
+        auto nscale = [&](int at) -> float {
+            // a volatile read is neither hoisted nor merged with its neighbours
+            if constexpr (PREP & PREP_L2NORM) return *static_cast<volatile const float *>(pNorm + at);
+            else {
+                return 1.0f;
+            }
+        };
+        // alpha of a gate value: e^g, or e^{-softplus(x)}
+        auto alpha_of = [](float gv) -> float {
+            if constexpr (PREP & PREP_SOFTPLUS) return alpha_softplus(gv);
+            else return __builtin_amdgcn_exp2f(gv * kLog2e);
+        };
         // Decay factors.  Per key channel: alpha of each (row, channel) and the
         // products over this lane's 8 rows (tot); for a per-head gate the same
         // per row (alh, toth); none without a gate (alpha = 1).
@@ -667,14 +721,14 @@ __global__ __launch_bounds__(512, 1) void chunked_ws_kernel(WsParams p)
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 if constexpr (GATE == GATE_HEAD) {
-                    alh[i] = __builtin_amdgcn_exp2f(bf_lo(gh[i]) * kLog2e);
+                    alh[i] = alpha_of(bf_lo(gh[i]));
                     toth *= alh[i];
                 }
 #pragma unroll
                 for (int d = 0; d < NCL / 2; ++d) {
                     if constexpr (GATE == GATE_CHANNEL) {
-                        al[i][2 * d] = __builtin_amdgcn_exp2f(bf_lo(gx[i][d]) * kLog2e);
-                        al[i][2 * d + 1] = __builtin_amdgcn_exp2f(bf_hi(gx[i][d]) * kLog2e);
+                        al[i][2 * d] = alpha_of(bf_lo(gx[i][d]));
+                        al[i][2 * d + 1] = alpha_of(bf_hi(gx[i][d]));
                         tot[2 * d] *= al[i][2 * d];
                         tot[2 * d + 1] *= al[i][2 * d + 1];
                     }
@@ -723,11 +777,12 @@ __global__ __launch_bounds__(512, 1) void chunked_ws_kernel(WsParams p)
                 gamh = preh * toth * posth;
             }
         }
-        // K_dn stays below 2^116 when gamma >= 2^-100 and |k| <= 2^16; with
-        // no gate K_dn = K and the fast path always holds
+        // K_dn stays below 2^116 when gamma >= 2^-100 and |k| <= 2^16 (always,
+        // for normalised k); with no gate K_dn = K and the fast path always holds
         bool ok = true;
         if constexpr (GATE != GATE_NONE) {
-            ok = (kbits & 0xffffu) <= 0x4780u && (kbits >> 16) <= 0x4780u;   // 0x4780: 2^16
+            if constexpr (!(PREP & PREP_L2NORM))
+                ok = (kbits & 0xffffu) <= 0x4780u && (kbits >> 16) <= 0x4780u;   // 0x4780: 2^16
             if constexpr (GATE == GATE_CHANNEL) {
 #pragma unroll
                 for (int e = 0; e < NCL; ++e) ok = ok && (gam[e] >= 7.888609052210118e-31f);
@@ -767,16 +822,26 @@ __global__ __launch_bounds__(512, 1) void chunked_ws_kernel(WsParams p)
             for (int i = 0; i < 8; ++i) {
                 uint32_t ku[NCL / 2], qu[NCL / 2];
                 if constexpr (GATE == GATE_HEAD) Eh *= alh[i];
+                float sk = 1.0f, sq = 1.0f;
+                if constexpr (PREP & PREP_L2NORM) {
+                    sk = row_norm(kx[i]);
+                    sq = row_norm(qx[i]);
+                    if (cg == 0) {
+                        pNorm[r0 + i] = sk;
+                        pNorm[C + r0 + i] = sq;
+                    }
+                }
 #pragma unroll
                 for (int d = 0; d < NCL / 2; ++d) {
                     if constexpr (GATE == GATE_CHANNEL) {
                         E[2 * d] *= al[i][2 * d];
                         E[2 * d + 1] *= al[i][2 * d + 1];
-                        ku[d] = pack2(-bf_lo(kx[i][d]) * E[2 * d], -bf_hi(kx[i][d]) * E[2 * d + 1]);
-                        qu[d] = pack2(bf_lo(qx[i][d]) * E[2 * d], bf_hi(qx[i][d]) * E[2 * d + 1]);
-                    } else if constexpr (GATE == GATE_HEAD) {
-                        ku[d] = pack2(-bf_lo(kx[i][d]) * Eh, -bf_hi(kx[i][d]) * Eh);
-                        qu[d] = pack2(bf_lo(qx[i][d]) * Eh, bf_hi(qx[i][d]) * Eh);
+                        ku[d] = pack2(-bf_lo(kx[i][d]) * (E[2 * d] * sk), -bf_hi(kx[i][d]) * (E[2 * d + 1] * sk));
+                        qu[d] = pack2(bf_lo(qx[i][d]) * (E[2 * d] * sq), bf_hi(qx[i][d]) * (E[2 * d + 1] * sq));
+                    } else if constexpr (GATE == GATE_HEAD || (PREP & PREP_L2NORM)) {
+                        const float ek = Eh * sk, eq = Eh * sq;   // Eh = 1 without a gate
+                        ku[d] = pack2(-bf_lo(kx[i][d]) * ek, -bf_hi(kx[i][d]) * ek);
+                        qu[d] = pack2(bf_lo(qx[i][d]) * eq, bf_hi(qx[i][d]) * eq);
                     } else {
                         // E = 1: the inputs themselves, K negated by its sign bits
                         ku[d] = kx[i][d] ^ 0x80008000u;
@@ -794,7 +859,7 @@ __global__ __launch_bounds__(512, 1) void chunked_ws_kernel(WsParams p)
             }
         }
         // reverse: K_right (rows of K_right^T, 8 tokens per channel) and K_dn rows
-        if constexpr (GATE != GATE_NONE) {
+        if constexpr (GATE != GATE_NONE || (PREP & PREP_L2NORM)) {
             float R[NCL], invg[NCL], kr[8][NCL], Rh = posth;
             const float invgh = __builtin_amdgcn_rcpf(gamh);
 #pragma unroll
@@ -805,17 +870,20 @@ __global__ __launch_bounds__(512, 1) void chunked_ws_kernel(WsParams p)
 #pragma unroll
             for (int i = 7; i >= 0; --i) {
                 uint32_t kd[NCL / 2];
+                const float sk = nscale(r0 + i);
 #pragma unroll
                 for (int d = 0; d < NCL / 2; ++d) {
                     if constexpr (GATE == GATE_CHANNEL) {
-                        kr[i][2 * d] = bf_lo(kx[i][d]) * R[2 * d];
-                        kr[i][2 * d + 1] = bf_hi(kx[i][d]) * R[2 * d + 1];
+                        kr[i][2 * d] = bf_lo(kx[i][d]) * (R[2 * d] * sk);
+                        kr[i][2 * d + 1] = bf_hi(kx[i][d]) * (R[2 * d + 1] * sk);
                         R[2 * d] *= al[i][2 * d];
                         R[2 * d + 1] *= al[i][2 * d + 1];
                         kd[d] = pack2(kr[i][2 * d] * invg[2 * d], kr[i][2 * d + 1] * invg[2 * d + 1]);
                     } else {
-                        kr[i][2 * d] = bf_lo(kx[i][d]) * Rh;
-                        kr[i][2 * d + 1] = bf_hi(kx[i][d]) * Rh;
+                        // a per-head gate, or none (Rh = gamma = 1)
+                        const float rk = Rh * sk;
+                        kr[i][2 * d] = bf_lo(kx[i][d]) * rk;
+                        kr[i][2 * d + 1] = bf_hi(kx[i][d]) * rk;
                         kd[d] = pack2(kr[i][2 * d] * invgh, kr[i][2 * d + 1] * invgh);
                     }
                 }
@@ -911,9 +979,10 @@ __global__ __launch_bounds__(512, 1) void chunked_ws_kernel(WsParams p)
         } else {
             // exact path for chunks whose decay leaves the range of K_dn
             if constexpr (GATE == GATE_CHANNEL)
-                exact_ap<DK>(lane, cl, tokk, tokk, 1u, bg, bk, bq, priv, pAt, sP, pBeta);
+                exact_ap<DK>(lane, cl, tokk, tokk, 1u, PREP, bg, bk, bq, priv, pAt, sP, pBeta, pNorm);
             else if constexpr (GATE == GATE_HEAD)
-                exact_ap<DK>(lane, cl, tokk, (uint32_t)H, 0u, gg + tb, bk, bq, priv, pAt, sP, pBeta);
+                exact_ap<DK>(lane, cl, tokk, (uint32_t)H, 0u, PREP, gg + tb, bk, bq, priv, pAt, sP, pBeta,
+                             pNorm);
         }
         __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
 
@@ -1009,25 +1078,37 @@ __global__ __launch_bounds__(512, 1) void chunked_ws_kernel(WsParams p)
     }
 }
 
-template <int DK, int NSTRIP, int GATE>
+template <int DK, int NSTRIP, int GATE, int PREP>
 static hipError_t launch_ws(const WsParams &p, hipStream_t stream)
 {
     const int groups = (p.units + 7) / 8;
     const dim3 grid(groups * 8 * p.nslices);
-    hipLaunchKernelGGL((chunked_ws_kernel<DK, NSTRIP, GATE>), grid, dim3(512), 0, stream, p);
+    hipLaunchKernelGGL((chunked_ws_kernel<DK, NSTRIP, GATE, PREP>), grid, dim3(512), 0, stream, p);
     return hipGetLastError();
 }
 
-template <int DK, int NSTRIP>
-static hipError_t launch_ws_gate(const WsParams &p, int gate, hipStream_t stream)
+template <int DK, int NSTRIP, int GATE>
+static hipError_t launch_ws_prep(const WsParams &p, int prep, hipStream_t stream)
 {
-    if (gate == GATE_HEAD) return launch_ws<DK, NSTRIP, GATE_HEAD>(p, stream);
-    if (gate == GATE_NONE) return launch_ws<DK, NSTRIP, GATE_NONE>(p, stream);
-    return launch_ws<DK, NSTRIP, GATE_CHANNEL>(p, stream);
+    if constexpr (GATE == GATE_NONE) prep &= PREP_L2NORM;   // no gate to transform
+    switch (prep) {
+    case PREP_L2NORM: return launch_ws<DK, NSTRIP, GATE, PREP_L2NORM>(p, stream);
+    case PREP_SOFTPLUS: return launch_ws<DK, NSTRIP, GATE, PREP_SOFTPLUS>(p, stream);
+    case PREP_L2NORM | PREP_SOFTPLUS: return launch_ws<DK, NSTRIP, GATE, PREP_L2NORM | PREP_SOFTPLUS>(p, stream);
+    default: return launch_ws<DK, NSTRIP, GATE, 0>(p, stream);
+    }
+}
+
+template <int DK, int NSTRIP>
+static hipError_t launch_ws_gate(const WsParams &p, int gate, int prep, hipStream_t stream)
+{
+    if (gate == GATE_HEAD) return launch_ws_prep<DK, NSTRIP, GATE_HEAD>(p, prep, stream);
+    if (gate == GATE_NONE) return launch_ws_prep<DK, NSTRIP, GATE_NONE>(p, prep, stream);
+    return launch_ws_prep<DK, NSTRIP, GATE_CHANNEL>(p, prep, stream);
 }
 
 hipError_t chunked_ws_launch(const void *q, const void *k, const void *v, const void *g,
-                             const void *beta, int gate, const float *S0, float *S_T,
+                             const void *beta, int gate, int prep, const float *S0, float *S_T,
                              const int32_t *state_idx, int pool, void *o,
                              const int32_t *cu_seqlens, const int32_t *order, int nseq, int T,
                              int H, int dk, int dv, int slice_width, hipStream_t stream)
@@ -1044,8 +1125,10 @@ hipError_t chunked_ws_launch(const void *q, const void *k, const void *v, const 
     p.nslices = dv / slice_width;
     const int nstrip = slice_width / 64;
     if (dk == 128)
-        return nstrip == 2 ? launch_ws_gate<128, 2>(p, gate, stream) : launch_ws_gate<128, 1>(p, gate, stream);
-    return nstrip == 2 ? launch_ws_gate<64, 2>(p, gate, stream) : launch_ws_gate<64, 1>(p, gate, stream);
+        return nstrip == 2 ? launch_ws_gate<128, 2>(p, gate, prep, stream)
+                           : launch_ws_gate<128, 1>(p, gate, prep, stream);
+    return nstrip == 2 ? launch_ws_gate<64, 2>(p, gate, prep, stream)
+                       : launch_ws_gate<64, 1>(p, gate, prep, stream);
 }
 
 }  // namespace kda

@@ -21,6 +21,9 @@
 // sums over rows go through LDS.  State traffic uses non-temporal loads and
 // stores: every byte is touched once per step, so caching it only costs.
 //
+// Optional input preparation: k and q divided by their L2 norms (formed with
+// k . q by the first wave; e and p use the raw vectors and are rescaled),
+// and the gate given as the softplus input x with alpha = 1 / (1 + e^x).
 // With L > 1 each sequence takes L consecutive tokens in one call (inputs
 // (N, L, H, .)): the state stays in registers across them and is read and
 // written once.  The gate is one value per key channel (alpha above), one
@@ -40,7 +43,7 @@ template <int DK, int DV, typename T, bool MULTI>
 __global__ __launch_bounds__(DEC_THREADS) void decode_step_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const T *__restrict__ log_alpha, const T *__restrict__ beta,
-    float *__restrict__ S_cache, T *__restrict__ o, int units, int H, int L_, int gate,
+    float *__restrict__ S_cache, T *__restrict__ o, int units, int H, int L_, int gate, int prep,
     const int32_t *__restrict__ state_idx, int pool)
 {
     // tokens per sequence: a compile-time 1 for the one-token instantiation
@@ -58,7 +61,7 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_step_kernel(
     __shared__ float s_a[DK], s_k[DK], s_q[DK];
     __shared__ __attribute__((aligned(16))) float s_red[2][RG][DV];
     __shared__ __attribute__((aligned(16))) float s_u[DV];
-    __shared__ float s_kq;
+    __shared__ float s_kq, s_ik, s_iq;   // k . q, 1/|k|, 1/|q| (1 without normalisation)
 
     // state row of a unit (n, h): n's slot, or -1 for no state.  The unit is
     // the same in every lane; saying so keeps the slot-map read a scalar load
@@ -133,7 +136,9 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_step_kernel(
         // before them, to be complete below; otherwise it sinks the wait into
         // the branches that use them and later waits for the prefetch too
         asm volatile("" ::"v"(cs.g), "v"(cs.k), "v"(cs.q), "v"(cs.v), "v"(cs.b));
-        const float a_ = gate == GATE_NONE ? 1.0f : expf(val(cs.g));
+        const float a_ = gate == GATE_NONE        ? 1.0f
+                       : (prep & PREP_SOFTPLUS) ? 1.0f / (1.0f + expf(val(cs.g)))
+                                                : expf(val(cs.g));
         const float k_ = val(cs.k), q_ = val(cs.q), v_ = val(cs.v), b_ = val(cs.b);
         if (t < DK) {
             s_a[t] = a_;
@@ -150,12 +155,26 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_step_kernel(
         }
         __syncthreads();
 
-        if (t < 64) {   // k . q by the first wave
-            float acc = 0.f;
-            for (int r = t; r < DK; r += 64) acc += s_k[r] * s_q[r];
+        if (t < 64) {   // k . q (and |k|^2, |q|^2 when normalising) by the first wave
+            float acc = 0.f, kk2 = 0.f, qq2 = 0.f;
+            for (int r = t; r < DK; r += 64) {
+                acc += s_k[r] * s_q[r];
+                kk2 += s_k[r] * s_k[r];
+                qq2 += s_q[r] * s_q[r];
+            }
 #pragma unroll
-            for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-            if (t == 0) s_kq = acc;
+            for (int off = 32; off > 0; off >>= 1) {
+                acc += __shfl_xor(acc, off);
+                kk2 += __shfl_xor(kk2, off);
+                qq2 += __shfl_xor(qq2, off);
+            }
+            if (t == 0) {
+                const float ik = (prep & PREP_L2NORM) ? inv_norm(kk2) : 1.0f;
+                const float iq = (prep & PREP_L2NORM) ? inv_norm(qq2) : 1.0f;
+                s_kq = acc * ik * iq;
+                s_ik = ik;
+                s_iq = iq;
+            }
         }
 
         f4v e = {0.f, 0.f, 0.f, 0.f}, pq = {0.f, 0.f, 0.f, 0.f};
@@ -177,13 +196,14 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_step_kernel(
                 es += s_red[0][r][t];
                 ps += s_red[1][r][t];
             }
-            const float u = b_ * (v_ - es);
+            // with normalisation e and p were formed with the raw k and q
+            const float u = b_ * (v_ - es * s_ik);
             s_u[t] = u;
-            store_elem(o + tok_row(unit, tk) * DV + t, ps + s_kq * u);
+            store_elem(o + tok_row(unit, tk) * DV + t, ps * s_iq + s_kq * u);
         }
         __syncthreads();
 
-        const f4v u4 = *reinterpret_cast<const f4v *>(&s_u[4 * cg]);
+        const f4v u4 = *reinterpret_cast<const f4v *>(&s_u[4 * cg]) * s_ik;
 #pragma unroll
         for (int i = 0; i < RPT; ++i) cur[i] += s_k[rg + i * RG] * u4;
         if (last) {
@@ -236,7 +256,7 @@ int cu_count();
 template <int DK, int DV, typename T>
 static hipError_t launch_decode(const void *q, const void *k, const void *v,
                                 const void *log_alpha, const void *beta, float *S,
-                                void *o, int units, int H, int L, int gate,
+                                void *o, int units, int H, int L, int gate, int prep,
                                 const int32_t *state_idx, int pool, hipStream_t stream)
 {
     // four workgroups per CU, each walking units with the grid stride
@@ -244,23 +264,24 @@ static hipError_t launch_decode(const void *q, const void *k, const void *v,
     if (L == 1)
         hipLaunchKernelGGL((decode_step_kernel<DK, DV, T, false>), dim3(grid), dim3(DEC_THREADS), 0,
                            stream, (const T *)q, (const T *)k, (const T *)v, (const T *)log_alpha,
-                           (const T *)beta, S, (T *)o, units, H, L, gate, state_idx, pool);
+                           (const T *)beta, S, (T *)o, units, H, L, gate, prep, state_idx, pool);
     else
         hipLaunchKernelGGL((decode_step_kernel<DK, DV, T, true>), dim3(grid), dim3(DEC_THREADS), 0,
                            stream, (const T *)q, (const T *)k, (const T *)v, (const T *)log_alpha,
-                           (const T *)beta, S, (T *)o, units, H, L, gate, state_idx, pool);
+                           (const T *)beta, S, (T *)o, units, H, L, gate, prep, state_idx, pool);
     return hipGetLastError();
 }
 
 template <typename T>
 static hipError_t dispatch_decode_t(const void *q, const void *k, const void *v,
                                     const void *log_alpha, const void *beta, float *S,
-                                    void *o, int units, int H, int L, int gate,
+                                    void *o, int units, int H, int L, int gate, int prep,
                                     const int32_t *state_idx, int pool, int dk, int dv,
                                     hipStream_t stream)
 {
 #define KDA_DEC(DK_, DV_) \
-    launch_decode<DK_, DV_, T>(q, k, v, log_alpha, beta, S, o, units, H, L, gate, state_idx, pool, stream)
+    launch_decode<DK_, DV_, T>(q, k, v, log_alpha, beta, S, o, units, H, L, gate, prep, state_idx, pool, \
+                               stream)
     if (dk == 128 && dv == 128) return KDA_DEC(128, 128);
     if (dk == 128 && dv == 64) return KDA_DEC(128, 64);
     if (dk == 64 && dv == 128) return KDA_DEC(64, 128);
@@ -270,17 +291,17 @@ static hipError_t dispatch_decode_t(const void *q, const void *k, const void *v,
 
 // Host-side launcher used by the C ABI (sizes already validated).
 hipError_t decode_step_launch(const void *q, const void *k, const void *v,
-                              const void *log_alpha, const void *beta, int gate, float *S,
+                              const void *log_alpha, const void *beta, int gate, int prep, float *S,
                               const int32_t *state_idx, int pool, void *o, int N, int L, int H,
                               int dk, int dv, bool bf16, hipStream_t stream)
 {
     const int units = N * H;
     if (units == 0 || L == 0) return hipSuccess;
     if (bf16)
-        return dispatch_decode_t<bf16_t>(q, k, v, log_alpha, beta, S, o, units, H, L, gate,
+        return dispatch_decode_t<bf16_t>(q, k, v, log_alpha, beta, S, o, units, H, L, gate, prep,
                                          state_idx, pool, dk, dv, stream);
-    return dispatch_decode_t<float>(q, k, v, log_alpha, beta, S, o, units, H, L, gate, state_idx,
-                                    pool, dk, dv, stream);
+    return dispatch_decode_t<float>(q, k, v, log_alpha, beta, S, o, units, H, L, gate, prep,
+                                    state_idx, pool, dk, dv, stream);
 }
 
 }  // namespace kda

@@ -40,6 +40,25 @@ constexpr float kLog2e = 1.4426950408889634f;
 // channel, or none (alpha = 1).
 enum : int { GATE_CHANNEL = 0, GATE_HEAD = 1, GATE_NONE = 2 };
 
+// Input preparation folded into the kernels (bits match kda_flags in kda.h):
+// q and k divided by their L2 norm over d_k per token and head; the gate
+// tensor holding x with log_alpha = -softplus(x).
+enum : int { PREP_L2NORM = 1, PREP_SOFTPLUS = 2 };
+// alpha = e^{-softplus(x)} = 1 / (1 + e^x), and its log2 (-softplus(x) log2 e,
+// in a form that neither overflows nor loses small values)
+__device__ __forceinline__ float alpha_softplus(float x) {
+    return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x * kLog2e));
+}
+__device__ __forceinline__ float log2_alpha_softplus(float x) {
+    const float ax = x < 0.0f ? -x : x;
+    return -((x > 0.0f ? x : 0.0f) * kLog2e +
+             __builtin_amdgcn_logf(1.0f + __builtin_amdgcn_exp2f(-ax * kLog2e)));
+}
+// 1 / |x| for a squared norm, a zero vector staying zero
+__device__ __forceinline__ float inv_norm(float sumsq) {
+    return sumsq > 0.0f ? __builtin_amdgcn_rsqf(sumsq) : 0.0f;
+}
+
 // Row of the state arrays that a sequence (or decode slot) reads and writes:
 // the sequence index itself, or state_idx[seq] when a slot map is given;
 // -1 (start from zeros, write nothing) for an index outside [0, pool).

@@ -20,6 +20,7 @@ KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_HIP = 0, 1, 2, 3
 KDA_F32, KDA_BF16 = 0, 1
 KDA_GATE_CHANNEL, KDA_GATE_HEAD, KDA_GATE_NONE = 0, 1, 2
 _GATES = {"channel": KDA_GATE_CHANNEL, "head": KDA_GATE_HEAD, "none": KDA_GATE_NONE}
+KDA_FLAG_L2NORM_QK, KDA_FLAG_GATE_SOFTPLUS = 1, 2
 
 _vp = ctypes.c_void_p
 _lib = None
@@ -53,12 +54,12 @@ def lib() -> ctypes.CDLL:
     L.kda_decode_step.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, ctypes.c_int,
                                   ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp, _vp]
     L.kda_fwd_chunked_ex.restype = ctypes.c_int
-    L.kda_fwd_chunked_ex.argtypes = [_vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp,
+    L.kda_fwd_chunked_ex.argtypes = [_vp, _vp, _vp, _vp, _vp, ctypes.c_int, ctypes.c_uint, _vp, _vp, _vp,
                                      ctypes.c_int, _vp, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                      ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp,
                                      _vp, ctypes.c_size_t, _vp]
     L.kda_decode_step_ex.restype = ctypes.c_int
-    L.kda_decode_step_ex.argtypes = [_vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp, _vp,
+    L.kda_decode_step_ex.argtypes = [_vp, _vp, _vp, _vp, _vp, ctypes.c_int, ctypes.c_uint, _vp, _vp,
                                      ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                      ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp, _vp]
     _lib = L
@@ -123,7 +124,8 @@ def _check_gate(log_alpha, gate: str, shape_k, dev, dt):
 def fwd_chunked(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, *,
                 output_final_state: bool = True, o=None, S_T=None,
                 workspace=None, gate: str = "channel", state_idx=None,
-                pool_size: Optional[int] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+                pool_size: Optional[int] = None,
+                flags: int = 0) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Chunkwise KDA forward (kda_fwd_chunked / kda_fwd_chunked_ex).
 
     q, k: (B, T, H, dk); v: (B, T, H, dv); beta: (B, T, H), all of one dtype
@@ -133,7 +135,8 @@ def fwd_chunked(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, *,
     (requires B == 1) or None.  With state_idx (int32 (N,), on the GPU), S0 and
     S_T are pools of pool_size rows (default: S0's or S_T's first dimension)
     and sequence s reads and writes row state_idx[s]; S_T is then never
-    allocated here (pass S_T=S0 to continue a pool in place).
+    allocated here (pass S_T=S0 to continue a pool in place).  flags: input
+    preparation, KDA_FLAG_L2NORM_QK | KDA_FLAG_GATE_SOFTPLUS (kda.h kda_flags).
     Returns (o, S_T); S_T is None when output_final_state is False.
     """
     _gate_code(gate)
@@ -180,7 +183,7 @@ def fwd_chunked(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, *,
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     ga = None if gcode == KDA_GATE_NONE else log_alpha
-    if gcode == KDA_GATE_CHANNEL and state_idx is None:
+    if gcode == KDA_GATE_CHANNEL and state_idx is None and not flags:
         st = lib().kda_fwd_chunked(_ptr(q), _ptr(k), _ptr(v), _ptr(ga), _ptr(beta),
                                    _ptr(S0), _ptr(cu_seqlens), N, B, T, H, dk, dv,
                                    _dtype_code(q), _ptr(o), _ptr(S_T), _ptr(workspace), ws_bytes,
@@ -188,7 +191,7 @@ def fwd_chunked(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, *,
         where = "kda_fwd_chunked"
     else:
         st = lib().kda_fwd_chunked_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(ga), _ptr(beta), gcode,
-                                      _ptr(S0), _ptr(S_T), _ptr(state_idx), int(rows),
+                                      int(flags), _ptr(S0), _ptr(S_T), _ptr(state_idx), int(rows),
                                       _ptr(cu_seqlens), N, B, T, H, dk, dv, _dtype_code(q),
                                       _ptr(o), _ptr(workspace), ws_bytes, _stream(dev))
         where = "kda_fwd_chunked_ex"
@@ -198,7 +201,7 @@ def fwd_chunked(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, *,
 
 
 def decode_step(q, k, v, log_alpha, beta, S_cache, *, o=None, gate: str = "channel",
-                state_idx=None) -> torch.Tensor:
+                state_idx=None, flags: int = 0) -> torch.Tensor:
     """KDA decode of S_cache in place (kda_decode_step / _ex); returns o.
 
     One token per sequence: q, k: (N, H, dk); v: (N, H, dv); beta: (N, H);
@@ -206,7 +209,8 @@ def decode_step(q, k, v, log_alpha, beta, S_cache, *, o=None, gate: str = "chann
     beta: (N, L, H), all of one dtype.  log_alpha has q's shape for
     gate="channel", beta's for gate="head", and is ignored for gate="none".
     S_cache: (N, H, dk, dv) fp32, or with state_idx (int32 (N,) on the GPU) a
-    pool (P, H, dk, dv) whose row state_idx[n] sequence n updates.
+    pool (P, H, dk, dv) whose row state_idx[n] sequence n updates.  flags: input
+    preparation (kda.h kda_flags).
     """
     _gate_code(gate)
     dev = q.device
@@ -235,14 +239,14 @@ def decode_step(q, k, v, log_alpha, beta, S_cache, *, o=None, gate: str = "chann
     else:
         _check(o, "o", dev, dt)
     ga = None if gcode == KDA_GATE_NONE else log_alpha
-    if gcode == KDA_GATE_CHANNEL and state_idx is None and L == 1:
+    if gcode == KDA_GATE_CHANNEL and state_idx is None and L == 1 and not flags:
         st = lib().kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(ga), _ptr(beta),
                                    _ptr(S_cache), N, H, dk, dv, _dtype_code(q), _ptr(o),
                                    _stream(dev))
         where = "kda_decode_step"
     else:
         st = lib().kda_decode_step_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(ga), _ptr(beta), gcode,
-                                      _ptr(S_cache), _ptr(state_idx), int(rows), N, L, H, dk, dv,
+                                      int(flags), _ptr(S_cache), _ptr(state_idx), int(rows), N, L, H, dk, dv,
                                       _dtype_code(q), _ptr(o), _stream(dev))
         where = "kda_decode_step_ex"
     if st != KDA_OK:

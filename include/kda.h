@@ -80,6 +80,24 @@ typedef enum {
     KDA_GATE_NONE = 2
 } kda_gate;
 
+/* Input preparation folded into the *_ex entry points (bits of `flags`):
+ * steps that usually come just before the operator, namely L2-normalised q
+ * and k, and a forget gate produced as -softplus of a pre-activation by the
+ * gate module in front of the layer ("The fourth layer remembers", the
+ * paragraph on the forget-gate module two labs share).
+ *   KDA_FLAG_L2NORM_QK      q and k are divided by their Euclidean norm over
+ *                           d_k, per token and head, before use (a zero vector
+ *                           stays zero).  q and k are not modified in memory.
+ *   KDA_FLAG_GATE_SOFTPLUS  the gate tensor holds x, and log_alpha = -softplus(x)
+ *                           = -log(1 + e^x), i.e. alpha = 1 / (1 + e^x) in (0, 1):
+ *                           any finite x (or -inf, alpha = 1) is valid.  No
+ *                           effect with KDA_GATE_NONE.
+ * Any other bit is KDA_ERR_INVALID_ARG. */
+typedef enum {
+    KDA_FLAG_L2NORM_QK = 1,
+    KDA_FLAG_GATE_SOFTPLUS = 2
+} kda_flags;
+
 /* Human-readable name of a status code (static storage, never NULL). */
 const char *kda_status_string(kda_status status);
 
@@ -130,6 +148,7 @@ kda_status kda_fwd_chunked(const void *q, const void *k, const void *v,
  *   gate            : layout of log_alpha (kda_gate): (B, T, H, dk) for
  *                     KDA_GATE_CHANNEL, (B, T, H) for KDA_GATE_HEAD, unused for
  *                     KDA_GATE_NONE.
+ *   flags           : input preparation, a combination of kda_flags (0: none).
  *   S0, S_T         : as in kda_fwd_chunked when state_idx is NULL.  Otherwise
  *                     pools of shape (pool_size, H, dk, dv) fp32 (each may be
  *                     NULL; S0 == S_T continues the pool in place).
@@ -141,11 +160,12 @@ kda_status kda_fwd_chunked(const void *q, const void *k, const void *v,
  *                     indices must be distinct when S_T is given.
  *   pool_size       : rows of the pools (used only with state_idx).
  * Every other argument, the supported sizes and the errors are those of
- * kda_fwd_chunked, which equals this call with KDA_GATE_CHANNEL and no
- * state_idx.
+ * kda_fwd_chunked, which equals this call with KDA_GATE_CHANNEL, no flags and
+ * no state_idx.
  */
 kda_status kda_fwd_chunked_ex(const void *q, const void *k, const void *v,
                               const void *log_alpha, const void *beta, kda_gate gate,
+                              unsigned flags,
                               const float *S0, float *S_T, const int32_t *state_idx, int pool_size,
                               const int32_t *cu_seqlens, int num_seqs,
                               int B, int T, int H, int dk, int dv, kda_dtype dtype,
@@ -178,6 +198,7 @@ kda_status kda_decode_step(const void *q, const void *k, const void *v,
  *   q, k            : (N, L, H, dk)      dtype
  *   v               : (N, L, H, dv)      dtype
  *   log_alpha       : (N, L, H, dk), (N, L, H) or unused, per `gate` (kda_gate)
+ *   flags           : input preparation, a combination of kda_flags (0: none)
  *   beta            : (N, L, H)          dtype
  *   o               : (N, L, H, dv)      dtype, written
  *   S_pool          : fp32 states, read and rewritten in place: (N, H, dk, dv)
@@ -187,10 +208,11 @@ kda_status kda_decode_step(const void *q, const void *k, const void *v,
  *                     means no state: o is computed from a zero state and
  *                     nothing is written.  Valid indices must be distinct.
  * Every other argument is that of kda_decode_step, which equals this call
- * with KDA_GATE_CHANNEL, no state_idx and L = 1.
+ * with KDA_GATE_CHANNEL, no flags, no state_idx and L = 1.
  */
 kda_status kda_decode_step_ex(const void *q, const void *k, const void *v,
                               const void *log_alpha, const void *beta, kda_gate gate,
+                              unsigned flags,
                               float *S_pool, const int32_t *state_idx, int pool_size,
                               int N, int L, int H, int dk, int dv, kda_dtype dtype, void *o,
                               void *stream);

@@ -15,6 +15,9 @@ from .oracle import (  # noqa: F401
     fwd_pooled,
     decode_pooled,
     GATES,
+    prepare,
+    FLAG_L2NORM_QK,
+    FLAG_GATE_SOFTPLUS,
     max_threads,
     default_threads,
 )

@@ -12,7 +12,9 @@ Two independent routes to the same result live here:
   diagonal gate, daily.dev summary of "You Could Have Come Up with Kimi Delta
   Attention").  It shares no code with the C loop.
 
-``channel_gate`` restates the two narrower gate layouts (one decay per head,
+``prepare`` applies the optional input preparation (L2-normalising q and k,
+the softplus form of the gate), ``channel_gate`` restates the two narrower
+gate layouts (one decay per head,
 or none) as the per-channel gate they stand for, and ``fwd_pooled`` /
 ``decode_pooled`` read and write states as rows of a pool through a slot map;
 both only rearrange inputs and outputs around ``fwd`` / ``decode``.
@@ -105,6 +107,34 @@ def _ptr(a: Optional[np.ndarray]):
 
 GATES = ("channel", "head", "none")
 
+# input preparation folded into the operator (flags of the *_ex entry points)
+FLAG_L2NORM_QK = 1
+FLAG_GATE_SOFTPLUS = 2
+
+
+def prepare(q, k, gate_in, flags: int):
+    """Inputs as the operator sees them after the optional preparation steps.
+
+    FLAG_L2NORM_QK: q and k divided by their Euclidean norm over d_k, per token
+    and head (a zero vector stays zero) -- the normalisation the workloads'
+    generator applies before the operator.
+    FLAG_GATE_SOFTPLUS: the gate tensor holds x and log_alpha = -softplus(x) =
+    -log(1 + e^x), the forget-gate form of the workloads' generator; alpha =
+    e^{-softplus(x)} lies in (0, 1).  None (no gate) stays None.
+    Returns (q, k, log_alpha) as float64.
+    """
+    q = _f64(q)
+    k = _f64(k)
+    if flags & FLAG_L2NORM_QK:
+        def unit(x):
+            n = np.sqrt(np.sum(x * x, axis=-1, keepdims=True))
+            return np.where(n > 0, x / np.where(n > 0, n, 1.0), 0.0)
+        q, k = unit(q), unit(k)
+    g = None if gate_in is None else _f64(gate_in)
+    if g is not None and flags & FLAG_GATE_SOFTPLUS:
+        g = -np.logaddexp(0.0, g)
+    return q, k, g
+
 
 def channel_gate(log_alpha, gate: str, shape_k) -> np.ndarray:
     """The per-key-channel log-gate that a gate layout stands for.
@@ -132,14 +162,18 @@ def channel_gate(log_alpha, gate: str, shape_k) -> np.ndarray:
 
 
 def fwd(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None,
-        nthreads: Optional[int] = None, lib=None, gate: str = "channel") -> Tuple[np.ndarray, np.ndarray]:
+        nthreads: Optional[int] = None, lib=None, gate: str = "channel",
+        flags: int = 0) -> Tuple[np.ndarray, np.ndarray]:
     """Literal recurrence over whole sequences.
 
     q, k: (B, T, H, dk); v: (B, T, H, dv); beta: (B, T, H); log_alpha in the
-    layout ``gate`` names (see channel_gate);
+    layout ``gate`` names (see channel_gate), or the softplus input with
+    FLAG_GATE_SOFTPLUS (see prepare);
     S0: (N, H, dk, dv) or None (zeros); cu_seqlens: (N+1,) ints or None.
     Returns (o (B, T, H, dv), S_T (N, H, dk, dv)) as float64.
     """
+    if flags:
+        q, k, log_alpha = prepare(q, k, log_alpha, flags)
     log_alpha = channel_gate(log_alpha, gate, np.shape(q))
     q, k, v, log_alpha, beta = map(_f64, (q, k, v, log_alpha, beta))
     B, T, H, dk = q.shape
@@ -170,13 +204,16 @@ def fwd(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None,
 
 
 def decode(q, k, v, log_alpha, beta, S, nthreads: Optional[int] = None, lib=None,
-           gate: str = "channel"):
+           gate: str = "channel", flags: int = 0):
     """One token for each of N independent states.
 
     q, k: (N, H, dk); v: (N, H, dv); beta: (N, H); S: (N, H, dk, dv);
-    log_alpha in the layout ``gate`` names (see channel_gate).
+    log_alpha in the layout ``gate`` names (see channel_gate), prepared per
+    ``flags`` (see prepare).
     Returns (o (N, H, dv), S_new (N, H, dk, dv)); the input S is not modified.
     """
+    if flags:
+        q, k, log_alpha = prepare(q, k, log_alpha, flags)
     log_alpha = channel_gate(log_alpha, gate, np.shape(q))
     q, k, v, log_alpha, beta = map(_f64, (q, k, v, log_alpha, beta))
     N, H, dk = q.shape
@@ -201,7 +238,7 @@ def pool_rows(state_idx, pool_size: int) -> np.ndarray:
 
 def fwd_pooled(q, k, v, log_alpha, beta, S0_pool, state_idx, cu_seqlens=None, gate="channel",
                S_T_pool=None, pool_size: Optional[int] = None, nthreads: Optional[int] = None,
-               lib=None):
+               lib=None, flags: int = 0):
     """Sequences continued from and into rows of state pools (slot-indexed states).
 
     Sequence s starts from row state_idx[s] of S0_pool (zeros when S0_pool is
@@ -223,7 +260,8 @@ def fwd_pooled(q, k, v, log_alpha, beta, S0_pool, state_idx, cu_seqlens=None, ga
         for s in range(N):
             if rows[s] >= 0:
                 S0[s] = pool0[rows[s]]
-    o, S_T = fwd(q, k, v, log_alpha, beta, S0, cu_seqlens, nthreads=nthreads, lib=lib, gate=gate)
+    o, S_T = fwd(q, k, v, log_alpha, beta, S0, cu_seqlens, nthreads=nthreads, lib=lib, gate=gate,
+                 flags=flags)
     if S_T_pool is None:
         return o, None
     new = np.array(S_T_pool, dtype=np.float64, copy=True)
@@ -234,7 +272,7 @@ def fwd_pooled(q, k, v, log_alpha, beta, S0_pool, state_idx, cu_seqlens=None, ga
 
 
 def decode_pooled(q, k, v, log_alpha, beta, pool, state_idx, gate="channel",
-                  nthreads: Optional[int] = None, lib=None):
+                  nthreads: Optional[int] = None, lib=None, flags: int = 0):
     """One token per sequence on rows of a state pool; returns (o, new pool).
 
     Sequence n updates row state_idx[n]; for an index outside the pool it
@@ -247,7 +285,8 @@ def decode_pooled(q, k, v, log_alpha, beta, pool, state_idx, gate="channel",
     for n in range(N):
         if rows[n] >= 0:
             S[n] = pool[rows[n]]
-    o, S_new = decode(q, k, v, log_alpha, beta, S, nthreads=nthreads, lib=lib, gate=gate)
+    o, S_new = decode(q, k, v, log_alpha, beta, S, nthreads=nthreads, lib=lib, gate=gate,
+                      flags=flags)
     for n in range(N):
         if rows[n] >= 0:
             pool[rows[n]] = S_new[n]

@@ -128,15 +128,15 @@ def test_decode_empty_is_ok(L):
     assert dec(L, N=0) == 0
 
 
-def fwd_ex(L, q=FAKE, k=FAKE, v=FAKE, g=FAKE, b=FAKE, gate=0, S0=None, S_T=None, idx=None, P=0,
-           cu=None, N=0, B=1, T=64, H=2, dk=128, dv=128, dt=1, o=FAKE, ws=None, wsb=0):
-    return L.kda_fwd_chunked_ex(q, k, v, g, b, gate, S0, S_T, idx, P, cu, N, B, T, H, dk, dv, dt,
-                                o, ws, wsb, None)
+def fwd_ex(L, q=FAKE, k=FAKE, v=FAKE, g=FAKE, b=FAKE, gate=0, flags=0, S0=None, S_T=None, idx=None,
+           P=0, cu=None, N=0, B=1, T=64, H=2, dk=128, dv=128, dt=1, o=FAKE, ws=None, wsb=0):
+    return L.kda_fwd_chunked_ex(q, k, v, g, b, gate, flags, S0, S_T, idx, P, cu, N, B, T, H, dk, dv,
+                                dt, o, ws, wsb, None)
 
 
-def dec_ex(L, q=FAKE, k=FAKE, v=FAKE, g=FAKE, b=FAKE, gate=0, S=FAKE, idx=None, P=0, N=4, T=1, H=2,
-           dk=128, dv=128, dt=1, o=FAKE):
-    return L.kda_decode_step_ex(q, k, v, g, b, gate, S, idx, P, N, T, H, dk, dv, dt, o, None)
+def dec_ex(L, q=FAKE, k=FAKE, v=FAKE, g=FAKE, b=FAKE, gate=0, flags=0, S=FAKE, idx=None, P=0, N=4,
+           T=1, H=2, dk=128, dv=128, dt=1, o=FAKE):
+    return L.kda_decode_step_ex(q, k, v, g, b, gate, flags, S, idx, P, N, T, H, dk, dv, dt, o, None)
 
 
 @pytest.mark.parametrize("gate", [-1, 3, 100])
@@ -166,6 +166,15 @@ def test_ex_slot_map_rules(L):
     assert dec_ex(L, dv=32) == 2
     assert fwd_ex(L, cu=FAKE, N=8, idx=FAKE, P=8) == 1  # varlen workspace missing
     assert fwd_ex(L, B=0, T=0, idx=FAKE, P=0) == 0
+
+
+@pytest.mark.parametrize("flags", [4, 8, 0x80000000])
+def test_ex_rejects_unknown_flags(L, flags):
+    assert fwd_ex(L, flags=flags) == 1
+    assert dec_ex(L, flags=flags) == 1
+    # known flags pass the checks (empty work)
+    assert fwd_ex(L, flags=3, B=0, T=0) == 0
+    assert dec_ex(L, flags=3, N=0) == 0
 
 
 def test_decode_ex_tokens_per_sequence(L):

@@ -1,4 +1,4 @@
-"""Pins for the oracle's gate layouts and state pools (CPU only).
+"""Pins for the oracle's gate layouts, state pools and input preparation (CPU only).
 
 oracle.channel_gate, oracle.fwd_pooled and oracle.decode_pooled only
 rearrange inputs and outputs around the token loop.  Each is compared here
@@ -151,3 +151,75 @@ def test_decode_pooled_against_brute_force():
             want[i] = S_ref[0]
     assert rel_err(new_pool, want) < 1e-12
     assert np.array_equal(new_pool[1], pool[1]) and np.array_equal(new_pool[2], pool[2])
+
+
+# --------------------------------------------------------------------------
+# Input preparation: L2-normalised q and k, softplus gate
+# --------------------------------------------------------------------------
+
+def test_prepare_l2norm_closed_forms():
+    rng = _rng(40)
+    q = rng.standard_normal((2, 5, 3, 7)) * rng.uniform(0.1, 50, size=(2, 5, 3, 1))
+    k = rng.standard_normal((2, 5, 3, 7))
+    k[0, 1, 2] = 0.0                                     # a zero key stays zero
+    qn, kn, g = oracle.prepare(q, k, None, oracle.FLAG_L2NORM_QK)
+    assert g is None
+    assert np.allclose(np.linalg.norm(qn, axis=-1), 1.0, atol=1e-14)
+    nz = np.linalg.norm(k, axis=-1) > 0
+    assert np.allclose(np.linalg.norm(kn, axis=-1)[nz], 1.0, atol=1e-14)
+    assert np.array_equal(kn[0, 1, 2], np.zeros(7))
+    # same direction: the normalised vector is a positive multiple of the input
+    ratio = qn / q
+    assert np.allclose(ratio, ratio[..., :1], rtol=1e-13) and (ratio > 0).all()
+    # without the flag nothing changes
+    q2, k2, _ = oracle.prepare(q, k, None, 0)
+    assert np.array_equal(q2, q) and np.array_equal(k2, k)
+
+
+def test_prepare_softplus_closed_forms():
+    x = np.array([0.0, 1.0, -1.0, 30.0, -30.0, 700.0, -700.0, 1e4])
+    _, _, g = oracle.prepare(np.zeros((1, 1)), np.zeros((1, 1)), x, oracle.FLAG_GATE_SOFTPLUS)
+    a = np.exp(g)
+    assert np.isfinite(g).all()
+    assert abs(a[0] - 0.5) < 1e-15                       # softplus(0) = ln 2
+    # alpha = sigmoid(-x) = 1 / (1 + e^x), written out independently
+    ref = np.array([1.0 / (1.0 + np.exp(v)) if v < 700 else 0.0 for v in x[:5]])
+    assert np.allclose(a[:5], ref, rtol=1e-14, atol=1e-300)
+    assert abs(g[3] + 30.0 + np.log1p(np.exp(-30.0))) < 1e-12
+    assert abs(g[4] + np.log1p(np.exp(-30.0))) < 1e-24
+    assert g[5] == -700.0 and g[7] == -1e4               # large x: log_alpha -> -x
+    assert (g <= 0).all()
+
+
+@pytest.mark.parametrize("flags", [1, 2, 3])
+def test_prepared_forward_against_brute_force(flags):
+    """The forward with preparation flags equals the brute force on inputs
+    prepared by hand (numpy's norm routine, the logistic function)."""
+    rng = _rng(41 + flags)
+    B, T, H, dk, dv = 2, 6, 2, 5, 4
+    q, k, v, g, beta, S0 = _rand_inputs(rng, B, T, H, dk, dv)
+    q = q * 3.0
+    x = rng.standard_normal((B, T, H, dk)) * 2.0
+    gate_in = x if flags & 2 else g
+    o, S_T = oracle.fwd(q, k, v, gate_in, beta, S0, nthreads=2, flags=flags)
+    qq, kk = q, k
+    if flags & 1:
+        qq = q / np.linalg.norm(q, axis=-1, keepdims=True)
+        kk = k / np.linalg.norm(k, axis=-1, keepdims=True)
+    gg = np.log(1.0 / (1.0 + np.exp(x))) if flags & 2 else g
+    o_ref, S_ref = oracle.brute_force(qq, kk, v, gg, beta, S0)
+    assert rel_err(o, o_ref) < 1e-12 and rel_err(S_T, S_ref) < 1e-12
+    # and the decode step agrees with the forward's first token
+    od, Sd = oracle.decode(q[:, 0], k[:, 0], v[:, 0], gate_in[:, 0], beta[:, 0], S0, nthreads=2,
+                           flags=flags)
+    o1, S1 = oracle.brute_force(qq[:, :1], kk[:, :1], v[:, :1], gg[:, :1], beta[:, :1], S0)
+    assert rel_err(od, o1[:, 0]) < 1e-12 and rel_err(Sd, S1) < 1e-12
+
+
+def test_l2norm_makes_forward_scale_invariant_in_q_and_k():
+    rng = _rng(44)
+    q, k, v, g, beta, S0 = _rand_inputs(rng, 1, 7, 2, 4, 3)
+    f = oracle.FLAG_L2NORM_QK
+    o1, S1 = oracle.fwd(q, k, v, g, beta, S0, nthreads=2, flags=f)
+    o2, S2 = oracle.fwd(5.0 * q, 0.25 * k, v, g, beta, S0, nthreads=2, flags=f)
+    assert rel_err(o2, o1) < 1e-13 and rel_err(S2, S1) < 1e-13
