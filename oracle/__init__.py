@@ -9,6 +9,8 @@ from .oracle import (  # noqa: F401
     load_path,
     fwd,
     decode,
+    bwd,
+    prepare_vjp,
     brute_force,
     channel_gate,
     pool_rows,

@@ -19,7 +19,12 @@ or none) as the per-channel gate they stand for, and ``fwd_pooled`` /
 ``decode_pooled`` read and write states as rows of a pool through a slot map;
 both only rearrange inputs and outputs around ``fwd`` / ``decode``.
 
-Every function here is pinned by tests/test_oracle_pins.py (values the pages
+``bwd`` differentiates the token loop in reverse (kda_oracle_bwd); it is
+pinned by tests/test_oracle_bwd.py (exact adjoint identities where the
+forward is linear, central differences of ``fwd``, a closed form at beta = 0,
+planted mistakes).
+
+Every other function here is pinned by tests/test_oracle_pins.py (values the pages
 print, closed forms, special cases that reduce to published recurrences, brute
 force), and tests/test_oracle_mutants.py checks that planted mistakes in the C
 loop fail those pins.
@@ -78,6 +83,10 @@ def load_path(path: str):
     lib.kda_oracle_decode.argtypes = [_dp, _dp, _dp, _dp, _dp, _dp, ctypes.c_int,
                                       ctypes.c_int, ctypes.c_int, ctypes.c_int, _dp,
                                       ctypes.c_int]
+    lib.kda_oracle_bwd.restype = ctypes.c_int
+    lib.kda_oracle_bwd.argtypes = [_dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _i64p, ctypes.c_int,
+                                   ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                   ctypes.c_int, _dp, _dp, _dp, _dp, _dp, _dp, ctypes.c_int]
     lib.kda_oracle_max_threads.restype = ctypes.c_int
     lib.kda_oracle_max_threads.argtypes = []
     return lib
@@ -134,6 +143,34 @@ def prepare(q, k, gate_in, flags: int):
     if g is not None and flags & FLAG_GATE_SOFTPLUS:
         g = -np.logaddexp(0.0, g)
     return q, k, g
+
+
+def prepare_vjp(q_in, k_in, gate_in, flags: int, dq, dk, dg):
+    """Gradients with respect to the raw inputs of ``prepare`` from those with
+    respect to its outputs (the chain rule through each step):
+
+    FLAG_L2NORM_QK: y = x / |x| gives dx = (dy - y (y . dy)) / |x| (zero for a
+    zero row, where the step is the constant 0).
+    FLAG_GATE_SOFTPLUS: g = -softplus(x) gives dx = -sigmoid(x) dg.
+    Returns (dq_in, dk_in, dgate_in) as float64 (dgate_in None without a gate).
+    """
+    dq, dk = _f64(dq), _f64(dk)
+    if flags & FLAG_L2NORM_QK:
+        def back(x, dy):
+            x = _f64(x)
+            n = np.sqrt(np.sum(x * x, axis=-1, keepdims=True))
+            safe = np.where(n > 0, n, 1.0)
+            y = x / safe
+            dx = (dy - y * np.sum(y * dy, axis=-1, keepdims=True)) / safe
+            return np.where(n > 0, dx, 0.0)
+        dq, dk = back(q_in, dq), back(k_in, dk)
+    if dg is None:
+        return dq, dk, None
+    dg = _f64(dg)
+    if flags & FLAG_GATE_SOFTPLUS:
+        x = _f64(gate_in)
+        dg = -np.exp(-np.logaddexp(0.0, -x)) * dg      # sigmoid(x), overflow-free
+    return dq, dk, dg
 
 
 def channel_gate(log_alpha, gate: str, shape_k) -> np.ndarray:
@@ -228,6 +265,60 @@ def decode(q, k, v, log_alpha, beta, S, nthreads: Optional[int] = None, lib=None
     if rc != 0:
         raise ValueError(f"kda_oracle_decode rejected its arguments (rc={rc})")
     return o, S_new
+
+
+def bwd(q, k, v, log_alpha, beta, S0, dO, dS_T=None, cu_seqlens=None,
+        nthreads: Optional[int] = None, lib=None, gate: str = "channel", flags: int = 0):
+    """Gradients of L = <dO, o> + <dS_T, S_T> through ``fwd`` (same arguments).
+
+    The token loop differentiated in reverse (kda_oracle_bwd in
+    kda_oracle.c), then, for the narrower gate layouts, the per-channel gate
+    gradient summed over the channels a per-head value stands for (none: no
+    gate gradient), and the chain rule through the optional preparation.
+    dO: like o (B, T, H, dv); dS_T: (N, H, dk, dv) or None (zero).
+    Returns (dq, dk, dv, dlog_alpha, dbeta, dS0) as float64; dlog_alpha has
+    the gate input's shape (None for gate "none"); dS0 has S_T's shape.
+    """
+    q_in, k_in, g_in = q, k, log_alpha
+    if flags:
+        q, k, log_alpha = prepare(q, k, log_alpha, flags)
+    log_alpha = channel_gate(log_alpha, gate, np.shape(q))
+    q, k, v, log_alpha, beta, dO = map(_f64, (q, k, v, log_alpha, beta, dO))
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    assert dO.shape == (B, T, H, dv)
+    if cu_seqlens is not None:
+        cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
+        N = cu.shape[0] - 1
+        assert B == 1
+    else:
+        cu = None
+        N = B
+    if S0 is not None:
+        S0 = _f64(S0)
+        assert S0.shape == (N, H, dk, dv)
+    if dS_T is not None:
+        dS_T = _f64(dS_T)
+        assert dS_T.shape == (N, H, dk, dv)
+    gq, gk, glog = (np.zeros((B, T, H, dk)) for _ in range(3))
+    gv = np.zeros((B, T, H, dv))
+    gb = np.zeros((B, T, H))
+    gS0 = np.zeros((N, H, dk, dv))
+    lib = lib if lib is not None else load()
+    nt = nthreads if nthreads else default_threads()
+    rc = lib.kda_oracle_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S0),
+                            _ptr(dO), _ptr(dS_T), cu.ctypes.data_as(_i64p) if cu is not None
+                            else ctypes.cast(None, _i64p), N, B, T, H, dk, dv,
+                            _ptr(gq), _ptr(gk), _ptr(gv), _ptr(glog), _ptr(gb), _ptr(gS0), nt)
+    if rc != 0:
+        raise ValueError(f"kda_oracle_bwd rejected its arguments (rc={rc})")
+    if gate == "head":
+        glog = glog.sum(axis=-1)
+    elif gate == "none":
+        glog = None
+    if flags:
+        gq, gk, glog = prepare_vjp(q_in, k_in, g_in, flags, gq, gk, glog)
+    return gq, gk, gv, glog, gb, gS0
 
 
 def pool_rows(state_idx, pool_size: int) -> np.ndarray:
