@@ -9,7 +9,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkda.so")
-SOURCES = ["kda_api.hip", "kda_decode.hip", "kda_chunked.hip", "kda_chunked_ws.hip"]
+SOURCES = ["kda_api.hip", "kda_decode.hip", "kda_chunked.hip", "kda_chunked_ws.hip",
+           "kda_bwd.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -16,6 +16,12 @@ hipError_t chunked_fwd_launch(const void *q, const void *k, const void *v, const
                               const int32_t *state_idx, int pool, void *o,
                               const int32_t *cu_seqlens, int num_seqs, int B, int T, int H,
                               int dk, int dv, bool bf16, void *workspace, hipStream_t stream);
+size_t bwd_workspace_bytes(int B, int T, int H, int dk, int dv, int num_seqs);
+hipError_t bwd_launch(const void *q, const void *k, const void *v, const void *g, const void *beta,
+                      int gate, const float *S0, const void *dO, const float *dST,
+                      const int32_t *cu_seqlens, int num_seqs, int B, int T, int H, int dk, int dv,
+                      bool bf16, void *dq, void *dk_out, void *dv_out, void *dg, void *dbeta,
+                      float *dS0, void *workspace, hipStream_t stream);
 }  // namespace kda
 
 namespace {
@@ -153,6 +159,53 @@ kda_status kda_decode_step(const void *q, const void *k, const void *v,
 {
     return kda_decode_step_ex(q, k, v, log_alpha, beta, KDA_GATE_CHANNEL, 0u, S_cache, nullptr, 0,
                               N, 1, H, dk, dv, dtype, o, stream);
+}
+
+size_t kda_bwd_workspace_bytes(int B, int T, int H, int dk, int dv, int num_seqs)
+{
+    if (B < 0 || T < 0 || H <= 0 || dk <= 0 || dv <= 0 || num_seqs < 0) return 0;
+    return kda::bwd_workspace_bytes(B, T, H, dk, dv, num_seqs);
+}
+
+kda_status kda_bwd_chunked(const void *q, const void *k, const void *v,
+                           const void *log_alpha, const void *beta, kda_gate gate,
+                           const float *S0, const void *dO, const float *dS_T,
+                           const int32_t *cu_seqlens, int num_seqs,
+                           int B, int T, int H, int dk, int dv, kda_dtype dtype,
+                           void *dq, void *dk_out, void *dv_out, void *dlog_alpha, void *dbeta,
+                           float *dS0, void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_INVALID_ARG;
+    if (!gate_ok(gate)) return KDA_ERR_INVALID_ARG;
+    if (B < 0 || T < 0 || H <= 0 || dk <= 0 || dv <= 0) return KDA_ERR_INVALID_ARG;
+    if (cu_seqlens && (B != 1 || num_seqs < 0)) return KDA_ERR_INVALID_ARG;
+    const int nseq = cu_seqlens ? num_seqs : B;
+    if (!dim_ok(dk) || !dim_ok(dv)) return KDA_ERR_UNSUPPORTED;
+    if (!sizes_fit(B, T, H, dk > dv ? dk : dv) || !sizes_fit(nseq, H, dk, dv)) return KDA_ERR_INVALID_ARG;
+    if ((long long)nseq * H * (dv / 32) >= ((long long)1 << 31)) return KDA_ERR_INVALID_ARG;
+    const long long slots = (long long)B * ((T + 31) / 32) + nseq + 1;
+    if (slots >= ((long long)1 << 31) || H > 65535) return KDA_ERR_INVALID_ARG;
+    const long long tokens = (long long)B * T;
+    const void *g = gate == KDA_GATE_NONE ? nullptr : log_alpha;
+    void *dg = gate == KDA_GATE_NONE ? nullptr : dlog_alpha;
+    if (tokens > 0) {
+        if (!q || !k || !v || !beta || !dO || !dq || !dk_out || !dv_out || !dbeta)
+            return KDA_ERR_INVALID_ARG;
+        if (gate != KDA_GATE_NONE && (!log_alpha || !dlog_alpha)) return KDA_ERR_INVALID_ARG;
+    }
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(g) || !aligned16(beta) ||
+        !aligned16(dO) || !aligned16(S0) || !aligned16(dS_T) || !aligned16(dq) ||
+        !aligned16(dk_out) || !aligned16(dv_out) || !aligned16(dg) || !aligned16(dbeta) ||
+        !aligned16(dS0))
+        return KDA_ERR_INVALID_ARG;
+    if (nseq == 0) return KDA_OK;
+    const size_t need = kda::bwd_workspace_bytes(B, T, H, dk, dv, nseq);
+    if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u))
+        return KDA_ERR_INVALID_ARG;
+    hipError_t e = kda::bwd_launch(q, k, v, g, beta, (int)gate, S0, dO, dS_T, cu_seqlens, nseq, B,
+                                   T, H, dk, dv, dtype == KDA_BF16, dq, dk_out, dv_out, dg, dbeta,
+                                   dS0, workspace, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
 }  // extern "C"

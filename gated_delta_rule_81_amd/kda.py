@@ -62,6 +62,13 @@ def lib() -> ctypes.CDLL:
     L.kda_decode_step_ex.argtypes = [_vp, _vp, _vp, _vp, _vp, ctypes.c_int, ctypes.c_uint, _vp, _vp,
                                      ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                      ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp, _vp]
+    L.kda_bwd_workspace_bytes.restype = ctypes.c_size_t
+    L.kda_bwd_workspace_bytes.argtypes = [ctypes.c_int] * 6
+    L.kda_bwd_chunked.restype = ctypes.c_int
+    L.kda_bwd_chunked.argtypes = [_vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp, _vp,
+                                  ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                  ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp, _vp,
+                                  _vp, _vp, _vp, ctypes.c_size_t, _vp]
     _lib = L
     return L
 
@@ -252,3 +259,73 @@ def decode_step(q, k, v, log_alpha, beta, S_cache, *, o=None, gate: str = "chann
     if st != KDA_OK:
         raise KdaError(st, where)
     return o
+
+
+def bwd_workspace_bytes(B: int, T: int, H: int, dk: int, dv: int, num_seqs: int) -> int:
+    return int(lib().kda_bwd_workspace_bytes(B, T, H, dk, dv, num_seqs))
+
+
+def bwd_chunked(q, k, v, log_alpha, beta, dO, S0=None, dS_T=None, cu_seqlens=None, *,
+                gate: str = "channel", workspace=None, out=None):
+    """Gradients through fwd_chunked (kda_bwd_chunked).
+
+    Inputs exactly as given to fwd_chunked (no flags, no slot map), plus dO
+    (like o) and dS_T ((N, H, dk, dv) fp32 or None).  workspace: a uint8 GPU
+    tensor of at least bwd_workspace_bytes(...) bytes (allocated here when
+    None).  out: optional preallocated (dq, dk, dv, dlog_alpha, dbeta, dS0).
+    Returns (dq, dk, dv, dlog_alpha, dbeta, dS0); dlog_alpha is None for
+    gate="none" and has log_alpha's shape otherwise.
+    """
+    dev = q.device
+    dt = q.dtype
+    for name, t in (("q", q), ("k", k), ("v", v), ("beta", beta), ("dO", dO)):
+        _check(t, name, dev, dt)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    gcode = _check_gate(log_alpha, gate, q.shape, dev, dt)
+    if (k.shape != q.shape or v.shape != (B, T, H, dv) or beta.shape != (B, T, H)
+            or dO.shape != v.shape):
+        raise ValueError("inconsistent input shapes")
+    if cu_seqlens is not None:
+        _check(cu_seqlens, "cu_seqlens", dev, torch.int32)
+        N = cu_seqlens.shape[0] - 1
+    else:
+        N = B
+    for name, t in (("S0", S0), ("dS_T", dS_T)):
+        if t is not None:
+            _check(t, name, dev, torch.float32)
+            if t.shape != (N, H, dk, dv):
+                raise ValueError(f"{name} must have shape {(N, H, dk, dv)}")
+    if out is None:
+        dq = torch.empty_like(q)
+        dk_ = torch.empty_like(k)
+        dv_ = torch.empty_like(v)
+        dg = None if gcode == KDA_GATE_NONE else torch.empty_like(log_alpha)
+        db = torch.empty_like(beta)
+        dS0 = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+    else:
+        dq, dk_, dv_, dg, db, dS0 = out
+        for name, t, like in (("dq", dq, q), ("dk", dk_, k), ("dv", dv_, v), ("dbeta", db, beta)):
+            _check(t, name, dev, dt)
+            if t.shape != like.shape:
+                raise ValueError(f"{name} must have shape {tuple(like.shape)}")
+        if gcode != KDA_GATE_NONE:
+            _check(dg, "dlog_alpha", dev, dt)
+            if dg.shape != log_alpha.shape:
+                raise ValueError("dlog_alpha must have log_alpha's shape")
+        if dS0 is not None:
+            _check(dS0, "dS0", dev, torch.float32)
+            if dS0.shape != (N, H, dk, dv):
+                raise ValueError(f"dS0 must have shape {(N, H, dk, dv)}")
+    need = bwd_workspace_bytes(B, T, H, dk, dv, N)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    ga = None if gcode == KDA_GATE_NONE else log_alpha
+    st = lib().kda_bwd_chunked(_ptr(q), _ptr(k), _ptr(v), _ptr(ga), _ptr(beta), gcode, _ptr(S0),
+                               _ptr(dO), _ptr(dS_T), _ptr(cu_seqlens), N, B, T, H, dk, dv,
+                               _dtype_code(q), _ptr(dq), _ptr(dk_), _ptr(dv_), _ptr(dg), _ptr(db),
+                               _ptr(dS0), _ptr(workspace), ws_bytes, _stream(dev))
+    if st != KDA_OK:
+        raise KdaError(st, "kda_bwd_chunked")
+    return dq, dk_, dv_, dg, db, dS0

@@ -20,7 +20,8 @@
  * form named in the daily.dev summary; training and prefill) and a one-token
  * decode step that rewrites a state cache in place (the recurrent form; the
  * per-token work is constant, "The fourth layer remembers").  Their *_ex
- * forms add the per-head and absent gates and slot-indexed state pools.
+ * forms add the per-head and absent gates and slot-indexed state pools, and
+ * kda_bwd_chunked differentiates the forward (training).
  *
  * Conventions shared by every entry point
  *   - All pointers are DEVICE pointers (HIP global memory) unless stated.
@@ -216,6 +217,47 @@ kda_status kda_decode_step_ex(const void *q, const void *k, const void *v,
                               float *S_pool, const int32_t *state_idx, int pool_size,
                               int N, int L, int H, int dk, int dv, kda_dtype dtype, void *o,
                               void *stream);
+
+/* Workspace size in bytes that kda_bwd_chunked needs for these sizes.  It
+ * holds, per chunk of 32 tokens and head, the state entering the chunk, the
+ * gradient of the state leaving it (fp32, dk x dv each) and three 32 x 32
+ * fp32 matrices.  num_seqs is the number of packed sequences when cu_seqlens
+ * is used, else B. */
+size_t kda_bwd_workspace_bytes(int B, int T, int H, int dk, int dv, int num_seqs);
+
+/*
+ * kda_bwd_chunked -- gradients through kda_fwd_chunked_ex (no flags, no slot
+ * map): given dL/do and dL/dS_T of a loss L, the gradients of L with respect
+ * to q, k, v, log_alpha, beta and S0.  The pages present the chunkwise form
+ * as the one used for efficient training (daily.dev summary of "You Could
+ * Have Come Up with Kimi Delta Attention", Summary section); this is that
+ * form differentiated, recomputing the forward's chunk states.
+ *
+ *   q, k, v, log_alpha, beta, gate, S0, cu_seqlens, num_seqs, B, T, H, dk,
+ *   dv, dtype       : exactly as given to the forward (S0 NULL = zeros).
+ *   dO              : (B, T, H, dv)      dtype, dL/do
+ *   dS_T            : (N, H, dk, dv)     fp32, dL/dS_T; NULL = zeros
+ *   dq, dk_out      : (B, T, H, dk)      dtype, written
+ *   dv_out          : (B, T, H, dv)      dtype, written
+ *   dlog_alpha      : log_alpha's shape for the gate layout, dtype, written
+ *                     (unused for KDA_GATE_NONE; the per-head layout gets the
+ *                     sum over key channels)
+ *   dbeta           : (B, T, H)          dtype, written
+ *   dS0             : (N, H, dk, dv)     fp32, written (also when S0 is NULL);
+ *                                        NULL = not written
+ *   workspace       : device scratch of at least kda_bwd_workspace_bytes(...)
+ *                     bytes, 256-byte aligned; its contents on entry do not matter.
+ * No output may alias an input or another output.
+ * Supported: dk, dv in {64, 128}; dtype KDA_BF16 or KDA_F32 (all arithmetic
+ * fp32).  Zero-length sequences are allowed (dS0 = dS_T).
+ */
+kda_status kda_bwd_chunked(const void *q, const void *k, const void *v,
+                           const void *log_alpha, const void *beta, kda_gate gate,
+                           const float *S0, const void *dO, const float *dS_T,
+                           const int32_t *cu_seqlens, int num_seqs,
+                           int B, int T, int H, int dk, int dv, kda_dtype dtype,
+                           void *dq, void *dk_out, void *dv_out, void *dlog_alpha, void *dbeta,
+                           float *dS0, void *workspace, size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

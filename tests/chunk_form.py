@@ -59,3 +59,100 @@ def chunked_forward(q, k, v, g, beta, S0, C):
                 o[b, t0:t1, h] = O
             S_T[b, h] = S
     return o, S_T
+
+
+def chunk_step_bwd(S, q, k, v, g, beta, dO, D):
+    """Gradients through one chunk (the reverse of ``chunk_step``).
+
+    S: the state entering the chunk; D: the loss gradient with respect to the
+    state leaving it.  Returns (dq, dk, dv, dg, dbeta, dS) with dS the gradient
+    with respect to S.  The within-chunk decay factors are taken pairwise,
+    F_ric = e^{Gamma_rc - Gamma_ic} for i <= r (never above 1), which is how
+    the GPU backward forms them:
+      M0 = [sum_c k_rc k_ic F_ric] (strictly lower), A = Diag(beta) M0,
+      P  = [sum_c q_rc k_ic F_ric] (lower, diagonal included),
+      T  = (I + A)^{-1},  T' = T Diag(beta),  X = V - K_up S,  U = T' X,
+      O  = Q_up S + P U,  S_next = Diag(gamma) S + K_right^T U.
+    Reverse, in the order the kernels take it:
+      dU = P^T dO + K_right D;   dX = T'^T dU;   dV = dX
+      dT' = dU X^T;  dP = tril_incl(dO U^T);  dbeta_i = sum_r T_ri dT'_ri
+      dA = strict_lower(-T^T (dT' Diag(beta)) T^T);  dbeta_r += sum_i dA_ri M0_ri
+      dM = Diag(beta) dA; then through the pairwise sums for M0 and P
+      dS = Diag(gamma) D + Q_up^T dO - K_up^T dX
+      dK_up = -dX S^T, dQ_up = dO S^T, dK_right = U D^T, dgamma = rowsum(D * S)
+    and the chain rule from K_up, Q_up, K_right, gamma to k, q and Gamma, then
+    dg_j = sum_{r >= j} dGamma_r + dGamma_c (Gamma_c enters gamma and K_right).
+    """
+    c, dk = q.shape
+    G = np.cumsum(g, axis=0)
+    Gc = G[-1]
+    F = np.exp(G[:, None, :] - G[None, :, :])          # (r, i, c)
+    F = F * np.tril(np.ones((c, c)))[:, :, None]       # i <= r only
+    M0 = np.tril(np.einsum("rc,ic,ric->ri", k, k, F), -1)
+    P = np.einsum("rc,ic,ric->ri", q, k, F)
+    A = beta[:, None] * M0
+    T = np.linalg.inv(np.eye(c) + A)
+    Tp = T * beta[None, :]
+    E = np.exp(G)
+    K_up, Q_up = k * E, q * E
+    K_right = k * np.exp(Gc - G)
+    gam = np.exp(Gc)
+    X = v - K_up @ S
+    U = Tp @ X
+    dU = P.T @ dO + K_right @ D
+    dX = Tp.T @ dU
+    dTp = dU @ X.T
+    dP = np.tril(dO @ U.T)
+    dbeta = np.sum(T * dTp, axis=0)
+    dT = dTp * beta[None, :]
+    dA = np.tril(-T.T @ dT @ T.T, -1)
+    dbeta = dbeta + np.sum(dA * M0, axis=1)
+    dM = beta[:, None] * dA
+    dS = gam[:, None] * D + Q_up.T @ dO - K_up.T @ dX
+    dK_up = -dX @ S.T
+    dQ_up = dO @ S.T
+    dK_right = U @ D.T
+    dgam = np.sum(D * S, axis=1)
+    # pairwise sums: M0 (weights dM) and P (weights dP)
+    dq = np.einsum("ri,ic,ric->rc", dP, k, F) + dQ_up * E
+    dk_ = (np.einsum("ri,ic,ric->rc", dM, k, F) + np.einsum("ri,rc,ric->ic", dM, k, F)
+           + np.einsum("ri,rc,ric->ic", dP, q, F) + dK_up * E + dK_right * np.exp(Gc - G))
+    W = (np.einsum("ri,rc,ic,ric->ric", dM, k, k, F) + np.einsum("ri,rc,ic,ric->ric", dP, q, k, F))
+    dG = W.sum(axis=1) - W.sum(axis=0)
+    dG = dG + dK_up * K_up + dQ_up * Q_up - dK_right * K_right
+    dGc = np.sum(dK_right * K_right, axis=0) + dgam * gam
+    dg = np.cumsum(dG[::-1], axis=0)[::-1] + dGc[None, :]
+    return dq, dk_, dX, dg, dbeta, dS
+
+
+def chunked_backward(q, k, v, g, beta, S0, dO, dS_T, C):
+    """Dense (B, T, H, .) inputs, chunk size C: the states entering each chunk
+    from a forward sweep, then the chunks in reverse.  Returns
+    (dq, dk, dv, dg, dbeta, dS0)."""
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    out = [np.zeros((B, T, H, dk)), np.zeros((B, T, H, dk)), np.zeros((B, T, H, dv)),
+           np.zeros((B, T, H, dk)), np.zeros((B, T, H))]
+    dS0 = np.zeros((B, H, dk, dv))
+    for b in range(B):
+        for h in range(H):
+            S = np.zeros((dk, dv)) if S0 is None else np.array(S0[b, h], dtype=np.float64)
+            starts = list(range(0, T, C))
+            states = []
+            for t0 in starts:
+                t1 = min(T, t0 + C)
+                states.append(S)
+                _, S = chunk_step(S, q[b, t0:t1, h], k[b, t0:t1, h], v[b, t0:t1, h],
+                                  g[b, t0:t1, h], beta[b, t0:t1, h])
+            D = np.zeros((dk, dv)) if dS_T is None else np.array(dS_T[b, h], dtype=np.float64)
+            for n in range(len(starts) - 1, -1, -1):
+                t0 = starts[n]
+                t1 = min(T, t0 + C)
+                r = chunk_step_bwd(states[n], q[b, t0:t1, h], k[b, t0:t1, h], v[b, t0:t1, h],
+                                   g[b, t0:t1, h], beta[b, t0:t1, h], dO[b, t0:t1, h], D)
+                for j in range(4):
+                    out[j][b, t0:t1, h] = r[j]
+                out[4][b, t0:t1, h] = r[4]
+                D = r[5]
+            dS0[b, h] = D
+    return tuple(out) + (dS0,)

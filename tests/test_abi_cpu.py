@@ -27,7 +27,8 @@ def L():
 
 
 def test_header_declares_expected_entry_points():
-    assert declared_functions() == ["kda_decode_step", "kda_decode_step_ex", "kda_fwd_chunked",
+    assert declared_functions() == ["kda_bwd_chunked", "kda_bwd_workspace_bytes",
+                                    "kda_decode_step", "kda_decode_step_ex", "kda_fwd_chunked",
                                     "kda_fwd_chunked_ex", "kda_fwd_workspace_bytes",
                                     "kda_status_string"]
 
@@ -203,3 +204,52 @@ def test_binding_rejects_cpu_and_mismatched_tensors():
     with pytest.raises(ValueError, match="GPU tensor"):
         kda.decode_step(q[0], q[0].clone(), q[0].clone(), q[0].clone(), torch.zeros(4, 2),
                         torch.zeros(4, 2, 64, 64))
+
+
+def bwd(L, q=FAKE, k=FAKE, v=FAKE, g=FAKE, b=FAKE, gate=0, S0=None, dO=FAKE, dST=None, cu=None,
+        N=0, B=1, T=64, H=2, dk=128, dv=128, dt=1, dq=FAKE, dk_=FAKE, dv_=FAKE, dg=FAKE,
+        db=FAKE, dS0=None, ws=None, wsb=0):
+    return L.kda_bwd_chunked(q, k, v, g, b, gate, S0, dO, dST, cu, N, B, T, H, dk, dv, dt, dq,
+                             dk_, dv_, dg, db, dS0, ws, wsb, None)
+
+
+def test_bwd_workspace_bytes(L):
+    from gated_delta_rule_81_amd import kda
+    # per (32-token chunk slot, head): two fp32 dk x dv matrices and three 32 x 32
+    n = kda.bwd_workspace_bytes(4, 8192, 32, 128, 128, 4)
+    slots = 32 * (4 * 256 + 4 + 1)
+    assert n >= slots * (2 * 128 * 128 + 3 * 32 * 32) * 4
+    assert n % 256 == 0
+    assert kda.bwd_workspace_bytes(1, 100, 2, 64, 64, 3) >= 2 * (4 + 3 + 1) * (2 * 64 * 64 + 3 * 1024) * 4
+    assert kda.bwd_workspace_bytes(-1, 100, 2, 64, 64, 1) == 0
+
+
+@pytest.mark.parametrize("kw", [dict(q=None), dict(k=None), dict(v=None), dict(g=None),
+                                dict(b=None), dict(dO=None), dict(dq=None), dict(dk_=None),
+                                dict(dv_=None), dict(dg=None), dict(db=None)])
+def test_bwd_null_pointers(L, kw):
+    assert bwd(L, ws=FAKE, wsb=1 << 40, **kw) == 1
+
+
+@pytest.mark.parametrize("kw", [dict(dk=32), dict(dv=256), dict(dk=96)])
+def test_bwd_unsupported_sizes(L, kw):
+    assert bwd(L, **kw) == 2
+
+
+@pytest.mark.parametrize("kw", [dict(dt=2), dict(gate=3), dict(B=-1), dict(H=0),
+                                dict(q=FAKE + 4), dict(dS0=FAKE + 8), dict(dg=FAKE + 2)])
+def test_bwd_invalid(L, kw):
+    assert bwd(L, ws=FAKE, wsb=1 << 40, **kw) == 1
+
+
+def test_bwd_workspace_rules(L):
+    from gated_delta_rule_81_amd import kda
+    need = kda.bwd_workspace_bytes(1, 64, 2, 128, 128, 1)
+    assert bwd(L) == 1                                   # no workspace
+    assert bwd(L, ws=FAKE, wsb=need - 1) == 1            # too small
+    assert bwd(L, ws=FAKE + 16, wsb=need) == 1           # not 256-byte aligned
+    # no gate: log_alpha and dlog_alpha unused
+    assert bwd(L, g=None, dg=None, gate=2, B=0) == 0
+    # varlen needs B == 1
+    assert bwd(L, cu=FAKE, N=2, B=2) == 1
+    assert bwd(L, B=0) == 0                              # nothing to do

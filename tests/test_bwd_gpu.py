@@ -1,0 +1,175 @@
+"""Backward (kda_bwd_chunked) on the GPU against the oracle's token-loop gradients.
+
+Every gradient (dq, dk, dv, dlog_alpha, dbeta, dS0) is compared element by
+element with oracle.bwd on the same inputs, at max |x - ref| / max |ref| per
+tensor within 1e-4 (fp32 inputs) or 2e-2 (bf16 inputs; the kernels compute in
+fp32 and round the gradients to bf16).  Shapes span several 32-token chunks
+and a ragged tail; packed sequences include an empty and a one-token one;
+strong-decay chunks drive the within-chunk decay far below fp32's range
+(the pairwise factors never leave it); the headline shape is checked on
+sampled (sequence, head) units.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import TOL, f64, rel_err, sample_units
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+NAMES = ("dq", "dk", "dv", "dlog_alpha", "dbeta", "dS0")
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _case(B, T, H, dk, dv, dt, seed, gate="channel", lengths=None, s0=True, dst=True,
+          strong=False, gate_mu=-1.0):
+    from gated_delta_rule_81_amd import synth
+    x = synth.random_fwd(B, T, H, dk, dv, dtype=dt, seed=seed, gate_mu=gate_mu,
+                         s0_std=0.5 if s0 else 0.0, lengths=lengths)
+    if not s0:
+        x["S0"] = None
+    g = torch.Generator().manual_seed(seed + 1000)
+    if strong:
+        # every third chunk decays by e^-30 per token on half the channels
+        la = x["log_alpha"].float()
+        Tt = la.shape[1]
+        for t0 in range(0, Tt, 96):
+            la[:, t0:t0 + 32, :, : dk // 2] = -30.0
+        x["log_alpha"] = la.to(dt)
+    if gate == "head":
+        x["log_alpha"] = x["log_alpha"][..., 0].contiguous()
+    elif gate == "none":
+        x["log_alpha"] = None
+    N = len(lengths) if lengths is not None else B
+    x["dO"] = torch.randn(x["v"].shape, generator=g).to(dt)
+    x["dS_T"] = torch.randn((N, H, dk, dv), generator=g) if dst else None
+    return x
+
+
+def _gpu(x, gate):
+    from gated_delta_rule_81_amd import kda
+    d = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in x.items()}
+    out = kda.bwd_chunked(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["dO"], d["S0"],
+                          d["dS_T"], d["cu_seqlens"], gate=gate)
+    torch.cuda.synchronize()
+    return out
+
+
+def _ref(x, gate):
+    import oracle
+    o64 = lambda t: None if t is None else f64(t)
+    cu = x["cu_seqlens"].tolist() if x["cu_seqlens"] is not None else None
+    return oracle.bwd(f64(x["q"]), f64(x["k"]), f64(x["v"]), o64(x["log_alpha"]), f64(x["beta"]),
+                      o64(x["S0"]), f64(x["dO"]), o64(x["dS_T"]), cu, gate=gate)
+
+
+def _compare(got, ref, tol, what):
+    errs = {}
+    for name, a, b in zip(NAMES, got, ref):
+        if b is None:
+            assert a is None, name
+            continue
+        errs[name] = rel_err(f64(a), b)
+    _say(f"  {what}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()) + f" (tol {tol})")
+    bad = {k: v for k, v in errs.items() if not v <= tol}
+    assert not bad, bad
+
+
+SMALL = [
+    # B, T, H, dk, dv, dtype
+    (2, 100, 2, 64, 64, torch.float32),
+    (1, 130, 3, 64, 128, torch.float32),
+    (1, 97, 2, 128, 128, torch.float32),
+    (2, 100, 2, 128, 64, torch.bfloat16),
+    (1, 161, 2, 128, 128, torch.bfloat16),
+    (2, 64, 1, 64, 64, torch.bfloat16),
+]
+
+
+@pytest.mark.parametrize("B,T,H,dk,dv,dt", SMALL)
+def test_bwd_small(B, T, H, dk, dv, dt):
+    _say(f"[bwd small] B={B} T={T} H={H} dk={dk} dv={dv} {dt}")
+    x = _case(B, T, H, dk, dv, dt, seed=31 + T)
+    _compare(_gpu(x, "channel"), _ref(x, "channel"), TOL[dt], "channel")
+
+
+@pytest.mark.parametrize("gate", ["head", "none"])
+@pytest.mark.parametrize("dt", [torch.float32, torch.bfloat16])
+def test_bwd_gate_layouts(gate, dt):
+    _say(f"[bwd gate={gate}] {dt}")
+    x = _case(1, 120, 2, 64, 64, dt, seed=41, gate=gate)
+    _compare(_gpu(x, gate), _ref(x, gate), TOL[dt], gate)
+
+
+@pytest.mark.parametrize("dt", [torch.float32, torch.bfloat16])
+def test_bwd_varlen_with_empty_and_short(dt):
+    lengths = [45, 0, 1, 70, 32, 0, 33]
+    _say(f"[bwd varlen] lengths={lengths} {dt}")
+    x = _case(1, 0, 2, 64, 128, dt, seed=43, lengths=lengths)
+    got = _gpu(x, "channel")
+    ref = _ref(x, "channel")
+    _compare(got, ref, TOL[dt], "varlen")
+    # an empty sequence passes dS_T straight to dS0
+    assert torch.equal(got[5][1].cpu(), x["dS_T"][1])
+
+
+@pytest.mark.parametrize("dt", [torch.float32, torch.bfloat16])
+def test_bwd_strong_decay(dt):
+    _say(f"[bwd strong decay] {dt}")
+    x = _case(1, 200, 2, 64, 64, dt, seed=47, strong=True)
+    _compare(_gpu(x, "channel"), _ref(x, "channel"), TOL[dt], "strong decay")
+
+
+def test_bwd_without_initial_state_or_final_gradient():
+    _say("[bwd S0=None dS_T=None] bf16")
+    x = _case(2, 90, 2, 128, 64, torch.bfloat16, seed=53, s0=False, dst=False)
+    _compare(_gpu(x, "channel"), _ref(x, "channel"), TOL[torch.bfloat16], "no S0 / dS_T")
+
+
+def test_bwd_h16_workload_full():
+    """B=1 H=16 T=4096 d=128 bf16 (the H16 workload's inputs), every unit."""
+    from gated_delta_rule_81_amd import synth
+    w = synth.FWD_H16_T4K
+    _say(f"[bwd {w.name}] full")
+    x = synth.fwd_inputs(w)
+    g = torch.Generator().manual_seed(501)
+    x["dO"] = torch.randn(x["v"].shape, generator=g).to(w.dtype)
+    x["dS_T"] = torch.randn(x["S0"].shape, generator=g) if x["S0"] is not None else None
+    _compare(_gpu(x, "channel"), _ref(x, "channel"), TOL[w.dtype], w.name)
+
+
+def test_bwd_headline_sampled_units():
+    """B=4 H=32 T=8192 d=128 bf16, the full call; 6 sampled (sequence, head)
+    units against the oracle (units are independent)."""
+    import oracle
+    from gated_delta_rule_81_amd import synth
+    w = synth.FWD_H32_T8K
+    _say(f"[bwd {w.name}] generating on the GPU")
+    x = synth.fwd_inputs(w, device=DEV)
+    g = torch.Generator(device=DEV).manual_seed(502)
+    x["dO"] = torch.randn(x["v"].shape, generator=g, device=DEV).to(w.dtype)
+    x["dS_T"] = torch.randn(x["S0"].shape, generator=g, device=DEV)
+    got = _gpu(x, "channel")
+    for name, t in zip(NAMES, got):
+        assert torch.isfinite(t.float()).all(), name
+    units = sample_units(w.B, w.H, 6, seed=503)
+    _say(f"  oracle on units {units}")
+    # the units as separate packed sequences of one oracle call (threads run them in parallel)
+    sl = lambda t, s, h: f64(t[s:s + 1, :, h:h + 1])
+    cat = lambda t: np.concatenate([sl(t, s, h) for s, h in units], axis=1)
+    st = lambda t: np.concatenate([f64(t[s:s + 1, h:h + 1]) for s, h in units], axis=0)
+    cu = [i * w.T for i in range(len(units) + 1)]
+    ref = oracle.bwd(cat(x["q"]), cat(x["k"]), cat(x["v"]), cat(x["log_alpha"]), cat(x["beta"]),
+                     st(x["S0"]), cat(x["dO"]), st(x["dS_T"]), cu)
+    mine = [cat(got[i]) for i in range(5)] + [st(got[5])]
+    errs = {name: rel_err(a, b) for name, a, b in zip(NAMES, mine, ref)}
+    _say("  " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    bad = {k: v for k, v in errs.items() if not v <= TOL[w.dtype]}
+    assert not bad, bad

@@ -64,3 +64,27 @@ def test_bwd_mutant_is_caught(tmp_path, name, old, new):
         except (AssertionError, ValueError, FloatingPointError):
             failed.append(pin.__name__)
     assert failed, f"mutant {name} passed every pin"
+
+
+@pytest.mark.parametrize("C", [1, 7, 32])
+def test_chunk_form_backward_matches_oracle(C):
+    """The chunked backward algebra (chunk_form.chunk_step_bwd, the form the GPU
+    kernels take) reaches the oracle's token-loop gradients in fp64, with a
+    ragged last chunk."""
+    import numpy as np
+    from chunk_form import chunked_backward
+    rng = np.random.default_rng(3)
+    B, T, H, dk, dv = 2, 77, 2, 6, 5
+    q = rng.normal(size=(B, T, H, dk))
+    k = rng.normal(size=(B, T, H, dk)) / np.sqrt(dk)
+    v = rng.normal(size=(B, T, H, dv))
+    g = -np.log1p(np.exp(rng.normal(-1, 1, size=(B, T, H, dk))))
+    b = rng.random((B, T, H))
+    S0 = rng.normal(size=(B, H, dk, dv))
+    dO = rng.normal(size=(B, T, H, dv))
+    dST = rng.normal(size=(B, H, dk, dv))
+    ref = oracle.bwd(q, k, v, g, b, S0, dO, dST)
+    got = chunked_backward(q, k, v, g, b, S0, dO, dST, C)
+    for name, x, y in zip(("dq", "dk", "dv", "dg", "dbeta", "dS0"), got, ref):
+        err = float(np.max(np.abs(x - y)) / np.max(np.abs(y)))
+        assert err < 1e-12, (name, err)
