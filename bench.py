@@ -152,6 +152,50 @@ def _fwd_bytes(tokens, H, dk, dv, N, gate_elems, elem=2):
             + 2 * N * H * dk * dv * 4)
 
 
+def _bwd_bytes(tokens, H, dk, dv, N, elem=2):
+    """Algorithmic bytes of one backward call: q, k, log_alpha, v, beta and dO
+    read, dq, dk, dlog_alpha, dv and dbeta written, and the fp32 S0 and dS_T
+    read and dS0 written (the recomputed chunk states are not counted)."""
+    per = (3 * dk + dv + 1 + dv) + (3 * dk + dv + 1)
+    return tokens * H * per * elem + 3 * N * H * dk * dv * 4
+
+
+def bench_backward(torch, kda, synth, steps=10, warmup=2):
+    """The backward (kda_bwd_chunked) on the B=4 H=32 T=8192 d=128 shape,
+    channel gate, with dO ~ N(0,1) in bf16 and dS_T ~ N(0,1)."""
+    w = synth.FWD_H32_T8K
+    log(f"[bench] backward: generating {w.name} on the GPU")
+    x = synth.fwd_inputs(w, device="cuda")
+    B, T, H, dk, dv, N = x["B"], x["T"], x["H"], x["dk"], x["dv"], x["N"]
+    g = torch.Generator(device="cuda").manual_seed(777)
+    dO = torch.randn(x["v"].shape, generator=g, device="cuda").to(w.dtype)
+    dST = torch.randn((N, H, dk, dv), generator=g, device="cuda")
+    out = (torch.empty_like(x["q"]), torch.empty_like(x["k"]), torch.empty_like(x["v"]),
+           torch.empty_like(x["log_alpha"]), torch.empty_like(x["beta"]),
+           torch.empty((N, H, dk, dv), dtype=torch.float32, device="cuda"))
+    ws = torch.empty(kda.bwd_workspace_bytes(B, T, H, dk, dv, N), dtype=torch.uint8, device="cuda")
+
+    def step():
+        kda.bwd_chunked(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], dO, x["S0"], dST,
+                        None, workspace=ws, out=out)
+
+    secs = time_loop(torch, step, steps, warmup) / steps
+    tokens = B * T
+    nbytes = _bwd_bytes(tokens, H, dk, dv, N)
+    gbs = nbytes / secs / 1e9
+    res = {"workload": w.name + "_backward", "us_per_call": round(secs * 1e6, 1),
+           "tokens": tokens, "tokens_per_s": round(tokens / secs, 1),
+           "workspace_bytes": ws.numel(),
+           "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                        "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                        "algorithmic_bytes_per_call": nbytes,
+                        "kernels": ["bwd_prep_kernel", "bwd_states_kernel", "bwd_dstates_kernel",
+                                    "bwd_grads_kernel"]}}
+    del x, dO, dST, out, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def bench_other_workloads(torch, kda, synth, steps=10, warmup=3):
     """The forward on the H16 and packed-varlen workloads, and the headline
     shape with a per-head gate, with no gate, and with the input preparation
@@ -409,6 +453,7 @@ def main():
         "roofline": roofline,
     }
     out["workloads"] = bench_other_workloads(torch, kda, synth)
+    out["backward"] = bench_backward(torch, kda, synth)
     if not args.no_decode:
         dc = bench_decode(torch, kda, synth, args.decode_steps)
         gbs = dc["bytes"] / dc["t_step"] / 1e9

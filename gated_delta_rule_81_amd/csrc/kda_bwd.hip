@@ -53,7 +53,13 @@ struct Params {
     void *dq, *dk, *dv, *dg, *dbeta;
     float *dS0;
     float *wS, *wD, *wT, *wP, *wM;   // workspace, per (chunk slot, head)
+    int32_t *wF;                     // per (chunk slot, head): 1 = exact path
 };
+
+// A chunk takes the factorised path (K_dn = K e^{-Gamma} as an MFMA operand)
+// when every channel's total log2 decay is at least -64, so that e^{-Gamma}
+// stays below 2^64; otherwise every pairwise decay factor is formed directly.
+constexpr float kFastMinLog2 = -64.0f;
 
 __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
@@ -122,86 +128,202 @@ __device__ __forceinline__ bool slot_chunk(const Params &p, long slot, long &t0,
     return true;
 }
 
-// log2 of alpha for token t, head h, key channel c (0 without a gate)
-template <typename Tin, int DK>
-__device__ __forceinline__ float log2_alpha(const Params &p, long t, int h, int c) {
-    if (p.gate == GATE_CHANNEL) return ld<Tin>(p.g, ((size_t)t * p.H + h) * DK + c) * kLog2e;
-    if (p.gate == GATE_HEAD) return ld<Tin>(p.g, (size_t)t * p.H + h) * kLog2e;
-    return 0.0f;
+// NE consecutive elements of one row, fetched with 16-byte (or 8-byte) loads
+// and kept as raw bits until used, so that a batch of loads is in flight
+// before the first wait.  A masked segment reads offset 0 (always a valid
+// address) and yields zeros.
+template <typename Tin, int NE> struct Seg;
+template <int NE> struct Seg<bf16_t, NE> {
+    static_assert(NE == 4 || NE % 8 == 0, "segment length");
+    uint32_t w[NE / 2];
+    bool ok;
+    __device__ __forceinline__ void load(const void *base, size_t off, bool valid) {
+        ok = valid;
+        const bf16_t *q = static_cast<const bf16_t *>(base) + (valid ? off : 0);
+        if constexpr (NE == 4) {
+            const uint2 v = *reinterpret_cast<const uint2 *>(q);
+            w[0] = v.x;
+            w[1] = v.y;
+        } else {
+#pragma unroll
+            for (int j = 0; j < NE / 8; ++j) {
+                const uint4 v = reinterpret_cast<const uint4 *>(q)[j];
+                w[4 * j] = v.x;
+                w[4 * j + 1] = v.y;
+                w[4 * j + 2] = v.z;
+                w[4 * j + 3] = v.w;
+            }
+        }
+    }
+    __device__ __forceinline__ float get(int j) const {
+        const uint32_t x = w[j >> 1];
+        const float f = __uint_as_float((j & 1) ? (x & 0xffff0000u) : (x << 16));
+        return ok ? f : 0.0f;
+    }
+};
+template <int NE> struct Seg<float, NE> {
+    static_assert(NE % 4 == 0, "segment length");
+    float w[NE];
+    bool ok;
+    __device__ __forceinline__ void load(const void *base, size_t off, bool valid) {
+        ok = valid;
+        const float *q = static_cast<const float *>(base) + (valid ? off : 0);
+#pragma unroll
+        for (int j = 0; j < NE / 4; ++j) {
+            const float4 v = reinterpret_cast<const float4 *>(q)[j];
+            w[4 * j] = v.x;
+            w[4 * j + 1] = v.y;
+            w[4 * j + 2] = v.z;
+            w[4 * j + 3] = v.w;
+        }
+    }
+    __device__ __forceinline__ float get(int j) const { return ok ? w[j] : 0.0f; }
+};
+// one element, raw
+template <typename Tin> struct One {
+    float w;
+    bool ok;
+    __device__ __forceinline__ void load(const void *base, size_t off, bool valid) {
+        ok = valid;
+        w = ld<Tin>(base, valid ? off : 0);
+    }
+    __device__ __forceinline__ float get() const { return ok ? w : 0.0f; }
+};
+
+// The rows of one chunk that every kernel reads: k (and q) and the gate,
+// thread t holding row t / 8, channels (t % 8) * DK/8 onwards; beta of row t.
+template <typename Tin, int DK, bool WITH_Q> struct ChunkIn {
+    static constexpr int NE = DK / 8, DKP = DK + 1;
+    Seg<Tin, NE> k, q, g;
+    One<Tin> gh, b;
+    // Every load is issued unconditionally (an unused one reads offset 0 of a
+    // valid tensor), so that no value merges across branches and forces an
+    // early wait.
+    __device__ __forceinline__ void load(const Params &p, long t0, int cl, int h) {
+        const int tid = threadIdx.x, r = tid >> 3, c0 = (tid & 7) * NE;
+        const bool ok = r < cl;
+        const size_t e = ((size_t)(t0 + r) * p.H + h) * DK + c0;
+        k.load(p.k, e, ok);
+        if constexpr (WITH_Q) q.load(p.q, e, ok);
+        const bool ch = p.gate == GATE_CHANNEL, hd = p.gate == GATE_HEAD;
+        g.load(ch ? p.g : p.k, e, ok && ch);
+        gh.load(hd ? p.g : p.beta, (size_t)(t0 + r) * p.H + h, ok && hd);
+        b.load(p.beta, (size_t)(t0 + tid) * p.H + h, tid < cl && tid < C);
+    }
+    // raw k (q), log2 gates and beta into LDS
+    __device__ __forceinline__ void store(const Params &p, float *sK, float *sQ, float *sG, float *sB) const {
+        const int tid = threadIdx.x, r = tid >> 3, c0 = (tid & 7) * NE;
+#pragma unroll
+        for (int j = 0; j < NE; ++j) {
+            sK[r * DKP + c0 + j] = k.get(j);
+            if constexpr (WITH_Q) sQ[r * DKP + c0 + j] = q.get(j);
+            float gv = 0.0f;
+            if (p.gate == GATE_CHANNEL) gv = g.get(j) * kLog2e;
+            else if (p.gate == GATE_HEAD) gv = gh.get() * kLog2e;
+            sG[r * DKP + c0 + j] = gv;
+        }
+        if (tid < C) sB[tid] = b.get();
+    }
+};
+
+// One 16 x 16 tile of a (d_k x d_v) fp32 state from global memory (or zeros),
+// as this lane's four accumulator rows.
+__device__ __forceinline__ void load_tile(f32x4 &t, const float *src, size_t row0, int ld, int col) {
+    const int lane = threadIdx.x & 63, lr = lane & 15, lj = lane >> 4;
+    if (!src) {
+        t = f32x4{0.f, 0.f, 0.f, 0.f};
+        return;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) t[i] = src[(row0 + 4 * lj + i) * ld + col + lr];
 }
 
-// Loads the chunk's k (and q) rows and log2-gates into LDS (zeros past the
-// chunk end), turns the gates into running sums per channel (in sG) with
-// totals gc[c] and gamma = 2^gc; then, per element, K_up = k 2^G,
-// Q_up = q 2^G, K_right = k 2^{G_c - G}.  sG may be sKrt (each element is
-// read before it is overwritten by the same thread).  Ends with a barrier.
-template <typename Tin, int DK, bool WITH_Q>
-__device__ void chunk_factors(const Params &p, long t0, int cl, int h, float *sKup, float *sQup,
-                              float *sG, float *sKrt, float *gc, float *gam) {
+// Running sums of the log2 gates down each channel (in place), their totals
+// gc and gamma = 2^gc.  Threads below DK take one channel each.
+template <int DK>
+__device__ __forceinline__ void gate_sums(float *sG, float *gc, float *gam) {
     constexpr int DKP = DK + 1;
     const int tid = threadIdx.x;
-    for (int idx = tid; idx < C * DK; idx += NT) {
-        const int r = idx / DK, c = idx % DK;
-        const bool ok = r < cl;
-        const size_t e = ((size_t)(t0 + r) * p.H + h) * DK + c;
-        sKup[r * DKP + c] = ok ? ld<Tin>(p.k, e) : 0.0f;
-        if constexpr (WITH_Q) sQup[r * DKP + c] = ok ? ld<Tin>(p.q, e) : 0.0f;
-        sG[r * DKP + c] = ok ? log2_alpha<Tin, DK>(p, t0 + r, h, c) : 0.0f;
-    }
-    __syncthreads();
     if (tid < DK) {
+        float x[C];
+#pragma unroll
+        for (int r = 0; r < C; ++r) x[r] = sG[r * DKP + tid];
         float run = 0.0f;
+#pragma unroll
         for (int r = 0; r < C; ++r) {
-            run += sG[r * DKP + tid];
+            run += x[r];
             sG[r * DKP + tid] = run;
         }
-        gc[tid] = run;
-        gam[tid] = __builtin_amdgcn_exp2f(run);
+        if (gc) gc[tid] = run;
+        if (gam) gam[tid] = __builtin_amdgcn_exp2f(run);
     }
-    __syncthreads();
-    for (int idx = tid; idx < C * DK; idx += NT) {
-        const int r = idx / DK, c = idx % DK;
-        const float G = sG[r * DKP + c], kv = sKup[r * DKP + c];
+}
+
+// K_up = k 2^G, Q_up = q 2^G, K_right = k 2^{G_c - G} on this thread's row
+// segment (sG may be sKrt: each element is read before it is overwritten).
+template <int DK, bool WITH_Q>
+__device__ __forceinline__ void scale_rows(float *sKup, float *sQup, const float *sG, float *sKrt,
+                                           const float *gc) {
+    constexpr int NE = DK / 8, DKP = DK + 1;
+    const int tid = threadIdx.x, r = tid >> 3, c0 = (tid & 7) * NE;
+#pragma unroll
+    for (int j = 0; j < NE; ++j) {
+        const int o = r * DKP + c0 + j;
+        const float G = sG[o], kv = sKup[o];
         const float E = __builtin_amdgcn_exp2f(G);
-        sKup[r * DKP + c] = kv * E;
-        if constexpr (WITH_Q) sQup[r * DKP + c] *= E;
-        sKrt[r * DKP + c] = kv * __builtin_amdgcn_exp2f(gc[c] - G);
+        sKup[o] = kv * E;
+        if constexpr (WITH_Q) sQup[o] *= E;
+        sKrt[o] = kv * __builtin_amdgcn_exp2f(gc[c0 + j] - G);
     }
-    __syncthreads();
 }
 
 // ---------------------------------------------------------------------------
 // M0, P and T of one chunk.
 template <typename Tin, int DK>
 __global__ void __launch_bounds__(NT) bwd_prep_kernel(Params p) {
-    constexpr int DKP = DK + 1, NCC = DK / 8;
+    constexpr int DKP = DK + 1, NCC = DK / 8, NE = DK / 8;
     __shared__ float sK[C * DKP], sQ[C * DKP], sG[C * DKP];
-    __shared__ float sM[C * CP], sP[C * CP], sB[C];
+    __shared__ float sM[C * CP], sP[C * CP], sB[C], gc[DK];
     const long slot = blockIdx.x;
-    const int h = blockIdx.y, tid = threadIdx.x;
+    const int h = blockIdx.y, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     long t0;
     int cl;
     if (!slot_chunk(p, slot, t0, cl)) return;
-    for (int idx = tid; idx < C * DK; idx += NT) {
-        const int r = idx / DK, c = idx % DK;
-        const bool ok = r < cl;
-        const size_t e = ((size_t)(t0 + r) * p.H + h) * DK + c;
-        sK[r * DKP + c] = ok ? ld<Tin>(p.k, e) : 0.0f;
-        sQ[r * DKP + c] = ok ? ld<Tin>(p.q, e) : 0.0f;
-        sG[r * DKP + c] = ok ? log2_alpha<Tin, DK>(p, t0 + r, h, c) : 0.0f;
-    }
-    if (tid < C) sB[tid] = tid < cl ? ld<Tin>(p.beta, (size_t)(t0 + tid) * p.H + h) : 0.0f;
-    __syncthreads();
-    if (tid < DK) {
-        float run = 0.0f;
-        for (int r = 0; r < C; ++r) {
-            run += sG[r * DKP + tid];
-            sG[r * DKP + tid] = run;
-        }
-    }
-    __syncthreads();
-    // pairwise sums: thread (row r, channel group cg) over channels cg + 8 cc
     {
+        ChunkIn<Tin, DK, true> in;
+        in.load(p, t0, cl, h);
+        in.store(p, sK, sQ, sG, sB);
+    }
+    __syncthreads();
+    gate_sums<DK>(sG, gc, nullptr);
+    const size_t wi = (size_t)slot * p.H + h;
+    const bool exact = __syncthreads_or(tid < DK && !(gc[tid] >= kFastMinLog2));
+    if (tid == 0) p.wF[wi] = exact ? 1 : 0;
+    if (!exact) {
+        // K_up = k 2^G, Q_up = q 2^G, K_dn = k 2^-G in place; then
+        // M0 = K_up K_dn^T (strictly lower) and P = Q_up K_dn^T (lower) on MFMA
+        const int r = tid >> 3, c0 = (tid & 7) * NE;
+#pragma unroll
+        for (int j = 0; j < NE; ++j) {
+            const int o = r * DKP + c0 + j;
+            const float G = sG[o], kv = sK[o];
+            sK[o] = kv * __builtin_amdgcn_exp2f(G);
+            sQ[o] *= __builtin_amdgcn_exp2f(G);
+            sG[o] = kv * __builtin_amdgcn_exp2f(-G);
+        }
+        __syncthreads();
+        const int tm = wave >> 1, tn = wave & 1, lr = lane & 15, lj = lane >> 4;
+        f32x4 m = {0.f, 0.f, 0.f, 0.f}, pp = {0.f, 0.f, 0.f, 0.f};
+        m = mm(m, sK + 16 * tm * DKP, DKP, 1, sG + 16 * tn * DKP, 1, DKP, DK);
+        pp = mm(pp, sQ + 16 * tm * DKP, DKP, 1, sG + 16 * tn * DKP, 1, DKP, DK);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = 16 * tm + 4 * lj + i, col = 16 * tn + lr;
+            sM[row * CP + col] = col < row ? m[i] : 0.0f;
+            sP[row * CP + col] = col <= row ? pp[i] : 0.0f;
+        }
+    } else {
+        // pairwise sums: thread (row r, channel group cg) over channels cg + 8 cc
         const int r = tid >> 3, cg = tid & 7;
         float kr[NCC], qr[NCC], gr[NCC];
 #pragma unroll
@@ -234,12 +356,13 @@ __global__ void __launch_bounds__(NT) bwd_prep_kernel(Params p) {
         }
     }
     __syncthreads();
-    const size_t wi = (size_t)slot * p.H + h;
     float *gT = p.wT + wi * C * C, *gP = p.wP + wi * C * C, *gM = p.wM + wi * C * C;
-    for (int idx = tid; idx < C * C; idx += NT) {
-        const int r = idx / C, i = idx % C;
-        gP[idx] = sP[r * CP + i];
-        gM[idx] = sM[r * CP + i];
+    {
+        const int r = (tid * 4) / C, i = (tid * 4) % C;
+        *reinterpret_cast<float4 *>(gP + tid * 4) =
+            make_float4(sP[r * CP + i], sP[r * CP + i + 1], sP[r * CP + i + 2], sP[r * CP + i + 3]);
+        *reinterpret_cast<float4 *>(gM + tid * 4) =
+            make_float4(sM[r * CP + i], sM[r * CP + i + 1], sM[r * CP + i + 2], sM[r * CP + i + 3]);
     }
     // T = (I + A)^{-1}, A = Diag(beta) M0 strictly lower: column i by lane i,
     // rows in order, T_ri = [r == i] - sum_{j < r} A_rj T_ji
@@ -248,18 +371,19 @@ __global__ void __launch_bounds__(NT) bwd_prep_kernel(Params p) {
         float t[C];
 #pragma unroll
         for (int r = 0; r < C; ++r) {
-            float acc = r == i ? 1.0f : 0.0f;
+            float acc = 0.0f;
 #pragma unroll
-            for (int j = 0; j < r; ++j) acc -= sB[r] * sM[r * CP + j] * t[j];
-            t[r] = acc;
-            gT[r * C + i] = acc;
+            for (int j = 0; j < r; ++j) acc += sM[r * CP + j] * t[j];
+            t[r] = (r == i ? 1.0f : 0.0f) - sB[r] * acc;
+            gT[r * C + i] = t[r];
         }
     }
 }
 
 // ---------------------------------------------------------------------------
 // Forward state chain of one (sequence, head, slice): the state entering
-// every chunk goes to the workspace.
+// every chunk goes to the workspace.  The next chunk's inputs are requested
+// while the current one is computed.
 template <typename Tin, int DK>
 __global__ void __launch_bounds__(NT) bwd_states_kernel(Params p) {
     constexpr int DKP = DK + 1, NTW = DK / 32;   // state tiles per wave
@@ -269,24 +393,30 @@ __global__ void __launch_bounds__(NT) bwd_states_kernel(Params p) {
     const int unit = blockIdx.x / nsl, slice = blockIdx.x % nsl;
     const int s = unit / p.H, h = unit % p.H, col0 = slice * W;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, lj = lane >> 4;
+    const int vr = tid >> 3, vc = (tid & 7) * 4;          // this thread's 4 values of a C x W tile
     long t0s, base;
     int len;
     seq_info(p, s, t0s, len, base);
     const int nch = (len + C - 1) / C;
+    ChunkIn<Tin, DK, false> in;
+    Seg<Tin, 4> vin;
+    Seg<float, 4> tin;
+    auto issue = [&](int n) {
+        const long t0 = t0s + (long)n * C;
+        const int cl = len - n * C < C ? len - n * C : C;
+        in.load(p, t0, cl, h);
+        vin.load(p.v, ((size_t)(t0 + vr) * p.H + h) * p.DV + col0 + vc, vr < cl);
+        tin.load(p.wT, ((size_t)(base + n) * p.H + h) * C * C + tid * 4, true);
+    };
+    if (nch > 0) issue(0);
     // state tiles of this wave: tile index w * NTW + x -> (tm, tn) over (DK/16) x (W/16)
     f32x4 S[NTW];
 #pragma unroll
     for (int x = 0; x < NTW; ++x) {
         const int tt = wave * NTW + x, tm = tt >> 1, tn = tt & 1;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = 16 * tm + 4 * lj + i, col = col0 + 16 * tn + lr;
-            S[x][i] = p.S0 ? p.S0[(((size_t)s * p.H + h) * DK + row) * p.DV + col] : 0.0f;
-        }
+        load_tile(S[x], p.S0, ((size_t)s * p.H + h) * DK + 16 * tm, p.DV, col0 + 16 * tn);
     }
     for (int n = 0; n < nch; ++n) {
-        const long t0 = t0s + (long)n * C;
-        const int cl = len - n * C < C ? len - n * C : C;
         const size_t wi = (size_t)(base + n) * p.H + h;
         float *gS = p.wS + wi * DK * p.DV;
 #pragma unroll
@@ -299,14 +429,18 @@ __global__ void __launch_bounds__(NT) bwd_states_kernel(Params p) {
                 gS[(size_t)row * p.DV + col0 + col] = S[x][i];
             }
         }
-        for (int idx = tid; idx < C * W; idx += NT) {
-            const int r = idx / W, c = idx % W;
-            sV[r * WP + c] = r < cl ? ld<Tin>(p.v, ((size_t)(t0 + r) * p.H + h) * p.DV + col0 + c) : 0.0f;
+        in.store(p, sKup, nullptr, sKrt, sB);     // sKrt holds the gate sums first
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            sV[vr * WP + vc + j] = vin.get(j);
+            sT[((tid * 4) / C) * CP + (tid * 4) % C + j] = tin.get(j);
         }
-        for (int idx = tid; idx < C * C; idx += NT) sT[(idx / C) * CP + idx % C] = p.wT[wi * C * C + idx];
-        if (tid < C) sB[tid] = tid < cl ? ld<Tin>(p.beta, (size_t)(t0 + tid) * p.H + h) : 0.0f;
-        // sKrt first holds the gate sums
-        chunk_factors<Tin, DK, false>(p, t0, cl, h, sKup, nullptr, sKrt, sKrt, gc, gam);
+        if (n + 1 < nch) issue(n + 1);
+        __syncthreads();
+        gate_sums<DK>(sKrt, gc, gam);
+        __syncthreads();
+        scale_rows<DK, false>(sKup, nullptr, sKrt, sKrt, gc);
+        __syncthreads();
         // X = V - K_up S, kept as beta X
         {
             const int tm = wave >> 1, tn = wave & 1;
@@ -343,7 +477,8 @@ __global__ void __launch_bounds__(NT) bwd_states_kernel(Params p) {
 // ---------------------------------------------------------------------------
 // State-gradient chain of one (sequence, head, slice), chunks in reverse: D
 // (the gradient of the state leaving each chunk) goes to the workspace, and
-// the gradient of the initial state to dS0.
+// the gradient of the initial state to dS0.  The next chunk's inputs are
+// requested while the current one is computed.
 template <typename Tin, int DK>
 __global__ void __launch_bounds__(NT) bwd_dstates_kernel(Params p) {
     constexpr int DKP = DK + 1, NTW = DK / 32;
@@ -353,24 +488,32 @@ __global__ void __launch_bounds__(NT) bwd_dstates_kernel(Params p) {
     const int unit = blockIdx.x / nsl, slice = blockIdx.x % nsl;
     const int s = unit / p.H, h = unit % p.H, col0 = slice * W;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, lj = lane >> 4;
+    const int vr = tid >> 3, vc = (tid & 7) * 4;
     long t0s, base;
     int len;
     seq_info(p, s, t0s, len, base);
     const int nch = (len + C - 1) / C;
     const size_t so = ((size_t)s * p.H + h) * DK;
+    ChunkIn<Tin, DK, true> in;
+    Seg<Tin, 4> oin;
+    Seg<float, 4> tin, pin;
+    auto issue = [&](int n) {
+        const long t0 = t0s + (long)n * C;
+        const int cl = len - n * C < C ? len - n * C : C;
+        const size_t wi = (size_t)(base + n) * p.H + h;
+        in.load(p, t0, cl, h);
+        oin.load(p.dO, ((size_t)(t0 + vr) * p.H + h) * p.DV + col0 + vc, vr < cl);
+        tin.load(p.wT, wi * C * C + tid * 4, true);
+        pin.load(p.wP, wi * C * C + tid * 4, true);
+    };
+    if (nch > 0) issue(nch - 1);
     f32x4 D[NTW];
 #pragma unroll
     for (int x = 0; x < NTW; ++x) {
         const int tt = wave * NTW + x, tm = tt >> 1, tn = tt & 1;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = 16 * tm + 4 * lj + i, col = col0 + 16 * tn + lr;
-            D[x][i] = p.dST ? p.dST[(so + row) * p.DV + col] : 0.0f;
-        }
+        load_tile(D[x], p.dST, so + 16 * tm, p.DV, col0 + 16 * tn);
     }
     for (int n = nch - 1; n >= 0; --n) {
-        const long t0 = t0s + (long)n * C;
-        const int cl = len - n * C < C ? len - n * C : C;
         const size_t wi = (size_t)(base + n) * p.H + h;
         float *gD = p.wD + wi * DK * p.DV;
 #pragma unroll
@@ -383,16 +526,20 @@ __global__ void __launch_bounds__(NT) bwd_dstates_kernel(Params p) {
                 gD[(size_t)row * p.DV + col0 + col] = D[x][i];
             }
         }
-        for (int idx = tid; idx < C * W; idx += NT) {
-            const int r = idx / W, c = idx % W;
-            sdO[r * WP + c] = r < cl ? ld<Tin>(p.dO, ((size_t)(t0 + r) * p.H + h) * p.DV + col0 + c) : 0.0f;
+        in.store(p, sKup, sQup, sKrt, sB);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int tr = (tid * 4) / C, tc = (tid * 4) % C + j;
+            sdO[vr * WP + vc + j] = oin.get(j);
+            sT[tr * CP + tc] = tin.get(j);
+            sP[tr * CP + tc] = pin.get(j);
         }
-        for (int idx = tid; idx < C * C; idx += NT) {
-            sT[(idx / C) * CP + idx % C] = p.wT[wi * C * C + idx];
-            sP[(idx / C) * CP + idx % C] = p.wP[wi * C * C + idx];
-        }
-        if (tid < C) sB[tid] = tid < cl ? ld<Tin>(p.beta, (size_t)(t0 + tid) * p.H + h) : 0.0f;
-        chunk_factors<Tin, DK, true>(p, t0, cl, h, sKup, sQup, sKrt, sKrt, gc, gam);
+        if (n > 0) issue(n - 1);
+        __syncthreads();
+        gate_sums<DK>(sKrt, gc, gam);
+        __syncthreads();
+        scale_rows<DK, true>(sKup, sQup, sKrt, sKrt, gc);
+        __syncthreads();
         // dU = P^T dO + K_right D
         {
             const int tm = wave >> 1, tn = wave & 1;
@@ -447,9 +594,10 @@ constexpr int grads_floats() {
     return 4 * C * (DK + 1) + 3 * C * CP + 2 * DK * WP + 6 * C * WP + 3 * DK + 2 * C;
 }
 
-template <typename Tin, int DK>
+template <typename Tin, int DK, bool EXACT>
 __global__ void __launch_bounds__(NT) bwd_grads_kernel(Params p) {
     constexpr int DKP = DK + 1, NTW = DK / 32, NPART = NT / DK;
+    constexpr int NES = DK * W / NT, TPR = W / NES;     // S / D slice: NES values per thread
     __shared__ float smem[grads_floats<DK>()];
     float *sKup = smem;                  // C x DKP: K_up, later dk
     float *sQup = sKup + C * DKP;        //          Q_up, later dq
@@ -475,53 +623,49 @@ __global__ void __launch_bounds__(NT) bwd_grads_kernel(Params p) {
     const long slot = blockIdx.x;
     const int h = blockIdx.y, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int lr = lane & 15, lj = lane >> 4;
+    const int vr = tid >> 3, vc = (tid & 7) * 4;          // C x W values of this thread
+    const int sr = tid / TPR, sc = (tid % TPR) * NES;     // DK x W values of this thread
     long t0;
     int cl;
     if (!slot_chunk(p, slot, t0, cl)) return;
     const size_t wi = (size_t)slot * p.H + h;
+    // each chunk is done by the instantiation of its path (set by the prep kernel)
+    if ((p.wF[wi] != 0) != EXACT) return;
     const float *gS = p.wS + wi * DK * p.DV, *gD = p.wD + wi * DK * p.DV;
 
-    for (int idx = tid; idx < C * C; idx += NT) {
-        const int r = idx / C, i = idx % C;
-        sT[r * CP + i] = p.wT[wi * C * C + idx];
-        sP[r * CP + i] = p.wP[wi * C * C + idx];
-        sM[r * CP + i] = p.wM[wi * C * C + idx];
-    }
-    if (tid < C) {
-        sB[tid] = tid < cl ? ld<Tin>(p.beta, (size_t)(t0 + tid) * p.H + h) : 0.0f;
-        dB[tid] = 0.0f;
-    }
-    if (tid < DK) dgam[tid] = 0.0f;
-    // sKrt holds the gate sums until K_right replaces them; keep a copy in sG
+    // every load of the chunk, then the first slice's, before the first wait
+    Seg<float, NES> sin, din;
+    Seg<Tin, 4> vin, oin;
+    auto issue_slice = [&](int col0) {
+        sin.load(gS, (size_t)sr * p.DV + col0 + sc, true);
+        din.load(gD, (size_t)sr * p.DV + col0 + sc, true);
+        const size_t e = ((size_t)(t0 + vr) * p.H + h) * p.DV + col0 + vc;
+        vin.load(p.v, e, vr < cl);
+        oin.load(p.dO, e, vr < cl);
+    };
     {
-        for (int idx = tid; idx < C * DK; idx += NT) {
-            const int r = idx / DK, c = idx % DK;
-            const bool ok = r < cl;
-            const size_t e = ((size_t)(t0 + r) * p.H + h) * DK + c;
-            sKup[r * DKP + c] = ok ? ld<Tin>(p.k, e) : 0.0f;
-            sQup[r * DKP + c] = ok ? ld<Tin>(p.q, e) : 0.0f;
-            sG[r * DKP + c] = ok ? log2_alpha<Tin, DK>(p, t0 + r, h, c) : 0.0f;
-        }
-        __syncthreads();
-        if (tid < DK) {
-            float run = 0.0f;
-            for (int r = 0; r < C; ++r) {
-                run += sG[r * DKP + tid];
-                sG[r * DKP + tid] = run;
-            }
-            gc[tid] = run;
-            gam[tid] = __builtin_amdgcn_exp2f(run);
-        }
-        __syncthreads();
-        for (int idx = tid; idx < C * DK; idx += NT) {
-            const int r = idx / DK, c = idx % DK;
-            const float G = sG[r * DKP + c], kv = sKup[r * DKP + c];
-            const float E = __builtin_amdgcn_exp2f(G);
-            sKup[r * DKP + c] = kv * E;
-            sQup[r * DKP + c] *= E;
-            sKrt[r * DKP + c] = kv * __builtin_amdgcn_exp2f(gc[c] - G);
+        ChunkIn<Tin, DK, true> in;
+        Seg<float, 4> tin, pin, min;
+        in.load(p, t0, cl, h);
+        tin.load(p.wT, wi * C * C + tid * 4, true);
+        pin.load(p.wP, wi * C * C + tid * 4, true);
+        min.load(p.wM, wi * C * C + tid * 4, true);
+        issue_slice(0);
+        in.store(p, sKup, sQup, sG, sB);
+        const int tr = (tid * 4) / C, tc = (tid * 4) % C;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            sT[tr * CP + tc + j] = tin.get(j);
+            sP[tr * CP + tc + j] = pin.get(j);
+            sM[tr * CP + tc + j] = min.get(j);
         }
     }
+    if (tid < C) dB[tid] = 0.0f;
+    if (tid < DK) dgam[tid] = 0.0f;
+    __syncthreads();
+    gate_sums<DK>(sG, gc, gam);
+    __syncthreads();
+    scale_rows<DK, true>(sKup, sQup, sG, sKrt, gc);
 
     // accumulators over the d_v slices: this wave's tiles of dQ_up, dK_up
     // (negated) and dK_right (C x DK, tile w * NTW + x -> (tm, tn) over 2 x
@@ -536,18 +680,17 @@ __global__ void __launch_bounds__(NT) bwd_grads_kernel(Params p) {
     const int tm = wave >> 1, tn = wave & 1;        // this wave's C x W / C x C tile
     for (int col0 = 0; col0 < p.DV; col0 += W) {
         __syncthreads();
-        for (int idx = tid; idx < DK * W; idx += NT) {
-            const int r = idx / W, c = idx % W;
-            sS[r * WP + c] = gS[(size_t)r * p.DV + col0 + c];
-            sD[r * WP + c] = gD[(size_t)r * p.DV + col0 + c];
+#pragma unroll
+        for (int j = 0; j < NES; ++j) {
+            sS[sr * WP + sc + j] = sin.get(j);
+            sD[sr * WP + sc + j] = din.get(j);
         }
-        for (int idx = tid; idx < C * W; idx += NT) {
-            const int r = idx / W, c = idx % W;
-            const bool ok = r < cl;
-            const size_t e = ((size_t)(t0 + r) * p.H + h) * p.DV + col0 + c;
-            sX[r * WP + c] = ok ? ld<Tin>(p.v, e) : 0.0f;
-            sdO[r * WP + c] = ok ? ld<Tin>(p.dO, e) : 0.0f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            sX[vr * WP + vc + j] = vin.get(j);
+            sdO[vr * WP + vc + j] = oin.get(j);
         }
+        if (col0 + W < p.DV) issue_slice(col0 + W);
         __syncthreads();
         // X = V - K_up S
         {
@@ -600,6 +743,7 @@ __global__ void __launch_bounds__(NT) bwd_grads_kernel(Params p) {
         }
         if (tid < DK) {
             float acc = 0.0f;
+#pragma unroll 8
             for (int j = 0; j < W; ++j) acc += sD[tid * WP + j] * sS[tid * WP + j];
             dgam[tid] += acc;
         }
@@ -613,27 +757,6 @@ __global__ void __launch_bounds__(NT) bwd_grads_kernel(Params p) {
     }
     __syncthreads();
 
-    // direct terms, element by element where the tiles lie:
-    //   dq = dQ_up e^G,  dk = dK_up e^G + dK_right e^{G_c - G},
-    //   dGamma = dK_up K_up + dQ_up Q_up - dK_right K_right,
-    // and dK_right K_right kept for the chunk-total term
-    float *sRK = sS;                     // C x DKP
-#pragma unroll
-    for (int x = 0; x < NTW; ++x) {
-        const int tt = wave * NTW + x, m0 = 16 * (tt / (DK / 16)), n0 = 16 * (tt % (DK / 16));
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = m0 + 4 * lj + i, col = n0 + lr, o = row * DKP + col;
-            const float G = sG[o], E = __builtin_amdgcn_exp2f(G);
-            const float R = __builtin_amdgcn_exp2f(gc[col] - G);
-            const float dQu = aQ[x][i], dKu = -aK[x][i], dKr = aR[x][i];
-            const float ku = sKup[o], qu = sQup[o], kr = sKrt[o];
-            sQup[o] = dQu * E;
-            sKup[o] = dKu * E + dKr * R;
-            sKrt[o] = dKu * ku + dQu * qu - dKr * kr;
-            sRK[o] = dKr * kr;
-        }
-    }
     // dT' and dP (lower, diagonal included) to LDS
     float *sdT = sX, *sdP = sBX, *sY = sU, *sdA = sdU;
 #pragma unroll
@@ -646,6 +769,7 @@ __global__ void __launch_bounds__(NT) bwd_grads_kernel(Params p) {
     // dbeta_i from T' = T Diag(beta); then dT = dT' Diag(beta)
     if (tid < C) {
         float acc = 0.0f;
+#pragma unroll 8
         for (int r = 0; r < C; ++r) acc += sT[r * CP + tid] * sdT[r * WP + tid];
         dB[tid] = acc;
     }
@@ -677,6 +801,7 @@ __global__ void __launch_bounds__(NT) bwd_grads_kernel(Params p) {
     if (tid < C) {
         const int r = tid;
         float acc = 0.0f;
+#pragma unroll 8
         for (int i = 0; i < C; ++i) {
             const float a = sdA[r * WP + i];
             acc += a * sM[r * CP + i];
@@ -686,6 +811,85 @@ __global__ void __launch_bounds__(NT) bwd_grads_kernel(Params p) {
     }
     __syncthreads();
 
+    float *sRK = sS;                     // C x DKP: dK_right K_right
+    if constexpr (!EXACT) {
+        // factorised decay: with K_dn = K e^{-Gamma},
+        //   Z1 = dP K_dn,  Z2 = dM K_dn,  Z3 = dM^T K_up + dP^T Q_up,
+        //   dq = (dQ_up + Z1) e^G,  dk = (dK_up + Z2) e^G + dK_right e^{G_c - G} + Z3 e^{-G},
+        //   dGamma = (dK_up + Z2) K_up + (dQ_up + Z1) Q_up - dK_right K_right - Z3 K_dn
+        float *sKdn = sD;                // C x DKP
+        {
+            constexpr int NE = DK / 8;
+            const int r = tid >> 3, c0 = (tid & 7) * NE;
+            Seg<Tin, NE> kin;
+            kin.load(p.k, ((size_t)(t0 + r) * p.H + h) * DK + c0, r < cl);
+#pragma unroll
+            for (int j = 0; j < NE; ++j) {
+                const int o = r * DKP + c0 + j;
+                sKdn[o] = kin.get(j) * __builtin_amdgcn_exp2f(-sG[o]);
+            }
+        }
+        __syncthreads();
+        f32x4 zrk[NTW];                  // dK_right K_right, stored after the barrier below
+#pragma unroll
+        for (int x = 0; x < NTW; ++x) {
+            const int tt = wave * NTW + x, m0 = 16 * (tt / (DK / 16)), n0 = 16 * (tt % (DK / 16));
+            f32x4 z1 = {0.f, 0.f, 0.f, 0.f}, z2 = z1, z3 = z1;
+            z1 = mm(z1, sdP + m0 * WP, WP, 1, sKdn + n0, DKP, 1, C);
+            z2 = mm(z2, sM + m0 * CP, CP, 1, sKdn + n0, DKP, 1, C);
+            z3 = mm(z3, sM + m0, 1, CP, sKup + n0, DKP, 1, C);
+            z3 = mm(z3, sdP + m0, 1, WP, sQup + n0, DKP, 1, C);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = m0 + 4 * lj + i, col = n0 + lr, o = row * DKP + col;
+                const float G = sG[o], E = __builtin_amdgcn_exp2f(G);
+                const float R = __builtin_amdgcn_exp2f(gc[col] - G);
+                const float Ei = __builtin_amdgcn_exp2f(-G);
+                // aK holds -dK_up
+                const float dQu = aQ[x][i] + z1[i], dKu = z2[i] - aK[x][i], dKr = aR[x][i];
+                const float ku = sKup[o], qu = sQup[o], kr = sKrt[o], kd = sKdn[o];
+                aQ[x][i] = dQu * E;
+                aK[x][i] = dKu * E + dKr * R + z3[i] * Ei;
+                aR[x][i] = dKu * ku + dQu * qu - dKr * kr - z3[i] * kd;
+                zrk[x][i] = dKr * kr;
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int x = 0; x < NTW; ++x) {
+            const int tt = wave * NTW + x, m0 = 16 * (tt / (DK / 16)), n0 = 16 * (tt % (DK / 16));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int o = (m0 + 4 * lj + i) * DKP + n0 + lr;
+                sQup[o] = aQ[x][i];
+                sKup[o] = aK[x][i];
+                sKrt[o] = aR[x][i];
+                sRK[o] = zrk[x][i];
+            }
+        }
+        __syncthreads();
+    } else {
+    // direct terms, element by element where the tiles lie:
+    //   dq = dQ_up e^G,  dk = dK_up e^G + dK_right e^{G_c - G},
+    //   dGamma = dK_up K_up + dQ_up Q_up - dK_right K_right,
+    // and dK_right K_right kept for the chunk-total term
+#pragma unroll
+    for (int x = 0; x < NTW; ++x) {
+        const int tt = wave * NTW + x, m0 = 16 * (tt / (DK / 16)), n0 = 16 * (tt % (DK / 16));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = m0 + 4 * lj + i, col = n0 + lr, o = row * DKP + col;
+            const float G = sG[o], E = __builtin_amdgcn_exp2f(G);
+            const float R = __builtin_amdgcn_exp2f(gc[col] - G);
+            const float dQu = aQ[x][i], dKu = -aK[x][i], dKr = aR[x][i];
+            const float ku = sKup[o], qu = sQup[o], kr = sKrt[o];
+            sQup[o] = dQu * E;
+            sKup[o] = dKu * E + dKr * R;
+            sKrt[o] = dKu * ku + dQu * qu - dKr * kr;
+            sRK[o] = dKr * kr;
+        }
+    }
+        __syncthreads();
     // pairwise sums of M0 and P, taken back to k, q and Gamma: thread (channel
     // c, part); part p takes the pairs (r, i <= r) with (r + i) % NPART == p.
     {
@@ -695,8 +899,10 @@ __global__ void __launch_bounds__(NT) bwd_grads_kernel(Params p) {
         for (int r = 0; r < C; ++r) {
             const bool ok = r < cl;
             const size_t e = ((size_t)(t0 + (ok ? r : 0)) * p.H + h) * DK + c;
-            kc[r] = ok ? ld<Tin>(p.k, e) : 0.0f;
-            qc[r] = ok ? ld<Tin>(p.q, e) : 0.0f;
+            kc[r] = ld<Tin>(p.k, e);
+            qc[r] = ld<Tin>(p.q, e);
+            kc[r] = ok ? kc[r] : 0.0f;
+            qc[r] = ok ? qc[r] : 0.0f;
             gcol[r] = sG[r * DKP + c];
             aq[r] = 0.0f;
             ak[r] = 0.0f;
@@ -732,25 +938,38 @@ __global__ void __launch_bounds__(NT) bwd_grads_kernel(Params p) {
             __syncthreads();
         }
     }
+    }
     // dlog_alpha: reverse running sum of dGamma plus the chunk-total term
     // sum_r dK_right K_right + dgamma gamma; outputs
     if (tid < DK) {
         const int c = tid;
+        float x[C];
         float tot = dgam[c] * gam[c];
-        for (int r = 0; r < C; ++r) tot += sRK[r * DKP + c];
+#pragma unroll
+        for (int r = 0; r < C; ++r) {
+            tot += sRK[r * DKP + c];
+            x[r] = sKrt[r * DKP + c];
+        }
         float run = tot;
+#pragma unroll
         for (int r = C - 1; r >= 0; --r) {
-            run += sKrt[r * DKP + c];
+            run += x[r];
             sKrt[r * DKP + c] = run;
         }
     }
     __syncthreads();
-    for (int idx = tid; idx < cl * DK; idx += NT) {
-        const int r = idx / DK, c = idx % DK;
-        const size_t e = ((size_t)(t0 + r) * p.H + h) * DK + c;
-        st<Tin>(p.dq, e, sQup[r * DKP + c]);
-        st<Tin>(p.dk, e, sKup[r * DKP + c]);
-        if (p.gate == GATE_CHANNEL) st<Tin>(p.dg, e, sKrt[r * DKP + c]);
+    {
+        constexpr int NE = DK / 8;
+        const int r = tid >> 3, c0 = (tid & 7) * NE;
+        if (r < cl) {
+            const size_t e = ((size_t)(t0 + r) * p.H + h) * DK + c0;
+#pragma unroll
+            for (int j = 0; j < NE; ++j) {
+                st<Tin>(p.dq, e + j, sQup[r * DKP + c0 + j]);
+                st<Tin>(p.dk, e + j, sKup[r * DKP + c0 + j]);
+                if (p.gate == GATE_CHANNEL) st<Tin>(p.dg, e + j, sKrt[r * DKP + c0 + j]);
+            }
+        }
     }
     if (tid < cl) {
         const size_t e = (size_t)(t0 + tid) * p.H + h;
@@ -770,7 +989,10 @@ hipError_t launch(const Params &p, long nslot, int nseq, hipStream_t stream) {
     if (nslot > 0) hipLaunchKernelGGL((bwd_prep_kernel<Tin, DK>), gchunks, dim3(NT), 0, stream, p);
     hipLaunchKernelGGL((bwd_states_kernel<Tin, DK>), dim3(gunits), dim3(NT), 0, stream, p);
     hipLaunchKernelGGL((bwd_dstates_kernel<Tin, DK>), dim3(gunits), dim3(NT), 0, stream, p);
-    if (nslot > 0) hipLaunchKernelGGL((bwd_grads_kernel<Tin, DK>), gchunks, dim3(NT), 0, stream, p);
+    if (nslot > 0) {
+        hipLaunchKernelGGL((bwd_grads_kernel<Tin, DK, false>), gchunks, dim3(NT), 0, stream, p);
+        hipLaunchKernelGGL((bwd_grads_kernel<Tin, DK, true>), gchunks, dim3(NT), 0, stream, p);
+    }
     return hipGetLastError();
 }
 
@@ -786,7 +1008,8 @@ size_t bwd_workspace_bytes(int B, int T, int H, int dk, int dv, int num_seqs) {
     const size_t per = (size_t)H * bwd_slots(B, T, num_seqs);
     const size_t a = (per * dk * dv * sizeof(float) + 255) & ~(size_t)255;
     const size_t b = (per * bwd::C * bwd::C * sizeof(float) + 255) & ~(size_t)255;
-    return 2 * a + 3 * b;
+    const size_t f = (per * sizeof(int32_t) + 255) & ~(size_t)255;
+    return 2 * a + 3 * b + f;
 }
 
 hipError_t bwd_launch(const void *q, const void *k, const void *v, const void *g, const void *beta,
@@ -808,6 +1031,7 @@ hipError_t bwd_launch(const void *q, const void *k, const void *v, const void *g
     p.wT = reinterpret_cast<float *>(w + 2 * a);
     p.wP = reinterpret_cast<float *>(w + 2 * a + b);
     p.wM = reinterpret_cast<float *>(w + 2 * a + 2 * b);
+    p.wF = reinterpret_cast<int32_t *>(w + 2 * a + 3 * b);
     const long nslot = cu_seqlens ? (long)(T / bwd::C) + num_seqs + 1
                                   : (long)B * ((T + bwd::C - 1) / bwd::C);
     // with no chunk anywhere only the state-gradient chain runs (dS0 = dS_T)
