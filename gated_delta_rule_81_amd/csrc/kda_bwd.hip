@@ -34,6 +34,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "kda_device.h"
 
 namespace kda {
@@ -217,6 +219,18 @@ template <typename Tin, int DK, bool WITH_Q> struct ChunkIn {
         for (int j = 0; j < NE; ++j) {
             sK[r * DKP + c0 + j] = k.get(j);
             if constexpr (WITH_Q) sQ[r * DKP + c0 + j] = q.get(j);
+            float gv = 0.0f;
+            if (p.gate == GATE_CHANNEL) gv = g.get(j) * kLog2e;
+            else if (p.gate == GATE_HEAD) gv = gh.get() * kLog2e;
+            sG[r * DKP + c0 + j] = gv;
+        }
+        if (tid < C) sB[tid] = b.get();
+    }
+    // only the log2 gates and beta (k and q stay in the registers)
+    __device__ __forceinline__ void store_gb(const Params &p, float *sG, float *sB) const {
+        const int tid = threadIdx.x, r = tid >> 3, c0 = (tid & 7) * NE;
+#pragma unroll
+        for (int j = 0; j < NE; ++j) {
             float gv = 0.0f;
             if (p.gate == GATE_CHANNEL) gv = g.get(j) * kLog2e;
             else if (p.gate == GATE_HEAD) gv = gh.get() * kLog2e;
@@ -631,10 +645,13 @@ __global__ void __launch_bounds__(NT) bwd_grads_kernel(Params p) {
     const size_t wi = (size_t)slot * p.H + h;
     // each chunk is done by the instantiation of its path (set by the prep kernel)
     if ((p.wF[wi] != 0) != EXACT) return;
-    const float *gS = p.wS + wi * DK * p.DV, *gD = p.wD + wi * DK * p.DV;
+    // states and state gradients are stored in the input precision's kind:
+    // fp32 for fp32 inputs, bf16 for bf16 inputs
+    const Tin *gS = reinterpret_cast<const Tin *>(p.wS) + wi * DK * p.DV;
+    const Tin *gD = reinterpret_cast<const Tin *>(p.wD) + wi * DK * p.DV;
 
     // every load of the chunk, then the first slice's, before the first wait
-    Seg<float, NES> sin, din;
+    Seg<Tin, NES> sin, din;
     Seg<Tin, 4> vin, oin;
     auto issue_slice = [&](int col0) {
         sin.load(gS, (size_t)sr * p.DV + col0 + sc, true);
@@ -982,15 +999,711 @@ __global__ void __launch_bounds__(NT) bwd_grads_kernel(Params p) {
     }
 }
 
+__device__ __forceinline__ f32x4 mfma8(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// acc += A B^T for one 16 x 16 tile: A [m][k] and Bt [n][k] bf16 row-major
+// with pitches la, lb (multiples of 8), K a multiple of 32.
+__device__ __forceinline__ f32x4 mmb(f32x4 acc, const __bf16 *A, int la, const __bf16 *Bt, int lb,
+                                     int K) {
+    const int lane = threadIdx.x & 63, r = lane & 15, j = lane >> 4;
+    const __bf16 *pa = A + r * la + 8 * j;
+    const __bf16 *pb = Bt + r * lb + 8 * j;
+#pragma unroll
+    for (int k0 = 0; k0 < K; k0 += 32)
+        acc = mfma8(*reinterpret_cast<const bf16x8 *>(pa + k0), *reinterpret_cast<const bf16x8 *>(pb + k0),
+                    acc);
+    return acc;
+}
+
+__device__ __forceinline__ __bf16 bf(float x) { return (__bf16)x; }
+__device__ __forceinline__ float fb(__bf16 x) { return (float)x; }
+
+// ---------------------------------------------------------------------------
+// bf16 inputs: the two state chains on bf16 MFMA.  The state (or its
+// gradient) stays fp32 in the accumulators; its bf16 copy is both the MFMA
+// operand and what the workspace keeps.  Every product contracts over 32
+// rows or over d_k, so each tile is one or four v_mfma_f32_16x16x32_bf16.
+
+// acc tile (rows 16 tm + 4 lj + i, cols 16 tn + lr) written transposed as
+// bf16: dst[col][row..row+3], one 8-byte store.
+__device__ __forceinline__ void store_t(__bf16 *dst, int pitch, int tm, int tn, f32x4 v) {
+    const int lane = threadIdx.x & 63, lr = lane & 15, lj = lane >> 4;
+    bf16x4 x;
+    x[0] = (__bf16)v[0];
+    x[1] = (__bf16)v[1];
+    x[2] = (__bf16)v[2];
+    x[3] = (__bf16)v[3];
+    *reinterpret_cast<bf16x4 *>(dst + (16 * tn + lr) * pitch + 16 * tm + 4 * lj) = x;
+}
+
+template <int DK> struct ChainLayout {
+    static constexpr int DKP = DK + 1, DKB = DK + 8, WB = W + 8, CB = C + 8;
+    static constexpr int G = 0;                          // fp32 [C][DKP]
+    static constexpr int XT = G + 4 * C * DKP;           // bf16 [W][DKB]: S^T or D^T
+    static constexpr int KA = XT + 2 * W * DKB;          // bf16 [C][DKB]: K_up or K_right
+    static constexpr int KT1 = KA + 2 * C * DKB;         // bf16 [DK][CB]: K_right^T or Q_up^T
+    static constexpr int KT2 = KT1 + 2 * DK * CB;        // bf16 [DK][CB]: K_up^T
+    static constexpr int M1 = KT2 + 2 * DK * CB;         // bf16 [C][CB]: T or T^T
+    static constexpr int M2 = M1 + 2 * C * CB;           // bf16 [C][CB]: P^T
+    static constexpr int Y1 = M2 + 2 * C * CB;           // bf16 [W][CB]: (beta X)^T or dO^T
+    static constexpr int Y2 = Y1 + 2 * W * CB;           // bf16 [W][CB]: U^T or dU^T
+    static constexpr int Y3 = Y2 + 2 * W * CB;           // bf16 [W][CB]: (-dX)^T
+    static constexpr int V = Y3 + 2 * W * CB;            // fp32 [C][WP]: V
+    static constexpr int GC = V + 4 * C * WP;            // fp32 [DK] x 2
+    static constexpr int GAM = GC + 4 * DK;
+    static constexpr int SB = GAM + 4 * DK;              // fp32 [C]
+    static constexpr int BYTES = SB + 4 * C;
+};
+
+template <int DK>
+__global__ void __launch_bounds__(NT) bwd_states_bf16_kernel(Params p) {
+    using L = ChainLayout<DK>;
+    constexpr int DKP = L::DKP, DKB = L::DKB, CB = L::CB, NTW = DK / 32, NE = DK / 8;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[L::BYTES];
+    float *sG = reinterpret_cast<float *>(smem + L::G);
+    __bf16 *St = reinterpret_cast<__bf16 *>(smem + L::XT);
+    __bf16 *Kub = reinterpret_cast<__bf16 *>(smem + L::KA);
+    __bf16 *Krt = reinterpret_cast<__bf16 *>(smem + L::KT1);
+    __bf16 *Tb = reinterpret_cast<__bf16 *>(smem + L::M1);
+    __bf16 *BXt = reinterpret_cast<__bf16 *>(smem + L::Y1);
+    __bf16 *Ut = reinterpret_cast<__bf16 *>(smem + L::Y2);
+    float *sV = reinterpret_cast<float *>(smem + L::V);
+    float *gc = reinterpret_cast<float *>(smem + L::GC);
+    float *gam = reinterpret_cast<float *>(smem + L::GAM);
+    float *sB = reinterpret_cast<float *>(smem + L::SB);
+    const int nsl = p.DV / W;
+    const int unit = blockIdx.x / nsl, slice = blockIdx.x % nsl;
+    const int s = unit / p.H, h = unit % p.H, col0 = slice * W;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, lj = lane >> 4;
+    const int vr = tid >> 3, vc = (tid & 7) * 4;
+    long t0s, base;
+    int len;
+    seq_info(p, s, t0s, len, base);
+    const int nch = (len + C - 1) / C;
+    ChunkIn<bf16_t, DK, false> in;
+    Seg<bf16_t, 4> vin;
+    Seg<float, 4> tin;
+    auto issue = [&](int n) {
+        const long t0 = t0s + (long)n * C;
+        const int cl = len - n * C < C ? len - n * C : C;
+        in.load(p, t0, cl, h);
+        vin.load(p.v, ((size_t)(t0 + vr) * p.H + h) * p.DV + col0 + vc, vr < cl);
+        tin.load(p.wT, ((size_t)(base + n) * p.H + h) * C * C + tid * 4, true);
+    };
+    if (nch > 0) issue(0);
+    f32x4 S[NTW];
+#pragma unroll
+    for (int x = 0; x < NTW; ++x) {
+        const int tt = wave * NTW + x, tm = tt >> 1, tn = tt & 1;
+        load_tile(S[x], p.S0, ((size_t)s * p.H + h) * DK + 16 * tm, p.DV, col0 + 16 * tn);
+    }
+    for (int n = 0; n < nch; ++n) {
+        const size_t wi = (size_t)(base + n) * p.H + h;
+        bf16_t *gS = reinterpret_cast<bf16_t *>(p.wS) + wi * DK * p.DV;
+#pragma unroll
+        for (int x = 0; x < NTW; ++x) {
+            const int tt = wave * NTW + x, tm = tt >> 1, tn = tt & 1;
+            store_t(St, DKB, tm, tn, S[x]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                gS[(size_t)(16 * tm + 4 * lj + i) * p.DV + col0 + 16 * tn + lr] = to_bf16(S[x][i]);
+        }
+        in.store_gb(p, sG, sB);
+        {
+            const int tr = (tid * 4) / C, tc = (tid * 4) % C;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                sV[vr * WP + vc + j] = vin.get(j);
+                Tb[tr * CB + tc + j] = (__bf16)tin.get(j);
+            }
+        }
+        __syncthreads();
+        gate_sums<DK>(sG, gc, gam);
+        __syncthreads();
+        {
+            const int r = tid >> 3, c0 = (tid & 7) * NE;
+#pragma unroll
+            for (int j = 0; j < NE; ++j) {
+                const float G = sG[r * DKP + c0 + j], kv = in.k.get(j);
+                Kub[r * DKB + c0 + j] = (__bf16)(kv * __builtin_amdgcn_exp2f(G));
+                Krt[(c0 + j) * CB + r] = (__bf16)(kv * __builtin_amdgcn_exp2f(gc[c0 + j] - G));
+            }
+        }
+        // the next chunk's inputs are requested now that k has been used
+        if (n + 1 < nch) issue(n + 1);
+        __syncthreads();
+        // (beta X)^T, X = V - K_up S
+        {
+            const int tm = wave >> 1, tn = wave & 1;
+            f32x4 a = {0.f, 0.f, 0.f, 0.f};
+            a = mmb(a, Kub + 16 * tm * DKB, DKB, St + 16 * tn * DKB, DKB, DK);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = 16 * tm + 4 * lj + i;
+                a[i] = sB[row] * (sV[row * WP + 16 * tn + lr] - a[i]);
+            }
+            store_t(BXt, CB, tm, tn, a);
+        }
+        __syncthreads();
+        // U^T, U = T (beta X)
+        {
+            const int tm = wave >> 1, tn = wave & 1;
+            f32x4 a = {0.f, 0.f, 0.f, 0.f};
+            a = mmb(a, Tb + 16 * tm * CB, CB, BXt + 16 * tn * CB, CB, C);
+            store_t(Ut, CB, tm, tn, a);
+        }
+        __syncthreads();
+        // S = Diag(gamma) S + K_right^T U
+#pragma unroll
+        for (int x = 0; x < NTW; ++x) {
+            const int tt = wave * NTW + x, tm = tt >> 1, tn = tt & 1;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) S[x][i] *= gam[16 * tm + 4 * lj + i];
+            S[x] = mmb(S[x], Krt + 16 * tm * CB, CB, Ut + 16 * tn * CB, CB, C);
+        }
+        __syncthreads();
+    }
+}
+
+template <int DK>
+__global__ void __launch_bounds__(NT) bwd_dstates_bf16_kernel(Params p) {
+    using L = ChainLayout<DK>;
+    constexpr int DKP = L::DKP, DKB = L::DKB, CB = L::CB, NTW = DK / 32, NE = DK / 8;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[L::BYTES];
+    float *sG = reinterpret_cast<float *>(smem + L::G);
+    __bf16 *Dt = reinterpret_cast<__bf16 *>(smem + L::XT);
+    __bf16 *Krb = reinterpret_cast<__bf16 *>(smem + L::KA);
+    __bf16 *Qt = reinterpret_cast<__bf16 *>(smem + L::KT1);
+    __bf16 *Kt = reinterpret_cast<__bf16 *>(smem + L::KT2);
+    __bf16 *TT = reinterpret_cast<__bf16 *>(smem + L::M1);
+    __bf16 *PT = reinterpret_cast<__bf16 *>(smem + L::M2);
+    __bf16 *dOt = reinterpret_cast<__bf16 *>(smem + L::Y1);
+    __bf16 *dUt = reinterpret_cast<__bf16 *>(smem + L::Y2);
+    __bf16 *mdXt = reinterpret_cast<__bf16 *>(smem + L::Y3);
+    float *gc = reinterpret_cast<float *>(smem + L::GC);
+    float *gam = reinterpret_cast<float *>(smem + L::GAM);
+    float *sB = reinterpret_cast<float *>(smem + L::SB);
+    const int nsl = p.DV / W;
+    const int unit = blockIdx.x / nsl, slice = blockIdx.x % nsl;
+    const int s = unit / p.H, h = unit % p.H, col0 = slice * W;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, lj = lane >> 4;
+    const int vr = tid >> 3, vc = (tid & 7) * 4;
+    long t0s, base;
+    int len;
+    seq_info(p, s, t0s, len, base);
+    const int nch = (len + C - 1) / C;
+    const size_t so = ((size_t)s * p.H + h) * DK;
+    ChunkIn<bf16_t, DK, true> in;
+    Seg<bf16_t, 4> oin;
+    Seg<float, 4> tin, pin;
+    auto issue = [&](int n) {
+        const long t0 = t0s + (long)n * C;
+        const int cl = len - n * C < C ? len - n * C : C;
+        const size_t wi = (size_t)(base + n) * p.H + h;
+        in.load(p, t0, cl, h);
+        oin.load(p.dO, ((size_t)(t0 + vr) * p.H + h) * p.DV + col0 + vc, vr < cl);
+        tin.load(p.wT, wi * C * C + tid * 4, true);
+        pin.load(p.wP, wi * C * C + tid * 4, true);
+    };
+    if (nch > 0) issue(nch - 1);
+    f32x4 D[NTW];
+#pragma unroll
+    for (int x = 0; x < NTW; ++x) {
+        const int tt = wave * NTW + x, tm = tt >> 1, tn = tt & 1;
+        load_tile(D[x], p.dST, so + 16 * tm, p.DV, col0 + 16 * tn);
+    }
+    for (int n = nch - 1; n >= 0; --n) {
+        const size_t wi = (size_t)(base + n) * p.H + h;
+        bf16_t *gD = reinterpret_cast<bf16_t *>(p.wD) + wi * DK * p.DV;
+#pragma unroll
+        for (int x = 0; x < NTW; ++x) {
+            const int tt = wave * NTW + x, tm = tt >> 1, tn = tt & 1;
+            store_t(Dt, DKB, tm, tn, D[x]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                gD[(size_t)(16 * tm + 4 * lj + i) * p.DV + col0 + 16 * tn + lr] = to_bf16(D[x][i]);
+        }
+        in.store_gb(p, sG, sB);
+        {
+            const int tr = (tid * 4) / C, tc = (tid * 4) % C;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                dOt[(vc + j) * CB + vr] = (__bf16)oin.get(j);
+                TT[(tc + j) * CB + tr] = (__bf16)tin.get(j);
+                PT[(tc + j) * CB + tr] = (__bf16)pin.get(j);
+            }
+        }
+        __syncthreads();
+        gate_sums<DK>(sG, gc, gam);
+        __syncthreads();
+        {
+            const int r = tid >> 3, c0 = (tid & 7) * NE;
+#pragma unroll
+            for (int j = 0; j < NE; ++j) {
+                const float G = sG[r * DKP + c0 + j], kv = in.k.get(j), E = __builtin_amdgcn_exp2f(G);
+                Krb[r * DKB + c0 + j] = (__bf16)(kv * __builtin_amdgcn_exp2f(gc[c0 + j] - G));
+                Qt[(c0 + j) * CB + r] = (__bf16)(in.q.get(j) * E);
+                Kt[(c0 + j) * CB + r] = (__bf16)(kv * E);
+            }
+        }
+        // the next chunk's inputs are requested now that k and q have been used
+        if (n > 0) issue(n - 1);
+        __syncthreads();
+        // dU^T, dU = P^T dO + K_right D
+        {
+            const int tm = wave >> 1, tn = wave & 1;
+            f32x4 a = {0.f, 0.f, 0.f, 0.f};
+            a = mmb(a, PT + 16 * tm * CB, CB, dOt + 16 * tn * CB, CB, C);
+            a = mmb(a, Krb + 16 * tm * DKB, DKB, Dt + 16 * tn * DKB, DKB, DK);
+            store_t(dUt, CB, tm, tn, a);
+        }
+        __syncthreads();
+        // (-dX)^T, dX = Diag(beta) T^T dU
+        {
+            const int tm = wave >> 1, tn = wave & 1;
+            f32x4 a = {0.f, 0.f, 0.f, 0.f};
+            a = mmb(a, TT + 16 * tm * CB, CB, dUt + 16 * tn * CB, CB, C);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a[i] *= -sB[16 * tm + 4 * lj + i];
+            store_t(mdXt, CB, tm, tn, a);
+        }
+        __syncthreads();
+        // D = Diag(gamma) D + Q_up^T dO - K_up^T dX
+#pragma unroll
+        for (int x = 0; x < NTW; ++x) {
+            const int tt = wave * NTW + x, tm = tt >> 1, tn = tt & 1;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) D[x][i] *= gam[16 * tm + 4 * lj + i];
+            D[x] = mmb(D[x], Qt + 16 * tm * CB, CB, dOt + 16 * tn * CB, CB, C);
+            D[x] = mmb(D[x], Kt + 16 * tm * CB, CB, mdXt + 16 * tn * CB, CB, C);
+        }
+        __syncthreads();
+    }
+    if (p.dS0) {
+#pragma unroll
+        for (int x = 0; x < NTW; ++x) {
+            const int tt = wave * NTW + x, tm = tt >> 1, tn = tt & 1;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = 16 * tm + 4 * lj + i, col = col0 + 16 * tn + lr;
+                p.dS0[(so + row) * p.DV + col] = D[x][i];
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// bf16 inputs, factorised path: the same chunk gradients with the d_v
+// products on bf16 MFMA (v_mfma_f32_16x16x32_bf16, fp32 accumulation).  Each
+// operand is staged in LDS as bf16 with its contraction index contiguous (a
+// matrix used both ways is kept in both orientations); the C x C algebra and
+// the decay-weighted sums stay fp32.
+template <int DK> struct GbLayout {
+    static constexpr int DKP = DK + 1, DKB = DK + 8, WB = W + 8, CB = C + 8;
+    // persistent
+    static constexpr int G = 0;                                   // fp32 [C][DKP]
+    static constexpr int KUB = G + 4 * C * DKP;                   // bf16 [C][DKB]
+    static constexpr int KRB = KUB + 2 * C * DKB;
+    static constexpr int TB = KRB + 2 * C * DKB;                  // bf16 [C][CB]
+    static constexpr int TTB = TB + 2 * C * CB;
+    static constexpr int PTB = TTB + 2 * C * CB;
+    static constexpr int T = PTB + 2 * C * CB;                    // fp32 [C][CP]
+    static constexpr int P = T + 4 * C * CP;
+    static constexpr int M = P + 4 * C * CP;
+    static constexpr int GC = M + 4 * C * CP;                     // fp32 [DK] x 3
+    static constexpr int GAM = GC + 4 * DK;
+    static constexpr int DGP = GAM + 4 * DK;                      // fp32 [NT]: dgamma parts
+    static constexpr int RKP = DGP + 4 * NT;                      // fp32 [2][DK]
+    static constexpr int SB = RKP + 8 * DK;                       // fp32 [C] x 2
+    static constexpr int DB = SB + 4 * C;
+    static constexpr int AREA = DB + 4 * C;
+    // slice phase (in the area)
+    static constexpr int SR = AREA;                               // bf16 [DK][WB]
+    static constexpr int DR = SR + 2 * DK * WB;
+    static constexpr int ST = DR + 2 * DK * WB;                   // bf16 [W][DKB]
+    static constexpr int DT = ST + 2 * W * DKB;
+    static constexpr int VR = DT + 2 * W * DKB;                   // bf16 [C][WB] / [W][CB]
+    static constexpr int DOR = VR + 2 * C * WB;
+    static constexpr int DOT = DOR + 2 * C * WB;
+    static constexpr int XR = DOT + 2 * W * CB;
+    static constexpr int BXT = XR + 2 * C * WB;
+    static constexpr int UR = BXT + 2 * W * CB;
+    static constexpr int DUR = UR + 2 * C * WB;
+    static constexpr int DUT = DUR + 2 * C * WB;
+    static constexpr int DXR = DUT + 2 * W * CB;
+    static constexpr int SLICE_END = DXR + 2 * C * WB;
+    // setup: raw k (fp32 [C][DKP]) in the area
+    static constexpr int KRAW = AREA;
+    // after the slices (in the area)
+    static constexpr int DTF = AREA;                              // fp32 [C][CP] x 4
+    static constexpr int DPF = DTF + 4 * C * CP;
+    static constexpr int YF = DPF + 4 * C * CP;
+    static constexpr int DAF = YF + 4 * C * CP;
+    static constexpr int FK = DAF + 4 * C * CP;                   // fp32 [C][DKP] x 3
+    static constexpr int FQ = FK + 4 * C * DKP;
+    static constexpr int FKD = FQ + 4 * C * DKP;
+    static constexpr int TAIL_END = FKD + 4 * C * DKP;
+    static constexpr int BYTES = SLICE_END > TAIL_END ? SLICE_END : TAIL_END;
+};
+
+template <int DK>
+__global__ void __launch_bounds__(NT) bwd_grads_bf16_kernel(Params p) {
+    using L = GbLayout<DK>;
+    constexpr int DKP = L::DKP, DKB = L::DKB, WB = L::WB, CB = L::CB;
+    constexpr int NTW = DK / 32, NE = DK / 8;
+    constexpr int NES = DK * W / NT, TPR = W / NES;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[L::BYTES];
+    float *sG = reinterpret_cast<float *>(smem + L::G);
+    __bf16 *sKub = reinterpret_cast<__bf16 *>(smem + L::KUB);
+    __bf16 *sKrb = reinterpret_cast<__bf16 *>(smem + L::KRB);
+    __bf16 *sTb = reinterpret_cast<__bf16 *>(smem + L::TB);
+    __bf16 *sTTb = reinterpret_cast<__bf16 *>(smem + L::TTB);
+    __bf16 *sPTb = reinterpret_cast<__bf16 *>(smem + L::PTB);
+    float *sT = reinterpret_cast<float *>(smem + L::T);
+    float *sP = reinterpret_cast<float *>(smem + L::P);
+    float *sM = reinterpret_cast<float *>(smem + L::M);
+    float *gc = reinterpret_cast<float *>(smem + L::GC);
+    float *gam = reinterpret_cast<float *>(smem + L::GAM);
+    float *dgp = reinterpret_cast<float *>(smem + L::DGP);
+    float *rkp = reinterpret_cast<float *>(smem + L::RKP);
+    float *sB = reinterpret_cast<float *>(smem + L::SB);
+    float *dB = reinterpret_cast<float *>(smem + L::DB);
+    __bf16 *Sr = reinterpret_cast<__bf16 *>(smem + L::SR);
+    __bf16 *Dr = reinterpret_cast<__bf16 *>(smem + L::DR);
+    __bf16 *St = reinterpret_cast<__bf16 *>(smem + L::ST);
+    __bf16 *Dt = reinterpret_cast<__bf16 *>(smem + L::DT);
+    __bf16 *Vr = reinterpret_cast<__bf16 *>(smem + L::VR);
+    __bf16 *dOr = reinterpret_cast<__bf16 *>(smem + L::DOR);
+    __bf16 *dOt = reinterpret_cast<__bf16 *>(smem + L::DOT);
+    __bf16 *Xr = reinterpret_cast<__bf16 *>(smem + L::XR);
+    __bf16 *BXt = reinterpret_cast<__bf16 *>(smem + L::BXT);
+    __bf16 *Ur = reinterpret_cast<__bf16 *>(smem + L::UR);
+    __bf16 *dUr = reinterpret_cast<__bf16 *>(smem + L::DUR);
+    __bf16 *dUt = reinterpret_cast<__bf16 *>(smem + L::DUT);
+    __bf16 *dXr = reinterpret_cast<__bf16 *>(smem + L::DXR);
+    float *kraw = reinterpret_cast<float *>(smem + L::KRAW);
+
+    const long slot = blockIdx.x;
+    const int h = blockIdx.y, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int lr = lane & 15, lj = lane >> 4;
+    const int vr = tid >> 3, vc = (tid & 7) * 4;
+    const int sr = tid / TPR, sc = (tid % TPR) * NES;
+    long t0;
+    int cl;
+    if (!slot_chunk(p, slot, t0, cl)) return;
+    const size_t wi = (size_t)slot * p.H + h;
+    if (p.wF[wi] != 0) return;                       // exact chunks: the fp32 kernel
+    // states and state gradients are kept as bf16 for bf16 inputs
+    const bf16_t *gS = reinterpret_cast<const bf16_t *>(p.wS) + wi * DK * p.DV;
+    const bf16_t *gD = reinterpret_cast<const bf16_t *>(p.wD) + wi * DK * p.DV;
+
+    Seg<bf16_t, NES> sin, din;
+    Seg<bf16_t, 4> vin, oin;
+    auto issue_slice = [&](int col0) {
+        sin.load(gS, (size_t)sr * p.DV + col0 + sc, true);
+        din.load(gD, (size_t)sr * p.DV + col0 + sc, true);
+        const size_t e = ((size_t)(t0 + vr) * p.H + h) * p.DV + col0 + vc;
+        vin.load(p.v, e, vr < cl);
+        oin.load(p.dO, e, vr < cl);
+    };
+    {
+        ChunkIn<bf16_t, DK, false> in;
+        Seg<float, 4> tin, pin, min;
+        in.load(p, t0, cl, h);
+        tin.load(p.wT, wi * C * C + tid * 4, true);
+        pin.load(p.wP, wi * C * C + tid * 4, true);
+        min.load(p.wM, wi * C * C + tid * 4, true);
+        issue_slice(0);
+        in.store(p, kraw, nullptr, sG, sB);
+        const int tr = (tid * 4) / C, tc = (tid * 4) % C;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float tv = tin.get(j), pv = pin.get(j);
+            sT[tr * CP + tc + j] = tv;
+            sP[tr * CP + tc + j] = pv;
+            sM[tr * CP + tc + j] = min.get(j);
+            sTb[tr * CB + tc + j] = bf(tv);
+            sTTb[(tc + j) * CB + tr] = bf(tv);
+            sPTb[(tc + j) * CB + tr] = bf(pv);
+        }
+    }
+    if (tid < C) dB[tid] = 0.0f;
+    __syncthreads();
+    gate_sums<DK>(sG, gc, gam);
+    __syncthreads();
+    {
+        const int r = tid >> 3, c0 = (tid & 7) * NE;
+#pragma unroll
+        for (int j = 0; j < NE; ++j) {
+            const int o = r * DKP + c0 + j;
+            const float G = sG[o], kv = kraw[o];
+            sKub[r * DKB + c0 + j] = bf(kv * __builtin_amdgcn_exp2f(G));
+            sKrb[r * DKB + c0 + j] = bf(kv * __builtin_amdgcn_exp2f(gc[c0 + j] - G));
+        }
+    }
+
+    f32x4 aQ[NTW], aK[NTW], aR[NTW], aT = {0.f, 0.f, 0.f, 0.f}, aP = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int x = 0; x < NTW; ++x) {
+        aQ[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+        aK[x] = aQ[x];
+        aR[x] = aQ[x];
+    }
+    float dgacc = 0.0f;                               // sum over this thread's S * D values
+    const int tm = wave >> 1, tn = wave & 1;
+    for (int col0 = 0; col0 < p.DV; col0 += W) {
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < NES; ++j) {
+            const float sv = sin.get(j), dv = din.get(j);
+            dgacc += sv * dv;
+            Sr[sr * WB + sc + j] = bf(sv);
+            Dr[sr * WB + sc + j] = bf(dv);
+            St[(sc + j) * DKB + sr] = bf(sv);
+            Dt[(sc + j) * DKB + sr] = bf(dv);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            Vr[vr * WB + vc + j] = bf(vin.get(j));
+            const __bf16 o = bf(oin.get(j));
+            dOr[vr * WB + vc + j] = o;
+            dOt[(vc + j) * CB + vr] = o;
+        }
+        if (col0 + W < p.DV) issue_slice(col0 + W);
+        __syncthreads();
+        // X = V - K_up S  (kept as X and as (beta X)^T)
+        {
+            f32x4 a = {0.f, 0.f, 0.f, 0.f};
+            a = mmb(a, sKub + 16 * tm * DKB, DKB, St + 16 * tn * DKB, DKB, DK);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = 16 * tm + 4 * lj + i, col = 16 * tn + lr;
+                const float x = fb(Vr[row * WB + col]) - a[i];
+                Xr[row * WB + col] = bf(x);
+                BXt[col * CB + row] = bf(sB[row] * x);
+            }
+        }
+        __syncthreads();
+        // U = T (beta X);  dU = P^T dO + K_right D
+        {
+            f32x4 a = {0.f, 0.f, 0.f, 0.f}, b = a;
+            a = mmb(a, sTb + 16 * tm * CB, CB, BXt + 16 * tn * CB, CB, C);
+            b = mmb(b, sPTb + 16 * tm * CB, CB, dOt + 16 * tn * CB, CB, C);
+            b = mmb(b, sKrb + 16 * tm * DKB, DKB, Dt + 16 * tn * DKB, DKB, DK);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = 16 * tm + 4 * lj + i, col = 16 * tn + lr;
+                Ur[row * WB + col] = bf(a[i]);
+                dUr[row * WB + col] = bf(b[i]);
+                dUt[col * CB + row] = bf(b[i]);
+            }
+        }
+        __syncthreads();
+        // dX = Diag(beta) T^T dU (and dV)
+        {
+            f32x4 a = {0.f, 0.f, 0.f, 0.f};
+            a = mmb(a, sTTb + 16 * tm * CB, CB, dUt + 16 * tn * CB, CB, C);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = 16 * tm + 4 * lj + i, col = 16 * tn + lr;
+                const float x = sB[row] * a[i];
+                dXr[row * WB + col] = bf(x);
+                if (row < cl) st<bf16_t>(p.dv, ((size_t)(t0 + row) * p.H + h) * p.DV + col0 + col, x);
+            }
+        }
+        // dT' += dU X^T;  dP += dO U^T;  dQ_up += dO S^T;  dK_right += U D^T
+        aT = mmb(aT, dUr + 16 * tm * WB, WB, Xr + 16 * tn * WB, WB, W);
+        aP = mmb(aP, dOr + 16 * tm * WB, WB, Ur + 16 * tn * WB, WB, W);
+#pragma unroll
+        for (int x = 0; x < NTW; ++x) {
+            const int tt = wave * NTW + x, m0 = 16 * (tt / (DK / 16)), n0 = 16 * (tt % (DK / 16));
+            aQ[x] = mmb(aQ[x], dOr + m0 * WB, WB, Sr + n0 * WB, WB, W);
+            aR[x] = mmb(aR[x], Ur + m0 * WB, WB, Dr + n0 * WB, WB, W);
+        }
+        __syncthreads();
+        // dK_up -= dX S^T
+#pragma unroll
+        for (int x = 0; x < NTW; ++x) {
+            const int tt = wave * NTW + x, m0 = 16 * (tt / (DK / 16)), n0 = 16 * (tt % (DK / 16));
+            aK[x] = mmb(aK[x], dXr + m0 * WB, WB, Sr + n0 * WB, WB, W);
+        }
+    }
+    dgp[tid] = dgacc;
+    __syncthreads();
+
+    // C x C algebra (fp32), as in the fp32 kernel
+    float *sdT = reinterpret_cast<float *>(smem + L::DTF), *sdP = reinterpret_cast<float *>(smem + L::DPF);
+    float *sY = reinterpret_cast<float *>(smem + L::YF), *sdA = reinterpret_cast<float *>(smem + L::DAF);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = 16 * tm + 4 * lj + i, col = 16 * tn + lr;
+        sdT[row * CP + col] = aT[i];
+        sdP[row * CP + col] = col <= row ? aP[i] : 0.0f;
+    }
+    __syncthreads();
+    if (tid < C) {
+        float acc = 0.0f;
+#pragma unroll 8
+        for (int r = 0; r < C; ++r) acc += sT[r * CP + tid] * sdT[r * CP + tid];
+        dB[tid] = acc;
+    }
+    __syncthreads();
+    for (int idx = tid; idx < C * C; idx += NT) {
+        const int r = idx / C, i = idx % C;
+        sdT[r * CP + i] *= sB[i];
+    }
+    __syncthreads();
+    {
+        f32x4 a = {0.f, 0.f, 0.f, 0.f};
+        a = mm(a, sT + 16 * tm, 1, CP, sdT + 16 * tn, CP, 1, C);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sY[(16 * tm + 4 * lj + i) * CP + 16 * tn + lr] = a[i];
+    }
+    __syncthreads();
+    {
+        f32x4 a = {0.f, 0.f, 0.f, 0.f};
+        a = mm(a, sY + 16 * tm * CP, CP, 1, sT + 16 * tn * CP, 1, CP, C);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = 16 * tm + 4 * lj + i, col = 16 * tn + lr;
+            sdA[row * CP + col] = col < row ? -a[i] : 0.0f;
+        }
+    }
+    __syncthreads();
+    if (tid < C) {
+        const int r = tid;
+        float acc = 0.0f;
+#pragma unroll 8
+        for (int i = 0; i < C; ++i) {
+            const float a = sdA[r * CP + i];
+            acc += a * sM[r * CP + i];
+            sM[r * CP + i] = sB[r] * a;
+        }
+        dB[r] += acc;
+    }
+    // fp32 K_up, Q_up, K_dn for the decay-weighted sums (raw k and q again)
+    float *fK = reinterpret_cast<float *>(smem + L::FK), *fQ = reinterpret_cast<float *>(smem + L::FQ);
+    float *fKd = reinterpret_cast<float *>(smem + L::FKD);
+    {
+        const int r = tid >> 3, c0 = (tid & 7) * NE;
+        Seg<bf16_t, NE> kin, qin;
+        const size_t e = ((size_t)(t0 + r) * p.H + h) * DK + c0;
+        kin.load(p.k, e, r < cl);
+        qin.load(p.q, e, r < cl);
+#pragma unroll
+        for (int j = 0; j < NE; ++j) {
+            const int o = r * DKP + c0 + j;
+            const float G = sG[o], E = __builtin_amdgcn_exp2f(G), Ei = __builtin_amdgcn_exp2f(-G);
+            fK[o] = kin.get(j) * E;
+            fQ[o] = qin.get(j) * E;
+            fKd[o] = kin.get(j) * Ei;
+        }
+    }
+    __syncthreads();
+    // factorised decay sums and the direct terms, combined per element:
+    //   Z1 = dP K_dn,  Z2 = dM K_dn,  Z3 = dM^T K_up + dP^T Q_up,
+    //   dq = (dQ_up + Z1) e^G,  dk = (dK_up + Z2) e^G + dK_right e^{G_c - G} + Z3 e^{-G},
+    //   dGamma = (dK_up + Z2) K_up + (dQ_up + Z1) Q_up - dK_right K_right - Z3 K_dn
+#pragma unroll
+    for (int x = 0; x < NTW; ++x) {
+        const int tt = wave * NTW + x, m0 = 16 * (tt / (DK / 16)), n0 = 16 * (tt % (DK / 16));
+        f32x4 z1 = {0.f, 0.f, 0.f, 0.f}, z2 = z1, z3 = z1;
+        z1 = mm(z1, sdP + m0 * CP, CP, 1, fKd + n0, DKP, 1, C);
+        z2 = mm(z2, sM + m0 * CP, CP, 1, fKd + n0, DKP, 1, C);
+        z3 = mm(z3, sM + m0, 1, CP, fK + n0, DKP, 1, C);
+        z3 = mm(z3, sdP + m0, 1, CP, fQ + n0, DKP, 1, C);
+        float rk = 0.0f;                              // this lane's 4 rows of dK_right K_right
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = m0 + 4 * lj + i, col = n0 + lr, o = row * DKP + col;
+            const float G = sG[o], E = __builtin_amdgcn_exp2f(G);
+            const float R = __builtin_amdgcn_exp2f(gc[col] - G);
+            const float Ei = __builtin_amdgcn_exp2f(-G);
+            const float dQu = aQ[x][i] + z1[i], dKu = z2[i] - aK[x][i], dKr = aR[x][i];
+            const float ku = fK[o], qu = fQ[o], kd = fKd[o];
+            const float kr = kd * E * R;
+            aQ[x][i] = dQu * E;
+            aK[x][i] = dKu * E + dKr * R + z3[i] * Ei;
+            aR[x][i] = dKu * ku + dQu * qu - dKr * kr - z3[i] * kd;
+            rk += dKr * kr;
+        }
+        rk += __shfl_xor(rk, 16);
+        rk += __shfl_xor(rk, 32);
+        if (lj == 0) rkp[(m0 >> 4) * DK + n0 + lr] = rk;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int x = 0; x < NTW; ++x) {
+        const int tt = wave * NTW + x, m0 = 16 * (tt / (DK / 16)), n0 = 16 * (tt % (DK / 16));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int o = (m0 + 4 * lj + i) * DKP + n0 + lr;
+            fQ[o] = aQ[x][i];
+            fK[o] = aK[x][i];
+            fKd[o] = aR[x][i];
+        }
+    }
+    __syncthreads();
+    // dlog_alpha: reverse running sum of dGamma plus the chunk-total term
+    if (tid < DK) {
+        const int c = tid;
+        float dgam = 0.0f;
+#pragma unroll
+        for (int t = 0; t < TPR; ++t) dgam += dgp[c * TPR + t];
+        float x[C];
+        const float tot = rkp[c] + rkp[DK + c] + dgam * gam[c];
+#pragma unroll
+        for (int r = 0; r < C; ++r) x[r] = fKd[r * DKP + c];
+        float run = tot;
+#pragma unroll
+        for (int r = C - 1; r >= 0; --r) {
+            run += x[r];
+            fKd[r * DKP + c] = run;
+        }
+    }
+    __syncthreads();
+    {
+        const int r = tid >> 3, c0 = (tid & 7) * NE;
+        if (r < cl) {
+            const size_t e = ((size_t)(t0 + r) * p.H + h) * DK + c0;
+#pragma unroll
+            for (int j = 0; j < NE; ++j) {
+                st<bf16_t>(p.dq, e + j, fQ[r * DKP + c0 + j]);
+                st<bf16_t>(p.dk, e + j, fK[r * DKP + c0 + j]);
+                if (p.gate == GATE_CHANNEL) st<bf16_t>(p.dg, e + j, fKd[r * DKP + c0 + j]);
+            }
+        }
+    }
+    if (tid < cl) {
+        const size_t e = (size_t)(t0 + tid) * p.H + h;
+        st<bf16_t>(p.dbeta, e, dB[tid]);
+        if (p.gate == GATE_HEAD) {
+            float acc = 0.0f;
+            for (int c = 0; c < DK; ++c) acc += fKd[tid * DKP + c];
+            st<bf16_t>(p.dg, e, acc);
+        }
+    }
+}
+
 template <typename Tin, int DK>
 hipError_t launch(const Params &p, long nslot, int nseq, hipStream_t stream) {
     const dim3 gchunks((unsigned)nslot, (unsigned)p.H);
     const unsigned gunits = (unsigned)((long)nseq * p.H * (p.DV / W));
     if (nslot > 0) hipLaunchKernelGGL((bwd_prep_kernel<Tin, DK>), gchunks, dim3(NT), 0, stream, p);
-    hipLaunchKernelGGL((bwd_states_kernel<Tin, DK>), dim3(gunits), dim3(NT), 0, stream, p);
-    hipLaunchKernelGGL((bwd_dstates_kernel<Tin, DK>), dim3(gunits), dim3(NT), 0, stream, p);
+    if constexpr (std::is_same<Tin, bf16_t>::value) {
+        hipLaunchKernelGGL((bwd_states_bf16_kernel<DK>), dim3(gunits), dim3(NT), 0, stream, p);
+        hipLaunchKernelGGL((bwd_dstates_bf16_kernel<DK>), dim3(gunits), dim3(NT), 0, stream, p);
+    } else {
+        hipLaunchKernelGGL((bwd_states_kernel<Tin, DK>), dim3(gunits), dim3(NT), 0, stream, p);
+        hipLaunchKernelGGL((bwd_dstates_kernel<Tin, DK>), dim3(gunits), dim3(NT), 0, stream, p);
+    }
     if (nslot > 0) {
-        hipLaunchKernelGGL((bwd_grads_kernel<Tin, DK, false>), gchunks, dim3(NT), 0, stream, p);
+        if constexpr (std::is_same<Tin, bf16_t>::value)
+            hipLaunchKernelGGL((bwd_grads_bf16_kernel<DK>), gchunks, dim3(NT), 0, stream, p);
+        else
+            hipLaunchKernelGGL((bwd_grads_kernel<Tin, DK, false>), gchunks, dim3(NT), 0, stream, p);
         hipLaunchKernelGGL((bwd_grads_kernel<Tin, DK, true>), gchunks, dim3(NT), 0, stream, p);
     }
     return hipGetLastError();
