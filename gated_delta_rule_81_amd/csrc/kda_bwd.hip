@@ -43,6 +43,7 @@ namespace bwd {
 
 constexpr int C = 32;        // chunk length
 constexpr int NT = 256;      // threads per workgroup
+constexpr int NT2 = 512;     // threads of the bf16 gradient kernel
 constexpr int W = 32;        // d_v columns per slice
 constexpr int CP = C + 1;    // LDS pitch of C x C and C x W matrices
 constexpr int WP = W + 1;
@@ -193,16 +194,17 @@ template <typename Tin> struct One {
 };
 
 // The rows of one chunk that every kernel reads: k (and q) and the gate,
-// thread t holding row t / 8, channels (t % 8) * DK/8 onwards; beta of row t.
-template <typename Tin, int DK, bool WITH_Q> struct ChunkIn {
-    static constexpr int NE = DK / 8, DKP = DK + 1;
+// thread t holding row t / TPROW, channels (t % TPROW) * DK/TPROW onwards
+// (TPROW threads per row: 8 with 256 threads, 16 with 512); beta of row t.
+template <typename Tin, int DK, bool WITH_Q, int TPROW = 8> struct ChunkIn {
+    static constexpr int NE = DK / TPROW, DKP = DK + 1;
     Seg<Tin, NE> k, q, g;
     One<Tin> gh, b;
     // Every load is issued unconditionally (an unused one reads offset 0 of a
     // valid tensor), so that no value merges across branches and forces an
     // early wait.
     __device__ __forceinline__ void load(const Params &p, long t0, int cl, int h) {
-        const int tid = threadIdx.x, r = tid >> 3, c0 = (tid & 7) * NE;
+        const int tid = threadIdx.x, r = tid / TPROW, c0 = (tid % TPROW) * NE;
         const bool ok = r < cl;
         const size_t e = ((size_t)(t0 + r) * p.H + h) * DK + c0;
         k.load(p.k, e, ok);
@@ -214,7 +216,7 @@ template <typename Tin, int DK, bool WITH_Q> struct ChunkIn {
     }
     // raw k (q), log2 gates and beta into LDS
     __device__ __forceinline__ void store(const Params &p, float *sK, float *sQ, float *sG, float *sB) const {
-        const int tid = threadIdx.x, r = tid >> 3, c0 = (tid & 7) * NE;
+        const int tid = threadIdx.x, r = tid / TPROW, c0 = (tid % TPROW) * NE;
 #pragma unroll
         for (int j = 0; j < NE; ++j) {
             sK[r * DKP + c0 + j] = k.get(j);
@@ -228,7 +230,7 @@ template <typename Tin, int DK, bool WITH_Q> struct ChunkIn {
     }
     // only the log2 gates and beta (k and q stay in the registers)
     __device__ __forceinline__ void store_gb(const Params &p, float *sG, float *sB) const {
-        const int tid = threadIdx.x, r = tid >> 3, c0 = (tid & 7) * NE;
+        const int tid = threadIdx.x, r = tid / TPROW, c0 = (tid % TPROW) * NE;
 #pragma unroll
         for (int j = 0; j < NE; ++j) {
             float gv = 0.0f;
@@ -1314,8 +1316,8 @@ template <int DK> struct GbLayout {
     static constexpr int M = P + 4 * C * CP;
     static constexpr int GC = M + 4 * C * CP;                     // fp32 [DK] x 3
     static constexpr int GAM = GC + 4 * DK;
-    static constexpr int DGP = GAM + 4 * DK;                      // fp32 [NT]: dgamma parts
-    static constexpr int RKP = DGP + 4 * NT;                      // fp32 [2][DK]
+    static constexpr int DGP = GAM + 4 * DK;                      // fp32 [NT2]: dgamma parts
+    static constexpr int RKP = DGP + 4 * NT2;                     // fp32 [2][DK]
     static constexpr int SB = RKP + 8 * DK;                       // fp32 [C] x 2
     static constexpr int DB = SB + 4 * C;
     static constexpr int AREA = DB + 4 * C;
@@ -1349,11 +1351,11 @@ template <int DK> struct GbLayout {
 };
 
 template <int DK>
-__global__ void __launch_bounds__(NT) bwd_grads_bf16_kernel(Params p) {
+__global__ void __launch_bounds__(NT2) bwd_grads_bf16_kernel(Params p) {
     using L = GbLayout<DK>;
     constexpr int DKP = L::DKP, DKB = L::DKB, WB = L::WB, CB = L::CB;
-    constexpr int NTW = DK / 32, NE = DK / 8;
-    constexpr int NES = DK * W / NT, TPR = W / NES;
+    constexpr int NTW = DK / 64, NE = DK / 16;      // 8 waves: 2 or 1 C x DK tiles each
+    constexpr int NES = DK * W / NT2, TPR = W / NES;
     __shared__ __attribute__((aligned(16))) unsigned char smem[L::BYTES];
     float *sG = reinterpret_cast<float *>(smem + L::G);
     __bf16 *sKub = reinterpret_cast<__bf16 *>(smem + L::KUB);
@@ -1388,7 +1390,8 @@ __global__ void __launch_bounds__(NT) bwd_grads_bf16_kernel(Params p) {
     const long slot = blockIdx.x;
     const int h = blockIdx.y, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int lr = lane & 15, lj = lane >> 4;
-    const int vr = tid >> 3, vc = (tid & 7) * 4;
+    const int vr = (tid & 255) >> 3, vc = (tid & 7) * 4;   // C x W tiles: the first 256 threads
+    const bool vt = tid < 256;
     const int sr = tid / TPR, sc = (tid % TPR) * NES;
     long t0;
     int cl;
@@ -1405,28 +1408,30 @@ __global__ void __launch_bounds__(NT) bwd_grads_bf16_kernel(Params p) {
         sin.load(gS, (size_t)sr * p.DV + col0 + sc, true);
         din.load(gD, (size_t)sr * p.DV + col0 + sc, true);
         const size_t e = ((size_t)(t0 + vr) * p.H + h) * p.DV + col0 + vc;
-        vin.load(p.v, e, vr < cl);
-        oin.load(p.dO, e, vr < cl);
+        vin.load(p.v, e, vt && vr < cl);
+        oin.load(p.dO, e, vt && vr < cl);
     };
     {
-        ChunkIn<bf16_t, DK, false> in;
+        ChunkIn<bf16_t, DK, false, 16> in;
         Seg<float, 4> tin, pin, min;
+        const int t4 = (tid & 255) * 4;
         in.load(p, t0, cl, h);
-        tin.load(p.wT, wi * C * C + tid * 4, true);
-        pin.load(p.wP, wi * C * C + tid * 4, true);
-        min.load(p.wM, wi * C * C + tid * 4, true);
+        tin.load(p.wT, wi * C * C + t4, vt);
+        pin.load(p.wP, wi * C * C + t4, vt);
+        min.load(p.wM, wi * C * C + t4, vt);
         issue_slice(0);
         in.store(p, kraw, nullptr, sG, sB);
-        const int tr = (tid * 4) / C, tc = (tid * 4) % C;
+        if (vt) {
+            const int tr = t4 / C, tc = t4 % C;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const float tv = tin.get(j), pv = pin.get(j);
-            sT[tr * CP + tc + j] = tv;
-            sP[tr * CP + tc + j] = pv;
-            sM[tr * CP + tc + j] = min.get(j);
-            sTb[tr * CB + tc + j] = bf(tv);
-            sTTb[(tc + j) * CB + tr] = bf(tv);
-            sPTb[(tc + j) * CB + tr] = bf(pv);
+            for (int j = 0; j < 4; ++j) {
+                const float tv = tin.get(j), pv = pin.get(j);
+                sT[tr * CP + tc + j] = tv;
+                sM[tr * CP + tc + j] = min.get(j);
+                sTb[tr * CB + tc + j] = bf(tv);
+                sTTb[(tc + j) * CB + tr] = bf(tv);
+                sPTb[(tc + j) * CB + tr] = bf(pv);
+            }
         }
     }
     if (tid < C) dB[tid] = 0.0f;
@@ -1434,7 +1439,7 @@ __global__ void __launch_bounds__(NT) bwd_grads_bf16_kernel(Params p) {
     gate_sums<DK>(sG, gc, gam);
     __syncthreads();
     {
-        const int r = tid >> 3, c0 = (tid & 7) * NE;
+        const int r = tid >> 4, c0 = (tid & 15) * NE;
 #pragma unroll
         for (int j = 0; j < NE; ++j) {
             const int o = r * DKP + c0 + j;
@@ -1452,7 +1457,9 @@ __global__ void __launch_bounds__(NT) bwd_grads_bf16_kernel(Params p) {
         aR[x] = aQ[x];
     }
     float dgacc = 0.0f;                               // sum over this thread's S * D values
-    const int tm = wave >> 1, tn = wave & 1;
+    // waves 0-3: the C x W tiles (tm, tn) and the dT' tiles; waves 4-7: the dP tiles
+    const int tm = (wave & 3) >> 1, tn = wave & 1;
+    const bool lo = wave < 4;
     for (int col0 = 0; col0 < p.DV; col0 += W) {
         __syncthreads();
 #pragma unroll
@@ -1464,17 +1471,19 @@ __global__ void __launch_bounds__(NT) bwd_grads_bf16_kernel(Params p) {
             St[(sc + j) * DKB + sr] = bf(sv);
             Dt[(sc + j) * DKB + sr] = bf(dv);
         }
+        if (vt) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            Vr[vr * WB + vc + j] = bf(vin.get(j));
-            const __bf16 o = bf(oin.get(j));
-            dOr[vr * WB + vc + j] = o;
-            dOt[(vc + j) * CB + vr] = o;
+            for (int j = 0; j < 4; ++j) {
+                Vr[vr * WB + vc + j] = bf(vin.get(j));
+                const __bf16 o = bf(oin.get(j));
+                dOr[vr * WB + vc + j] = o;
+                dOt[(vc + j) * CB + vr] = o;
+            }
         }
         if (col0 + W < p.DV) issue_slice(col0 + W);
         __syncthreads();
         // X = V - K_up S  (kept as X and as (beta X)^T)
-        {
+        if (lo) {
             f32x4 a = {0.f, 0.f, 0.f, 0.f};
             a = mmb(a, sKub + 16 * tm * DKB, DKB, St + 16 * tn * DKB, DKB, DK);
 #pragma unroll
@@ -1487,7 +1496,7 @@ __global__ void __launch_bounds__(NT) bwd_grads_bf16_kernel(Params p) {
         }
         __syncthreads();
         // U = T (beta X);  dU = P^T dO + K_right D
-        {
+        if (lo) {
             f32x4 a = {0.f, 0.f, 0.f, 0.f}, b = a;
             a = mmb(a, sTb + 16 * tm * CB, CB, BXt + 16 * tn * CB, CB, C);
             b = mmb(b, sPTb + 16 * tm * CB, CB, dOt + 16 * tn * CB, CB, C);
@@ -1502,7 +1511,7 @@ __global__ void __launch_bounds__(NT) bwd_grads_bf16_kernel(Params p) {
         }
         __syncthreads();
         // dX = Diag(beta) T^T dU (and dV)
-        {
+        if (lo) {
             f32x4 a = {0.f, 0.f, 0.f, 0.f};
             a = mmb(a, sTTb + 16 * tm * CB, CB, dUt + 16 * tn * CB, CB, C);
 #pragma unroll
@@ -1513,9 +1522,10 @@ __global__ void __launch_bounds__(NT) bwd_grads_bf16_kernel(Params p) {
                 if (row < cl) st<bf16_t>(p.dv, ((size_t)(t0 + row) * p.H + h) * p.DV + col0 + col, x);
             }
         }
-        // dT' += dU X^T;  dP += dO U^T;  dQ_up += dO S^T;  dK_right += U D^T
-        aT = mmb(aT, dUr + 16 * tm * WB, WB, Xr + 16 * tn * WB, WB, W);
-        aP = mmb(aP, dOr + 16 * tm * WB, WB, Ur + 16 * tn * WB, WB, W);
+        // dT' += dU X^T (waves 0-3);  dP += dO U^T (waves 4-7);
+        // dQ_up += dO S^T;  dK_right += U D^T
+        if (lo) aT = mmb(aT, dUr + 16 * tm * WB, WB, Xr + 16 * tn * WB, WB, W);
+        else aP = mmb(aP, dOr + 16 * tm * WB, WB, Ur + 16 * tn * WB, WB, W);
 #pragma unroll
         for (int x = 0; x < NTW; ++x) {
             const int tt = wave * NTW + x, m0 = 16 * (tt / (DK / 16)), n0 = 16 * (tt % (DK / 16));
@@ -1539,8 +1549,8 @@ __global__ void __launch_bounds__(NT) bwd_grads_bf16_kernel(Params p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int row = 16 * tm + 4 * lj + i, col = 16 * tn + lr;
-        sdT[row * CP + col] = aT[i];
-        sdP[row * CP + col] = col <= row ? aP[i] : 0.0f;
+        if (lo) sdT[row * CP + col] = aT[i];
+        else sdP[row * CP + col] = col <= row ? aP[i] : 0.0f;
     }
     __syncthreads();
     if (tid < C) {
@@ -1550,19 +1560,19 @@ __global__ void __launch_bounds__(NT) bwd_grads_bf16_kernel(Params p) {
         dB[tid] = acc;
     }
     __syncthreads();
-    for (int idx = tid; idx < C * C; idx += NT) {
+    for (int idx = tid; idx < C * C; idx += NT2) {
         const int r = idx / C, i = idx % C;
         sdT[r * CP + i] *= sB[i];
     }
     __syncthreads();
-    {
+    if (lo) {
         f32x4 a = {0.f, 0.f, 0.f, 0.f};
         a = mm(a, sT + 16 * tm, 1, CP, sdT + 16 * tn, CP, 1, C);
 #pragma unroll
         for (int i = 0; i < 4; ++i) sY[(16 * tm + 4 * lj + i) * CP + 16 * tn + lr] = a[i];
     }
     __syncthreads();
-    {
+    if (lo) {
         f32x4 a = {0.f, 0.f, 0.f, 0.f};
         a = mm(a, sY + 16 * tm * CP, CP, 1, sT + 16 * tn * CP, 1, CP, C);
 #pragma unroll
@@ -1587,7 +1597,7 @@ __global__ void __launch_bounds__(NT) bwd_grads_bf16_kernel(Params p) {
     float *fK = reinterpret_cast<float *>(smem + L::FK), *fQ = reinterpret_cast<float *>(smem + L::FQ);
     float *fKd = reinterpret_cast<float *>(smem + L::FKD);
     {
-        const int r = tid >> 3, c0 = (tid & 7) * NE;
+        const int r = tid >> 4, c0 = (tid & 15) * NE;
         Seg<bf16_t, NE> kin, qin;
         const size_t e = ((size_t)(t0 + r) * p.H + h) * DK + c0;
         kin.load(p.k, e, r < cl);
@@ -1665,7 +1675,7 @@ __global__ void __launch_bounds__(NT) bwd_grads_bf16_kernel(Params p) {
     }
     __syncthreads();
     {
-        const int r = tid >> 3, c0 = (tid & 7) * NE;
+        const int r = tid >> 4, c0 = (tid & 15) * NE;
         if (r < cl) {
             const size_t e = ((size_t)(t0 + r) * p.H + h) * DK + c0;
 #pragma unroll
@@ -1701,7 +1711,7 @@ hipError_t launch(const Params &p, long nslot, int nseq, hipStream_t stream) {
     }
     if (nslot > 0) {
         if constexpr (std::is_same<Tin, bf16_t>::value)
-            hipLaunchKernelGGL((bwd_grads_bf16_kernel<DK>), gchunks, dim3(NT), 0, stream, p);
+            hipLaunchKernelGGL((bwd_grads_bf16_kernel<DK>), gchunks, dim3(NT2), 0, stream, p);
         else
             hipLaunchKernelGGL((bwd_grads_kernel<Tin, DK, false>), gchunks, dim3(NT), 0, stream, p);
         hipLaunchKernelGGL((bwd_grads_kernel<Tin, DK, true>), gchunks, dim3(NT), 0, stream, p);
