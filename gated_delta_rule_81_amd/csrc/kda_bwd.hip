@@ -1040,31 +1040,105 @@ __device__ __forceinline__ void store_t(__bf16 *dst, int pitch, int tm, int tn, 
     *reinterpret_cast<bf16x4 *>(dst + (16 * tn + lr) * pitch + 16 * tm + 4 * lj) = x;
 }
 
-template <int DK> struct ChainLayout {
-    static constexpr int DKP = DK + 1, DKB = DK + 8, WB = W + 8, CB = C + 8;
-    static constexpr int G = 0;                          // fp32 [C][DKP]
-    static constexpr int XT = G + 4 * C * DKP;           // bf16 [W][DKB]: S^T or D^T
-    static constexpr int KA = XT + 2 * W * DKB;          // bf16 [C][DKB]: K_up or K_right
-    static constexpr int KT1 = KA + 2 * C * DKB;         // bf16 [DK][CB]: K_right^T or Q_up^T
-    static constexpr int KT2 = KT1 + 2 * DK * CB;        // bf16 [DK][CB]: K_up^T
-    static constexpr int M1 = KT2 + 2 * DK * CB;         // bf16 [C][CB]: T or T^T
-    static constexpr int M2 = M1 + 2 * C * CB;           // bf16 [C][CB]: P^T
-    static constexpr int Y1 = M2 + 2 * C * CB;           // bf16 [W][CB]: (beta X)^T or dO^T
-    static constexpr int Y2 = Y1 + 2 * W * CB;           // bf16 [W][CB]: U^T or dU^T
-    static constexpr int Y3 = Y2 + 2 * W * CB;           // bf16 [W][CB]: (-dX)^T
-    static constexpr int V = Y3 + 2 * W * CB;            // fp32 [C][WP]: V
-    static constexpr int GC = V + 4 * C * WP;            // fp32 [DK] x 2
+// One workgroup of 8 waves per (sequence, head, 64-column slice of d_v).
+// Raw k and q sit in LDS so that the scaling step can run one thread per key
+// channel: its row-major outputs are then contiguous across lanes and its
+// transposed ones are one vector store per thread, with no bank conflicts.
+constexpr int W2 = 64;                 // d_v columns per chain workgroup
+template <int DK, bool GRAD> struct ChainLayout {
+    static constexpr int DKP = DK + 1, DKB = DK + 8, CB = C + 8, W2P = W2 + 1;
+    static constexpr int G = 0;                            // fp32 [C][DKP]
+    static constexpr int KRAW = G + 4 * C * DKP;           // bf16 [C][DKB]
+    static constexpr int QRAW = KRAW + 2 * C * DKB;        // bf16 [C][DKB] (gradient chain)
+    static constexpr int XT = QRAW + (GRAD ? 2 * C * DKB : 0);   // bf16 [W2][DKB]: S^T / D^T
+    static constexpr int KA = XT + 2 * W2 * DKB;           // bf16 [C][DKB]: K_up / K_right
+    static constexpr int KT1 = KA + 2 * C * DKB;           // bf16 [DK][CB]: K_right^T / Q_up^T
+    static constexpr int KT2 = KT1 + 2 * DK * CB;          // bf16 [DK][CB]: K_up^T (gradient chain)
+    static constexpr int M1 = KT2 + (GRAD ? 2 * DK * CB : 0);    // bf16 [C][CB]: T / T^T
+    static constexpr int M2 = M1 + 2 * C * CB;             // bf16 [C][CB]: P^T (gradient chain)
+    static constexpr int Y1 = M2 + (GRAD ? 2 * C * CB : 0);      // bf16 [W2][CB]: (beta X)^T / dO^T
+    static constexpr int Y2 = Y1 + 2 * W2 * CB;            // bf16 [W2][CB]: U^T / dU^T
+    static constexpr int Y3 = Y2 + 2 * W2 * CB;            // bf16 [W2][CB]: (-dX)^T (gradient chain)
+    static constexpr int V = Y3 + (GRAD ? 2 * W2 * CB : 0);      // fp32 [C][W2P]: V (state chain)
+    static constexpr int GC = V + (GRAD ? 0 : 4 * C * W2P);       // fp32 [DK]
     static constexpr int GAM = GC + 4 * DK;
-    static constexpr int SB = GAM + 4 * DK;              // fp32 [C]
+    static constexpr int SB = GAM + 4 * DK;                // fp32 [C]
     static constexpr int BYTES = SB + 4 * C;
 };
 
+// K_up = k 2^G and K_right = k 2^{G_c - G} (state chain: K_up row-major,
+// K_right transposed), or K_right row-major and Q_up, K_up transposed
+// (gradient chain).  Thread (channel c, block of RPT rows).
+template <int DK, bool GRAD>
+__device__ __forceinline__ void chain_scale(const float *sG, const __bf16 *kraw, const __bf16 *qraw,
+                                            const float *gc, __bf16 *rowA, __bf16 *trA, __bf16 *trB) {
+    constexpr int DKP = DK + 1, DKB = DK + 8, CB = C + 8, RPT = C * DK / NT2;
+    const int c = threadIdx.x % DK, r0 = (threadIdx.x / DK) * RPT;
+    bf16x8 ta[RPT / 8 > 0 ? RPT / 8 : 1], tb[RPT / 8 > 0 ? RPT / 8 : 1];
+    bf16x4 ua, ub;
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const int r = r0 + i;
+        const float G = sG[r * DKP + c], kv = (float)kraw[r * DKB + c];
+        const float E = __builtin_amdgcn_exp2f(G), R = __builtin_amdgcn_exp2f(gc[c] - G);
+        __bf16 a, b;
+        if constexpr (GRAD) {
+            rowA[r * DKB + c] = (__bf16)(kv * R);
+            a = (__bf16)((float)qraw[r * DKB + c] * E);
+            b = (__bf16)(kv * E);
+        } else {
+            rowA[r * DKB + c] = (__bf16)(kv * E);
+            a = (__bf16)(kv * R);
+            b = a;
+        }
+        if constexpr (RPT >= 8) {
+            ta[i >> 3][i & 7] = a;
+            tb[i >> 3][i & 7] = b;
+        } else {
+            ua[i] = a;
+            ub[i] = b;
+        }
+    }
+    if constexpr (RPT >= 8) {
+#pragma unroll
+        for (int v = 0; v < RPT / 8; ++v) {
+            *reinterpret_cast<bf16x8 *>(trA + c * CB + r0 + 8 * v) = ta[v];
+            if constexpr (GRAD) *reinterpret_cast<bf16x8 *>(trB + c * CB + r0 + 8 * v) = tb[v];
+        }
+    } else {
+        *reinterpret_cast<bf16x4 *>(trA + c * CB + r0) = ua;
+        if constexpr (GRAD) *reinterpret_cast<bf16x4 *>(trB + c * CB + r0) = ub;
+    }
+}
+
+// raw k (and q) rows of a chunk into LDS as bf16, log2 gates and beta as fp32
+template <int DK, bool WITH_Q>
+__device__ __forceinline__ void chain_store_in(const Params &p, const ChunkIn<bf16_t, DK, WITH_Q, 16> &in,
+                                               __bf16 *kraw, __bf16 *qraw, float *sG, float *sB) {
+    constexpr int DKB = DK + 8, NE = DK / 16;
+    const int tid = threadIdx.x, r = tid >> 4, c0 = (tid & 15) * NE;
+    if constexpr (NE == 8) {
+        *reinterpret_cast<uint4 *>(kraw + r * DKB + c0) =
+            in.k.ok ? make_uint4(in.k.w[0], in.k.w[1], in.k.w[2], in.k.w[3]) : make_uint4(0, 0, 0, 0);
+        if constexpr (WITH_Q)
+            *reinterpret_cast<uint4 *>(qraw + r * DKB + c0) =
+                in.q.ok ? make_uint4(in.q.w[0], in.q.w[1], in.q.w[2], in.q.w[3]) : make_uint4(0, 0, 0, 0);
+    } else {
+        *reinterpret_cast<uint2 *>(kraw + r * DKB + c0) = in.k.ok ? make_uint2(in.k.w[0], in.k.w[1]) : make_uint2(0, 0);
+        if constexpr (WITH_Q)
+            *reinterpret_cast<uint2 *>(qraw + r * DKB + c0) =
+                in.q.ok ? make_uint2(in.q.w[0], in.q.w[1]) : make_uint2(0, 0);
+    }
+    in.store_gb(p, sG, sB);
+}
+
 template <int DK>
-__global__ void __launch_bounds__(NT) bwd_states_bf16_kernel(Params p) {
-    using L = ChainLayout<DK>;
-    constexpr int DKP = L::DKP, DKB = L::DKB, CB = L::CB, NTW = DK / 32, NE = DK / 8;
+__global__ void __launch_bounds__(NT2) bwd_states_bf16_kernel(Params p) {
+    using L = ChainLayout<DK, false>;
+    constexpr int DKB = L::DKB, CB = L::CB, W2P = L::W2P, NTW = DK / 32;   // 4 or 2 state tiles per wave
     __shared__ __attribute__((aligned(16))) unsigned char smem[L::BYTES];
     float *sG = reinterpret_cast<float *>(smem + L::G);
+    __bf16 *kraw = reinterpret_cast<__bf16 *>(smem + L::KRAW);
     __bf16 *St = reinterpret_cast<__bf16 *>(smem + L::XT);
     __bf16 *Kub = reinterpret_cast<__bf16 *>(smem + L::KA);
     __bf16 *Krt = reinterpret_cast<__bf16 *>(smem + L::KT1);
@@ -1075,16 +1149,17 @@ __global__ void __launch_bounds__(NT) bwd_states_bf16_kernel(Params p) {
     float *gc = reinterpret_cast<float *>(smem + L::GC);
     float *gam = reinterpret_cast<float *>(smem + L::GAM);
     float *sB = reinterpret_cast<float *>(smem + L::SB);
-    const int nsl = p.DV / W;
+    const int nsl = p.DV / W2;
     const int unit = blockIdx.x / nsl, slice = blockIdx.x % nsl;
-    const int s = unit / p.H, h = unit % p.H, col0 = slice * W;
+    const int s = unit / p.H, h = unit % p.H, col0 = slice * W2;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, lj = lane >> 4;
-    const int vr = tid >> 3, vc = (tid & 7) * 4;
+    const int vr = tid >> 4, vc = (tid & 15) * 4;            // C x W2 values of this thread
+    const int t4 = (tid & 255) * 4;                          // C x C values (first 256 threads)
     long t0s, base;
     int len;
     seq_info(p, s, t0s, len, base);
     const int nch = (len + C - 1) / C;
-    ChunkIn<bf16_t, DK, false> in;
+    ChunkIn<bf16_t, DK, false, 16> in;
     Seg<bf16_t, 4> vin;
     Seg<float, 4> tin;
     auto issue = [&](int n) {
@@ -1092,75 +1167,66 @@ __global__ void __launch_bounds__(NT) bwd_states_bf16_kernel(Params p) {
         const int cl = len - n * C < C ? len - n * C : C;
         in.load(p, t0, cl, h);
         vin.load(p.v, ((size_t)(t0 + vr) * p.H + h) * p.DV + col0 + vc, vr < cl);
-        tin.load(p.wT, ((size_t)(base + n) * p.H + h) * C * C + tid * 4, true);
+        tin.load(p.wT, ((size_t)(base + n) * p.H + h) * C * C + t4, tid < 256);
     };
     if (nch > 0) issue(0);
+    // state tiles: index w * NTW + x -> (tm, tn) over (DK/16) x (W2/16)
     f32x4 S[NTW];
 #pragma unroll
     for (int x = 0; x < NTW; ++x) {
-        const int tt = wave * NTW + x, tm = tt >> 1, tn = tt & 1;
+        const int tt = wave * NTW + x, tm = tt >> 2, tn = tt & 3;
         load_tile(S[x], p.S0, ((size_t)s * p.H + h) * DK + 16 * tm, p.DV, col0 + 16 * tn);
     }
+    const int xm = wave >> 2, xn = wave & 3;                 // this wave's C x W2 tile
     for (int n = 0; n < nch; ++n) {
         const size_t wi = (size_t)(base + n) * p.H + h;
         bf16_t *gS = reinterpret_cast<bf16_t *>(p.wS) + wi * DK * p.DV;
 #pragma unroll
         for (int x = 0; x < NTW; ++x) {
-            const int tt = wave * NTW + x, tm = tt >> 1, tn = tt & 1;
+            const int tt = wave * NTW + x, tm = tt >> 2, tn = tt & 3;
             store_t(St, DKB, tm, tn, S[x]);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 gS[(size_t)(16 * tm + 4 * lj + i) * p.DV + col0 + 16 * tn + lr] = to_bf16(S[x][i]);
         }
-        in.store_gb(p, sG, sB);
-        {
-            const int tr = (tid * 4) / C, tc = (tid * 4) % C;
+        chain_store_in<DK, false>(p, in, kraw, nullptr, sG, sB);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                sV[vr * WP + vc + j] = vin.get(j);
-                Tb[tr * CB + tc + j] = (__bf16)tin.get(j);
-            }
+        for (int j = 0; j < 4; ++j) sV[vr * W2P + vc + j] = vin.get(j);
+        if (tid < 256) {
+            bf16x4 tv;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) tv[j] = (__bf16)tin.get(j);
+            *reinterpret_cast<bf16x4 *>(Tb + (t4 / C) * CB + t4 % C) = tv;
         }
+        if (n + 1 < nch) issue(n + 1);
         __syncthreads();
         gate_sums<DK>(sG, gc, gam);
         __syncthreads();
-        {
-            const int r = tid >> 3, c0 = (tid & 7) * NE;
-#pragma unroll
-            for (int j = 0; j < NE; ++j) {
-                const float G = sG[r * DKP + c0 + j], kv = in.k.get(j);
-                Kub[r * DKB + c0 + j] = (__bf16)(kv * __builtin_amdgcn_exp2f(G));
-                Krt[(c0 + j) * CB + r] = (__bf16)(kv * __builtin_amdgcn_exp2f(gc[c0 + j] - G));
-            }
-        }
-        // the next chunk's inputs are requested now that k has been used
-        if (n + 1 < nch) issue(n + 1);
+        chain_scale<DK, false>(sG, kraw, nullptr, gc, Kub, Krt, nullptr);
         __syncthreads();
         // (beta X)^T, X = V - K_up S
         {
-            const int tm = wave >> 1, tn = wave & 1;
             f32x4 a = {0.f, 0.f, 0.f, 0.f};
-            a = mmb(a, Kub + 16 * tm * DKB, DKB, St + 16 * tn * DKB, DKB, DK);
+            a = mmb(a, Kub + 16 * xm * DKB, DKB, St + 16 * xn * DKB, DKB, DK);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int row = 16 * tm + 4 * lj + i;
-                a[i] = sB[row] * (sV[row * WP + 16 * tn + lr] - a[i]);
+                const int row = 16 * xm + 4 * lj + i;
+                a[i] = sB[row] * (sV[row * W2P + 16 * xn + lr] - a[i]);
             }
-            store_t(BXt, CB, tm, tn, a);
+            store_t(BXt, CB, xm, xn, a);
         }
         __syncthreads();
         // U^T, U = T (beta X)
         {
-            const int tm = wave >> 1, tn = wave & 1;
             f32x4 a = {0.f, 0.f, 0.f, 0.f};
-            a = mmb(a, Tb + 16 * tm * CB, CB, BXt + 16 * tn * CB, CB, C);
-            store_t(Ut, CB, tm, tn, a);
+            a = mmb(a, Tb + 16 * xm * CB, CB, BXt + 16 * xn * CB, CB, C);
+            store_t(Ut, CB, xm, xn, a);
         }
         __syncthreads();
         // S = Diag(gamma) S + K_right^T U
 #pragma unroll
         for (int x = 0; x < NTW; ++x) {
-            const int tt = wave * NTW + x, tm = tt >> 1, tn = tt & 1;
+            const int tt = wave * NTW + x, tm = tt >> 2, tn = tt & 3;
 #pragma unroll
             for (int i = 0; i < 4; ++i) S[x][i] *= gam[16 * tm + 4 * lj + i];
             S[x] = mmb(S[x], Krt + 16 * tm * CB, CB, Ut + 16 * tn * CB, CB, C);
@@ -1170,11 +1236,13 @@ __global__ void __launch_bounds__(NT) bwd_states_bf16_kernel(Params p) {
 }
 
 template <int DK>
-__global__ void __launch_bounds__(NT) bwd_dstates_bf16_kernel(Params p) {
-    using L = ChainLayout<DK>;
-    constexpr int DKP = L::DKP, DKB = L::DKB, CB = L::CB, NTW = DK / 32, NE = DK / 8;
+__global__ void __launch_bounds__(NT2) bwd_dstates_bf16_kernel(Params p) {
+    using L = ChainLayout<DK, true>;
+    constexpr int DKB = L::DKB, CB = L::CB, NTW = DK / 32;
     __shared__ __attribute__((aligned(16))) unsigned char smem[L::BYTES];
     float *sG = reinterpret_cast<float *>(smem + L::G);
+    __bf16 *kraw = reinterpret_cast<__bf16 *>(smem + L::KRAW);
+    __bf16 *qraw = reinterpret_cast<__bf16 *>(smem + L::QRAW);
     __bf16 *Dt = reinterpret_cast<__bf16 *>(smem + L::XT);
     __bf16 *Krb = reinterpret_cast<__bf16 *>(smem + L::KA);
     __bf16 *Qt = reinterpret_cast<__bf16 *>(smem + L::KT1);
@@ -1187,95 +1255,97 @@ __global__ void __launch_bounds__(NT) bwd_dstates_bf16_kernel(Params p) {
     float *gc = reinterpret_cast<float *>(smem + L::GC);
     float *gam = reinterpret_cast<float *>(smem + L::GAM);
     float *sB = reinterpret_cast<float *>(smem + L::SB);
-    const int nsl = p.DV / W;
+    const int nsl = p.DV / W2;
     const int unit = blockIdx.x / nsl, slice = blockIdx.x % nsl;
-    const int s = unit / p.H, h = unit % p.H, col0 = slice * W;
+    const int s = unit / p.H, h = unit % p.H, col0 = slice * W2;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, lj = lane >> 4;
-    const int vr = tid >> 3, vc = (tid & 7) * 4;
+    // dO^T: thread (column oc, rows 4 ob .. 4 ob + 3); T^T, P^T: thread (column
+    // ti, rows 2 tb, 2 tb + 1)
+    const int oc = tid & 63, ob = tid >> 6, ti = tid & 31, tb = tid >> 5;
     long t0s, base;
     int len;
     seq_info(p, s, t0s, len, base);
     const int nch = (len + C - 1) / C;
     const size_t so = ((size_t)s * p.H + h) * DK;
-    ChunkIn<bf16_t, DK, true> in;
-    Seg<bf16_t, 4> oin;
-    Seg<float, 4> tin, pin;
+    ChunkIn<bf16_t, DK, true, 16> in;
+    One<bf16_t> oin[4];
+    One<float> tin[2], pin[2];
     auto issue = [&](int n) {
         const long t0 = t0s + (long)n * C;
         const int cl = len - n * C < C ? len - n * C : C;
         const size_t wi = (size_t)(base + n) * p.H + h;
         in.load(p, t0, cl, h);
-        oin.load(p.dO, ((size_t)(t0 + vr) * p.H + h) * p.DV + col0 + vc, vr < cl);
-        tin.load(p.wT, wi * C * C + tid * 4, true);
-        pin.load(p.wP, wi * C * C + tid * 4, true);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 4 * ob + i;
+            oin[i].load(p.dO, ((size_t)(t0 + r) * p.H + h) * p.DV + col0 + oc, r < cl);
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            tin[i].load(p.wT, wi * C * C + (2 * tb + i) * C + ti, true);
+            pin[i].load(p.wP, wi * C * C + (2 * tb + i) * C + ti, true);
+        }
     };
     if (nch > 0) issue(nch - 1);
     f32x4 D[NTW];
 #pragma unroll
     for (int x = 0; x < NTW; ++x) {
-        const int tt = wave * NTW + x, tm = tt >> 1, tn = tt & 1;
+        const int tt = wave * NTW + x, tm = tt >> 2, tn = tt & 3;
         load_tile(D[x], p.dST, so + 16 * tm, p.DV, col0 + 16 * tn);
     }
+    const int xm = wave >> 2, xn = wave & 3;
     for (int n = nch - 1; n >= 0; --n) {
         const size_t wi = (size_t)(base + n) * p.H + h;
         bf16_t *gD = reinterpret_cast<bf16_t *>(p.wD) + wi * DK * p.DV;
 #pragma unroll
         for (int x = 0; x < NTW; ++x) {
-            const int tt = wave * NTW + x, tm = tt >> 1, tn = tt & 1;
+            const int tt = wave * NTW + x, tm = tt >> 2, tn = tt & 3;
             store_t(Dt, DKB, tm, tn, D[x]);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 gD[(size_t)(16 * tm + 4 * lj + i) * p.DV + col0 + 16 * tn + lr] = to_bf16(D[x][i]);
         }
-        in.store_gb(p, sG, sB);
+        chain_store_in<DK, true>(p, in, kraw, qraw, sG, sB);
         {
-            const int tr = (tid * 4) / C, tc = (tid * 4) % C;
+            bf16x4 ov;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                dOt[(vc + j) * CB + vr] = (__bf16)oin.get(j);
-                TT[(tc + j) * CB + tr] = (__bf16)tin.get(j);
-                PT[(tc + j) * CB + tr] = (__bf16)pin.get(j);
-            }
+            for (int i = 0; i < 4; ++i) ov[i] = (__bf16)oin[i].get();
+            *reinterpret_cast<bf16x4 *>(dOt + oc * CB + 4 * ob) = ov;
+            bf16x2 tv, pv;
+            tv[0] = (__bf16)tin[0].get();
+            tv[1] = (__bf16)tin[1].get();
+            pv[0] = (__bf16)pin[0].get();
+            pv[1] = (__bf16)pin[1].get();
+            *reinterpret_cast<bf16x2 *>(TT + ti * CB + 2 * tb) = tv;
+            *reinterpret_cast<bf16x2 *>(PT + ti * CB + 2 * tb) = pv;
         }
+        if (n > 0) issue(n - 1);
         __syncthreads();
         gate_sums<DK>(sG, gc, gam);
         __syncthreads();
-        {
-            const int r = tid >> 3, c0 = (tid & 7) * NE;
-#pragma unroll
-            for (int j = 0; j < NE; ++j) {
-                const float G = sG[r * DKP + c0 + j], kv = in.k.get(j), E = __builtin_amdgcn_exp2f(G);
-                Krb[r * DKB + c0 + j] = (__bf16)(kv * __builtin_amdgcn_exp2f(gc[c0 + j] - G));
-                Qt[(c0 + j) * CB + r] = (__bf16)(in.q.get(j) * E);
-                Kt[(c0 + j) * CB + r] = (__bf16)(kv * E);
-            }
-        }
-        // the next chunk's inputs are requested now that k and q have been used
-        if (n > 0) issue(n - 1);
+        chain_scale<DK, true>(sG, kraw, qraw, gc, Krb, Qt, Kt);
         __syncthreads();
         // dU^T, dU = P^T dO + K_right D
         {
-            const int tm = wave >> 1, tn = wave & 1;
             f32x4 a = {0.f, 0.f, 0.f, 0.f};
-            a = mmb(a, PT + 16 * tm * CB, CB, dOt + 16 * tn * CB, CB, C);
-            a = mmb(a, Krb + 16 * tm * DKB, DKB, Dt + 16 * tn * DKB, DKB, DK);
-            store_t(dUt, CB, tm, tn, a);
+            a = mmb(a, PT + 16 * xm * CB, CB, dOt + 16 * xn * CB, CB, C);
+            a = mmb(a, Krb + 16 * xm * DKB, DKB, Dt + 16 * xn * DKB, DKB, DK);
+            store_t(dUt, CB, xm, xn, a);
         }
         __syncthreads();
         // (-dX)^T, dX = Diag(beta) T^T dU
         {
-            const int tm = wave >> 1, tn = wave & 1;
             f32x4 a = {0.f, 0.f, 0.f, 0.f};
-            a = mmb(a, TT + 16 * tm * CB, CB, dUt + 16 * tn * CB, CB, C);
+            a = mmb(a, TT + 16 * xm * CB, CB, dUt + 16 * xn * CB, CB, C);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) a[i] *= -sB[16 * tm + 4 * lj + i];
-            store_t(mdXt, CB, tm, tn, a);
+            for (int i = 0; i < 4; ++i) a[i] *= -sB[16 * xm + 4 * lj + i];
+            store_t(mdXt, CB, xm, xn, a);
         }
         __syncthreads();
         // D = Diag(gamma) D + Q_up^T dO - K_up^T dX
 #pragma unroll
         for (int x = 0; x < NTW; ++x) {
-            const int tt = wave * NTW + x, tm = tt >> 1, tn = tt & 1;
+            const int tt = wave * NTW + x, tm = tt >> 2, tn = tt & 3;
 #pragma unroll
             for (int i = 0; i < 4; ++i) D[x][i] *= gam[16 * tm + 4 * lj + i];
             D[x] = mmb(D[x], Qt + 16 * tm * CB, CB, dOt + 16 * tn * CB, CB, C);
@@ -1286,7 +1356,7 @@ __global__ void __launch_bounds__(NT) bwd_dstates_bf16_kernel(Params p) {
     if (p.dS0) {
 #pragma unroll
         for (int x = 0; x < NTW; ++x) {
-            const int tt = wave * NTW + x, tm = tt >> 1, tn = tt & 1;
+            const int tt = wave * NTW + x, tm = tt >> 2, tn = tt & 3;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int row = 16 * tm + 4 * lj + i, col = col0 + 16 * tn + lr;
@@ -1703,8 +1773,9 @@ hipError_t launch(const Params &p, long nslot, int nseq, hipStream_t stream) {
     const unsigned gunits = (unsigned)((long)nseq * p.H * (p.DV / W));
     if (nslot > 0) hipLaunchKernelGGL((bwd_prep_kernel<Tin, DK>), gchunks, dim3(NT), 0, stream, p);
     if constexpr (std::is_same<Tin, bf16_t>::value) {
-        hipLaunchKernelGGL((bwd_states_bf16_kernel<DK>), dim3(gunits), dim3(NT), 0, stream, p);
-        hipLaunchKernelGGL((bwd_dstates_bf16_kernel<DK>), dim3(gunits), dim3(NT), 0, stream, p);
+        const unsigned gu2 = (unsigned)((long)nseq * p.H * (p.DV / W2));
+        hipLaunchKernelGGL((bwd_states_bf16_kernel<DK>), dim3(gu2), dim3(NT2), 0, stream, p);
+        hipLaunchKernelGGL((bwd_dstates_bf16_kernel<DK>), dim3(gu2), dim3(NT2), 0, stream, p);
     } else {
         hipLaunchKernelGGL((bwd_states_kernel<Tin, DK>), dim3(gunits), dim3(NT), 0, stream, p);
         hipLaunchKernelGGL((bwd_dstates_kernel<Tin, DK>), dim3(gunits), dim3(NT), 0, stream, p);
