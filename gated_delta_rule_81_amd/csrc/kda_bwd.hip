@@ -81,6 +81,28 @@ __device__ __forceinline__ f32x4 mm(f32x4 acc, const float *a, int am, int ak, c
     return acc;
 }
 
+// bf16 MFMA: v_mfma_f32_16x16x32_bf16
+__device__ __forceinline__ f32x4 mfma8(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// acc += A B^T for one 16 x 16 tile: A [m][k] and Bt [n][k] bf16 row-major
+// with pitches la, lb (multiples of 8), K a multiple of 32.
+__device__ __forceinline__ f32x4 mmb(f32x4 acc, const __bf16 *A, int la, const __bf16 *Bt, int lb,
+                                     int K) {
+    const int lane = threadIdx.x & 63, r = lane & 15, j = lane >> 4;
+    const __bf16 *pa = A + r * la + 8 * j;
+    const __bf16 *pb = Bt + r * lb + 8 * j;
+#pragma unroll
+    for (int k0 = 0; k0 < K; k0 += 32)
+        acc = mfma8(*reinterpret_cast<const bf16x8 *>(pa + k0), *reinterpret_cast<const bf16x8 *>(pb + k0),
+                    acc);
+    return acc;
+}
+
+__device__ __forceinline__ __bf16 bf(float x) { return (__bf16)x; }
+__device__ __forceinline__ float fb(__bf16 x) { return (float)x; }
+
 template <typename Tin>
 __device__ __forceinline__ float ld(const void *p, size_t i) {
     return load_elem(static_cast<const Tin *>(p) + i);
@@ -297,9 +319,13 @@ __device__ __forceinline__ void scale_rows(float *sKup, float *sQup, const float
 // M0, P and T of one chunk.
 template <typename Tin, int DK>
 __global__ void __launch_bounds__(NT) bwd_prep_kernel(Params p) {
-    constexpr int DKP = DK + 1, NCC = DK / 8, NE = DK / 8;
-    __shared__ float sK[C * DKP], sQ[C * DKP], sG[C * DKP];
-    __shared__ float sM[C * CP], sP[C * CP], sB[C], gc[DK];
+    constexpr int DKP = DK + 1, NCC = DK / 8, NE = DK / 8, DKB = DK + 8;
+    // sK and sQ are contiguous: on the bf16 fast path their space takes the
+    // bf16 K_up, Q_up and K_dn operands
+    __shared__ __attribute__((aligned(16))) float sKQ[2 * C * DKP];
+    __shared__ float sG[C * DKP];
+    __shared__ float sM[C * CP], sP[C * CP], sT[C * CP], sY[16 * 17], sB[C], gc[DK];
+    float *sK = sKQ, *sQ = sKQ + C * DKP;
     const long slot = blockIdx.x;
     const int h = blockIdx.y, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     long t0;
@@ -316,22 +342,46 @@ __global__ void __launch_bounds__(NT) bwd_prep_kernel(Params p) {
     const bool exact = __syncthreads_or(tid < DK && !(gc[tid] >= kFastMinLog2));
     if (tid == 0) p.wF[wi] = exact ? 1 : 0;
     if (!exact) {
-        // K_up = k 2^G, Q_up = q 2^G, K_dn = k 2^-G in place; then
-        // M0 = K_up K_dn^T (strictly lower) and P = Q_up K_dn^T (lower) on MFMA
+        // K_up = k 2^G, Q_up = q 2^G, K_dn = k 2^-G; then M0 = K_up K_dn^T
+        // (strictly lower) and P = Q_up K_dn^T (lower) on MFMA (bf16 operands
+        // for bf16 inputs, fp32 otherwise)
         const int r = tid >> 3, c0 = (tid & 7) * NE;
-#pragma unroll
-        for (int j = 0; j < NE; ++j) {
-            const int o = r * DKP + c0 + j;
-            const float G = sG[o], kv = sK[o];
-            sK[o] = kv * __builtin_amdgcn_exp2f(G);
-            sQ[o] *= __builtin_amdgcn_exp2f(G);
-            sG[o] = kv * __builtin_amdgcn_exp2f(-G);
-        }
-        __syncthreads();
         const int tm = wave >> 1, tn = wave & 1, lr = lane & 15, lj = lane >> 4;
         f32x4 m = {0.f, 0.f, 0.f, 0.f}, pp = {0.f, 0.f, 0.f, 0.f};
-        m = mm(m, sK + 16 * tm * DKP, DKP, 1, sG + 16 * tn * DKP, 1, DKP, DK);
-        pp = mm(pp, sQ + 16 * tm * DKP, DKP, 1, sG + 16 * tn * DKP, 1, DKP, DK);
+        if constexpr (std::is_same<Tin, bf16_t>::value) {
+            float kv[NE], qv[NE], gv[NE];
+#pragma unroll
+            for (int j = 0; j < NE; ++j) {
+                const int o = r * DKP + c0 + j;
+                kv[j] = sK[o];
+                qv[j] = sQ[o];
+                gv[j] = sG[o];
+            }
+            __syncthreads();
+            __bf16 *Kub = reinterpret_cast<__bf16 *>(sKQ), *Qub = Kub + C * DKB, *Kdb = Qub + C * DKB;
+#pragma unroll
+            for (int j = 0; j < NE; ++j) {
+                const float E = __builtin_amdgcn_exp2f(gv[j]), Ei = __builtin_amdgcn_exp2f(-gv[j]);
+                Kub[r * DKB + c0 + j] = (__bf16)(kv[j] * E);
+                Qub[r * DKB + c0 + j] = (__bf16)(qv[j] * E);
+                Kdb[r * DKB + c0 + j] = (__bf16)(kv[j] * Ei);
+            }
+            __syncthreads();
+            m = mmb(m, Kub + 16 * tm * DKB, DKB, Kdb + 16 * tn * DKB, DKB, DK);
+            pp = mmb(pp, Qub + 16 * tm * DKB, DKB, Kdb + 16 * tn * DKB, DKB, DK);
+        } else {
+#pragma unroll
+            for (int j = 0; j < NE; ++j) {
+                const int o = r * DKP + c0 + j;
+                const float G = sG[o], kv = sK[o];
+                sK[o] = kv * __builtin_amdgcn_exp2f(G);
+                sQ[o] *= __builtin_amdgcn_exp2f(G);
+                sG[o] = kv * __builtin_amdgcn_exp2f(-G);
+            }
+            __syncthreads();
+            m = mm(m, sK + 16 * tm * DKP, DKP, 1, sG + 16 * tn * DKP, 1, DKP, DK);
+            pp = mm(pp, sQ + 16 * tm * DKP, DKP, 1, sG + 16 * tn * DKP, 1, DKP, DK);
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int row = 16 * tm + 4 * lj + i, col = 16 * tn + lr;
@@ -380,19 +430,40 @@ __global__ void __launch_bounds__(NT) bwd_prep_kernel(Params p) {
         *reinterpret_cast<float4 *>(gM + tid * 4) =
             make_float4(sM[r * CP + i], sM[r * CP + i + 1], sM[r * CP + i + 2], sM[r * CP + i + 3]);
     }
-    // T = (I + A)^{-1}, A = Diag(beta) M0 strictly lower: column i by lane i,
-    // rows in order, T_ri = [r == i] - sum_{j < r} A_rj T_ji
+    // T = (I + A)^{-1}, A = Diag(beta) M0 strictly lower, by 16 x 16 blocks:
+    // the diagonal blocks by substitution (lane l: block l / 16, column
+    // l % 16; T_ri = [r == i] - sum_{j < r} A_rj T_ji), then
+    // T_10 = -T_11 A_10 T_00 on MFMA; T_01 = 0.
     if (tid < C) {
-        const int i = tid;
-        float t[C];
+        const int b = tid >> 4, i = tid & 15, o = 16 * b;
+        float t[16];
 #pragma unroll
-        for (int r = 0; r < C; ++r) {
+        for (int r = 0; r < 16; ++r) {
             float acc = 0.0f;
 #pragma unroll
-            for (int j = 0; j < r; ++j) acc += sM[r * CP + j] * t[j];
-            t[r] = (r == i ? 1.0f : 0.0f) - sB[r] * acc;
-            gT[r * C + i] = t[r];
+            for (int j = 0; j < r; ++j) acc += sM[(o + r) * CP + o + j] * t[j];
+            t[r] = (r == i ? 1.0f : 0.0f) - sB[o + r] * acc;
+            sT[(o + r) * CP + o + i] = t[r];
+            sT[(o + r) * CP + (16 - o) + i] = 0.0f;        // T_01 (rewritten below for T_10)
         }
+    }
+    __syncthreads();
+    if (wave == 0) {
+        const int lr = lane & 15, lj = lane >> 4;
+        f32x4 y = {0.f, 0.f, 0.f, 0.f};
+        y = mm(y, sM + 16 * CP, CP, 1, sT, CP, 1, 16);   // M0_10 T_00
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sY[(4 * lj + i) * 17 + lr] = sB[16 + 4 * lj + i] * y[i];
+        f32x4 t = {0.f, 0.f, 0.f, 0.f};
+        t = mm(t, sT + 16 * CP + 16, CP, 1, sY, 17, 1, 16);  // T_11 (A_10 T_00)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sT[(16 + 4 * lj + i) * CP + lr] = -t[i];
+    }
+    __syncthreads();
+    {
+        const int r = (tid * 4) / C, i = (tid * 4) % C;
+        *reinterpret_cast<float4 *>(gT + tid * 4) =
+            make_float4(sT[r * CP + i], sT[r * CP + i + 1], sT[r * CP + i + 2], sT[r * CP + i + 3]);
     }
 }
 
@@ -1001,26 +1072,6 @@ __global__ void __launch_bounds__(NT) bwd_grads_kernel(Params p) {
     }
 }
 
-__device__ __forceinline__ f32x4 mfma8(bf16x8 a, bf16x8 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-// acc += A B^T for one 16 x 16 tile: A [m][k] and Bt [n][k] bf16 row-major
-// with pitches la, lb (multiples of 8), K a multiple of 32.
-__device__ __forceinline__ f32x4 mmb(f32x4 acc, const __bf16 *A, int la, const __bf16 *Bt, int lb,
-                                     int K) {
-    const int lane = threadIdx.x & 63, r = lane & 15, j = lane >> 4;
-    const __bf16 *pa = A + r * la + 8 * j;
-    const __bf16 *pb = Bt + r * lb + 8 * j;
-#pragma unroll
-    for (int k0 = 0; k0 < K; k0 += 32)
-        acc = mfma8(*reinterpret_cast<const bf16x8 *>(pa + k0), *reinterpret_cast<const bf16x8 *>(pb + k0),
-                    acc);
-    return acc;
-}
-
-__device__ __forceinline__ __bf16 bf(float x) { return (__bf16)x; }
-__device__ __forceinline__ float fb(__bf16 x) { return (float)x; }
 
 // ---------------------------------------------------------------------------
 // bf16 inputs: the two state chains on bf16 MFMA.  The state (or its
