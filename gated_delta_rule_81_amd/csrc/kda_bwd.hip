@@ -1796,15 +1796,21 @@ __global__ void __launch_bounds__(NT2) bwd_grads_bf16_kernel(Params p) {
     }
     __syncthreads();
     {
+        // each thread's NE consecutive gradients as one vector store
+        using vec = typename std::conditional<NE == 8, bf16x8, bf16x4>::type;
         const int r = tid >> 4, c0 = (tid & 15) * NE;
         if (r < cl) {
             const size_t e = ((size_t)(t0 + r) * p.H + h) * DK + c0;
+            vec a, b, g;
 #pragma unroll
             for (int j = 0; j < NE; ++j) {
-                st<bf16_t>(p.dq, e + j, fQ[r * DKP + c0 + j]);
-                st<bf16_t>(p.dk, e + j, fK[r * DKP + c0 + j]);
-                if (p.gate == GATE_CHANNEL) st<bf16_t>(p.dg, e + j, fKd[r * DKP + c0 + j]);
+                a[j] = (__bf16)fQ[r * DKP + c0 + j];
+                b[j] = (__bf16)fK[r * DKP + c0 + j];
+                g[j] = (__bf16)fKd[r * DKP + c0 + j];
             }
+            *reinterpret_cast<vec *>(static_cast<bf16_t *>(p.dq) + e) = a;
+            *reinterpret_cast<vec *>(static_cast<bf16_t *>(p.dk) + e) = b;
+            if (p.gate == GATE_CHANNEL) *reinterpret_cast<vec *>(static_cast<bf16_t *>(p.dg) + e) = g;
         }
     }
     if (tid < cl) {
