@@ -56,6 +56,7 @@ struct Params {
     void *dq, *dk, *dv, *dg, *dbeta;
     float *dS0;
     float *wS, *wD, *wT, *wP, *wM;   // workspace, per (chunk slot, head)
+    bf16_t *wX, *wU, *wdU, *wdX;      // bf16 inputs: X, U, dU, dX of each chunk (C x d_v)
     int32_t *wF;                     // per (chunk slot, head): 1 = exact path
 };
 
@@ -1259,10 +1260,13 @@ __global__ void __launch_bounds__(NT2) bwd_states_bf16_kernel(Params p) {
         {
             f32x4 a = {0.f, 0.f, 0.f, 0.f};
             a = mmb(a, Kub + 16 * xm * DKB, DKB, St + 16 * xn * DKB, DKB, DK);
+            bf16_t *gX = p.wX + wi * C * p.DV + col0 + 16 * xn + lr;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int row = 16 * xm + 4 * lj + i;
-                a[i] = sB[row] * (sV[row * W2P + 16 * xn + lr] - a[i]);
+                const float x = sV[row * W2P + 16 * xn + lr] - a[i];
+                gX[(size_t)row * p.DV] = to_bf16(x);          // X, for the gradient kernel
+                a[i] = sB[row] * x;
             }
             store_t(BXt, CB, xm, xn, a);
         }
@@ -1272,6 +1276,9 @@ __global__ void __launch_bounds__(NT2) bwd_states_bf16_kernel(Params p) {
             f32x4 a = {0.f, 0.f, 0.f, 0.f};
             a = mmb(a, Tb + 16 * xm * CB, CB, BXt + 16 * xn * CB, CB, C);
             store_t(Ut, CB, xm, xn, a);
+            bf16_t *gU = p.wU + wi * C * p.DV + col0 + 16 * xn + lr;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) gU[(size_t)(16 * xm + 4 * lj + i) * p.DV] = to_bf16(a[i]);
         }
         __syncthreads();
         // S = Diag(gamma) S + K_right^T U
@@ -1382,14 +1389,28 @@ __global__ void __launch_bounds__(NT2) bwd_dstates_bf16_kernel(Params p) {
             a = mmb(a, PT + 16 * xm * CB, CB, dOt + 16 * xn * CB, CB, C);
             a = mmb(a, Krb + 16 * xm * DKB, DKB, Dt + 16 * xn * DKB, DKB, DK);
             store_t(dUt, CB, xm, xn, a);
+            bf16_t *gdU = p.wdU + wi * C * p.DV + col0 + 16 * xn + lr;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) gdU[(size_t)(16 * xm + 4 * lj + i) * p.DV] = to_bf16(a[i]);
         }
         __syncthreads();
         // (-dX)^T, dX = Diag(beta) T^T dU
         {
             f32x4 a = {0.f, 0.f, 0.f, 0.f};
             a = mmb(a, TT + 16 * xm * CB, CB, dUt + 16 * xn * CB, CB, C);
+            // dX (= dV): to the workspace for the gradient kernel, and to dv
+            const long t0 = t0s + (long)n * C;
+            const int cl = len - n * C < C ? len - n * C : C;
+            bf16_t *gdX = p.wdX + wi * C * p.DV + col0 + 16 * xn + lr;
+            bf16_t *gdv = static_cast<bf16_t *>(p.dv) + col0 + 16 * xn + lr;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) a[i] *= -sB[16 * xm + 4 * lj + i];
+            for (int i = 0; i < 4; ++i) {
+                const int row = 16 * xm + 4 * lj + i;
+                const float dx = sB[row] * a[i];
+                gdX[(size_t)row * p.DV] = to_bf16(dx);
+                if (row < cl) gdv[((size_t)(t0 + row) * p.H + h) * p.DV] = to_bf16(dx);
+                a[i] = -dx;
+            }
             store_t(mdXt, CB, xm, xn, a);
         }
         __syncthreads();
@@ -1423,42 +1444,31 @@ __global__ void __launch_bounds__(NT2) bwd_dstates_bf16_kernel(Params p) {
 // operand is staged in LDS as bf16 with its contraction index contiguous (a
 // matrix used both ways is kept in both orientations); the C x C algebra and
 // the decay-weighted sums stay fp32.
+// With X, U (state chain), dU and dX (gradient chain) in the workspace, every
+// product left contracts over d_v, which is contiguous in every operand: the
+// slices go to LDS row-major as they come, with no transposed copies.
+constexpr int W3 = 64;                 // d_v columns per slice of the gradient kernel
 template <int DK> struct GbLayout {
-    static constexpr int DKP = DK + 1, DKB = DK + 8, WB = W + 8, CB = C + 8;
-    // persistent
+    static constexpr int DKP = DK + 1, WB = W3 + 8;
     static constexpr int G = 0;                                   // fp32 [C][DKP]
-    static constexpr int KUB = G + 4 * C * DKP;                   // bf16 [C][DKB]
-    static constexpr int KRB = KUB + 2 * C * DKB;
-    static constexpr int TB = KRB + 2 * C * DKB;                  // bf16 [C][CB]
-    static constexpr int TTB = TB + 2 * C * CB;
-    static constexpr int PTB = TTB + 2 * C * CB;
-    static constexpr int T = PTB + 2 * C * CB;                    // fp32 [C][CP]
-    static constexpr int P = T + 4 * C * CP;
-    static constexpr int M = P + 4 * C * CP;
+    static constexpr int T = G + 4 * C * DKP;                     // fp32 [C][CP]
+    static constexpr int M = T + 4 * C * CP;
     static constexpr int GC = M + 4 * C * CP;                     // fp32 [DK] x 3
     static constexpr int GAM = GC + 4 * DK;
-    static constexpr int DGP = GAM + 4 * DK;                      // fp32 [NT2]: dgamma parts
-    static constexpr int RKP = DGP + 4 * NT2;                     // fp32 [2][DK]
+    static constexpr int DGP = GAM + 4 * DK;
+    static constexpr int RKP = DGP + 4 * DK;                      // fp32 [2][DK]
     static constexpr int SB = RKP + 8 * DK;                       // fp32 [C] x 2
     static constexpr int DB = SB + 4 * C;
     static constexpr int AREA = DB + 4 * C;
-    // slice phase (in the area)
-    static constexpr int SR = AREA;                               // bf16 [DK][WB]
+    // slice phase (in the area): bf16, row-major
+    static constexpr int SR = AREA;                               // [DK][WB]
     static constexpr int DR = SR + 2 * DK * WB;
-    static constexpr int ST = DR + 2 * DK * WB;                   // bf16 [W][DKB]
-    static constexpr int DT = ST + 2 * W * DKB;
-    static constexpr int VR = DT + 2 * W * DKB;                   // bf16 [C][WB] / [W][CB]
-    static constexpr int DOR = VR + 2 * C * WB;
-    static constexpr int DOT = DOR + 2 * C * WB;
-    static constexpr int XR = DOT + 2 * W * CB;
-    static constexpr int BXT = XR + 2 * C * WB;
-    static constexpr int UR = BXT + 2 * W * CB;
+    static constexpr int XR = DR + 2 * DK * WB;                   // [C][WB]
+    static constexpr int UR = XR + 2 * C * WB;
     static constexpr int DUR = UR + 2 * C * WB;
-    static constexpr int DUT = DUR + 2 * C * WB;
-    static constexpr int DXR = DUT + 2 * W * CB;
-    static constexpr int SLICE_END = DXR + 2 * C * WB;
-    // setup: raw k (fp32 [C][DKP]) in the area
-    static constexpr int KRAW = AREA;
+    static constexpr int DXR = DUR + 2 * C * WB;
+    static constexpr int DOR = DXR + 2 * C * WB;
+    static constexpr int SLICE_END = DOR + 2 * C * WB;
     // after the slices (in the area)
     static constexpr int DTF = AREA;                              // fp32 [C][CP] x 4
     static constexpr int DPF = DTF + 4 * C * CP;
@@ -1474,18 +1484,12 @@ template <int DK> struct GbLayout {
 template <int DK>
 __global__ void __launch_bounds__(NT2) bwd_grads_bf16_kernel(Params p) {
     using L = GbLayout<DK>;
-    constexpr int DKP = L::DKP, DKB = L::DKB, WB = L::WB, CB = L::CB;
+    constexpr int DKP = L::DKP, WB = L::WB;
     constexpr int NTW = DK / 64, NE = DK / 16;      // 8 waves: 2 or 1 C x DK tiles each
-    constexpr int NES = DK * W / NT2, TPR = W / NES;
+    constexpr int NES = DK * W3 / NT2, TPR = W3 / NES;   // S / D slice values per thread
     __shared__ __attribute__((aligned(16))) unsigned char smem[L::BYTES];
     float *sG = reinterpret_cast<float *>(smem + L::G);
-    __bf16 *sKub = reinterpret_cast<__bf16 *>(smem + L::KUB);
-    __bf16 *sKrb = reinterpret_cast<__bf16 *>(smem + L::KRB);
-    __bf16 *sTb = reinterpret_cast<__bf16 *>(smem + L::TB);
-    __bf16 *sTTb = reinterpret_cast<__bf16 *>(smem + L::TTB);
-    __bf16 *sPTb = reinterpret_cast<__bf16 *>(smem + L::PTB);
     float *sT = reinterpret_cast<float *>(smem + L::T);
-    float *sP = reinterpret_cast<float *>(smem + L::P);
     float *sM = reinterpret_cast<float *>(smem + L::M);
     float *gc = reinterpret_cast<float *>(smem + L::GC);
     float *gam = reinterpret_cast<float *>(smem + L::GAM);
@@ -1495,25 +1499,18 @@ __global__ void __launch_bounds__(NT2) bwd_grads_bf16_kernel(Params p) {
     float *dB = reinterpret_cast<float *>(smem + L::DB);
     __bf16 *Sr = reinterpret_cast<__bf16 *>(smem + L::SR);
     __bf16 *Dr = reinterpret_cast<__bf16 *>(smem + L::DR);
-    __bf16 *St = reinterpret_cast<__bf16 *>(smem + L::ST);
-    __bf16 *Dt = reinterpret_cast<__bf16 *>(smem + L::DT);
-    __bf16 *Vr = reinterpret_cast<__bf16 *>(smem + L::VR);
-    __bf16 *dOr = reinterpret_cast<__bf16 *>(smem + L::DOR);
-    __bf16 *dOt = reinterpret_cast<__bf16 *>(smem + L::DOT);
     __bf16 *Xr = reinterpret_cast<__bf16 *>(smem + L::XR);
-    __bf16 *BXt = reinterpret_cast<__bf16 *>(smem + L::BXT);
     __bf16 *Ur = reinterpret_cast<__bf16 *>(smem + L::UR);
     __bf16 *dUr = reinterpret_cast<__bf16 *>(smem + L::DUR);
-    __bf16 *dUt = reinterpret_cast<__bf16 *>(smem + L::DUT);
     __bf16 *dXr = reinterpret_cast<__bf16 *>(smem + L::DXR);
-    float *kraw = reinterpret_cast<float *>(smem + L::KRAW);
+    __bf16 *dOr = reinterpret_cast<__bf16 *>(smem + L::DOR);
 
     const long slot = blockIdx.x;
     const int h = blockIdx.y, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int lr = lane & 15, lj = lane >> 4;
-    const int vr = (tid & 255) >> 3, vc = (tid & 7) * 4;   // C x W tiles: the first 256 threads
-    const bool vt = tid < 256;
-    const int sr = tid / TPR, sc = (tid % TPR) * NES;
+    const int sr = tid / TPR, sc = (tid % TPR) * NES;     // S / D: row sr, columns sc ..
+    const int vr = tid >> 4, vc = (tid & 15) * 4;         // C x W3: row vr, columns vc ..
+    const bool vt = tid < 256;                            // C x C values: the first 256 threads
     long t0;
     int cl;
     if (!slot_chunk(p, slot, t0, cl)) return;
@@ -1522,53 +1519,41 @@ __global__ void __launch_bounds__(NT2) bwd_grads_bf16_kernel(Params p) {
     // states and state gradients are kept as bf16 for bf16 inputs
     const bf16_t *gS = reinterpret_cast<const bf16_t *>(p.wS) + wi * DK * p.DV;
     const bf16_t *gD = reinterpret_cast<const bf16_t *>(p.wD) + wi * DK * p.DV;
+    const size_t cx = wi * C * p.DV;
 
     Seg<bf16_t, NES> sin, din;
-    Seg<bf16_t, 4> vin, oin;
+    Seg<bf16_t, 4> xin, uin, duin, dxin, oin;
     auto issue_slice = [&](int col0) {
         sin.load(gS, (size_t)sr * p.DV + col0 + sc, true);
         din.load(gD, (size_t)sr * p.DV + col0 + sc, true);
-        const size_t e = ((size_t)(t0 + vr) * p.H + h) * p.DV + col0 + vc;
-        vin.load(p.v, e, vt && vr < cl);
-        oin.load(p.dO, e, vt && vr < cl);
+        const size_t w = cx + (size_t)vr * p.DV + col0 + vc;
+        xin.load(p.wX, w, true);
+        uin.load(p.wU, w, true);
+        duin.load(p.wdU, w, true);
+        dxin.load(p.wdX, w, true);
+        oin.load(p.dO, ((size_t)(t0 + vr) * p.H + h) * p.DV + col0 + vc, vr < cl);
     };
     {
         ChunkIn<bf16_t, DK, false, 16> in;
-        Seg<float, 4> tin, pin, min;
+        Seg<float, 4> tin, min;
         const int t4 = (tid & 255) * 4;
         in.load(p, t0, cl, h);
         tin.load(p.wT, wi * C * C + t4, vt);
-        pin.load(p.wP, wi * C * C + t4, vt);
         min.load(p.wM, wi * C * C + t4, vt);
         issue_slice(0);
-        in.store(p, kraw, nullptr, sG, sB);
+        in.store_gb(p, sG, sB);
         if (vt) {
             const int tr = t4 / C, tc = t4 % C;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const float tv = tin.get(j), pv = pin.get(j);
-                sT[tr * CP + tc + j] = tv;
+                sT[tr * CP + tc + j] = tin.get(j);
                 sM[tr * CP + tc + j] = min.get(j);
-                sTb[tr * CB + tc + j] = bf(tv);
-                sTTb[(tc + j) * CB + tr] = bf(tv);
-                sPTb[(tc + j) * CB + tr] = bf(pv);
             }
         }
     }
     if (tid < C) dB[tid] = 0.0f;
     __syncthreads();
     gate_sums<DK>(sG, gc, gam);
-    __syncthreads();
-    {
-        const int r = tid >> 4, c0 = (tid & 15) * NE;
-#pragma unroll
-        for (int j = 0; j < NE; ++j) {
-            const int o = r * DKP + c0 + j;
-            const float G = sG[o], kv = kraw[o];
-            sKub[r * DKB + c0 + j] = bf(kv * __builtin_amdgcn_exp2f(G));
-            sKrb[r * DKB + c0 + j] = bf(kv * __builtin_amdgcn_exp2f(gc[c0 + j] - G));
-        }
-    }
 
     f32x4 aQ[NTW], aK[NTW], aR[NTW], aT = {0.f, 0.f, 0.f, 0.f}, aP = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -1577,94 +1562,54 @@ __global__ void __launch_bounds__(NT2) bwd_grads_bf16_kernel(Params p) {
         aK[x] = aQ[x];
         aR[x] = aQ[x];
     }
-    float dgacc = 0.0f;                               // sum over this thread's S * D values
-    // waves 0-3: the C x W tiles (tm, tn) and the dT' tiles; waves 4-7: the dP tiles
+    float dgacc = 0.0f;                               // S * D over this thread's values
+    // waves 0-3: the dT' tiles; waves 4-7: the dP tiles (tile (tm, tn) of C x C)
     const int tm = (wave & 3) >> 1, tn = wave & 1;
     const bool lo = wave < 4;
-    for (int col0 = 0; col0 < p.DV; col0 += W) {
+    auto put = [](__bf16 *dst, const auto &seg, int n) {
+        // raw bf16 bits of a segment, as one vector store of n values
+        if (n == 16) {
+            reinterpret_cast<uint4 *>(dst)[0] = make_uint4(seg.w[0], seg.w[1], seg.w[2], seg.w[3]);
+            reinterpret_cast<uint4 *>(dst)[1] = make_uint4(seg.w[4], seg.w[5], seg.w[6], seg.w[7]);
+        } else if (n == 8) {
+            reinterpret_cast<uint4 *>(dst)[0] = make_uint4(seg.w[0], seg.w[1], seg.w[2], seg.w[3]);
+        } else {
+            reinterpret_cast<uint2 *>(dst)[0] = make_uint2(seg.w[0], seg.w[1]);
+        }
+    };
+    for (int col0 = 0; col0 < p.DV; col0 += W3) {
         __syncthreads();
 #pragma unroll
-        for (int j = 0; j < NES; ++j) {
-            const float sv = sin.get(j), dv = din.get(j);
-            dgacc += sv * dv;
-            Sr[sr * WB + sc + j] = bf(sv);
-            Dr[sr * WB + sc + j] = bf(dv);
-            St[(sc + j) * DKB + sr] = bf(sv);
-            Dt[(sc + j) * DKB + sr] = bf(dv);
-        }
-        if (vt) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                Vr[vr * WB + vc + j] = bf(vin.get(j));
-                const __bf16 o = bf(oin.get(j));
-                dOr[vr * WB + vc + j] = o;
-                dOt[(vc + j) * CB + vr] = o;
-            }
-        }
-        if (col0 + W < p.DV) issue_slice(col0 + W);
+        for (int j = 0; j < NES; ++j) dgacc += sin.get(j) * din.get(j);
+        put(Sr + sr * WB + sc, sin, NES);
+        put(Dr + sr * WB + sc, din, NES);
+        put(Xr + vr * WB + vc, xin, 4);
+        put(Ur + vr * WB + vc, uin, 4);
+        put(dUr + vr * WB + vc, duin, 4);
+        put(dXr + vr * WB + vc, dxin, 4);
+        if (oin.ok) put(dOr + vr * WB + vc, oin, 4);
+        else *reinterpret_cast<uint2 *>(dOr + vr * WB + vc) = make_uint2(0u, 0u);
+        if (col0 + W3 < p.DV) issue_slice(col0 + W3);
         __syncthreads();
-        // X = V - K_up S  (kept as X and as (beta X)^T)
-        if (lo) {
-            f32x4 a = {0.f, 0.f, 0.f, 0.f};
-            a = mmb(a, sKub + 16 * tm * DKB, DKB, St + 16 * tn * DKB, DKB, DK);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = 16 * tm + 4 * lj + i, col = 16 * tn + lr;
-                const float x = fb(Vr[row * WB + col]) - a[i];
-                Xr[row * WB + col] = bf(x);
-                BXt[col * CB + row] = bf(sB[row] * x);
-            }
-        }
-        __syncthreads();
-        // U = T (beta X);  dU = P^T dO + K_right D
-        if (lo) {
-            f32x4 a = {0.f, 0.f, 0.f, 0.f}, b = a;
-            a = mmb(a, sTb + 16 * tm * CB, CB, BXt + 16 * tn * CB, CB, C);
-            b = mmb(b, sPTb + 16 * tm * CB, CB, dOt + 16 * tn * CB, CB, C);
-            b = mmb(b, sKrb + 16 * tm * DKB, DKB, Dt + 16 * tn * DKB, DKB, DK);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = 16 * tm + 4 * lj + i, col = 16 * tn + lr;
-                Ur[row * WB + col] = bf(a[i]);
-                dUr[row * WB + col] = bf(b[i]);
-                dUt[col * CB + row] = bf(b[i]);
-            }
-        }
-        __syncthreads();
-        // dX = Diag(beta) T^T dU (and dV)
-        if (lo) {
-            f32x4 a = {0.f, 0.f, 0.f, 0.f};
-            a = mmb(a, sTTb + 16 * tm * CB, CB, dUt + 16 * tn * CB, CB, C);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = 16 * tm + 4 * lj + i, col = 16 * tn + lr;
-                const float x = sB[row] * a[i];
-                dXr[row * WB + col] = bf(x);
-                if (row < cl) st<bf16_t>(p.dv, ((size_t)(t0 + row) * p.H + h) * p.DV + col0 + col, x);
-            }
-        }
         // dT' += dU X^T (waves 0-3);  dP += dO U^T (waves 4-7);
-        // dQ_up += dO S^T;  dK_right += U D^T
-        if (lo) aT = mmb(aT, dUr + 16 * tm * WB, WB, Xr + 16 * tn * WB, WB, W);
-        else aP = mmb(aP, dOr + 16 * tm * WB, WB, Ur + 16 * tn * WB, WB, W);
+        // dQ_up += dO S^T;  -dK_up += dX S^T;  dK_right += U D^T
+        if (lo) aT = mmb(aT, dUr + 16 * tm * WB, WB, Xr + 16 * tn * WB, WB, W3);
+        else aP = mmb(aP, dOr + 16 * tm * WB, WB, Ur + 16 * tn * WB, WB, W3);
 #pragma unroll
         for (int x = 0; x < NTW; ++x) {
             const int tt = wave * NTW + x, m0 = 16 * (tt / (DK / 16)), n0 = 16 * (tt % (DK / 16));
-            aQ[x] = mmb(aQ[x], dOr + m0 * WB, WB, Sr + n0 * WB, WB, W);
-            aR[x] = mmb(aR[x], Ur + m0 * WB, WB, Dr + n0 * WB, WB, W);
-        }
-        __syncthreads();
-        // dK_up -= dX S^T
-#pragma unroll
-        for (int x = 0; x < NTW; ++x) {
-            const int tt = wave * NTW + x, m0 = 16 * (tt / (DK / 16)), n0 = 16 * (tt % (DK / 16));
-            aK[x] = mmb(aK[x], dXr + m0 * WB, WB, Sr + n0 * WB, WB, W);
+            aQ[x] = mmb(aQ[x], dOr + m0 * WB, WB, Sr + n0 * WB, WB, W3);
+            aK[x] = mmb(aK[x], dXr + m0 * WB, WB, Sr + n0 * WB, WB, W3);
+            aR[x] = mmb(aR[x], Ur + m0 * WB, WB, Dr + n0 * WB, WB, W3);
         }
     }
-    dgp[tid] = dgacc;
+    // dgamma per channel: the S * D sums of the TPR threads of a row
+#pragma unroll
+    for (int off = 1; off < TPR; off <<= 1) dgacc += __shfl_xor(dgacc, off);
+    if (tid % TPR == 0) dgp[sr] = dgacc;
     __syncthreads();
 
-    // C x C algebra (fp32), as in the fp32 kernel
+    // C x C algebra (fp32)
     float *sdT = reinterpret_cast<float *>(smem + L::DTF), *sdP = reinterpret_cast<float *>(smem + L::DPF);
     float *sY = reinterpret_cast<float *>(smem + L::YF), *sdA = reinterpret_cast<float *>(smem + L::DAF);
 #pragma unroll
@@ -1780,11 +1725,8 @@ __global__ void __launch_bounds__(NT2) bwd_grads_bf16_kernel(Params p) {
     // dlog_alpha: reverse running sum of dGamma plus the chunk-total term
     if (tid < DK) {
         const int c = tid;
-        float dgam = 0.0f;
-#pragma unroll
-        for (int t = 0; t < TPR; ++t) dgam += dgp[c * TPR + t];
         float x[C];
-        const float tot = rkp[c] + rkp[DK + c] + dgam * gam[c];
+        const float tot = rkp[c] + rkp[DK + c] + dgp[c] * gam[c];
 #pragma unroll
         for (int r = 0; r < C; ++r) x[r] = fKd[r * DKP + c];
         float run = tot;
@@ -1860,7 +1802,8 @@ size_t bwd_workspace_bytes(int B, int T, int H, int dk, int dv, int num_seqs) {
     const size_t a = (per * dk * dv * sizeof(float) + 255) & ~(size_t)255;
     const size_t b = (per * bwd::C * bwd::C * sizeof(float) + 255) & ~(size_t)255;
     const size_t f = (per * sizeof(int32_t) + 255) & ~(size_t)255;
-    return 2 * a + 3 * b + f;
+    const size_t x = (per * bwd::C * dv * sizeof(bf16_t) + 255) & ~(size_t)255;
+    return 2 * a + 3 * b + f + 4 * x;
 }
 
 hipError_t bwd_launch(const void *q, const void *k, const void *v, const void *g, const void *beta,
@@ -1883,6 +1826,15 @@ hipError_t bwd_launch(const void *q, const void *k, const void *v, const void *g
     p.wP = reinterpret_cast<float *>(w + 2 * a + b);
     p.wM = reinterpret_cast<float *>(w + 2 * a + 2 * b);
     p.wF = reinterpret_cast<int32_t *>(w + 2 * a + 3 * b);
+    {
+        const size_t f = (per * sizeof(int32_t) + 255) & ~(size_t)255;
+        const size_t x = (per * bwd::C * dv * sizeof(bf16_t) + 255) & ~(size_t)255;
+        char *wx = w + 2 * a + 3 * b + f;
+        p.wX = reinterpret_cast<bf16_t *>(wx);
+        p.wU = reinterpret_cast<bf16_t *>(wx + x);
+        p.wdU = reinterpret_cast<bf16_t *>(wx + 2 * x);
+        p.wdX = reinterpret_cast<bf16_t *>(wx + 3 * x);
+    }
     const long nslot = cu_seqlens ? (long)(T / bwd::C) + num_seqs + 1
                                   : (long)B * ((T + bwd::C - 1) / bwd::C);
     // with no chunk anywhere only the state-gradient chain runs (dS0 = dS_T)
