@@ -205,15 +205,26 @@ template <int NE> struct Seg<float, NE> {
     }
     __device__ __forceinline__ float get(int j) const { return ok ? w[j] : 0.0f; }
 };
-// one element, raw
-template <typename Tin> struct One {
+// one element, kept as raw bits until used (a conversion at load time would
+// make the compiler wait for the load right there)
+template <typename Tin> struct One;
+template <> struct One<float> {
     float w;
     bool ok;
     __device__ __forceinline__ void load(const void *base, size_t off, bool valid) {
         ok = valid;
-        w = ld<Tin>(base, valid ? off : 0);
+        w = static_cast<const float *>(base)[valid ? off : 0];
     }
     __device__ __forceinline__ float get() const { return ok ? w : 0.0f; }
+};
+template <> struct One<bf16_t> {
+    uint32_t w;
+    bool ok;
+    __device__ __forceinline__ void load(const void *base, size_t off, bool valid) {
+        ok = valid;
+        w = static_cast<const bf16_t *>(base)[valid ? off : 0].x;
+    }
+    __device__ __forceinline__ float get() const { return ok ? __uint_as_float(w << 16) : 0.0f; }
 };
 
 // The rows of one chunk that every kernel reads: k (and q) and the gate,
@@ -264,6 +275,29 @@ template <typename Tin, int DK, bool WITH_Q, int TPROW = 8> struct ChunkIn {
         if (tid < C) sB[tid] = b.get();
     }
 };
+
+// Buffer descriptor over the memory from `base` on (scalar registers; any
+// offset from 2^31 on is out of bounds: its stores are dropped).  The chains
+// store through these with per-lane offsets fixed for the whole sequence and
+// data kept in registers of their own until the next chunk: a store whose
+// address or data register is rewritten while it is pending makes the
+// compiler wait for the store to complete first.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t brsrc(const void *base) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    void *u = reinterpret_cast<void *>(((uint64_t)hi << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(u, 0, 0x7ffffff0, 0x00020000);
+}
+constexpr uint32_t kDrop = 0x80000000u;   // out-of-bounds offset: the store is dropped
+__device__ __forceinline__ void bst16(uint32_t v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+    __builtin_amdgcn_raw_buffer_store_b16((unsigned short)v, r, off, 0, 0);
+}
+// a value the compiler may neither recompute nor share: pinned in a register
+template <typename T> __device__ __forceinline__ T pinned(T x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
 
 // One 16 x 16 tile of a (d_k x d_v) fp32 state from global memory (or zeros),
 // as this lane's four accumulator rows.
@@ -1096,10 +1130,13 @@ __device__ __forceinline__ void store_t(__bf16 *dst, int pitch, int tm, int tn, 
 // Raw k and q sit in LDS so that the scaling step can run one thread per key
 // channel: its row-major outputs are then contiguous across lanes and its
 // transposed ones are one vector store per thread, with no bank conflicts.
+// Each chunk takes four barriers: the next chunk's inputs go to LDS in the
+// same step as the state update, and its scaling (running gate sums
+// included) in the same step as the state's store.
 constexpr int W2 = 64;                 // d_v columns per chain workgroup
 template <int DK, bool GRAD> struct ChainLayout {
     static constexpr int DKP = DK + 1, DKB = DK + 8, CB = C + 8, W2P = W2 + 1;
-    static constexpr int G = 0;                            // fp32 [C][DKP]
+    static constexpr int G = 0;                            // fp32 [C][DKP]: log2 gates
     static constexpr int KRAW = G + 4 * C * DKP;           // bf16 [C][DKB]
     static constexpr int QRAW = KRAW + 2 * C * DKB;        // bf16 [C][DKB] (gradient chain)
     static constexpr int XT = QRAW + (GRAD ? 2 * C * DKB : 0);   // bf16 [W2][DKB]: S^T / D^T
@@ -1108,47 +1145,68 @@ template <int DK, bool GRAD> struct ChainLayout {
     static constexpr int KT2 = KT1 + 2 * DK * CB;          // bf16 [DK][CB]: K_up^T (gradient chain)
     static constexpr int M1 = KT2 + (GRAD ? 2 * DK * CB : 0);    // bf16 [C][CB]: T / T^T
     static constexpr int M2 = M1 + 2 * C * CB;             // bf16 [C][CB]: P^T (gradient chain)
-    static constexpr int Y1 = M2 + (GRAD ? 2 * C * CB : 0);      // bf16 [W2][CB]: (beta X)^T / dO^T
-    static constexpr int Y2 = Y1 + 2 * W2 * CB;            // bf16 [W2][CB]: U^T / dU^T
+    static constexpr int Y1 = M2 + (GRAD ? 2 * C * CB : 0);      // bf16 [W2][CB]: (beta X)^T / dO^T x 2
+    static constexpr int Y2 = Y1 + (GRAD ? 4 : 2) * W2 * CB;     // bf16 [W2][CB]: U^T / dU^T
     static constexpr int Y3 = Y2 + 2 * W2 * CB;            // bf16 [W2][CB]: (-dX)^T (gradient chain)
-    static constexpr int V = Y3 + (GRAD ? 2 * W2 * CB : 0);      // fp32 [C][W2P]: V (state chain)
-    static constexpr int GC = V + (GRAD ? 0 : 4 * C * W2P);       // fp32 [DK]
+    static constexpr int V = Y3 + (GRAD ? 2 * W2 * CB : 0);      // fp32 [C][W2P] x 2: V (state chain)
+    static constexpr int GC = V + (GRAD ? 0 : 8 * C * W2P);       // fp32 [DK]
     static constexpr int GAM = GC + 4 * DK;
     static constexpr int SB = GAM + 4 * DK;                // fp32 [C]
     static constexpr int BYTES = SB + 4 * C;
 };
 
-// K_up = k 2^G and K_right = k 2^{G_c - G} (state chain: K_up row-major,
-// K_right transposed), or K_right row-major and Q_up, K_up transposed
-// (gradient chain).  Thread (channel c, block of RPT rows).
+// Running log2-gate sums G (inclusive) and K_up = k 2^G, K_right = k 2^{G_c - G}
+// (state chain: K_up row-major, K_right transposed), or K_right row-major and
+// Q_up, K_up transposed (gradient chain); gc = G_c and gamma = 2^G_c.
+// Thread (channel c, block of RPT rows) reads its channel's 32 raw log2 gates
+// itself, so no separate pass over the gates is needed.
 template <int DK, bool GRAD>
 __device__ __forceinline__ void chain_scale(const float *sG, const __bf16 *kraw, const __bf16 *qraw,
-                                            const float *gc, __bf16 *rowA, __bf16 *trA, __bf16 *trB) {
+                                            float *gc, float *gam, __bf16 *rowA, __bf16 *trA,
+                                            __bf16 *trB) {
     constexpr int DKP = DK + 1, DKB = DK + 8, CB = C + 8, RPT = C * DK / NT2;
     const int c = threadIdx.x % DK, r0 = (threadIdx.x / DK) * RPT;
+    float g[C];
+#pragma unroll
+    for (int r = 0; r < C; ++r) g[r] = sG[r * DKP + c];
+    float tot = 0.0f;
+#pragma unroll
+    for (int r = 0; r < C; ++r) {
+        tot += g[r];
+        g[r] = tot;                              // inclusive running sum
+    }
+    if (r0 == 0) {
+        gc[c] = tot;
+        gam[c] = __builtin_amdgcn_exp2f(tot);
+    }
     bf16x8 ta[RPT / 8 > 0 ? RPT / 8 : 1], tb[RPT / 8 > 0 ? RPT / 8 : 1];
     bf16x4 ua, ub;
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
         const int r = r0 + i;
-        const float G = sG[r * DKP + c], kv = (float)kraw[r * DKB + c];
-        const float E = __builtin_amdgcn_exp2f(G), R = __builtin_amdgcn_exp2f(gc[c] - G);
-        __bf16 a, b;
+        // g[r0 + i] with r0 uniform per wave: select by the row block
+        float G = 0.0f;
+#pragma unroll
+        for (int b = 0; b < C / RPT; ++b)
+            if (r0 == b * RPT) G = g[b * RPT + i];
+        const float kv = (float)kraw[r * DKB + c];
+        const float E = __builtin_amdgcn_exp2f(G), R = __builtin_amdgcn_exp2f(tot - G);
+        __bf16 a, bb;
         if constexpr (GRAD) {
             rowA[r * DKB + c] = (__bf16)(kv * R);
             a = (__bf16)((float)qraw[r * DKB + c] * E);
-            b = (__bf16)(kv * E);
+            bb = (__bf16)(kv * E);
         } else {
             rowA[r * DKB + c] = (__bf16)(kv * E);
             a = (__bf16)(kv * R);
-            b = a;
+            bb = a;
         }
         if constexpr (RPT >= 8) {
             ta[i >> 3][i & 7] = a;
-            tb[i >> 3][i & 7] = b;
+            tb[i >> 3][i & 7] = bb;
         } else {
             ua[i] = a;
-            ub[i] = b;
+            ub[i] = bb;
         }
     }
     if constexpr (RPT >= 8) {
@@ -1184,6 +1242,22 @@ __device__ __forceinline__ void chain_store_in(const Params &p, const ChunkIn<bf
     in.store_gb(p, sG, sB);
 }
 
+// (sequence-head unit, d_v slice) of a chain workgroup.  With two slices per
+// unit and a multiple of 8 units, the slices of a unit are numbered 8 apart:
+// workgroups b and b + 8 run on the same XCD, so the second read of the
+// chunk's shared inputs (k, q, gates, T, P) is served from that XCD's L2.
+__device__ __forceinline__ void chain_unit(const Params &p, int b, int &unit, int &slice) {
+    const int nsl = p.DV / W2;
+    const long units = (long)p.num_seqs * p.H;
+    if (nsl == 2 && units % 8 == 0) {
+        unit = (b >> 4) * 8 + (b & 7);
+        slice = (b >> 3) & 1;
+    } else {
+        unit = b / nsl;
+        slice = b % nsl;
+    }
+}
+
 template <int DK>
 __global__ void __launch_bounds__(NT2) bwd_states_bf16_kernel(Params p) {
     using L = ChainLayout<DK, false>;
@@ -1197,12 +1271,12 @@ __global__ void __launch_bounds__(NT2) bwd_states_bf16_kernel(Params p) {
     __bf16 *Tb = reinterpret_cast<__bf16 *>(smem + L::M1);
     __bf16 *BXt = reinterpret_cast<__bf16 *>(smem + L::Y1);
     __bf16 *Ut = reinterpret_cast<__bf16 *>(smem + L::Y2);
-    float *sV = reinterpret_cast<float *>(smem + L::V);
+    float *sV0 = reinterpret_cast<float *>(smem + L::V);       // V of even / odd chunks
     float *gc = reinterpret_cast<float *>(smem + L::GC);
     float *gam = reinterpret_cast<float *>(smem + L::GAM);
     float *sB = reinterpret_cast<float *>(smem + L::SB);
-    const int nsl = p.DV / W2;
-    const int unit = blockIdx.x / nsl, slice = blockIdx.x % nsl;
+    int unit, slice;
+    chain_unit(p, blockIdx.x, unit, slice);
     const int s = unit / p.H, h = unit % p.H, col0 = slice * W2;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, lj = lane >> 4;
     const int vr = tid >> 4, vc = (tid & 15) * 4;            // C x W2 values of this thread
@@ -1221,27 +1295,10 @@ __global__ void __launch_bounds__(NT2) bwd_states_bf16_kernel(Params p) {
         vin.load(p.v, ((size_t)(t0 + vr) * p.H + h) * p.DV + col0 + vc, vr < cl);
         tin.load(p.wT, ((size_t)(base + n) * p.H + h) * C * C + t4, tid < 256);
     };
-    if (nch > 0) issue(0);
-    // state tiles: index w * NTW + x -> (tm, tn) over (DK/16) x (W2/16)
-    f32x4 S[NTW];
-#pragma unroll
-    for (int x = 0; x < NTW; ++x) {
-        const int tt = wave * NTW + x, tm = tt >> 2, tn = tt & 3;
-        load_tile(S[x], p.S0, ((size_t)s * p.H + h) * DK + 16 * tm, p.DV, col0 + 16 * tn);
-    }
-    const int xm = wave >> 2, xn = wave & 3;                 // this wave's C x W2 tile
-    for (int n = 0; n < nch; ++n) {
-        const size_t wi = (size_t)(base + n) * p.H + h;
-        bf16_t *gS = reinterpret_cast<bf16_t *>(p.wS) + wi * DK * p.DV;
-#pragma unroll
-        for (int x = 0; x < NTW; ++x) {
-            const int tt = wave * NTW + x, tm = tt >> 2, tn = tt & 3;
-            store_t(St, DKB, tm, tn, S[x]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                gS[(size_t)(16 * tm + 4 * lj + i) * p.DV + col0 + 16 * tn + lr] = to_bf16(S[x][i]);
-        }
+    // chunk n's inputs into LDS (V into the buffer of n's parity)
+    auto stage = [&](int n) {
         chain_store_in<DK, false>(p, in, kraw, nullptr, sG, sB);
+        float *sV = sV0 + (n & 1) * C * W2P;
 #pragma unroll
         for (int j = 0; j < 4; ++j) sV[vr * W2P + vc + j] = vin.get(j);
         if (tid < 256) {
@@ -1250,22 +1307,76 @@ __global__ void __launch_bounds__(NT2) bwd_states_bf16_kernel(Params p) {
             for (int j = 0; j < 4; ++j) tv[j] = (__bf16)tin.get(j);
             *reinterpret_cast<bf16x4 *>(Tb + (t4 / C) * CB + t4 % C) = tv;
         }
-        if (n + 1 < nch) issue(n + 1);
+    };
+    f32x4 S[NTW];
+#pragma unroll
+    for (int x = 0; x < NTW; ++x) {
+        const int tt = wave * NTW + x, tm = tt >> 2, tn = tt & 3;
+        load_tile(S[x], p.S0, ((size_t)s * p.H + h) * DK + 16 * tm, p.DV, col0 + 16 * tn);
+        // the initial state has landed before the loop (otherwise the wait for
+        // it would sit inside the loop, draining the memory queue every chunk)
+        S[x] = pinned(S[x]);
+    }
+    // per-lane byte offsets of this lane's tile elements (fixed for the sequence)
+    uint32_t oS[NTW][4], oX[4];
+#pragma unroll
+    for (int x = 0; x < NTW; ++x) {
+        const int tt = wave * NTW + x, tm = tt >> 2, tn = tt & 3;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            oS[x][i] = pinned((uint32_t)(((16 * tm + 4 * lj + i) * p.DV + 16 * tn + lr) * 2));
+    }
+    const int xm = wave >> 2, xn = wave & 3;                 // this wave's C x W2 tile
+#pragma unroll
+    for (int i = 0; i < 4; ++i) oX[i] = pinned((uint32_t)(((16 * xm + 4 * lj + i) * p.DV + 16 * xn + lr) * 2));
+    uint32_t dS[NTW][4], dX[4], dU[4];                       // stored values, kept until the next chunk
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        dX[i] = 0u;
+        dU[i] = 0u;
+#pragma unroll
+        for (int x = 0; x < NTW; ++x) dS[x][i] = 0u;
+    }
+    // the state entering chunk n: to S^T in LDS and to the workspace
+    auto put_state = [&](int n) {
+        const __amdgpu_buffer_rsrc_t r =
+            brsrc(reinterpret_cast<bf16_t *>(p.wS) + ((size_t)(base + n) * p.H + h) * DK * p.DV + col0);
+#pragma unroll
+        for (int x = 0; x < NTW; ++x) {
+            const int tt = wave * NTW + x, tm = tt >> 2, tn = tt & 3;
+            store_t(St, DKB, tm, tn, S[x]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                asm volatile("" ::"v"(dS[x][i]));
+                dS[x][i] = to_bf16(S[x][i]).x;
+                bst16(dS[x][i], r, oS[x][i]);
+            }
+        }
+    };
+    if (nch > 0) {
+        issue(0);
+        stage(0);
+        if (nch > 1) issue(1);
         __syncthreads();
-        gate_sums<DK>(sG, gc, gam);
+        put_state(0);
+        chain_scale<DK, false>(sG, kraw, nullptr, gc, gam, Kub, Krt, nullptr);
         __syncthreads();
-        chain_scale<DK, false>(sG, kraw, nullptr, gc, Kub, Krt, nullptr);
-        __syncthreads();
+    }
+    for (int n = 0; n < nch; ++n) {
+        const size_t wi = (size_t)(base + n) * p.H + h;
+        const float *sV = sV0 + (n & 1) * C * W2P;
         // (beta X)^T, X = V - K_up S
         {
             f32x4 a = {0.f, 0.f, 0.f, 0.f};
             a = mmb(a, Kub + 16 * xm * DKB, DKB, St + 16 * xn * DKB, DKB, DK);
-            bf16_t *gX = p.wX + wi * C * p.DV + col0 + 16 * xn + lr;
+            const __amdgpu_buffer_rsrc_t r = brsrc(p.wX + wi * C * p.DV + col0);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int row = 16 * xm + 4 * lj + i;
                 const float x = sV[row * W2P + 16 * xn + lr] - a[i];
-                gX[(size_t)row * p.DV] = to_bf16(x);          // X, for the gradient kernel
+                asm volatile("" ::"v"(dX[i]));
+                dX[i] = to_bf16(x).x;
+                bst16(dX[i], r, oX[i]);                       // X, for the gradient kernel
                 a[i] = sB[row] * x;
             }
             store_t(BXt, CB, xm, xn, a);
@@ -1276,18 +1387,31 @@ __global__ void __launch_bounds__(NT2) bwd_states_bf16_kernel(Params p) {
             f32x4 a = {0.f, 0.f, 0.f, 0.f};
             a = mmb(a, Tb + 16 * xm * CB, CB, BXt + 16 * xn * CB, CB, C);
             store_t(Ut, CB, xm, xn, a);
-            bf16_t *gU = p.wU + wi * C * p.DV + col0 + 16 * xn + lr;
+            const __amdgpu_buffer_rsrc_t r = brsrc(p.wU + wi * C * p.DV + col0);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) gU[(size_t)(16 * xm + 4 * lj + i) * p.DV] = to_bf16(a[i]);
+            for (int i = 0; i < 4; ++i) {
+                asm volatile("" ::"v"(dU[i]));
+                dU[i] = to_bf16(a[i]).x;
+                bst16(dU[i], r, oX[i]);
+            }
         }
         __syncthreads();
-        // S = Diag(gamma) S + K_right^T U
+        // S = Diag(gamma) S + K_right^T U; the next chunk's inputs to LDS meanwhile
 #pragma unroll
         for (int x = 0; x < NTW; ++x) {
             const int tt = wave * NTW + x, tm = tt >> 2, tn = tt & 3;
 #pragma unroll
             for (int i = 0; i < 4; ++i) S[x][i] *= gam[16 * tm + 4 * lj + i];
             S[x] = mmb(S[x], Krt + 16 * tm * CB, CB, Ut + 16 * tn * CB, CB, C);
+        }
+        if (n + 1 < nch) {
+            stage(n + 1);
+            if (n + 2 < nch) issue(n + 2);
+        }
+        __syncthreads();
+        if (n + 1 < nch) {
+            put_state(n + 1);
+            chain_scale<DK, false>(sG, kraw, nullptr, gc, gam, Kub, Krt, nullptr);
         }
         __syncthreads();
     }
@@ -1307,14 +1431,14 @@ __global__ void __launch_bounds__(NT2) bwd_dstates_bf16_kernel(Params p) {
     __bf16 *Kt = reinterpret_cast<__bf16 *>(smem + L::KT2);
     __bf16 *TT = reinterpret_cast<__bf16 *>(smem + L::M1);
     __bf16 *PT = reinterpret_cast<__bf16 *>(smem + L::M2);
-    __bf16 *dOt = reinterpret_cast<__bf16 *>(smem + L::Y1);
+    __bf16 *dOt0 = reinterpret_cast<__bf16 *>(smem + L::Y1);   // dO^T of even / odd chunks
     __bf16 *dUt = reinterpret_cast<__bf16 *>(smem + L::Y2);
     __bf16 *mdXt = reinterpret_cast<__bf16 *>(smem + L::Y3);
     float *gc = reinterpret_cast<float *>(smem + L::GC);
     float *gam = reinterpret_cast<float *>(smem + L::GAM);
     float *sB = reinterpret_cast<float *>(smem + L::SB);
-    const int nsl = p.DV / W2;
-    const int unit = blockIdx.x / nsl, slice = blockIdx.x % nsl;
+    int unit, slice;
+    chain_unit(p, blockIdx.x, unit, slice);
     const int s = unit / p.H, h = unit % p.H, col0 = slice * W2;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, lj = lane >> 4;
     // dO^T: thread (column oc, rows 4 ob .. 4 ob + 3); T^T, P^T: thread (column
@@ -1344,54 +1468,92 @@ __global__ void __launch_bounds__(NT2) bwd_dstates_bf16_kernel(Params p) {
             pin[i].load(p.wP, wi * C * C + (2 * tb + i) * C + ti, true);
         }
     };
-    if (nch > 0) issue(nch - 1);
+    // chunk n's inputs into LDS (dO^T into the buffer of n's parity)
+    auto stage = [&](int n) {
+        chain_store_in<DK, true>(p, in, kraw, qraw, sG, sB);
+        bf16x4 ov;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ov[i] = (__bf16)oin[i].get();
+        *reinterpret_cast<bf16x4 *>(dOt0 + (n & 1) * W2 * CB + oc * CB + 4 * ob) = ov;
+        bf16x2 tv, pv;
+        tv[0] = (__bf16)tin[0].get();
+        tv[1] = (__bf16)tin[1].get();
+        pv[0] = (__bf16)pin[0].get();
+        pv[1] = (__bf16)pin[1].get();
+        *reinterpret_cast<bf16x2 *>(TT + ti * CB + 2 * tb) = tv;
+        *reinterpret_cast<bf16x2 *>(PT + ti * CB + 2 * tb) = pv;
+    };
     f32x4 D[NTW];
 #pragma unroll
     for (int x = 0; x < NTW; ++x) {
         const int tt = wave * NTW + x, tm = tt >> 2, tn = tt & 3;
         load_tile(D[x], p.dST, so + 16 * tm, p.DV, col0 + 16 * tn);
+        D[x] = pinned(D[x]);                        // landed before the loop (see the state chain)
+    }
+    // per-lane byte offsets of this lane's tile elements (fixed for the sequence)
+    uint32_t oD[NTW][4], oX[4], oV[4];
+#pragma unroll
+    for (int x = 0; x < NTW; ++x) {
+        const int tt = wave * NTW + x, tm = tt >> 2, tn = tt & 3;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            oD[x][i] = pinned((uint32_t)(((16 * tm + 4 * lj + i) * p.DV + 16 * tn + lr) * 2));
     }
     const int xm = wave >> 2, xn = wave & 3;
-    for (int n = nch - 1; n >= 0; --n) {
-        const size_t wi = (size_t)(base + n) * p.H + h;
-        bf16_t *gD = reinterpret_cast<bf16_t *>(p.wD) + wi * DK * p.DV;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        oX[i] = pinned((uint32_t)(((16 * xm + 4 * lj + i) * p.DV + 16 * xn + lr) * 2));
+        oV[i] = pinned((uint32_t)(((16 * xm + 4 * lj + i) * p.H * p.DV + 16 * xn + lr) * 2));
+    }
+    uint32_t dD[NTW][4], dUv[4], dXv[4];                      // stored values, kept until the next chunk
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        dUv[i] = 0u;
+        dXv[i] = 0u;
+#pragma unroll
+        for (int x = 0; x < NTW; ++x) dD[x][i] = 0u;
+    }
+    // D, the gradient of the state leaving chunk n: to D^T in LDS and to the workspace
+    auto put_grad = [&](int n) {
+        const __amdgpu_buffer_rsrc_t r =
+            brsrc(reinterpret_cast<bf16_t *>(p.wD) + ((size_t)(base + n) * p.H + h) * DK * p.DV + col0);
 #pragma unroll
         for (int x = 0; x < NTW; ++x) {
             const int tt = wave * NTW + x, tm = tt >> 2, tn = tt & 3;
             store_t(Dt, DKB, tm, tn, D[x]);
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                gD[(size_t)(16 * tm + 4 * lj + i) * p.DV + col0 + 16 * tn + lr] = to_bf16(D[x][i]);
+            for (int i = 0; i < 4; ++i) {
+                asm volatile("" ::"v"(dD[x][i]));
+                dD[x][i] = to_bf16(D[x][i]).x;
+                bst16(dD[x][i], r, oD[x][i]);
+            }
         }
-        chain_store_in<DK, true>(p, in, kraw, qraw, sG, sB);
-        {
-            bf16x4 ov;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) ov[i] = (__bf16)oin[i].get();
-            *reinterpret_cast<bf16x4 *>(dOt + oc * CB + 4 * ob) = ov;
-            bf16x2 tv, pv;
-            tv[0] = (__bf16)tin[0].get();
-            tv[1] = (__bf16)tin[1].get();
-            pv[0] = (__bf16)pin[0].get();
-            pv[1] = (__bf16)pin[1].get();
-            *reinterpret_cast<bf16x2 *>(TT + ti * CB + 2 * tb) = tv;
-            *reinterpret_cast<bf16x2 *>(PT + ti * CB + 2 * tb) = pv;
-        }
-        if (n > 0) issue(n - 1);
+    };
+    if (nch > 0) {
+        issue(nch - 1);
+        stage(nch - 1);
+        if (nch > 1) issue(nch - 2);
         __syncthreads();
-        gate_sums<DK>(sG, gc, gam);
+        put_grad(nch - 1);
+        chain_scale<DK, true>(sG, kraw, qraw, gc, gam, Krb, Qt, Kt);
         __syncthreads();
-        chain_scale<DK, true>(sG, kraw, qraw, gc, Krb, Qt, Kt);
-        __syncthreads();
+    }
+    for (int n = nch - 1; n >= 0; --n) {
+        const size_t wi = (size_t)(base + n) * p.H + h;
+        const __bf16 *dOt = dOt0 + (n & 1) * W2 * CB;
         // dU^T, dU = P^T dO + K_right D
         {
             f32x4 a = {0.f, 0.f, 0.f, 0.f};
             a = mmb(a, PT + 16 * xm * CB, CB, dOt + 16 * xn * CB, CB, C);
             a = mmb(a, Krb + 16 * xm * DKB, DKB, Dt + 16 * xn * DKB, DKB, DK);
             store_t(dUt, CB, xm, xn, a);
-            bf16_t *gdU = p.wdU + wi * C * p.DV + col0 + 16 * xn + lr;
+            const __amdgpu_buffer_rsrc_t r = brsrc(p.wdU + wi * C * p.DV + col0);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) gdU[(size_t)(16 * xm + 4 * lj + i) * p.DV] = to_bf16(a[i]);
+            for (int i = 0; i < 4; ++i) {
+                asm volatile("" ::"v"(dUv[i]));
+                dUv[i] = to_bf16(a[i]).x;
+                bst16(dUv[i], r, oX[i]);
+            }
         }
         __syncthreads();
         // (-dX)^T, dX = Diag(beta) T^T dU
@@ -1401,20 +1563,23 @@ __global__ void __launch_bounds__(NT2) bwd_dstates_bf16_kernel(Params p) {
             // dX (= dV): to the workspace for the gradient kernel, and to dv
             const long t0 = t0s + (long)n * C;
             const int cl = len - n * C < C ? len - n * C : C;
-            bf16_t *gdX = p.wdX + wi * C * p.DV + col0 + 16 * xn + lr;
-            bf16_t *gdv = static_cast<bf16_t *>(p.dv) + col0 + 16 * xn + lr;
+            const __amdgpu_buffer_rsrc_t rx = brsrc(p.wdX + wi * C * p.DV + col0);
+            const __amdgpu_buffer_rsrc_t rv =
+                brsrc(static_cast<bf16_t *>(p.dv) + ((size_t)t0 * p.H + h) * p.DV + col0);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int row = 16 * xm + 4 * lj + i;
                 const float dx = sB[row] * a[i];
-                gdX[(size_t)row * p.DV] = to_bf16(dx);
-                if (row < cl) gdv[((size_t)(t0 + row) * p.H + h) * p.DV] = to_bf16(dx);
+                asm volatile("" ::"v"(dXv[i]));
+                dXv[i] = to_bf16(dx).x;
+                bst16(dXv[i], rx, oX[i]);
+                bst16(dXv[i], rv, row < cl ? oV[i] : kDrop);
                 a[i] = -dx;
             }
             store_t(mdXt, CB, xm, xn, a);
         }
         __syncthreads();
-        // D = Diag(gamma) D + Q_up^T dO - K_up^T dX
+        // D = Diag(gamma) D + Q_up^T dO - K_up^T dX; the next chunk's inputs to LDS meanwhile
 #pragma unroll
         for (int x = 0; x < NTW; ++x) {
             const int tt = wave * NTW + x, tm = tt >> 2, tn = tt & 3;
@@ -1422,6 +1587,15 @@ __global__ void __launch_bounds__(NT2) bwd_dstates_bf16_kernel(Params p) {
             for (int i = 0; i < 4; ++i) D[x][i] *= gam[16 * tm + 4 * lj + i];
             D[x] = mmb(D[x], Qt + 16 * tm * CB, CB, dOt + 16 * tn * CB, CB, C);
             D[x] = mmb(D[x], Kt + 16 * tm * CB, CB, mdXt + 16 * tn * CB, CB, C);
+        }
+        if (n > 0) {
+            stage(n - 1);
+            if (n > 1) issue(n - 2);
+        }
+        __syncthreads();
+        if (n > 0) {
+            put_grad(n - 1);
+            chain_scale<DK, true>(sG, kraw, qraw, gc, gam, Krb, Qt, Kt);
         }
         __syncthreads();
     }
@@ -1566,28 +1740,31 @@ __global__ void __launch_bounds__(NT2) bwd_grads_bf16_kernel(Params p) {
     // waves 0-3: the dT' tiles; waves 4-7: the dP tiles (tile (tm, tn) of C x C)
     const int tm = (wave & 3) >> 1, tn = wave & 1;
     const bool lo = wave < 4;
-    auto put = [](__bf16 *dst, const auto &seg, int n) {
-        // raw bf16 bits of a segment, as one vector store of n values
-        if (n == 16) {
+    auto put = [](__bf16 *dst, const auto &seg, auto count) {
+        // raw bf16 bits of a segment, as vector stores
+        constexpr int n = decltype(count)::value;
+        if constexpr (n == 16) {
             reinterpret_cast<uint4 *>(dst)[0] = make_uint4(seg.w[0], seg.w[1], seg.w[2], seg.w[3]);
             reinterpret_cast<uint4 *>(dst)[1] = make_uint4(seg.w[4], seg.w[5], seg.w[6], seg.w[7]);
-        } else if (n == 8) {
+        } else if constexpr (n == 8) {
             reinterpret_cast<uint4 *>(dst)[0] = make_uint4(seg.w[0], seg.w[1], seg.w[2], seg.w[3]);
         } else {
             reinterpret_cast<uint2 *>(dst)[0] = make_uint2(seg.w[0], seg.w[1]);
         }
     };
+    using n4 = std::integral_constant<int, 4>;
+    using nes = std::integral_constant<int, NES>;
     for (int col0 = 0; col0 < p.DV; col0 += W3) {
         __syncthreads();
 #pragma unroll
         for (int j = 0; j < NES; ++j) dgacc += sin.get(j) * din.get(j);
-        put(Sr + sr * WB + sc, sin, NES);
-        put(Dr + sr * WB + sc, din, NES);
-        put(Xr + vr * WB + vc, xin, 4);
-        put(Ur + vr * WB + vc, uin, 4);
-        put(dUr + vr * WB + vc, duin, 4);
-        put(dXr + vr * WB + vc, dxin, 4);
-        if (oin.ok) put(dOr + vr * WB + vc, oin, 4);
+        put(Sr + sr * WB + sc, sin, nes{});
+        put(Dr + sr * WB + sc, din, nes{});
+        put(Xr + vr * WB + vc, xin, n4{});
+        put(Ur + vr * WB + vc, uin, n4{});
+        put(dUr + vr * WB + vc, duin, n4{});
+        put(dXr + vr * WB + vc, dxin, n4{});
+        if (oin.ok) put(dOr + vr * WB + vc, oin, n4{});
         else *reinterpret_cast<uint2 *>(dOr + vr * WB + vc) = make_uint2(0u, 0u);
         if (col0 + W3 < p.DV) issue_slice(col0 + W3);
         __syncthreads();
