@@ -1622,12 +1622,12 @@ __global__ void __launch_bounds__(NT2) bwd_dstates_bf16_kernel(Params p) {
 // product left contracts over d_v, which is contiguous in every operand: the
 // slices go to LDS row-major as they come, with no transposed copies.
 constexpr int W3 = 64;                 // d_v columns per slice of the gradient kernel
+// LDS of the bf16 gradient kernel, at most 80 KB so that two 512-thread
+// workgroups share a CU (one loads while the other runs its C x C algebra).
 template <int DK> struct GbLayout {
     static constexpr int DKP = DK + 1, WB = W3 + 8;
     static constexpr int G = 0;                                   // fp32 [C][DKP]
-    static constexpr int T = G + 4 * C * DKP;                     // fp32 [C][CP]
-    static constexpr int M = T + 4 * C * CP;
-    static constexpr int GC = M + 4 * C * CP;                     // fp32 [DK] x 3
+    static constexpr int GC = G + 4 * C * DKP;                    // fp32 [DK] x 3
     static constexpr int GAM = GC + 4 * DK;
     static constexpr int DGP = GAM + 4 * DK;
     static constexpr int RKP = DGP + 4 * DK;                      // fp32 [2][DK]
@@ -1643,28 +1643,34 @@ template <int DK> struct GbLayout {
     static constexpr int DXR = DUR + 2 * C * WB;
     static constexpr int DOR = DXR + 2 * C * WB;
     static constexpr int SLICE_END = DOR + 2 * C * WB;
-    // after the slices (in the area)
-    static constexpr int DTF = AREA;                              // fp32 [C][CP] x 4
-    static constexpr int DPF = DTF + 4 * C * CP;
-    static constexpr int YF = DPF + 4 * C * CP;
-    static constexpr int DAF = YF + 4 * C * CP;
-    static constexpr int FK = DAF + 4 * C * CP;                   // fp32 [C][DKP] x 3
+    // after the slices (in the area): M (then beta dA), dP and dA live to the
+    // end; T, dT' and Y only through the C x C algebra, then K_up, Q_up, K_dn
+    // take their place
+    static constexpr int MF = AREA;                               // fp32 [C][CP] x 6
+    static constexpr int DPF = MF + 4 * C * CP;
+    static constexpr int DAF = DPF + 4 * C * CP;
+    static constexpr int TF = DAF + 4 * C * CP;
+    static constexpr int DTF = TF + 4 * C * CP;
+    static constexpr int YF = DTF + 4 * C * CP;
+    static constexpr int FK = TF;                                 // fp32 [C][DKP] x 3
     static constexpr int FQ = FK + 4 * C * DKP;
     static constexpr int FKD = FQ + 4 * C * DKP;
     static constexpr int TAIL_END = FKD + 4 * C * DKP;
     static constexpr int BYTES = SLICE_END > TAIL_END ? SLICE_END : TAIL_END;
+    static_assert(YF + 4 * C * CP <= TAIL_END, "C x C buffers");
+    static_assert(BYTES <= 80 * 1024, "two workgroups per CU");
 };
 
 template <int DK>
-__global__ void __launch_bounds__(NT2) bwd_grads_bf16_kernel(Params p) {
+__global__ void __launch_bounds__(NT2, 4) bwd_grads_bf16_kernel(Params p) {
     using L = GbLayout<DK>;
     constexpr int DKP = L::DKP, WB = L::WB;
     constexpr int NTW = DK / 64, NE = DK / 16;      // 8 waves: 2 or 1 C x DK tiles each
     constexpr int NES = DK * W3 / NT2, TPR = W3 / NES;   // S / D slice values per thread
     __shared__ __attribute__((aligned(16))) unsigned char smem[L::BYTES];
     float *sG = reinterpret_cast<float *>(smem + L::G);
-    float *sT = reinterpret_cast<float *>(smem + L::T);
-    float *sM = reinterpret_cast<float *>(smem + L::M);
+    float *sT = reinterpret_cast<float *>(smem + L::TF);
+    float *sM = reinterpret_cast<float *>(smem + L::MF);
     float *gc = reinterpret_cast<float *>(smem + L::GC);
     float *gam = reinterpret_cast<float *>(smem + L::GAM);
     float *dgp = reinterpret_cast<float *>(smem + L::DGP);
@@ -1695,36 +1701,36 @@ __global__ void __launch_bounds__(NT2) bwd_grads_bf16_kernel(Params p) {
     const bf16_t *gD = reinterpret_cast<const bf16_t *>(p.wD) + wi * DK * p.DV;
     const size_t cx = wi * C * p.DV;
 
-    Seg<bf16_t, NES> sin, din;
-    Seg<bf16_t, 4> xin, uin, duin, dxin, oin;
-    auto issue_slice = [&](int col0) {
-        sin.load(gS, (size_t)sr * p.DV + col0 + sc, true);
-        din.load(gD, (size_t)sr * p.DV + col0 + sc, true);
-        const size_t w = cx + (size_t)vr * p.DV + col0 + vc;
-        xin.load(p.wX, w, true);
-        uin.load(p.wU, w, true);
-        duin.load(p.wdU, w, true);
-        dxin.load(p.wdX, w, true);
-        oin.load(p.dO, ((size_t)(t0 + vr) * p.H + h) * p.DV + col0 + vc, vr < cl);
+    // one d_v slice of S, D (d_k x W3) and X, U, dU, dX, dO (C x W3)
+    struct SliceIn {
+        Seg<bf16_t, NES> s, d;
+        Seg<bf16_t, 4> x, u, du, dx, o;
     };
-    {
-        ChunkIn<bf16_t, DK, false, 16> in;
-        Seg<float, 4> tin, min;
-        const int t4 = (tid & 255) * 4;
-        in.load(p, t0, cl, h);
-        tin.load(p.wT, wi * C * C + t4, vt);
-        min.load(p.wM, wi * C * C + t4, vt);
-        issue_slice(0);
-        in.store_gb(p, sG, sB);
-        if (vt) {
-            const int tr = t4 / C, tc = t4 % C;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                sT[tr * CP + tc + j] = tin.get(j);
-                sM[tr * CP + tc + j] = min.get(j);
-            }
-        }
-    }
+    auto issue_slice = [&](SliceIn &in, int col0) {
+        in.s.load(gS, (size_t)sr * p.DV + col0 + sc, true);
+        in.d.load(gD, (size_t)sr * p.DV + col0 + sc, true);
+        const size_t w = cx + (size_t)vr * p.DV + col0 + vc;
+        in.x.load(p.wX, w, true);
+        in.u.load(p.wU, w, true);
+        in.du.load(p.wdU, w, true);
+        in.dx.load(p.wdX, w, true);
+        in.o.load(p.dO, ((size_t)(t0 + vr) * p.H + h) * p.DV + col0 + vc, vr < cl);
+    };
+    // both slices (d_v = 2 W3) are in flight from the start; with d_v = W3
+    // the second repeats the first and is not used
+    SliceIn s0, s1;
+    // k and q stay in registers (this thread's row tid / 16, NE columns) until
+    // the decay-weighted sums after the C x C algebra
+    // as are T and M (first 256 threads, 4 values each), whose LDS the slices use
+    ChunkIn<bf16_t, DK, true, 16> in;
+    Seg<float, 4> tin, min;
+    const int t4 = (tid & 255) * 4;
+    in.load(p, t0, cl, h);
+    tin.load(p.wT, wi * C * C + t4, vt);
+    min.load(p.wM, wi * C * C + t4, vt);
+    issue_slice(s0, 0);
+    issue_slice(s1, p.DV > W3 ? W3 : 0);
+    in.store_gb(p, sG, sB);
     if (tid < C) dB[tid] = 0.0f;
     __syncthreads();
     gate_sums<DK>(sG, gc, gam);
@@ -1754,19 +1760,18 @@ __global__ void __launch_bounds__(NT2) bwd_grads_bf16_kernel(Params p) {
     };
     using n4 = std::integral_constant<int, 4>;
     using nes = std::integral_constant<int, NES>;
-    for (int col0 = 0; col0 < p.DV; col0 += W3) {
+    auto slice = [&](const SliceIn &in) {
         __syncthreads();
 #pragma unroll
-        for (int j = 0; j < NES; ++j) dgacc += sin.get(j) * din.get(j);
-        put(Sr + sr * WB + sc, sin, nes{});
-        put(Dr + sr * WB + sc, din, nes{});
-        put(Xr + vr * WB + vc, xin, n4{});
-        put(Ur + vr * WB + vc, uin, n4{});
-        put(dUr + vr * WB + vc, duin, n4{});
-        put(dXr + vr * WB + vc, dxin, n4{});
-        if (oin.ok) put(dOr + vr * WB + vc, oin, n4{});
+        for (int j = 0; j < NES; ++j) dgacc += in.s.get(j) * in.d.get(j);
+        put(Sr + sr * WB + sc, in.s, nes{});
+        put(Dr + sr * WB + sc, in.d, nes{});
+        put(Xr + vr * WB + vc, in.x, n4{});
+        put(Ur + vr * WB + vc, in.u, n4{});
+        put(dUr + vr * WB + vc, in.du, n4{});
+        put(dXr + vr * WB + vc, in.dx, n4{});
+        if (in.o.ok) put(dOr + vr * WB + vc, in.o, n4{});
         else *reinterpret_cast<uint2 *>(dOr + vr * WB + vc) = make_uint2(0u, 0u);
-        if (col0 + W3 < p.DV) issue_slice(col0 + W3);
         __syncthreads();
         // dT' += dU X^T (waves 0-3);  dP += dO U^T (waves 4-7);
         // dQ_up += dO S^T;  -dK_up += dX S^T;  dK_right += U D^T
@@ -1779,7 +1784,9 @@ __global__ void __launch_bounds__(NT2) bwd_grads_bf16_kernel(Params p) {
             aK[x] = mmb(aK[x], dXr + m0 * WB, WB, Sr + n0 * WB, WB, W3);
             aR[x] = mmb(aR[x], Ur + m0 * WB, WB, Dr + n0 * WB, WB, W3);
         }
-    }
+    };
+    slice(s0);
+    if (p.DV > W3) slice(s1);
     // dgamma per channel: the S * D sums of the TPR threads of a row
 #pragma unroll
     for (int off = 1; off < TPR; off <<= 1) dgacc += __shfl_xor(dgacc, off);
@@ -1789,6 +1796,14 @@ __global__ void __launch_bounds__(NT2) bwd_grads_bf16_kernel(Params p) {
     // C x C algebra (fp32)
     float *sdT = reinterpret_cast<float *>(smem + L::DTF), *sdP = reinterpret_cast<float *>(smem + L::DPF);
     float *sY = reinterpret_cast<float *>(smem + L::YF), *sdA = reinterpret_cast<float *>(smem + L::DAF);
+    if (vt) {
+        const int tr = t4 / C, tc = t4 % C;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            sT[tr * CP + tc + j] = tin.get(j);
+            sM[tr * CP + tc + j] = min.get(j);
+        }
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int row = 16 * tm + 4 * lj + i, col = 16 * tn + lr;
@@ -1836,22 +1851,18 @@ __global__ void __launch_bounds__(NT2) bwd_grads_bf16_kernel(Params p) {
         }
         dB[r] += acc;
     }
-    // fp32 K_up, Q_up, K_dn for the decay-weighted sums (raw k and q again)
+    // fp32 K_up, Q_up, K_dn for the decay-weighted sums
     float *fK = reinterpret_cast<float *>(smem + L::FK), *fQ = reinterpret_cast<float *>(smem + L::FQ);
     float *fKd = reinterpret_cast<float *>(smem + L::FKD);
     {
         const int r = tid >> 4, c0 = (tid & 15) * NE;
-        Seg<bf16_t, NE> kin, qin;
-        const size_t e = ((size_t)(t0 + r) * p.H + h) * DK + c0;
-        kin.load(p.k, e, r < cl);
-        qin.load(p.q, e, r < cl);
 #pragma unroll
         for (int j = 0; j < NE; ++j) {
             const int o = r * DKP + c0 + j;
             const float G = sG[o], E = __builtin_amdgcn_exp2f(G), Ei = __builtin_amdgcn_exp2f(-G);
-            fK[o] = kin.get(j) * E;
-            fQ[o] = qin.get(j) * E;
-            fKd[o] = kin.get(j) * Ei;
+            fK[o] = in.k.get(j) * E;
+            fQ[o] = in.q.get(j) * E;
+            fKd[o] = in.k.get(j) * Ei;
         }
     }
     __syncthreads();
