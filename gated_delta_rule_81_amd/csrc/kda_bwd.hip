@@ -56,7 +56,8 @@ struct Params {
     void *dq, *dk, *dv, *dg, *dbeta;
     float *dS0;
     float *wS, *wD, *wT, *wP, *wM;   // workspace, per (chunk slot, head)
-    bf16_t *wX, *wU, *wdU, *wdX;      // bf16 inputs: X, U, dU, dX of each chunk (C x d_v)
+    bf16_t *wX, *wU, *wdU;            // bf16 inputs: X, U, dU of each chunk (C x d_v); dX is dv
+    bf16_t *wTb, *wTt, *wPt;          // bf16 inputs: T, T^T and P^T (C x C) for the state chains
     int32_t *wF;                     // per (chunk slot, head): 1 = exact path
 };
 
@@ -457,11 +458,14 @@ __global__ void __launch_bounds__(NT) bwd_prep_kernel(Params p) {
         }
     }
     __syncthreads();
+    constexpr bool kBf16 = std::is_same<Tin, bf16_t>::value;
     float *gT = p.wT + wi * C * C, *gP = p.wP + wi * C * C, *gM = p.wM + wi * C * C;
     {
         const int r = (tid * 4) / C, i = (tid * 4) % C;
-        *reinterpret_cast<float4 *>(gP + tid * 4) =
-            make_float4(sP[r * CP + i], sP[r * CP + i + 1], sP[r * CP + i + 2], sP[r * CP + i + 3]);
+        // fp32 P: the fp32 kernels, and for bf16 inputs only the exact chunks'
+        if (!kBf16 || exact)
+            *reinterpret_cast<float4 *>(gP + tid * 4) =
+                make_float4(sP[r * CP + i], sP[r * CP + i + 1], sP[r * CP + i + 2], sP[r * CP + i + 3]);
         *reinterpret_cast<float4 *>(gM + tid * 4) =
             make_float4(sM[r * CP + i], sM[r * CP + i + 1], sM[r * CP + i + 2], sM[r * CP + i + 3]);
     }
@@ -499,6 +503,19 @@ __global__ void __launch_bounds__(NT) bwd_prep_kernel(Params p) {
         const int r = (tid * 4) / C, i = (tid * 4) % C;
         *reinterpret_cast<float4 *>(gT + tid * 4) =
             make_float4(sT[r * CP + i], sT[r * CP + i + 1], sT[r * CP + i + 2], sT[r * CP + i + 3]);
+        if constexpr (kBf16) {
+            // the state chains' bf16 operands: T, T^T and P^T, row-major
+            bf16x4 a, b, c;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                a[j] = (__bf16)sT[r * CP + i + j];
+                b[j] = (__bf16)sT[(i + j) * CP + r];
+                c[j] = (__bf16)sP[(i + j) * CP + r];
+            }
+            *reinterpret_cast<bf16x4 *>(p.wTb + wi * C * C + tid * 4) = a;
+            *reinterpret_cast<bf16x4 *>(p.wTt + wi * C * C + tid * 4) = b;
+            *reinterpret_cast<bf16x4 *>(p.wPt + wi * C * C + tid * 4) = c;
+        }
     }
 }
 
@@ -717,7 +734,7 @@ constexpr int grads_floats() {
 }
 
 template <typename Tin, int DK, bool EXACT>
-__global__ void __launch_bounds__(NT) bwd_grads_kernel(Params p) {
+__global__ void __launch_bounds__(NT) bwd_grads_kernel(Params p, long nslot) {
     constexpr int DKP = DK + 1, NTW = DK / 32, NPART = NT / DK;
     constexpr int NES = DK * W / NT, TPR = W / NES;     // S / D slice: NES values per thread
     __shared__ float smem[grads_floats<DK>()];
@@ -742,368 +759,387 @@ __global__ void __launch_bounds__(NT) bwd_grads_kernel(Params p) {
     float *sB = dgam + DK;               // C
     float *dB = sB + C;
 
-    const long slot = blockIdx.x;
     const int h = blockIdx.y, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int lr = lane & 15, lj = lane >> 4;
     const int vr = tid >> 3, vc = (tid & 7) * 4;          // C x W values of this thread
     const int sr = tid / TPR, sc = (tid % TPR) * NES;     // DK x W values of this thread
-    long t0;
-    int cl;
-    if (!slot_chunk(p, slot, t0, cl)) return;
-    const size_t wi = (size_t)slot * p.H + h;
-    // each chunk is done by the instantiation of its path (set by the prep kernel)
-    if ((p.wF[wi] != 0) != EXACT) return;
-    // states and state gradients are stored in the input precision's kind:
-    // fp32 for fp32 inputs, bf16 for bf16 inputs
-    const Tin *gS = reinterpret_cast<const Tin *>(p.wS) + wi * DK * p.DV;
-    const Tin *gD = reinterpret_cast<const Tin *>(p.wD) + wi * DK * p.DV;
+    auto chunk = [&](long slot) {
+        long t0;
+        int cl;
+        if (!slot_chunk(p, slot, t0, cl)) return;
+        const size_t wi = (size_t)slot * p.H + h;
+        // each chunk is done by the instantiation of its path (set by the prep kernel)
+        if ((p.wF[wi] != 0) != EXACT) return;
+        // states and state gradients are stored in the input precision's kind:
+        // fp32 for fp32 inputs, bf16 for bf16 inputs
+        const Tin *gS = reinterpret_cast<const Tin *>(p.wS) + wi * DK * p.DV;
+        const Tin *gD = reinterpret_cast<const Tin *>(p.wD) + wi * DK * p.DV;
 
-    // every load of the chunk, then the first slice's, before the first wait
-    Seg<Tin, NES> sin, din;
-    Seg<Tin, 4> vin, oin;
-    auto issue_slice = [&](int col0) {
-        sin.load(gS, (size_t)sr * p.DV + col0 + sc, true);
-        din.load(gD, (size_t)sr * p.DV + col0 + sc, true);
-        const size_t e = ((size_t)(t0 + vr) * p.H + h) * p.DV + col0 + vc;
-        vin.load(p.v, e, vr < cl);
-        oin.load(p.dO, e, vr < cl);
-    };
-    {
-        ChunkIn<Tin, DK, true> in;
-        Seg<float, 4> tin, pin, min;
-        in.load(p, t0, cl, h);
-        tin.load(p.wT, wi * C * C + tid * 4, true);
-        pin.load(p.wP, wi * C * C + tid * 4, true);
-        min.load(p.wM, wi * C * C + tid * 4, true);
-        issue_slice(0);
-        in.store(p, sKup, sQup, sG, sB);
-        const int tr = (tid * 4) / C, tc = (tid * 4) % C;
+        // every load of the chunk, then the first slice's, before the first wait
+        Seg<Tin, NES> sin, din;
+        Seg<Tin, 4> vin, oin;
+        auto issue_slice = [&](int col0) {
+            sin.load(gS, (size_t)sr * p.DV + col0 + sc, true);
+            din.load(gD, (size_t)sr * p.DV + col0 + sc, true);
+            const size_t e = ((size_t)(t0 + vr) * p.H + h) * p.DV + col0 + vc;
+            vin.load(p.v, e, vr < cl);
+            oin.load(p.dO, e, vr < cl);
+        };
+        {
+            ChunkIn<Tin, DK, true> in;
+            Seg<float, 4> tin, pin, min;
+            in.load(p, t0, cl, h);
+            tin.load(p.wT, wi * C * C + tid * 4, true);
+            pin.load(p.wP, wi * C * C + tid * 4, true);
+            min.load(p.wM, wi * C * C + tid * 4, true);
+            issue_slice(0);
+            in.store(p, sKup, sQup, sG, sB);
+            const int tr = (tid * 4) / C, tc = (tid * 4) % C;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            sT[tr * CP + tc + j] = tin.get(j);
-            sP[tr * CP + tc + j] = pin.get(j);
-            sM[tr * CP + tc + j] = min.get(j);
+            for (int j = 0; j < 4; ++j) {
+                sT[tr * CP + tc + j] = tin.get(j);
+                sP[tr * CP + tc + j] = pin.get(j);
+                sM[tr * CP + tc + j] = min.get(j);
+            }
         }
-    }
-    if (tid < C) dB[tid] = 0.0f;
-    if (tid < DK) dgam[tid] = 0.0f;
-    __syncthreads();
-    gate_sums<DK>(sG, gc, gam);
-    __syncthreads();
-    scale_rows<DK, true>(sKup, sQup, sG, sKrt, gc);
+        if (tid < C) dB[tid] = 0.0f;
+        if (tid < DK) dgam[tid] = 0.0f;
+        __syncthreads();
+        gate_sums<DK>(sG, gc, gam);
+        __syncthreads();
+        scale_rows<DK, true>(sKup, sQup, sG, sKrt, gc);
 
-    // accumulators over the d_v slices: this wave's tiles of dQ_up, dK_up
-    // (negated) and dK_right (C x DK, tile w * NTW + x -> (tm, tn) over 2 x
-    // DK/16), and of dT' and dP (C x C, tile w -> (w >> 1, w & 1))
-    f32x4 aQ[NTW], aK[NTW], aR[NTW], aT = {0.f, 0.f, 0.f, 0.f}, aP = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int x = 0; x < NTW; ++x) {
-        aQ[x] = f32x4{0.f, 0.f, 0.f, 0.f};
-        aK[x] = aQ[x];
-        aR[x] = aQ[x];
-    }
-    const int tm = wave >> 1, tn = wave & 1;        // this wave's C x W / C x C tile
-    for (int col0 = 0; col0 < p.DV; col0 += W) {
-        __syncthreads();
-#pragma unroll
-        for (int j = 0; j < NES; ++j) {
-            sS[sr * WP + sc + j] = sin.get(j);
-            sD[sr * WP + sc + j] = din.get(j);
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            sX[vr * WP + vc + j] = vin.get(j);
-            sdO[vr * WP + vc + j] = oin.get(j);
-        }
-        if (col0 + W < p.DV) issue_slice(col0 + W);
-        __syncthreads();
-        // X = V - K_up S
-        {
-            f32x4 a = {0.f, 0.f, 0.f, 0.f};
-            a = mm(a, sKup + 16 * tm * DKP, DKP, 1, sS + 16 * tn, WP, 1, DK);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = 16 * tm + 4 * lj + i, o = row * WP + 16 * tn + lr;
-                const float x = sX[o] - a[i];
-                sX[o] = x;
-                sBX[o] = sB[row] * x;
-            }
-        }
-        __syncthreads();
-        // U = T (beta X);  dU = P^T dO + K_right D
-        {
-            f32x4 a = {0.f, 0.f, 0.f, 0.f};
-            a = mm(a, sT + 16 * tm * CP, CP, 1, sBX + 16 * tn, WP, 1, C);
-            f32x4 b = {0.f, 0.f, 0.f, 0.f};
-            b = mm(b, sP + 16 * tm, 1, CP, sdO + 16 * tn, WP, 1, C);
-            b = mm(b, sKrt + 16 * tm * DKP, DKP, 1, sD + 16 * tn, WP, 1, DK);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int o = (16 * tm + 4 * lj + i) * WP + 16 * tn + lr;
-                sU[o] = a[i];
-                sdU[o] = b[i];
-            }
-        }
-        __syncthreads();
-        // dX = Diag(beta) T^T dU (also dV)
-        {
-            f32x4 a = {0.f, 0.f, 0.f, 0.f};
-            a = mm(a, sT + 16 * tm, 1, CP, sdU + 16 * tn, WP, 1, C);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = 16 * tm + 4 * lj + i, col = 16 * tn + lr;
-                const float x = sB[row] * a[i];
-                sdX[row * WP + col] = x;
-                if (row < cl) st<Tin>(p.dv, ((size_t)(t0 + row) * p.H + h) * p.DV + col0 + col, x);
-            }
-        }
-        // dT' += dU X^T;  dP += dO U^T;  dQ_up += dO S^T;  dK_right += U D^T
-        aT = mm(aT, sdU + 16 * tm * WP, WP, 1, sX + 16 * tn * WP, 1, WP, W);
-        aP = mm(aP, sdO + 16 * tm * WP, WP, 1, sU + 16 * tn * WP, 1, WP, W);
+        // accumulators over the d_v slices: this wave's tiles of dQ_up, dK_up
+        // (negated) and dK_right (C x DK, tile w * NTW + x -> (tm, tn) over 2 x
+        // DK/16), and of dT' and dP (C x C, tile w -> (w >> 1, w & 1))
+        f32x4 aQ[NTW], aK[NTW], aR[NTW], aT = {0.f, 0.f, 0.f, 0.f}, aP = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int x = 0; x < NTW; ++x) {
-            const int tt = wave * NTW + x, m0 = 16 * (tt / (DK / 16)), n0 = 16 * (tt % (DK / 16));
-            aQ[x] = mm(aQ[x], sdO + m0 * WP, WP, 1, sS + n0 * WP, 1, WP, W);
-            aR[x] = mm(aR[x], sU + m0 * WP, WP, 1, sD + n0 * WP, 1, WP, W);
+            aQ[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+            aK[x] = aQ[x];
+            aR[x] = aQ[x];
         }
-        if (tid < DK) {
-            float acc = 0.0f;
+        const int tm = wave >> 1, tn = wave & 1;        // this wave's C x W / C x C tile
+        for (int col0 = 0; col0 < p.DV; col0 += W) {
+            __syncthreads();
+#pragma unroll
+            for (int j = 0; j < NES; ++j) {
+                sS[sr * WP + sc + j] = sin.get(j);
+                sD[sr * WP + sc + j] = din.get(j);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                sX[vr * WP + vc + j] = vin.get(j);
+                sdO[vr * WP + vc + j] = oin.get(j);
+            }
+            if (col0 + W < p.DV) issue_slice(col0 + W);
+            __syncthreads();
+            // X = V - K_up S
+            {
+                f32x4 a = {0.f, 0.f, 0.f, 0.f};
+                a = mm(a, sKup + 16 * tm * DKP, DKP, 1, sS + 16 * tn, WP, 1, DK);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int row = 16 * tm + 4 * lj + i, o = row * WP + 16 * tn + lr;
+                    const float x = sX[o] - a[i];
+                    sX[o] = x;
+                    sBX[o] = sB[row] * x;
+                }
+            }
+            __syncthreads();
+            // U = T (beta X);  dU = P^T dO + K_right D
+            {
+                f32x4 a = {0.f, 0.f, 0.f, 0.f};
+                a = mm(a, sT + 16 * tm * CP, CP, 1, sBX + 16 * tn, WP, 1, C);
+                f32x4 b = {0.f, 0.f, 0.f, 0.f};
+                b = mm(b, sP + 16 * tm, 1, CP, sdO + 16 * tn, WP, 1, C);
+                b = mm(b, sKrt + 16 * tm * DKP, DKP, 1, sD + 16 * tn, WP, 1, DK);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int o = (16 * tm + 4 * lj + i) * WP + 16 * tn + lr;
+                    sU[o] = a[i];
+                    sdU[o] = b[i];
+                }
+            }
+            __syncthreads();
+            // dX = Diag(beta) T^T dU (also dV)
+            {
+                f32x4 a = {0.f, 0.f, 0.f, 0.f};
+                a = mm(a, sT + 16 * tm, 1, CP, sdU + 16 * tn, WP, 1, C);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int row = 16 * tm + 4 * lj + i, col = 16 * tn + lr;
+                    const float x = sB[row] * a[i];
+                    sdX[row * WP + col] = x;
+                    if (row < cl) st<Tin>(p.dv, ((size_t)(t0 + row) * p.H + h) * p.DV + col0 + col, x);
+                }
+            }
+            // dT' += dU X^T;  dP += dO U^T;  dQ_up += dO S^T;  dK_right += U D^T
+            aT = mm(aT, sdU + 16 * tm * WP, WP, 1, sX + 16 * tn * WP, 1, WP, W);
+            aP = mm(aP, sdO + 16 * tm * WP, WP, 1, sU + 16 * tn * WP, 1, WP, W);
+#pragma unroll
+            for (int x = 0; x < NTW; ++x) {
+                const int tt = wave * NTW + x, m0 = 16 * (tt / (DK / 16)), n0 = 16 * (tt % (DK / 16));
+                aQ[x] = mm(aQ[x], sdO + m0 * WP, WP, 1, sS + n0 * WP, 1, WP, W);
+                aR[x] = mm(aR[x], sU + m0 * WP, WP, 1, sD + n0 * WP, 1, WP, W);
+            }
+            if (tid < DK) {
+                float acc = 0.0f;
 #pragma unroll 8
-            for (int j = 0; j < W; ++j) acc += sD[tid * WP + j] * sS[tid * WP + j];
-            dgam[tid] += acc;
+                for (int j = 0; j < W; ++j) acc += sD[tid * WP + j] * sS[tid * WP + j];
+                dgam[tid] += acc;
+            }
+            __syncthreads();
+            // dK_up -= dX S^T
+#pragma unroll
+            for (int x = 0; x < NTW; ++x) {
+                const int tt = wave * NTW + x, m0 = 16 * (tt / (DK / 16)), n0 = 16 * (tt % (DK / 16));
+                aK[x] = mm(aK[x], sdX + m0 * WP, WP, 1, sS + n0 * WP, 1, WP, W);
+            }
         }
         __syncthreads();
-        // dK_up -= dX S^T
-#pragma unroll
-        for (int x = 0; x < NTW; ++x) {
-            const int tt = wave * NTW + x, m0 = 16 * (tt / (DK / 16)), n0 = 16 * (tt % (DK / 16));
-            aK[x] = mm(aK[x], sdX + m0 * WP, WP, 1, sS + n0 * WP, 1, WP, W);
-        }
-    }
-    __syncthreads();
 
-    // dT' and dP (lower, diagonal included) to LDS
-    float *sdT = sX, *sdP = sBX, *sY = sU, *sdA = sdU;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int row = 16 * tm + 4 * lj + i, col = 16 * tn + lr;
-        sdT[row * WP + col] = aT[i];
-        sdP[row * WP + col] = col <= row ? aP[i] : 0.0f;
-    }
-    __syncthreads();
-    // dbeta_i from T' = T Diag(beta); then dT = dT' Diag(beta)
-    if (tid < C) {
-        float acc = 0.0f;
-#pragma unroll 8
-        for (int r = 0; r < C; ++r) acc += sT[r * CP + tid] * sdT[r * WP + tid];
-        dB[tid] = acc;
-    }
-    __syncthreads();
-    for (int idx = tid; idx < C * C; idx += NT) {
-        const int r = idx / C, i = idx % C;
-        sdT[r * WP + i] *= sB[i];
-    }
-    __syncthreads();
-    // Y = T^T dT;  dA = -(Y T^T), strictly lower
-    {
-        f32x4 a = {0.f, 0.f, 0.f, 0.f};
-        a = mm(a, sT + 16 * tm, 1, CP, sdT + 16 * tn, WP, 1, C);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sY[(16 * tm + 4 * lj + i) * WP + 16 * tn + lr] = a[i];
-    }
-    __syncthreads();
-    {
-        f32x4 a = {0.f, 0.f, 0.f, 0.f};
-        a = mm(a, sY + 16 * tm * WP, WP, 1, sT + 16 * tn * CP, 1, CP, C);
+        // dT' and dP (lower, diagonal included) to LDS
+        float *sdT = sX, *sdP = sBX, *sY = sU, *sdA = sdU;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int row = 16 * tm + 4 * lj + i, col = 16 * tn + lr;
-            sdA[row * WP + col] = col < row ? -a[i] : 0.0f;
+            sdT[row * WP + col] = aT[i];
+            sdP[row * WP + col] = col <= row ? aP[i] : 0.0f;
         }
-    }
-    __syncthreads();
-    // dbeta_r += sum_i dA_ri M0_ri;  dM = Diag(beta) dA (over M0's place)
-    if (tid < C) {
-        const int r = tid;
-        float acc = 0.0f;
+        __syncthreads();
+        // dbeta_i from T' = T Diag(beta); then dT = dT' Diag(beta)
+        if (tid < C) {
+            float acc = 0.0f;
 #pragma unroll 8
-        for (int i = 0; i < C; ++i) {
-            const float a = sdA[r * WP + i];
-            acc += a * sM[r * CP + i];
-            sM[r * CP + i] = sB[r] * a;
+            for (int r = 0; r < C; ++r) acc += sT[r * CP + tid] * sdT[r * WP + tid];
+            dB[tid] = acc;
         }
-        dB[r] += acc;
-    }
-    __syncthreads();
-
-    float *sRK = sS;                     // C x DKP: dK_right K_right
-    if constexpr (!EXACT) {
-        // factorised decay: with K_dn = K e^{-Gamma},
-        //   Z1 = dP K_dn,  Z2 = dM K_dn,  Z3 = dM^T K_up + dP^T Q_up,
-        //   dq = (dQ_up + Z1) e^G,  dk = (dK_up + Z2) e^G + dK_right e^{G_c - G} + Z3 e^{-G},
-        //   dGamma = (dK_up + Z2) K_up + (dQ_up + Z1) Q_up - dK_right K_right - Z3 K_dn
-        float *sKdn = sD;                // C x DKP
+        __syncthreads();
+        for (int idx = tid; idx < C * C; idx += NT) {
+            const int r = idx / C, i = idx % C;
+            sdT[r * WP + i] *= sB[i];
+        }
+        __syncthreads();
+        // Y = T^T dT;  dA = -(Y T^T), strictly lower
         {
-            constexpr int NE = DK / 8;
-            const int r = tid >> 3, c0 = (tid & 7) * NE;
-            Seg<Tin, NE> kin;
-            kin.load(p.k, ((size_t)(t0 + r) * p.H + h) * DK + c0, r < cl);
+            f32x4 a = {0.f, 0.f, 0.f, 0.f};
+            a = mm(a, sT + 16 * tm, 1, CP, sdT + 16 * tn, WP, 1, C);
 #pragma unroll
-            for (int j = 0; j < NE; ++j) {
-                const int o = r * DKP + c0 + j;
-                sKdn[o] = kin.get(j) * __builtin_amdgcn_exp2f(-sG[o]);
+            for (int i = 0; i < 4; ++i) sY[(16 * tm + 4 * lj + i) * WP + 16 * tn + lr] = a[i];
+        }
+        __syncthreads();
+        {
+            f32x4 a = {0.f, 0.f, 0.f, 0.f};
+            a = mm(a, sY + 16 * tm * WP, WP, 1, sT + 16 * tn * CP, 1, CP, C);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = 16 * tm + 4 * lj + i, col = 16 * tn + lr;
+                sdA[row * WP + col] = col < row ? -a[i] : 0.0f;
             }
         }
         __syncthreads();
-        f32x4 zrk[NTW];                  // dK_right K_right, stored after the barrier below
+        // dbeta_r += sum_i dA_ri M0_ri;  dM = Diag(beta) dA (over M0's place)
+        if (tid < C) {
+            const int r = tid;
+            float acc = 0.0f;
+#pragma unroll 8
+            for (int i = 0; i < C; ++i) {
+                const float a = sdA[r * WP + i];
+                acc += a * sM[r * CP + i];
+                sM[r * CP + i] = sB[r] * a;
+            }
+            dB[r] += acc;
+        }
+        __syncthreads();
+
+        float *sRK = sS;                     // C x DKP: dK_right K_right
+        if constexpr (!EXACT) {
+            // factorised decay: with K_dn = K e^{-Gamma},
+            //   Z1 = dP K_dn,  Z2 = dM K_dn,  Z3 = dM^T K_up + dP^T Q_up,
+            //   dq = (dQ_up + Z1) e^G,  dk = (dK_up + Z2) e^G + dK_right e^{G_c - G} + Z3 e^{-G},
+            //   dGamma = (dK_up + Z2) K_up + (dQ_up + Z1) Q_up - dK_right K_right - Z3 K_dn
+            float *sKdn = sD;                // C x DKP
+            {
+                constexpr int NE = DK / 8;
+                const int r = tid >> 3, c0 = (tid & 7) * NE;
+                Seg<Tin, NE> kin;
+                kin.load(p.k, ((size_t)(t0 + r) * p.H + h) * DK + c0, r < cl);
+#pragma unroll
+                for (int j = 0; j < NE; ++j) {
+                    const int o = r * DKP + c0 + j;
+                    sKdn[o] = kin.get(j) * __builtin_amdgcn_exp2f(-sG[o]);
+                }
+            }
+            __syncthreads();
+            f32x4 zrk[NTW];                  // dK_right K_right, stored after the barrier below
+#pragma unroll
+            for (int x = 0; x < NTW; ++x) {
+                const int tt = wave * NTW + x, m0 = 16 * (tt / (DK / 16)), n0 = 16 * (tt % (DK / 16));
+                f32x4 z1 = {0.f, 0.f, 0.f, 0.f}, z2 = z1, z3 = z1;
+                z1 = mm(z1, sdP + m0 * WP, WP, 1, sKdn + n0, DKP, 1, C);
+                z2 = mm(z2, sM + m0 * CP, CP, 1, sKdn + n0, DKP, 1, C);
+                z3 = mm(z3, sM + m0, 1, CP, sKup + n0, DKP, 1, C);
+                z3 = mm(z3, sdP + m0, 1, WP, sQup + n0, DKP, 1, C);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int row = m0 + 4 * lj + i, col = n0 + lr, o = row * DKP + col;
+                    const float G = sG[o], E = __builtin_amdgcn_exp2f(G);
+                    const float R = __builtin_amdgcn_exp2f(gc[col] - G);
+                    const float Ei = __builtin_amdgcn_exp2f(-G);
+                    // aK holds -dK_up
+                    const float dQu = aQ[x][i] + z1[i], dKu = z2[i] - aK[x][i], dKr = aR[x][i];
+                    const float ku = sKup[o], qu = sQup[o], kr = sKrt[o], kd = sKdn[o];
+                    aQ[x][i] = dQu * E;
+                    aK[x][i] = dKu * E + dKr * R + z3[i] * Ei;
+                    aR[x][i] = dKu * ku + dQu * qu - dKr * kr - z3[i] * kd;
+                    zrk[x][i] = dKr * kr;
+                }
+            }
+            __syncthreads();
+#pragma unroll
+            for (int x = 0; x < NTW; ++x) {
+                const int tt = wave * NTW + x, m0 = 16 * (tt / (DK / 16)), n0 = 16 * (tt % (DK / 16));
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int o = (m0 + 4 * lj + i) * DKP + n0 + lr;
+                    sQup[o] = aQ[x][i];
+                    sKup[o] = aK[x][i];
+                    sKrt[o] = aR[x][i];
+                    sRK[o] = zrk[x][i];
+                }
+            }
+            __syncthreads();
+        } else {
+        // direct terms, element by element where the tiles lie:
+        //   dq = dQ_up e^G,  dk = dK_up e^G + dK_right e^{G_c - G},
+        //   dGamma = dK_up K_up + dQ_up Q_up - dK_right K_right,
+        // and dK_right K_right kept for the chunk-total term
 #pragma unroll
         for (int x = 0; x < NTW; ++x) {
             const int tt = wave * NTW + x, m0 = 16 * (tt / (DK / 16)), n0 = 16 * (tt % (DK / 16));
-            f32x4 z1 = {0.f, 0.f, 0.f, 0.f}, z2 = z1, z3 = z1;
-            z1 = mm(z1, sdP + m0 * WP, WP, 1, sKdn + n0, DKP, 1, C);
-            z2 = mm(z2, sM + m0 * CP, CP, 1, sKdn + n0, DKP, 1, C);
-            z3 = mm(z3, sM + m0, 1, CP, sKup + n0, DKP, 1, C);
-            z3 = mm(z3, sdP + m0, 1, WP, sQup + n0, DKP, 1, C);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int row = m0 + 4 * lj + i, col = n0 + lr, o = row * DKP + col;
                 const float G = sG[o], E = __builtin_amdgcn_exp2f(G);
                 const float R = __builtin_amdgcn_exp2f(gc[col] - G);
-                const float Ei = __builtin_amdgcn_exp2f(-G);
-                // aK holds -dK_up
-                const float dQu = aQ[x][i] + z1[i], dKu = z2[i] - aK[x][i], dKr = aR[x][i];
-                const float ku = sKup[o], qu = sQup[o], kr = sKrt[o], kd = sKdn[o];
-                aQ[x][i] = dQu * E;
-                aK[x][i] = dKu * E + dKr * R + z3[i] * Ei;
-                aR[x][i] = dKu * ku + dQu * qu - dKr * kr - z3[i] * kd;
-                zrk[x][i] = dKr * kr;
+                const float dQu = aQ[x][i], dKu = -aK[x][i], dKr = aR[x][i];
+                const float ku = sKup[o], qu = sQup[o], kr = sKrt[o];
+                sQup[o] = dQu * E;
+                sKup[o] = dKu * E + dKr * R;
+                sKrt[o] = dKu * ku + dQu * qu - dKr * kr;
+                sRK[o] = dKr * kr;
             }
         }
-        __syncthreads();
+            __syncthreads();
+        // pairwise sums of M0 and P, taken back to k, q and Gamma: thread (channel
+        // c, part); part p takes the pairs (r, i <= r) with (r + i) % NPART == p.
+        {
+            const int c = tid % DK, part = tid / DK;
+            float kc[C], qc[C], gcol[C], aq[C], ak[C], ag[C];
 #pragma unroll
-        for (int x = 0; x < NTW; ++x) {
-            const int tt = wave * NTW + x, m0 = 16 * (tt / (DK / 16)), n0 = 16 * (tt % (DK / 16));
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int o = (m0 + 4 * lj + i) * DKP + n0 + lr;
-                sQup[o] = aQ[x][i];
-                sKup[o] = aK[x][i];
-                sKrt[o] = aR[x][i];
-                sRK[o] = zrk[x][i];
+            for (int r = 0; r < C; ++r) {
+                const bool ok = r < cl;
+                const size_t e = ((size_t)(t0 + (ok ? r : 0)) * p.H + h) * DK + c;
+                kc[r] = ld<Tin>(p.k, e);
+                qc[r] = ld<Tin>(p.q, e);
+                kc[r] = ok ? kc[r] : 0.0f;
+                qc[r] = ok ? qc[r] : 0.0f;
+                gcol[r] = sG[r * DKP + c];
+                aq[r] = 0.0f;
+                ak[r] = 0.0f;
+                ag[r] = 0.0f;
             }
-        }
-        __syncthreads();
-    } else {
-    // direct terms, element by element where the tiles lie:
-    //   dq = dQ_up e^G,  dk = dK_up e^G + dK_right e^{G_c - G},
-    //   dGamma = dK_up K_up + dQ_up Q_up - dK_right K_right,
-    // and dK_right K_right kept for the chunk-total term
 #pragma unroll
-    for (int x = 0; x < NTW; ++x) {
-        const int tt = wave * NTW + x, m0 = 16 * (tt / (DK / 16)), n0 = 16 * (tt % (DK / 16));
+            for (int r = 0; r < C; ++r) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = m0 + 4 * lj + i, col = n0 + lr, o = row * DKP + col;
-            const float G = sG[o], E = __builtin_amdgcn_exp2f(G);
-            const float R = __builtin_amdgcn_exp2f(gc[col] - G);
-            const float dQu = aQ[x][i], dKu = -aK[x][i], dKr = aR[x][i];
-            const float ku = sKup[o], qu = sQup[o], kr = sKrt[o];
-            sQup[o] = dQu * E;
-            sKup[o] = dKu * E + dKr * R;
-            sKrt[o] = dKu * ku + dQu * qu - dKr * kr;
-            sRK[o] = dKr * kr;
-        }
-    }
-        __syncthreads();
-    // pairwise sums of M0 and P, taken back to k, q and Gamma: thread (channel
-    // c, part); part p takes the pairs (r, i <= r) with (r + i) % NPART == p.
-    {
-        const int c = tid % DK, part = tid / DK;
-        float kc[C], qc[C], gcol[C], aq[C], ak[C], ag[C];
-#pragma unroll
-        for (int r = 0; r < C; ++r) {
-            const bool ok = r < cl;
-            const size_t e = ((size_t)(t0 + (ok ? r : 0)) * p.H + h) * DK + c;
-            kc[r] = ld<Tin>(p.k, e);
-            qc[r] = ld<Tin>(p.q, e);
-            kc[r] = ok ? kc[r] : 0.0f;
-            qc[r] = ok ? qc[r] : 0.0f;
-            gcol[r] = sG[r * DKP + c];
-            aq[r] = 0.0f;
-            ak[r] = 0.0f;
-            ag[r] = 0.0f;
-        }
-#pragma unroll
-        for (int r = 0; r < C; ++r) {
-#pragma unroll
-            for (int i = 0; i <= r; ++i) {
-                if ((r + i) % NPART != part) continue;
-                const float F = __builtin_amdgcn_exp2f(gcol[r] - gcol[i]);
-                const float a = sdP[r * WP + i] * F;
-                const float b = sM[r * CP + i] * F;      // dM, zero on the diagonal
-                aq[r] += a * kc[i];
-                ak[r] += b * kc[i];
-                const float t = a * qc[r] + b * kc[r];
-                ak[i] += t;
-                const float w = t * kc[i];
-                ag[r] += w;
-                ag[i] -= w;
-            }
-        }
-        // add the parts into the direct terms, one part at a time
-        for (int pp = 0; pp < NPART; ++pp) {
-            if (part == pp) {
-#pragma unroll
-                for (int r = 0; r < C; ++r) {
-                    sQup[r * DKP + c] += aq[r];
-                    sKup[r * DKP + c] += ak[r];
-                    sKrt[r * DKP + c] += ag[r];
+                for (int i = 0; i <= r; ++i) {
+                    if ((r + i) % NPART != part) continue;
+                    const float F = __builtin_amdgcn_exp2f(gcol[r] - gcol[i]);
+                    const float a = sdP[r * WP + i] * F;
+                    const float b = sM[r * CP + i] * F;      // dM, zero on the diagonal
+                    aq[r] += a * kc[i];
+                    ak[r] += b * kc[i];
+                    const float t = a * qc[r] + b * kc[r];
+                    ak[i] += t;
+                    const float w = t * kc[i];
+                    ag[r] += w;
+                    ag[i] -= w;
                 }
             }
-            __syncthreads();
-        }
-    }
-    }
-    // dlog_alpha: reverse running sum of dGamma plus the chunk-total term
-    // sum_r dK_right K_right + dgamma gamma; outputs
-    if (tid < DK) {
-        const int c = tid;
-        float x[C];
-        float tot = dgam[c] * gam[c];
+            // add the parts into the direct terms, one part at a time
+            for (int pp = 0; pp < NPART; ++pp) {
+                if (part == pp) {
 #pragma unroll
-        for (int r = 0; r < C; ++r) {
-            tot += sRK[r * DKP + c];
-            x[r] = sKrt[r * DKP + c];
-        }
-        float run = tot;
-#pragma unroll
-        for (int r = C - 1; r >= 0; --r) {
-            run += x[r];
-            sKrt[r * DKP + c] = run;
-        }
-    }
-    __syncthreads();
-    {
-        constexpr int NE = DK / 8;
-        const int r = tid >> 3, c0 = (tid & 7) * NE;
-        if (r < cl) {
-            const size_t e = ((size_t)(t0 + r) * p.H + h) * DK + c0;
-#pragma unroll
-            for (int j = 0; j < NE; ++j) {
-                st<Tin>(p.dq, e + j, sQup[r * DKP + c0 + j]);
-                st<Tin>(p.dk, e + j, sKup[r * DKP + c0 + j]);
-                if (p.gate == GATE_CHANNEL) st<Tin>(p.dg, e + j, sKrt[r * DKP + c0 + j]);
+                    for (int r = 0; r < C; ++r) {
+                        sQup[r * DKP + c] += aq[r];
+                        sKup[r * DKP + c] += ak[r];
+                        sKrt[r * DKP + c] += ag[r];
+                    }
+                }
+                __syncthreads();
             }
         }
-    }
-    if (tid < cl) {
-        const size_t e = (size_t)(t0 + tid) * p.H + h;
-        st<Tin>(p.dbeta, e, dB[tid]);
-        if (p.gate == GATE_HEAD) {
-            float acc = 0.0f;
-            for (int c = 0; c < DK; ++c) acc += sKrt[tid * DKP + c];
-            st<Tin>(p.dg, e, acc);
         }
+        // dlog_alpha: reverse running sum of dGamma plus the chunk-total term
+        // sum_r dK_right K_right + dgamma gamma; outputs
+        if (tid < DK) {
+            const int c = tid;
+            float x[C];
+            float tot = dgam[c] * gam[c];
+#pragma unroll
+            for (int r = 0; r < C; ++r) {
+                tot += sRK[r * DKP + c];
+                x[r] = sKrt[r * DKP + c];
+            }
+            float run = tot;
+#pragma unroll
+            for (int r = C - 1; r >= 0; --r) {
+                run += x[r];
+                sKrt[r * DKP + c] = run;
+            }
+        }
+        __syncthreads();
+        {
+            constexpr int NE = DK / 8;
+            const int r = tid >> 3, c0 = (tid & 7) * NE;
+            if (r < cl) {
+                const size_t e = ((size_t)(t0 + r) * p.H + h) * DK + c0;
+#pragma unroll
+                for (int j = 0; j < NE; ++j) {
+                    st<Tin>(p.dq, e + j, sQup[r * DKP + c0 + j]);
+                    st<Tin>(p.dk, e + j, sKup[r * DKP + c0 + j]);
+                    if (p.gate == GATE_CHANNEL) st<Tin>(p.dg, e + j, sKrt[r * DKP + c0 + j]);
+                }
+            }
+        }
+        if (tid < cl) {
+            const size_t e = (size_t)(t0 + tid) * p.H + h;
+            st<Tin>(p.dbeta, e, dB[tid]);
+            if (p.gate == GATE_HEAD) {
+                float acc = 0.0f;
+                for (int c = 0; c < DK; ++c) acc += sKrt[tid * DKP + c];
+                st<Tin>(p.dg, e, acc);
+            }
+        }
+    };
+    if constexpr (EXACT) {
+        // exact chunks are rare: a reduced grid strides over the slots, NT of
+        // them at a time, whose flags the threads read together first
+        const long step = gridDim.x;
+        for (long first = blockIdx.x; first < nslot; first += step * NT) {
+            const long mine = first + tid * step;
+            long t0;
+            int cl;
+            const bool ex = mine < nslot && slot_chunk(p, mine, t0, cl) && p.wF[(size_t)mine * p.H + h] != 0;
+            if (!__syncthreads_or(ex)) continue;
+            for (int j = 0; j < NT && first + j * step < nslot; ++j) {
+                chunk(first + j * step);
+                __syncthreads();                      // this chunk is done with LDS
+            }
+        }
+    } else {
+        chunk(blockIdx.x);
     }
 }
 
@@ -1287,13 +1323,13 @@ __global__ void __launch_bounds__(NT2) bwd_states_bf16_kernel(Params p) {
     const int nch = (len + C - 1) / C;
     ChunkIn<bf16_t, DK, false, 16> in;
     Seg<bf16_t, 4> vin;
-    Seg<float, 4> tin;
+    Seg<bf16_t, 4> tin;
     auto issue = [&](int n) {
         const long t0 = t0s + (long)n * C;
         const int cl = len - n * C < C ? len - n * C : C;
         in.load(p, t0, cl, h);
         vin.load(p.v, ((size_t)(t0 + vr) * p.H + h) * p.DV + col0 + vc, vr < cl);
-        tin.load(p.wT, ((size_t)(base + n) * p.H + h) * C * C + t4, tid < 256);
+        tin.load(p.wTb, ((size_t)(base + n) * p.H + h) * C * C + t4, tid < 256);
     };
     // chunk n's inputs into LDS (V into the buffer of n's parity)
     auto stage = [&](int n) {
@@ -1301,12 +1337,7 @@ __global__ void __launch_bounds__(NT2) bwd_states_bf16_kernel(Params p) {
         float *sV = sV0 + (n & 1) * C * W2P;
 #pragma unroll
         for (int j = 0; j < 4; ++j) sV[vr * W2P + vc + j] = vin.get(j);
-        if (tid < 256) {
-            bf16x4 tv;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) tv[j] = (__bf16)tin.get(j);
-            *reinterpret_cast<bf16x4 *>(Tb + (t4 / C) * CB + t4 % C) = tv;
-        }
+        if (tid < 256) *reinterpret_cast<uint2 *>(Tb + (t4 / C) * CB + t4 % C) = make_uint2(tin.w[0], tin.w[1]);
     };
     f32x4 S[NTW];
 #pragma unroll
@@ -1441,9 +1472,9 @@ __global__ void __launch_bounds__(NT2) bwd_dstates_bf16_kernel(Params p) {
     chain_unit(p, blockIdx.x, unit, slice);
     const int s = unit / p.H, h = unit % p.H, col0 = slice * W2;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, lj = lane >> 4;
-    // dO^T: thread (column oc, rows 4 ob .. 4 ob + 3); T^T, P^T: thread (column
-    // ti, rows 2 tb, 2 tb + 1)
-    const int oc = tid & 63, ob = tid >> 6, ti = tid & 31, tb = tid >> 5;
+    // dO^T: thread (column oc, rows 4 ob .. 4 ob + 3); T^T, P^T: thread (row
+    // tr, columns tc, tc + 1)
+    const int oc = tid & 63, ob = tid >> 6, tr = tid >> 4, tc = 2 * (tid & 15);
     long t0s, base;
     int len;
     seq_info(p, s, t0s, len, base);
@@ -1451,7 +1482,7 @@ __global__ void __launch_bounds__(NT2) bwd_dstates_bf16_kernel(Params p) {
     const size_t so = ((size_t)s * p.H + h) * DK;
     ChunkIn<bf16_t, DK, true, 16> in;
     One<bf16_t> oin[4];
-    One<float> tin[2], pin[2];
+    uint32_t tin, pin;                                   // two bf16 each
     auto issue = [&](int n) {
         const long t0 = t0s + (long)n * C;
         const int cl = len - n * C < C ? len - n * C : C;
@@ -1462,11 +1493,8 @@ __global__ void __launch_bounds__(NT2) bwd_dstates_bf16_kernel(Params p) {
             const int r = 4 * ob + i;
             oin[i].load(p.dO, ((size_t)(t0 + r) * p.H + h) * p.DV + col0 + oc, r < cl);
         }
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            tin[i].load(p.wT, wi * C * C + (2 * tb + i) * C + ti, true);
-            pin[i].load(p.wP, wi * C * C + (2 * tb + i) * C + ti, true);
-        }
+        tin = *reinterpret_cast<const uint32_t *>(p.wTt + wi * C * C + 2 * tid);
+        pin = *reinterpret_cast<const uint32_t *>(p.wPt + wi * C * C + 2 * tid);
     };
     // chunk n's inputs into LDS (dO^T into the buffer of n's parity)
     auto stage = [&](int n) {
@@ -1475,13 +1503,8 @@ __global__ void __launch_bounds__(NT2) bwd_dstates_bf16_kernel(Params p) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) ov[i] = (__bf16)oin[i].get();
         *reinterpret_cast<bf16x4 *>(dOt0 + (n & 1) * W2 * CB + oc * CB + 4 * ob) = ov;
-        bf16x2 tv, pv;
-        tv[0] = (__bf16)tin[0].get();
-        tv[1] = (__bf16)tin[1].get();
-        pv[0] = (__bf16)pin[0].get();
-        pv[1] = (__bf16)pin[1].get();
-        *reinterpret_cast<bf16x2 *>(TT + ti * CB + 2 * tb) = tv;
-        *reinterpret_cast<bf16x2 *>(PT + ti * CB + 2 * tb) = pv;
+        *reinterpret_cast<uint32_t *>(TT + tr * CB + tc) = tin;
+        *reinterpret_cast<uint32_t *>(PT + tr * CB + tc) = pin;
     };
     f32x4 D[NTW];
 #pragma unroll
@@ -1560,10 +1583,9 @@ __global__ void __launch_bounds__(NT2) bwd_dstates_bf16_kernel(Params p) {
         {
             f32x4 a = {0.f, 0.f, 0.f, 0.f};
             a = mmb(a, TT + 16 * xm * CB, CB, dUt + 16 * xn * CB, CB, C);
-            // dX (= dV): to the workspace for the gradient kernel, and to dv
+            // dX (= dV) to dv, where the gradient kernel reads it back
             const long t0 = t0s + (long)n * C;
             const int cl = len - n * C < C ? len - n * C : C;
-            const __amdgpu_buffer_rsrc_t rx = brsrc(p.wdX + wi * C * p.DV + col0);
             const __amdgpu_buffer_rsrc_t rv =
                 brsrc(static_cast<bf16_t *>(p.dv) + ((size_t)t0 * p.H + h) * p.DV + col0);
 #pragma unroll
@@ -1572,7 +1594,6 @@ __global__ void __launch_bounds__(NT2) bwd_dstates_bf16_kernel(Params p) {
                 const float dx = sB[row] * a[i];
                 asm volatile("" ::"v"(dXv[i]));
                 dXv[i] = to_bf16(dx).x;
-                bst16(dXv[i], rx, oX[i]);
                 bst16(dXv[i], rv, row < cl ? oV[i] : kDrop);
                 a[i] = -dx;
             }
@@ -1618,9 +1639,10 @@ __global__ void __launch_bounds__(NT2) bwd_dstates_bf16_kernel(Params p) {
 // operand is staged in LDS as bf16 with its contraction index contiguous (a
 // matrix used both ways is kept in both orientations); the C x C algebra and
 // the decay-weighted sums stay fp32.
-// With X, U (state chain), dU and dX (gradient chain) in the workspace, every
-// product left contracts over d_v, which is contiguous in every operand: the
-// slices go to LDS row-major as they come, with no transposed copies.
+// With X, U (state chain) and dU (gradient chain) in the workspace, and dX
+// written as dv by the gradient chain, every product left contracts over d_v,
+// which is contiguous in every operand: the slices go to LDS row-major as they
+// come, with no transposed copies.
 constexpr int W3 = 64;                 // d_v columns per slice of the gradient kernel
 // LDS of the bf16 gradient kernel, at most 80 KB so that two 512-thread
 // workgroups share a CU (one loads while the other runs its C x C algebra).
@@ -1713,8 +1735,9 @@ __global__ void __launch_bounds__(NT2, 4) bwd_grads_bf16_kernel(Params p) {
         in.x.load(p.wX, w, true);
         in.u.load(p.wU, w, true);
         in.du.load(p.wdU, w, true);
-        in.dx.load(p.wdX, w, true);
-        in.o.load(p.dO, ((size_t)(t0 + vr) * p.H + h) * p.DV + col0 + vc, vr < cl);
+        const size_t e = ((size_t)(t0 + vr) * p.H + h) * p.DV + col0 + vc;
+        in.dx.load(p.dv, e, vr < cl);
+        in.o.load(p.dO, e, vr < cl);
     };
     // both slices (d_v = 2 W3) are in flight from the start; with d_v = W3
     // the second repeats the first and is not used
@@ -1769,9 +1792,13 @@ __global__ void __launch_bounds__(NT2, 4) bwd_grads_bf16_kernel(Params p) {
         put(Xr + vr * WB + vc, in.x, n4{});
         put(Ur + vr * WB + vc, in.u, n4{});
         put(dUr + vr * WB + vc, in.du, n4{});
-        put(dXr + vr * WB + vc, in.dx, n4{});
-        if (in.o.ok) put(dOr + vr * WB + vc, in.o, n4{});
-        else *reinterpret_cast<uint2 *>(dOr + vr * WB + vc) = make_uint2(0u, 0u);
+        if (in.o.ok) {                                // rows past the sequence end: zeros
+            put(dXr + vr * WB + vc, in.dx, n4{});
+            put(dOr + vr * WB + vc, in.o, n4{});
+        } else {
+            *reinterpret_cast<uint2 *>(dXr + vr * WB + vc) = make_uint2(0u, 0u);
+            *reinterpret_cast<uint2 *>(dOr + vr * WB + vc) = make_uint2(0u, 0u);
+        }
         __syncthreads();
         // dT' += dU X^T (waves 0-3);  dP += dO U^T (waves 4-7);
         // dQ_up += dO S^T;  -dK_up += dX S^T;  dK_right += U D^T
@@ -1971,8 +1998,11 @@ hipError_t launch(const Params &p, long nslot, int nseq, hipStream_t stream) {
         if constexpr (std::is_same<Tin, bf16_t>::value)
             hipLaunchKernelGGL((bwd_grads_bf16_kernel<DK>), gchunks, dim3(NT2), 0, stream, p);
         else
-            hipLaunchKernelGGL((bwd_grads_kernel<Tin, DK, false>), gchunks, dim3(NT), 0, stream, p);
-        hipLaunchKernelGGL((bwd_grads_kernel<Tin, DK, true>), gchunks, dim3(NT), 0, stream, p);
+            hipLaunchKernelGGL((bwd_grads_kernel<Tin, DK, false>), gchunks, dim3(NT), 0, stream, p, nslot);
+        // exact chunks are rare: about 2048 workgroups stride over the slots
+        const long gx = std::max(1L, std::min(nslot, 2048L / p.H));
+        hipLaunchKernelGGL((bwd_grads_kernel<Tin, DK, true>), dim3((unsigned)gx, (unsigned)p.H), dim3(NT), 0,
+                           stream, p, nslot);
     }
     return hipGetLastError();
 }
@@ -1991,7 +2021,8 @@ size_t bwd_workspace_bytes(int B, int T, int H, int dk, int dv, int num_seqs) {
     const size_t b = (per * bwd::C * bwd::C * sizeof(float) + 255) & ~(size_t)255;
     const size_t f = (per * sizeof(int32_t) + 255) & ~(size_t)255;
     const size_t x = (per * bwd::C * dv * sizeof(bf16_t) + 255) & ~(size_t)255;
-    return 2 * a + 3 * b + f + 4 * x;
+    const size_t y = (per * bwd::C * bwd::C * sizeof(bf16_t) + 255) & ~(size_t)255;
+    return 2 * a + 3 * b + f + 3 * x + 3 * y;
 }
 
 hipError_t bwd_launch(const void *q, const void *k, const void *v, const void *g, const void *beta,
@@ -2021,7 +2052,11 @@ hipError_t bwd_launch(const void *q, const void *k, const void *v, const void *g
         p.wX = reinterpret_cast<bf16_t *>(wx);
         p.wU = reinterpret_cast<bf16_t *>(wx + x);
         p.wdU = reinterpret_cast<bf16_t *>(wx + 2 * x);
-        p.wdX = reinterpret_cast<bf16_t *>(wx + 3 * x);
+        const size_t y = (per * bwd::C * bwd::C * sizeof(bf16_t) + 255) & ~(size_t)255;
+        char *wy = wx + 3 * x;
+        p.wTb = reinterpret_cast<bf16_t *>(wy);
+        p.wTt = reinterpret_cast<bf16_t *>(wy + y);
+        p.wPt = reinterpret_cast<bf16_t *>(wy + 2 * y);
     }
     const long nslot = cu_seqlens ? (long)(T / bwd::C) + num_seqs + 1
                                   : (long)B * ((T + bwd::C - 1) / bwd::C);

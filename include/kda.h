@@ -220,9 +220,9 @@ kda_status kda_decode_step_ex(const void *q, const void *k, const void *v,
 
 /* Workspace size in bytes that kda_bwd_chunked needs for these sizes.  It
  * holds, per chunk of 32 tokens and head, the state entering the chunk, the
- * gradient of the state leaving it (fp32, dk x dv each) and three 32 x 32
- * fp32 matrices.  num_seqs is the number of packed sequences when cu_seqlens
- * is used, else B. */
+ * gradient of the state leaving it (fp32, dk x dv each), three 32 x 32 fp32
+ * matrices, a flag, three 32 x dv and three 32 x 32 bf16 matrices.  num_seqs
+ * is the number of packed sequences when cu_seqlens is used, else B. */
 size_t kda_bwd_workspace_bytes(int B, int T, int H, int dk, int dv, int num_seqs);
 
 /*
