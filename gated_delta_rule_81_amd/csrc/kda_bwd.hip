@@ -21,7 +21,8 @@
 //   back to k, q and Gamma; dlog_alpha is the reverse running sum of dGamma
 //   plus the chunk-total term (Gamma_c enters gamma and K_right).
 //
-// Four launches:
+// fp32 inputs, four launches (all arithmetic fp32: MFMA 16x16x4 for the
+// products, VALU for the pairwise decay sums):
 //   bwd_prep_kernel    one workgroup per (chunk, head): M0, P (pairwise, no
 //                      exponent ever positive) and T by forward substitution;
 //   bwd_states_kernel  one per (sequence, head, 32-column slice of d_v): the
@@ -29,8 +30,14 @@
 //   bwd_dstates_kernel same units, chunks in reverse: the state-gradient chain,
 //                      storing D for each chunk, and dS0;
 //   bwd_grads_kernel   one per (chunk, head): every input gradient of the chunk.
-// All arithmetic is fp32 (fp32 MFMA 16x16x4 for the products, VALU for the
-// pairwise decay sums); inputs and outputs are bf16 or fp32.
+// bf16 inputs (products on bf16 MFMA 16x16x32 with fp32 accumulation):
+//   the forward's fused chunk kernel (kda_chunked_ws.hip) in its saving
+//   instantiation: M0, P, T and the forward state chain, storing the state
+//   entering each chunk with X and U;
+//   bwd_dstates_bf16_kernel  the state-gradient chain (64-column slices);
+//   bwd_grads_bf16_kernel    the chunk gradients where every pairwise decay
+//                            factor stays below 2^64 (factorised), and
+//   bwd_grads_kernel         the exact instantiation for the other chunks.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -39,6 +46,14 @@
 #include "kda_device.h"
 
 namespace kda {
+int chunked_slice_width(int units, int dv);
+hipError_t chunked_ws_save_launch(const void *q, const void *k, const void *v, const void *g,
+                                  const void *beta, int gate, const float *S0,
+                                  const int32_t *cu_seqlens, int nseq, int T, int H, int dk, int dv,
+                                  int slice_width, bf16_t *wS, bf16_t *wX, bf16_t *wU, bf16_t *wTt,
+                                  bf16_t *wPt, float *wT, float *wM, float *wP, int32_t *wF,
+                                  hipStream_t stream);
+
 namespace bwd {
 
 constexpr int C = 32;        // chunk length
@@ -57,7 +72,7 @@ struct Params {
     float *dS0;
     float *wS, *wD, *wT, *wP, *wM;   // workspace, per (chunk slot, head)
     bf16_t *wX, *wU, *wdU;            // bf16 inputs: X, U, dU of each chunk (C x d_v); dX is dv
-    bf16_t *wTb, *wTt, *wPt;          // bf16 inputs: T, T^T and P^T (C x C) for the state chains
+    bf16_t *wTt, *wPt;                // bf16 inputs: T^T and P^T (C x C) for the gradient chain
     int32_t *wF;                     // per (chunk slot, head): 1 = exact path
 };
 
@@ -355,9 +370,7 @@ __device__ __forceinline__ void scale_rows(float *sKup, float *sQup, const float
 // M0, P and T of one chunk.
 template <typename Tin, int DK>
 __global__ void __launch_bounds__(NT) bwd_prep_kernel(Params p) {
-    constexpr int DKP = DK + 1, NCC = DK / 8, NE = DK / 8, DKB = DK + 8;
-    // sK and sQ are contiguous: on the bf16 fast path their space takes the
-    // bf16 K_up, Q_up and K_dn operands
+    constexpr int DKP = DK + 1, NCC = DK / 8, NE = DK / 8;
     __shared__ __attribute__((aligned(16))) float sKQ[2 * C * DKP];
     __shared__ float sG[C * DKP];
     __shared__ float sM[C * CP], sP[C * CP], sT[C * CP], sY[16 * 17], sB[C], gc[DK];
@@ -379,45 +392,21 @@ __global__ void __launch_bounds__(NT) bwd_prep_kernel(Params p) {
     if (tid == 0) p.wF[wi] = exact ? 1 : 0;
     if (!exact) {
         // K_up = k 2^G, Q_up = q 2^G, K_dn = k 2^-G; then M0 = K_up K_dn^T
-        // (strictly lower) and P = Q_up K_dn^T (lower) on MFMA (bf16 operands
-        // for bf16 inputs, fp32 otherwise)
+        // (strictly lower) and P = Q_up K_dn^T (lower) on fp32 MFMA
         const int r = tid >> 3, c0 = (tid & 7) * NE;
         const int tm = wave >> 1, tn = wave & 1, lr = lane & 15, lj = lane >> 4;
         f32x4 m = {0.f, 0.f, 0.f, 0.f}, pp = {0.f, 0.f, 0.f, 0.f};
-        if constexpr (std::is_same<Tin, bf16_t>::value) {
-            float kv[NE], qv[NE], gv[NE];
 #pragma unroll
-            for (int j = 0; j < NE; ++j) {
-                const int o = r * DKP + c0 + j;
-                kv[j] = sK[o];
-                qv[j] = sQ[o];
-                gv[j] = sG[o];
-            }
-            __syncthreads();
-            __bf16 *Kub = reinterpret_cast<__bf16 *>(sKQ), *Qub = Kub + C * DKB, *Kdb = Qub + C * DKB;
-#pragma unroll
-            for (int j = 0; j < NE; ++j) {
-                const float E = __builtin_amdgcn_exp2f(gv[j]), Ei = __builtin_amdgcn_exp2f(-gv[j]);
-                Kub[r * DKB + c0 + j] = (__bf16)(kv[j] * E);
-                Qub[r * DKB + c0 + j] = (__bf16)(qv[j] * E);
-                Kdb[r * DKB + c0 + j] = (__bf16)(kv[j] * Ei);
-            }
-            __syncthreads();
-            m = mmb(m, Kub + 16 * tm * DKB, DKB, Kdb + 16 * tn * DKB, DKB, DK);
-            pp = mmb(pp, Qub + 16 * tm * DKB, DKB, Kdb + 16 * tn * DKB, DKB, DK);
-        } else {
-#pragma unroll
-            for (int j = 0; j < NE; ++j) {
-                const int o = r * DKP + c0 + j;
-                const float G = sG[o], kv = sK[o];
-                sK[o] = kv * __builtin_amdgcn_exp2f(G);
-                sQ[o] *= __builtin_amdgcn_exp2f(G);
-                sG[o] = kv * __builtin_amdgcn_exp2f(-G);
-            }
-            __syncthreads();
-            m = mm(m, sK + 16 * tm * DKP, DKP, 1, sG + 16 * tn * DKP, 1, DKP, DK);
-            pp = mm(pp, sQ + 16 * tm * DKP, DKP, 1, sG + 16 * tn * DKP, 1, DKP, DK);
+        for (int j = 0; j < NE; ++j) {
+            const int o = r * DKP + c0 + j;
+            const float G = sG[o], kv = sK[o];
+            sK[o] = kv * __builtin_amdgcn_exp2f(G);
+            sQ[o] *= __builtin_amdgcn_exp2f(G);
+            sG[o] = kv * __builtin_amdgcn_exp2f(-G);
         }
+        __syncthreads();
+        m = mm(m, sK + 16 * tm * DKP, DKP, 1, sG + 16 * tn * DKP, 1, DKP, DK);
+        pp = mm(pp, sQ + 16 * tm * DKP, DKP, 1, sG + 16 * tn * DKP, 1, DKP, DK);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int row = 16 * tm + 4 * lj + i, col = 16 * tn + lr;
@@ -458,14 +447,11 @@ __global__ void __launch_bounds__(NT) bwd_prep_kernel(Params p) {
         }
     }
     __syncthreads();
-    constexpr bool kBf16 = std::is_same<Tin, bf16_t>::value;
     float *gT = p.wT + wi * C * C, *gP = p.wP + wi * C * C, *gM = p.wM + wi * C * C;
     {
         const int r = (tid * 4) / C, i = (tid * 4) % C;
-        // fp32 P: the fp32 kernels, and for bf16 inputs only the exact chunks'
-        if (!kBf16 || exact)
-            *reinterpret_cast<float4 *>(gP + tid * 4) =
-                make_float4(sP[r * CP + i], sP[r * CP + i + 1], sP[r * CP + i + 2], sP[r * CP + i + 3]);
+        *reinterpret_cast<float4 *>(gP + tid * 4) =
+            make_float4(sP[r * CP + i], sP[r * CP + i + 1], sP[r * CP + i + 2], sP[r * CP + i + 3]);
         *reinterpret_cast<float4 *>(gM + tid * 4) =
             make_float4(sM[r * CP + i], sM[r * CP + i + 1], sM[r * CP + i + 2], sM[r * CP + i + 3]);
     }
@@ -503,19 +489,6 @@ __global__ void __launch_bounds__(NT) bwd_prep_kernel(Params p) {
         const int r = (tid * 4) / C, i = (tid * 4) % C;
         *reinterpret_cast<float4 *>(gT + tid * 4) =
             make_float4(sT[r * CP + i], sT[r * CP + i + 1], sT[r * CP + i + 2], sT[r * CP + i + 3]);
-        if constexpr (kBf16) {
-            // the state chains' bf16 operands: T, T^T and P^T, row-major
-            bf16x4 a, b, c;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                a[j] = (__bf16)sT[r * CP + i + j];
-                b[j] = (__bf16)sT[(i + j) * CP + r];
-                c[j] = (__bf16)sP[(i + j) * CP + r];
-            }
-            *reinterpret_cast<bf16x4 *>(p.wTb + wi * C * C + tid * 4) = a;
-            *reinterpret_cast<bf16x4 *>(p.wTt + wi * C * C + tid * 4) = b;
-            *reinterpret_cast<bf16x4 *>(p.wPt + wi * C * C + tid * 4) = c;
-        }
     }
 }
 
@@ -1162,41 +1135,40 @@ __device__ __forceinline__ void store_t(__bf16 *dst, int pitch, int tm, int tn, 
     *reinterpret_cast<bf16x4 *>(dst + (16 * tn + lr) * pitch + 16 * tm + 4 * lj) = x;
 }
 
-// One workgroup of 8 waves per (sequence, head, 64-column slice of d_v).
-// Raw k and q sit in LDS so that the scaling step can run one thread per key
-// channel: its row-major outputs are then contiguous across lanes and its
-// transposed ones are one vector store per thread, with no bank conflicts.
-// Each chunk takes four barriers: the next chunk's inputs go to LDS in the
-// same step as the state update, and its scaling (running gate sums
-// included) in the same step as the state's store.
+// The gradient chain for bf16 inputs: one workgroup of 8 waves per
+// (sequence, head, 64-column slice of d_v).  Raw k and q sit in LDS so that
+// the scaling step can run one thread per key channel: its row-major outputs
+// are then contiguous across lanes and its transposed ones are one vector
+// store per thread, with no bank conflicts.  Each chunk takes four barriers:
+// the next chunk's inputs go to LDS in the same step as the state-gradient
+// update, and its scaling (running gate sums included) in the same step as
+// the store of the state gradient.
 constexpr int W2 = 64;                 // d_v columns per chain workgroup
-template <int DK, bool GRAD> struct ChainLayout {
-    static constexpr int DKP = DK + 1, DKB = DK + 8, CB = C + 8, W2P = W2 + 1;
+template <int DK> struct ChainLayout {
+    static constexpr int DKP = DK + 1, DKB = DK + 8, CB = C + 8;
     static constexpr int G = 0;                            // fp32 [C][DKP]: log2 gates
     static constexpr int KRAW = G + 4 * C * DKP;           // bf16 [C][DKB]
-    static constexpr int QRAW = KRAW + 2 * C * DKB;        // bf16 [C][DKB] (gradient chain)
-    static constexpr int XT = QRAW + (GRAD ? 2 * C * DKB : 0);   // bf16 [W2][DKB]: S^T / D^T
-    static constexpr int KA = XT + 2 * W2 * DKB;           // bf16 [C][DKB]: K_up / K_right
-    static constexpr int KT1 = KA + 2 * C * DKB;           // bf16 [DK][CB]: K_right^T / Q_up^T
-    static constexpr int KT2 = KT1 + 2 * DK * CB;          // bf16 [DK][CB]: K_up^T (gradient chain)
-    static constexpr int M1 = KT2 + (GRAD ? 2 * DK * CB : 0);    // bf16 [C][CB]: T / T^T
-    static constexpr int M2 = M1 + 2 * C * CB;             // bf16 [C][CB]: P^T (gradient chain)
-    static constexpr int Y1 = M2 + (GRAD ? 2 * C * CB : 0);      // bf16 [W2][CB]: (beta X)^T / dO^T x 2
-    static constexpr int Y2 = Y1 + (GRAD ? 4 : 2) * W2 * CB;     // bf16 [W2][CB]: U^T / dU^T
-    static constexpr int Y3 = Y2 + 2 * W2 * CB;            // bf16 [W2][CB]: (-dX)^T (gradient chain)
-    static constexpr int V = Y3 + (GRAD ? 2 * W2 * CB : 0);      // fp32 [C][W2P] x 2: V (state chain)
-    static constexpr int GC = V + (GRAD ? 0 : 8 * C * W2P);       // fp32 [DK]
+    static constexpr int QRAW = KRAW + 2 * C * DKB;        // bf16 [C][DKB]
+    static constexpr int XT = QRAW + 2 * C * DKB;          // bf16 [W2][DKB]: D^T
+    static constexpr int KA = XT + 2 * W2 * DKB;           // bf16 [C][DKB]: K_right
+    static constexpr int KT1 = KA + 2 * C * DKB;           // bf16 [DK][CB]: Q_up^T
+    static constexpr int KT2 = KT1 + 2 * DK * CB;          // bf16 [DK][CB]: K_up^T
+    static constexpr int M1 = KT2 + 2 * DK * CB;           // bf16 [C][CB]: T^T
+    static constexpr int M2 = M1 + 2 * C * CB;             // bf16 [C][CB]: P^T
+    static constexpr int Y1 = M2 + 2 * C * CB;             // bf16 [W2][CB] x 2: dO^T
+    static constexpr int Y2 = Y1 + 4 * W2 * CB;            // bf16 [W2][CB]: dU^T
+    static constexpr int Y3 = Y2 + 2 * W2 * CB;            // bf16 [W2][CB]: (-dX)^T
+    static constexpr int GC = Y3 + 2 * W2 * CB;            // fp32 [DK]
     static constexpr int GAM = GC + 4 * DK;
     static constexpr int SB = GAM + 4 * DK;                // fp32 [C]
     static constexpr int BYTES = SB + 4 * C;
 };
 
-// Running log2-gate sums G (inclusive) and K_up = k 2^G, K_right = k 2^{G_c - G}
-// (state chain: K_up row-major, K_right transposed), or K_right row-major and
-// Q_up, K_up transposed (gradient chain); gc = G_c and gamma = 2^G_c.
+// Running log2-gate sums G (inclusive), K_right = k 2^{G_c - G} row-major and
+// Q_up = q 2^G, K_up = k 2^G transposed; gc = G_c and gamma = 2^G_c.
 // Thread (channel c, block of RPT rows) reads its channel's 32 raw log2 gates
 // itself, so no separate pass over the gates is needed.
-template <int DK, bool GRAD>
+template <int DK>
 __device__ __forceinline__ void chain_scale(const float *sG, const __bf16 *kraw, const __bf16 *qraw,
                                             float *gc, float *gam, __bf16 *rowA, __bf16 *trA,
                                             __bf16 *trB) {
@@ -1227,16 +1199,8 @@ __device__ __forceinline__ void chain_scale(const float *sG, const __bf16 *kraw,
             if (r0 == b * RPT) G = g[b * RPT + i];
         const float kv = (float)kraw[r * DKB + c];
         const float E = __builtin_amdgcn_exp2f(G), R = __builtin_amdgcn_exp2f(tot - G);
-        __bf16 a, bb;
-        if constexpr (GRAD) {
-            rowA[r * DKB + c] = (__bf16)(kv * R);
-            a = (__bf16)((float)qraw[r * DKB + c] * E);
-            bb = (__bf16)(kv * E);
-        } else {
-            rowA[r * DKB + c] = (__bf16)(kv * E);
-            a = (__bf16)(kv * R);
-            bb = a;
-        }
+        rowA[r * DKB + c] = (__bf16)(kv * R);
+        const __bf16 a = (__bf16)((float)qraw[r * DKB + c] * E), bb = (__bf16)(kv * E);
         if constexpr (RPT >= 8) {
             ta[i >> 3][i & 7] = a;
             tb[i >> 3][i & 7] = bb;
@@ -1249,31 +1213,29 @@ __device__ __forceinline__ void chain_scale(const float *sG, const __bf16 *kraw,
 #pragma unroll
         for (int v = 0; v < RPT / 8; ++v) {
             *reinterpret_cast<bf16x8 *>(trA + c * CB + r0 + 8 * v) = ta[v];
-            if constexpr (GRAD) *reinterpret_cast<bf16x8 *>(trB + c * CB + r0 + 8 * v) = tb[v];
+            *reinterpret_cast<bf16x8 *>(trB + c * CB + r0 + 8 * v) = tb[v];
         }
     } else {
         *reinterpret_cast<bf16x4 *>(trA + c * CB + r0) = ua;
-        if constexpr (GRAD) *reinterpret_cast<bf16x4 *>(trB + c * CB + r0) = ub;
+        *reinterpret_cast<bf16x4 *>(trB + c * CB + r0) = ub;
     }
 }
 
-// raw k (and q) rows of a chunk into LDS as bf16, log2 gates and beta as fp32
-template <int DK, bool WITH_Q>
-__device__ __forceinline__ void chain_store_in(const Params &p, const ChunkIn<bf16_t, DK, WITH_Q, 16> &in,
+// raw k and q rows of a chunk into LDS as bf16, log2 gates and beta as fp32
+template <int DK>
+__device__ __forceinline__ void chain_store_in(const Params &p, const ChunkIn<bf16_t, DK, true, 16> &in,
                                                __bf16 *kraw, __bf16 *qraw, float *sG, float *sB) {
     constexpr int DKB = DK + 8, NE = DK / 16;
     const int tid = threadIdx.x, r = tid >> 4, c0 = (tid & 15) * NE;
     if constexpr (NE == 8) {
         *reinterpret_cast<uint4 *>(kraw + r * DKB + c0) =
             in.k.ok ? make_uint4(in.k.w[0], in.k.w[1], in.k.w[2], in.k.w[3]) : make_uint4(0, 0, 0, 0);
-        if constexpr (WITH_Q)
-            *reinterpret_cast<uint4 *>(qraw + r * DKB + c0) =
-                in.q.ok ? make_uint4(in.q.w[0], in.q.w[1], in.q.w[2], in.q.w[3]) : make_uint4(0, 0, 0, 0);
+        *reinterpret_cast<uint4 *>(qraw + r * DKB + c0) =
+            in.q.ok ? make_uint4(in.q.w[0], in.q.w[1], in.q.w[2], in.q.w[3]) : make_uint4(0, 0, 0, 0);
     } else {
         *reinterpret_cast<uint2 *>(kraw + r * DKB + c0) = in.k.ok ? make_uint2(in.k.w[0], in.k.w[1]) : make_uint2(0, 0);
-        if constexpr (WITH_Q)
-            *reinterpret_cast<uint2 *>(qraw + r * DKB + c0) =
-                in.q.ok ? make_uint2(in.q.w[0], in.q.w[1]) : make_uint2(0, 0);
+        *reinterpret_cast<uint2 *>(qraw + r * DKB + c0) =
+            in.q.ok ? make_uint2(in.q.w[0], in.q.w[1]) : make_uint2(0, 0);
     }
     in.store_gb(p, sG, sB);
 }
@@ -1295,162 +1257,8 @@ __device__ __forceinline__ void chain_unit(const Params &p, int b, int &unit, in
 }
 
 template <int DK>
-__global__ void __launch_bounds__(NT2) bwd_states_bf16_kernel(Params p) {
-    using L = ChainLayout<DK, false>;
-    constexpr int DKB = L::DKB, CB = L::CB, W2P = L::W2P, NTW = DK / 32;   // 4 or 2 state tiles per wave
-    __shared__ __attribute__((aligned(16))) unsigned char smem[L::BYTES];
-    float *sG = reinterpret_cast<float *>(smem + L::G);
-    __bf16 *kraw = reinterpret_cast<__bf16 *>(smem + L::KRAW);
-    __bf16 *St = reinterpret_cast<__bf16 *>(smem + L::XT);
-    __bf16 *Kub = reinterpret_cast<__bf16 *>(smem + L::KA);
-    __bf16 *Krt = reinterpret_cast<__bf16 *>(smem + L::KT1);
-    __bf16 *Tb = reinterpret_cast<__bf16 *>(smem + L::M1);
-    __bf16 *BXt = reinterpret_cast<__bf16 *>(smem + L::Y1);
-    __bf16 *Ut = reinterpret_cast<__bf16 *>(smem + L::Y2);
-    float *sV0 = reinterpret_cast<float *>(smem + L::V);       // V of even / odd chunks
-    float *gc = reinterpret_cast<float *>(smem + L::GC);
-    float *gam = reinterpret_cast<float *>(smem + L::GAM);
-    float *sB = reinterpret_cast<float *>(smem + L::SB);
-    int unit, slice;
-    chain_unit(p, blockIdx.x, unit, slice);
-    const int s = unit / p.H, h = unit % p.H, col0 = slice * W2;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, lj = lane >> 4;
-    const int vr = tid >> 4, vc = (tid & 15) * 4;            // C x W2 values of this thread
-    const int t4 = (tid & 255) * 4;                          // C x C values (first 256 threads)
-    long t0s, base;
-    int len;
-    seq_info(p, s, t0s, len, base);
-    const int nch = (len + C - 1) / C;
-    ChunkIn<bf16_t, DK, false, 16> in;
-    Seg<bf16_t, 4> vin;
-    Seg<bf16_t, 4> tin;
-    auto issue = [&](int n) {
-        const long t0 = t0s + (long)n * C;
-        const int cl = len - n * C < C ? len - n * C : C;
-        in.load(p, t0, cl, h);
-        vin.load(p.v, ((size_t)(t0 + vr) * p.H + h) * p.DV + col0 + vc, vr < cl);
-        tin.load(p.wTb, ((size_t)(base + n) * p.H + h) * C * C + t4, tid < 256);
-    };
-    // chunk n's inputs into LDS (V into the buffer of n's parity)
-    auto stage = [&](int n) {
-        chain_store_in<DK, false>(p, in, kraw, nullptr, sG, sB);
-        float *sV = sV0 + (n & 1) * C * W2P;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) sV[vr * W2P + vc + j] = vin.get(j);
-        if (tid < 256) *reinterpret_cast<uint2 *>(Tb + (t4 / C) * CB + t4 % C) = make_uint2(tin.w[0], tin.w[1]);
-    };
-    f32x4 S[NTW];
-#pragma unroll
-    for (int x = 0; x < NTW; ++x) {
-        const int tt = wave * NTW + x, tm = tt >> 2, tn = tt & 3;
-        load_tile(S[x], p.S0, ((size_t)s * p.H + h) * DK + 16 * tm, p.DV, col0 + 16 * tn);
-        // the initial state has landed before the loop (otherwise the wait for
-        // it would sit inside the loop, draining the memory queue every chunk)
-        S[x] = pinned(S[x]);
-    }
-    // per-lane byte offsets of this lane's tile elements (fixed for the sequence)
-    uint32_t oS[NTW][4], oX[4];
-#pragma unroll
-    for (int x = 0; x < NTW; ++x) {
-        const int tt = wave * NTW + x, tm = tt >> 2, tn = tt & 3;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            oS[x][i] = pinned((uint32_t)(((16 * tm + 4 * lj + i) * p.DV + 16 * tn + lr) * 2));
-    }
-    const int xm = wave >> 2, xn = wave & 3;                 // this wave's C x W2 tile
-#pragma unroll
-    for (int i = 0; i < 4; ++i) oX[i] = pinned((uint32_t)(((16 * xm + 4 * lj + i) * p.DV + 16 * xn + lr) * 2));
-    uint32_t dS[NTW][4], dX[4], dU[4];                       // stored values, kept until the next chunk
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        dX[i] = 0u;
-        dU[i] = 0u;
-#pragma unroll
-        for (int x = 0; x < NTW; ++x) dS[x][i] = 0u;
-    }
-    // the state entering chunk n: to S^T in LDS and to the workspace
-    auto put_state = [&](int n) {
-        const __amdgpu_buffer_rsrc_t r =
-            brsrc(reinterpret_cast<bf16_t *>(p.wS) + ((size_t)(base + n) * p.H + h) * DK * p.DV + col0);
-#pragma unroll
-        for (int x = 0; x < NTW; ++x) {
-            const int tt = wave * NTW + x, tm = tt >> 2, tn = tt & 3;
-            store_t(St, DKB, tm, tn, S[x]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                asm volatile("" ::"v"(dS[x][i]));
-                dS[x][i] = to_bf16(S[x][i]).x;
-                bst16(dS[x][i], r, oS[x][i]);
-            }
-        }
-    };
-    if (nch > 0) {
-        issue(0);
-        stage(0);
-        if (nch > 1) issue(1);
-        __syncthreads();
-        put_state(0);
-        chain_scale<DK, false>(sG, kraw, nullptr, gc, gam, Kub, Krt, nullptr);
-        __syncthreads();
-    }
-    for (int n = 0; n < nch; ++n) {
-        const size_t wi = (size_t)(base + n) * p.H + h;
-        const float *sV = sV0 + (n & 1) * C * W2P;
-        // (beta X)^T, X = V - K_up S
-        {
-            f32x4 a = {0.f, 0.f, 0.f, 0.f};
-            a = mmb(a, Kub + 16 * xm * DKB, DKB, St + 16 * xn * DKB, DKB, DK);
-            const __amdgpu_buffer_rsrc_t r = brsrc(p.wX + wi * C * p.DV + col0);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = 16 * xm + 4 * lj + i;
-                const float x = sV[row * W2P + 16 * xn + lr] - a[i];
-                asm volatile("" ::"v"(dX[i]));
-                dX[i] = to_bf16(x).x;
-                bst16(dX[i], r, oX[i]);                       // X, for the gradient kernel
-                a[i] = sB[row] * x;
-            }
-            store_t(BXt, CB, xm, xn, a);
-        }
-        __syncthreads();
-        // U^T, U = T (beta X)
-        {
-            f32x4 a = {0.f, 0.f, 0.f, 0.f};
-            a = mmb(a, Tb + 16 * xm * CB, CB, BXt + 16 * xn * CB, CB, C);
-            store_t(Ut, CB, xm, xn, a);
-            const __amdgpu_buffer_rsrc_t r = brsrc(p.wU + wi * C * p.DV + col0);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                asm volatile("" ::"v"(dU[i]));
-                dU[i] = to_bf16(a[i]).x;
-                bst16(dU[i], r, oX[i]);
-            }
-        }
-        __syncthreads();
-        // S = Diag(gamma) S + K_right^T U; the next chunk's inputs to LDS meanwhile
-#pragma unroll
-        for (int x = 0; x < NTW; ++x) {
-            const int tt = wave * NTW + x, tm = tt >> 2, tn = tt & 3;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) S[x][i] *= gam[16 * tm + 4 * lj + i];
-            S[x] = mmb(S[x], Krt + 16 * tm * CB, CB, Ut + 16 * tn * CB, CB, C);
-        }
-        if (n + 1 < nch) {
-            stage(n + 1);
-            if (n + 2 < nch) issue(n + 2);
-        }
-        __syncthreads();
-        if (n + 1 < nch) {
-            put_state(n + 1);
-            chain_scale<DK, false>(sG, kraw, nullptr, gc, gam, Kub, Krt, nullptr);
-        }
-        __syncthreads();
-    }
-}
-
-template <int DK>
 __global__ void __launch_bounds__(NT2) bwd_dstates_bf16_kernel(Params p) {
-    using L = ChainLayout<DK, true>;
+    using L = ChainLayout<DK>;
     constexpr int DKB = L::DKB, CB = L::CB, NTW = DK / 32;
     __shared__ __attribute__((aligned(16))) unsigned char smem[L::BYTES];
     float *sG = reinterpret_cast<float *>(smem + L::G);
@@ -1498,7 +1306,7 @@ __global__ void __launch_bounds__(NT2) bwd_dstates_bf16_kernel(Params p) {
     };
     // chunk n's inputs into LDS (dO^T into the buffer of n's parity)
     auto stage = [&](int n) {
-        chain_store_in<DK, true>(p, in, kraw, qraw, sG, sB);
+        chain_store_in<DK>(p, in, kraw, qraw, sG, sB);
         bf16x4 ov;
 #pragma unroll
         for (int i = 0; i < 4; ++i) ov[i] = (__bf16)oin[i].get();
@@ -1558,7 +1366,7 @@ __global__ void __launch_bounds__(NT2) bwd_dstates_bf16_kernel(Params p) {
         if (nch > 1) issue(nch - 2);
         __syncthreads();
         put_grad(nch - 1);
-        chain_scale<DK, true>(sG, kraw, qraw, gc, gam, Krb, Qt, Kt);
+        chain_scale<DK>(sG, kraw, qraw, gc, gam, Krb, Qt, Kt);
         __syncthreads();
     }
     for (int n = nch - 1; n >= 0; --n) {
@@ -1616,7 +1424,7 @@ __global__ void __launch_bounds__(NT2) bwd_dstates_bf16_kernel(Params p) {
         __syncthreads();
         if (n > 0) {
             put_grad(n - 1);
-            chain_scale<DK, true>(sG, kraw, qraw, gc, gam, Krb, Qt, Kt);
+            chain_scale<DK>(sG, kraw, qraw, gc, gam, Krb, Qt, Kt);
         }
         __syncthreads();
     }
@@ -1985,12 +1793,21 @@ template <typename Tin, int DK>
 hipError_t launch(const Params &p, long nslot, int nseq, hipStream_t stream) {
     const dim3 gchunks((unsigned)nslot, (unsigned)p.H);
     const unsigned gunits = (unsigned)((long)nseq * p.H * (p.DV / W));
-    if (nslot > 0) hipLaunchKernelGGL((bwd_prep_kernel<Tin, DK>), gchunks, dim3(NT), 0, stream, p);
     if constexpr (std::is_same<Tin, bf16_t>::value) {
+        // the forward's fused chunk kernel, keeping what the gradients need
+        // (states, X, U, T, M0, T^T, P^T, flags), then the gradient chain
+        const int units = nseq * p.H;
+        if (units > 0) {
+            const hipError_t e = chunked_ws_save_launch(
+                p.q, p.k, p.v, p.g, p.beta, p.gate, p.S0, p.cu, nseq, p.T, p.H, DK, p.DV,
+                chunked_slice_width(units, p.DV), reinterpret_cast<bf16_t *>(p.wS), p.wX, p.wU, p.wTt,
+                p.wPt, p.wT, p.wM, p.wP, p.wF, stream);
+            if (e != hipSuccess) return e;
+        }
         const unsigned gu2 = (unsigned)((long)nseq * p.H * (p.DV / W2));
-        hipLaunchKernelGGL((bwd_states_bf16_kernel<DK>), dim3(gu2), dim3(NT2), 0, stream, p);
         hipLaunchKernelGGL((bwd_dstates_bf16_kernel<DK>), dim3(gu2), dim3(NT2), 0, stream, p);
     } else {
+        if (nslot > 0) hipLaunchKernelGGL((bwd_prep_kernel<Tin, DK>), gchunks, dim3(NT), 0, stream, p);
         hipLaunchKernelGGL((bwd_states_kernel<Tin, DK>), dim3(gunits), dim3(NT), 0, stream, p);
         hipLaunchKernelGGL((bwd_dstates_kernel<Tin, DK>), dim3(gunits), dim3(NT), 0, stream, p);
     }
@@ -2022,7 +1839,7 @@ size_t bwd_workspace_bytes(int B, int T, int H, int dk, int dv, int num_seqs) {
     const size_t f = (per * sizeof(int32_t) + 255) & ~(size_t)255;
     const size_t x = (per * bwd::C * dv * sizeof(bf16_t) + 255) & ~(size_t)255;
     const size_t y = (per * bwd::C * bwd::C * sizeof(bf16_t) + 255) & ~(size_t)255;
-    return 2 * a + 3 * b + f + 3 * x + 3 * y;
+    return 2 * a + 3 * b + f + 3 * x + 2 * y;
 }
 
 hipError_t bwd_launch(const void *q, const void *k, const void *v, const void *g, const void *beta,
@@ -2054,9 +1871,8 @@ hipError_t bwd_launch(const void *q, const void *k, const void *v, const void *g
         p.wdU = reinterpret_cast<bf16_t *>(wx + 2 * x);
         const size_t y = (per * bwd::C * bwd::C * sizeof(bf16_t) + 255) & ~(size_t)255;
         char *wy = wx + 3 * x;
-        p.wTb = reinterpret_cast<bf16_t *>(wy);
-        p.wTt = reinterpret_cast<bf16_t *>(wy + y);
-        p.wPt = reinterpret_cast<bf16_t *>(wy + 2 * y);
+        p.wTt = reinterpret_cast<bf16_t *>(wy);
+        p.wPt = reinterpret_cast<bf16_t *>(wy + y);
     }
     const long nslot = cu_seqlens ? (long)(T / bwd::C) + num_seqs + 1
                                   : (long)B * ((T + bwd::C - 1) / bwd::C);

@@ -47,6 +47,20 @@ struct WsParams {
     const int32_t *order;
     const int32_t *state_idx;   // slot map of S0 / S_T rows (NULL: row = sequence)
     int T, H, DV, units, nslices, pool;
+    // What the backward keeps of the forward (SAVE instantiation), per
+    // (chunk slot, head); a sequence's chunks take consecutive slots from
+    // floor(cu_seqlens[s] / 32) + s (packed) or s * ceil(T / 32) (dense):
+    //   wS  bf16 [d_k][d_v]  the state entering the chunk
+    //   wX  bf16 [32][d_v]   X = V - K_up S
+    //   wU  bf16 [32][d_v]   U = T Diag(beta) X
+    //   wT  fp32 [32][32]    T = (I + A)^{-1}
+    //   wM  fp32 [32][32]    M0 = strict_lower(K_up K_dn^T)  (A = Diag(beta) M0)
+    //   wP  fp32 [32][32]    P, written only for chunks flagged in wF
+    //   wTt, wPt  bf16 [32][32]  T^T and P^T
+    //   wF  int32            1 when some channel decays by more than 2^64 over the chunk
+    bf16_t *wS, *wX, *wU, *wTt, *wPt;
+    float *wT, *wM, *wP;
+    int32_t *wF;
 };
 
 namespace ws {
@@ -212,12 +226,12 @@ __device__ __forceinline__ void tri_pair(int pidx, int &r, int &i) {
 // P (bf16, slot).  Kept out of line: it runs only for chunks with extreme
 // decay, and its registers stay out of the hot path's budget.
 template <int DK>
-__device__ __attribute__((noinline)) void exact_ap(int lane, int cl, uint32_t tokk,
-                                                   uint32_t gstride, uint32_t gch, int prep,
-                                                   const bf16_t *bg, const bf16_t *bk,
-                                                   const bf16_t *bq, unsigned char *priv,
-                                                   float *pAt, bf16_t *sP, const float *pBeta,
-                                                   const float *pNorm)
+__device__ __forceinline__ void exact_ap_body(int lane, int cl, uint32_t tokk, uint32_t gstride,
+                                              uint32_t gch, int prep, const bf16_t *bg,
+                                              const bf16_t *bk, const bf16_t *bq,
+                                              unsigned char *priv, float *pAt, bf16_t *sP,
+                                              const float *pBeta, const float *pNorm, float *gM,
+                                              float *gP)
 {
     using namespace ws;
     constexpr int CPL = DK / 64;
@@ -289,16 +303,45 @@ __device__ __attribute__((noinline)) void exact_ap(int lane, int cl, uint32_t to
             tri_pair(pidx, r, i);
             pAt[i * LA + r] = (i < r) ? resA[u] * pBeta[r] : 0.0f;
             sP[idx4(r, i)] = to_bf16(resP[u]);
+            // for the backward (when asked): M0 and fp32 P, row-major
+            if (gM) gM[r * C + i] = (i < r) ? resA[u] : 0.0f;
+            if (gP) gP[r * C + i] = resP[u];
         }
     }
     // strict upper part of P
     for (int idx = lane; idx < C * C; idx += 64) {
         const int r = idx / C, i = idx % C;
-        if (i > r) sP[idx4(r, i)] = to_bf16(0.0f);
+        if (i > r) {
+            sP[idx4(r, i)] = to_bf16(0.0f);
+            if (gM) gM[idx] = 0.0f;
+            if (gP) gP[idx] = 0.0f;
+        }
     }
 }
+template <int DK>
+__device__ __attribute__((noinline)) void exact_ap(int lane, int cl, uint32_t tokk,
+                                                   uint32_t gstride, uint32_t gch, int prep,
+                                                   const bf16_t *bg, const bf16_t *bk,
+                                                   const bf16_t *bq, unsigned char *priv,
+                                                   float *pAt, bf16_t *sP, const float *pBeta,
+                                                   const float *pNorm)
+{
+    exact_ap_body<DK>(lane, cl, tokk, gstride, gch, prep, bg, bk, bq, priv, pAt, sP, pBeta, pNorm,
+                      nullptr, nullptr);
+}
+// the same, also writing M0 and fp32 P for the backward (either may be NULL)
+template <int DK>
+__device__ __attribute__((noinline)) void exact_ap_save(int lane, int cl, uint32_t tokk,
+                                                        uint32_t gstride, uint32_t gch,
+                                                        const bf16_t *bg, const bf16_t *bk,
+                                                        const bf16_t *bq, unsigned char *priv,
+                                                        float *pAt, bf16_t *sP, const float *pBeta,
+                                                        float *gM, float *gP)
+{
+    exact_ap_body<DK>(lane, cl, tokk, gstride, gch, 0, bg, bk, bq, priv, pAt, sP, pBeta, nullptr, gM, gP);
+}
 
-template <int DK, int NSTRIP, int GATE, int PREP>
+template <int DK, int NSTRIP, int GATE, int PREP, bool SAVE>
 __global__ __launch_bounds__(512, 1) void chunked_ws_kernel(WsParams p)
 {
     using namespace ws;
@@ -338,6 +381,8 @@ __global__ __launch_bounds__(512, 1) void chunked_ws_kernel(WsParams p)
     const int nchunks = (int)((len + C - 1) / C);
     const int col0 = slice * DVS;
     const long strow = state_row(p.state_idx, p.pool, seq);
+    // first workspace slot of the sequence (SAVE)
+    const long sbase = !SAVE ? 0 : p.cu_seqlens ? t0 / C + seq : (long)seq * ((p.T + C - 1) / C);
 
     const int tid = threadIdx.x;
     // the wave index is uniform across a wave; say so, so that everything
@@ -428,9 +473,14 @@ __global__ __launch_bounds__(512, 1) void chunked_ws_kernel(WsParams p)
             // the next chunk's loads at once (a whole chunk of latency slack).
             // Only the v loads must have landed, not the o stores issued after
             // them: vmcnt counts both, in order, so wait down to the 8 * NSTRIP
-            // stores (without this the compiler waits for everything here)
-            if constexpr (NSTRIP == 1) __builtin_amdgcn_s_waitcnt(0x0F78);   // vmcnt(8)
-            else __builtin_amdgcn_s_waitcnt(0x4F70);                        // vmcnt(16)
+            // stores (without this the compiler waits for everything here); the
+            // SAVE instantiation issues 8 per fragment of S, X and U instead
+            // (the counter field holds at most 63)
+            {
+                constexpr int nst = SAVE ? (8 * NRUN + 16) * NSTRIP : 8 * NSTRIP;
+                constexpr int vm = nst < 63 ? nst : 63;
+                __builtin_amdgcn_s_waitcnt(0x0F70 | (vm & 15) | ((vm >> 4) << 14));
+            }
             float xv[NSTRIP][8];
             const uint32_t vsh = (mr & 1) ? 0u : 16u;   // odd columns are the high half
 #pragma unroll
@@ -460,10 +510,10 @@ __global__ __launch_bounds__(512, 1) void chunked_ws_kernel(WsParams p)
                     for (int rr = 0; rr < NRUN; ++rr) {
                         const int off = row * DK + (((4 * rr + jg) ^ kr) << 3);
                         fku[h][rr] = *reinterpret_cast<const bf16x8 *>(&sKU[off]);
-                        fqu[h][rr] = *reinterpret_cast<const bf16x8 *>(&sQU[off]);
+                        if constexpr (!SAVE) fqu[h][rr] = *reinterpret_cast<const bf16x8 *>(&sQU[off]);
                     }
                     ftp[h] = *reinterpret_cast<const bf16x8 *>(&sTp[row * C + ((jg ^ key4(row)) << 3)]);
-                    fpm[h] = *reinterpret_cast<const bf16x8 *>(&sP[row * C + ((jg ^ key4(row)) << 3)]);
+                    if constexpr (!SAVE) fpm[h] = *reinterpret_cast<const bf16x8 *>(&sP[row * C + ((jg ^ key4(row)) << 3)]);
                 }
             };
             auto read_kr = [&]() {
@@ -489,6 +539,28 @@ __global__ __launch_bounds__(512, 1) void chunked_ws_kernel(WsParams p)
                 bf16x8 sf[NRUN];
 #pragma unroll
                 for (int rr = 0; rr < NRUN; ++rr) sf[rr] = pack8(S[s][2 * rr], S[s][2 * rr + 1]);
+                // the lane's bf16 values of a [rows][d_v] array, element e of a
+                // fragment being row r0 + e of column co
+                auto save_col = [&](bf16_t *base, uint32_t rows, const bf16x8 &f, uint32_t r0) {
+                    const __amdgpu_buffer_rsrc_t rs = buf_rsrc(base + ((size_t)(sbase + n) * H + head) * rows * DV + col0);
+                    const uint32_t co = 16 * (w + 4 * s) + mr;
+                    // the fragment as four words, element e the half e & 1 of word e / 2
+                    // (element-wise bit casts of the bf16 vector do not survive here)
+                    const uint4 fw = __builtin_bit_cast(uint4, f);
+                    const uint32_t wd[4] = {fw.x, fw.y, fw.z, fw.w};
+                    // one address register per fragment; the row step is uniform
+                    const uint32_t voff = (r0 * (uint32_t)DV + co) * 2u;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        __builtin_amdgcn_raw_buffer_store_b16(
+                            (unsigned short)((e & 1) ? (wd[e >> 1] >> 16) : wd[e >> 1]), rs, voff,
+                            e * DV * 2, 0);
+                };
+                if constexpr (SAVE) {
+                    // S entering the chunk: fragment rr holds rows 32 rr + 8 jg + e
+#pragma unroll
+                    for (int rr = 0; rr < NRUN; ++rr) save_col(p.wS, DK, sf[rr], 32 * rr + 8 * jg);
+                }
                 if constexpr (NSTRIP > 1) read_frags();
                 // the decay of the old state does not wait for the chain below
                 if constexpr (NSTRIP == 1) {
@@ -514,14 +586,17 @@ __global__ __launch_bounds__(512, 1) void chunked_ws_kernel(WsParams p)
 #pragma unroll
                     for (int h = 0; h < 2; ++h) {
                         X[h] = mfma_bf16(fku[h][rr], sf[rr], X[h]);
-                        O[h] = mfma_bf16(fqu[h][rr], sf[rr], O[h]);
+                        if constexpr (!SAVE) O[h] = mfma_bf16(fqu[h][rr], sf[rr], O[h]);
                     }
                 // U = T' X
                 const bf16x8 xf = pack8(X[0], X[1]);
+                // chunk rows 8 jg + e (crow): X and U to the workspace
+                if constexpr (SAVE) save_col(p.wX, C, xf, 8 * jg);
                 f32x4 U[2];
 #pragma unroll
                 for (int h = 0; h < 2; ++h) U[h] = mfma_bf16(ftp[h], xf, f32x4{0.f, 0.f, 0.f, 0.f});
                 const bf16x8 uf = pack8(U[0], U[1]);
+                if constexpr (SAVE) save_col(p.wU, C, uf, 8 * jg);
                 // S = Diag(gamma) S + K_right^T U;  O += P U
                 if constexpr (NSTRIP > 1) {
 #pragma unroll
@@ -539,17 +614,19 @@ __global__ __launch_bounds__(512, 1) void chunked_ws_kernel(WsParams p)
 #pragma unroll
                     for (int tt = 0; tt < NKT; ++tt) S[s][tt] = mfma_bf16(fkr[tt], uf, S[s][tt]);
                 }
+                if constexpr (!SAVE) {
 #pragma unroll
-                for (int h = 0; h < 2; ++h) O[h] = mfma_bf16(fpm[h], uf, O[h]);
-                // store O
+                    for (int h = 0; h < 2; ++h) O[h] = mfma_bf16(fpm[h], uf, O[h]);
+                    // store O
 #pragma unroll
-                for (int h = 0; h < 2; ++h)
+                    for (int h = 0; h < 2; ++h)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int row = crow(h, 4 * jg + i);
-                        const uint32_t off = row < cl ? vlane + (uint32_t)(4 * h + i) * tokv * 2u + 128u * s : OOB_OFF;
-                        __builtin_amdgcn_raw_buffer_store_b16(to_bf16(O[h][i]).x, ro, off, 0, 0);
-                    }
+                        for (int i = 0; i < 4; ++i) {
+                            const int row = crow(h, 4 * jg + i);
+                            const uint32_t off = row < cl ? vlane + (uint32_t)(4 * h + i) * tokv * 2u + 128u * s : OOB_OFF;
+                            __builtin_amdgcn_raw_buffer_store_b16(to_bf16(O[h][i]).x, ro, off, 0, 0);
+                        }
+                }
             }
             // all reads of the slot are done once their values were consumed
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
@@ -925,6 +1002,22 @@ __global__ __launch_bounds__(512, 1) void chunked_ws_kernel(WsParams p)
             }
         }
         const bool fast = __builtin_amdgcn_ballot_w64(!ok) == 0;
+        // SAVE: the backward's own test for its exact path, some channel
+        // decaying by more than 2^64 over the chunk
+        bool flag64 = false;
+        if constexpr (SAVE && GATE != GATE_NONE) {
+            bool big = false;
+            if constexpr (GATE == GATE_CHANNEL) {
+#pragma unroll
+                for (int e = 0; e < NCL; ++e) big = big || !(gam[e] >= 5.421010862427522e-20f);
+            } else {
+                big = !(gamh >= 5.421010862427522e-20f);
+            }
+            flag64 = __builtin_amdgcn_ballot_w64(big) != 0;
+        }
+        // the workspace of this chunk (SAVE; written by slice 0 only)
+        const size_t wcc = ((size_t)(sbase + n) * H + head) * C * C;
+        const bool keep = SAVE && slice == 0;
         __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
 
         // ---- A and P -----------------------------------------------------------
@@ -976,13 +1069,51 @@ __global__ __launch_bounds__(512, 1) void chunked_ws_kernel(WsParams p)
             }
             // upper block (0,1) of P is zero
             *reinterpret_cast<uint2 *>(&sP[idx4(mr, 16 + 4 * jg)]) = make_uint2(0u, 0u);
+            if (keep) {
+                // M0 (accA is -M0: the slot's K_up is negated), and P when flagged
+                float *gM = p.wM + wcc;
+#pragma unroll
+                for (int t = 0; t < 3; ++t) {
+                    const int R = (t == 0) ? 0 : 1, I = (t == 2) ? 1 : 0;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int row = 16 * R + 4 * jg + i, col = 16 * I + mr;
+                        gM[row * C + col] = col < row ? -accA[t][i] : 0.0f;
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) gM[(4 * jg + i) * C + 16 + mr] = 0.0f;
+                if (flag64) {
+                    float *gP = p.wP + wcc;
+#pragma unroll
+                    for (int t = 0; t < 3; ++t) {
+                        const int R = (t == 0) ? 0 : 1, I = (t == 2) ? 1 : 0;
+                        const int row = 16 * R + mr, c0 = 16 * I + 4 * jg;
+                        *reinterpret_cast<float4 *>(&gP[row * C + c0]) =
+                            make_float4(c0 <= row ? accP[t][0] : 0.0f, c0 + 1 <= row ? accP[t][1] : 0.0f,
+                                        c0 + 2 <= row ? accP[t][2] : 0.0f, c0 + 3 <= row ? accP[t][3] : 0.0f);
+                    }
+                    *reinterpret_cast<float4 *>(&gP[mr * C + 16 + 4 * jg]) = make_float4(0.f, 0.f, 0.f, 0.f);
+                }
+            }
         } else {
             // exact path for chunks whose decay leaves the range of K_dn
-            if constexpr (GATE == GATE_CHANNEL)
-                exact_ap<DK>(lane, cl, tokk, tokk, 1u, PREP, bg, bk, bq, priv, pAt, sP, pBeta, pNorm);
-            else if constexpr (GATE == GATE_HEAD)
-                exact_ap<DK>(lane, cl, tokk, (uint32_t)H, 0u, PREP, gg + tb, bk, bq, priv, pAt, sP, pBeta,
-                             pNorm);
+            if constexpr (SAVE) {
+                // (no input preparation in this instantiation)
+                float *gM = keep ? p.wM + wcc : nullptr;
+                float *gP = keep && flag64 ? p.wP + wcc : nullptr;
+                if constexpr (GATE == GATE_CHANNEL)
+                    exact_ap_save<DK>(lane, cl, tokk, tokk, 1u, bg, bk, bq, priv, pAt, sP, pBeta, gM, gP);
+                else if constexpr (GATE == GATE_HEAD)
+                    exact_ap_save<DK>(lane, cl, tokk, (uint32_t)H, 0u, gg + tb, bk, bq, priv, pAt, sP, pBeta,
+                                      gM, gP);
+            } else {
+                if constexpr (GATE == GATE_CHANNEL)
+                    exact_ap<DK>(lane, cl, tokk, tokk, 1u, PREP, bg, bk, bq, priv, pAt, sP, pBeta, pNorm);
+                else if constexpr (GATE == GATE_HEAD)
+                    exact_ap<DK>(lane, cl, tokk, (uint32_t)H, 0u, PREP, gg + tb, bk, bq, priv, pAt, sP, pBeta,
+                                 pNorm);
+            }
         }
         __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
 
@@ -1069,21 +1200,56 @@ __global__ __launch_bounds__(512, 1) void chunked_ws_kernel(WsParams p)
         }
 
         // next chunk's g and k (requested once the inverse no longer needs
-        // registers; not live across the out-of-line exact path)
-        if (n + NPROD < nchunks) load_gk(n + NPROD);
+        // registers; not live across the out-of-line exact path).  SAVE
+        // requests them after its stores below, which need registers too.
+        if constexpr (!SAVE) {
+            if (n + NPROD < nchunks) load_gk(n + NPROD);
+        }
 
         // ---- publish -------------------------------------------------------------
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
         if (lane == 0) __hip_atomic_store(&s_full[slot], n + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+
+        // ---- for the backward: T, T^T, P^T and the flag ----------------------------
+        // (the slot's P stays unchanged until the slot is freed, pT until the
+        // next chunk)
+        if (keep) {
+            const int r = lane >> 1, cb = (lane & 1) * 16;
+            const bool lower = (cb >> 4) <= (r >> 4), upper = (cb >> 4) >= (r >> 4);
+            float *gT = p.wT + wcc + r * C + cb;
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const float4 tv = *reinterpret_cast<const float4 *>(&pT[r * LA + cb + 4 * q4]);
+                *reinterpret_cast<float4 *>(gT + 4 * q4) = lower ? tv : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+            // row r of T^T and P^T: T[c][r] and P[c][r] for c = cb .. cb + 15
+            uint32_t tt[8], pt[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int c = cb + 2 * j;
+                tt[j] = upper ? pack2(pT[c * LA + r], pT[(c + 1) * LA + r]) : 0u;
+                pt[j] = (uint32_t)sP[idx4(c, r)].x | ((uint32_t)sP[idx4(c + 1, r)].x << 16);
+            }
+            uint4 *dT = reinterpret_cast<uint4 *>(p.wTt + wcc + r * C + cb);
+            uint4 *dP = reinterpret_cast<uint4 *>(p.wPt + wcc + r * C + cb);
+            dT[0] = make_uint4(tt[0], tt[1], tt[2], tt[3]);
+            dT[1] = make_uint4(tt[4], tt[5], tt[6], tt[7]);
+            dP[0] = make_uint4(pt[0], pt[1], pt[2], pt[3]);
+            dP[1] = make_uint4(pt[4], pt[5], pt[6], pt[7]);
+            if (lane == 0) p.wF[wcc / (C * C)] = flag64 ? 1 : 0;
+        }
+        if constexpr (SAVE) {
+            if (n + NPROD < nchunks) load_gk(n + NPROD);
+        }
     }
 }
 
-template <int DK, int NSTRIP, int GATE, int PREP>
+template <int DK, int NSTRIP, int GATE, int PREP, bool SAVE = false>
 static hipError_t launch_ws(const WsParams &p, hipStream_t stream)
 {
     const int groups = (p.units + 7) / 8;
     const dim3 grid(groups * 8 * p.nslices);
-    hipLaunchKernelGGL((chunked_ws_kernel<DK, NSTRIP, GATE, PREP>), grid, dim3(512), 0, stream, p);
+    hipLaunchKernelGGL((chunked_ws_kernel<DK, NSTRIP, GATE, PREP, SAVE>), grid, dim3(512), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -1113,7 +1279,7 @@ hipError_t chunked_ws_launch(const void *q, const void *k, const void *v, const 
                              const int32_t *cu_seqlens, const int32_t *order, int nseq, int T,
                              int H, int dk, int dv, int slice_width, hipStream_t stream)
 {
-    WsParams p;
+    WsParams p = {};
     p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta;
     p.S0 = S0; p.S_T = S_T; p.o = o;
     p.cu_seqlens = cu_seqlens;
@@ -1129,6 +1295,40 @@ hipError_t chunked_ws_launch(const void *q, const void *k, const void *v, const 
                            : launch_ws_gate<128, 1>(p, gate, prep, stream);
     return nstrip == 2 ? launch_ws_gate<64, 2>(p, gate, prep, stream)
                        : launch_ws_gate<64, 1>(p, gate, prep, stream);
+}
+
+template <int DK, int NSTRIP>
+static hipError_t launch_ws_save(const WsParams &p, int gate, hipStream_t stream)
+{
+    if (gate == GATE_HEAD) return launch_ws<DK, NSTRIP, GATE_HEAD, 0, true>(p, stream);
+    if (gate == GATE_NONE) return launch_ws<DK, NSTRIP, GATE_NONE, 0, true>(p, stream);
+    return launch_ws<DK, NSTRIP, GATE_CHANNEL, 0, true>(p, stream);
+}
+
+// The forward's chunk chain for the backward (bf16 inputs): no o and no final
+// state; per chunk and head the state entering it, X, U, T, M0, the bf16 T^T
+// and P^T, P where flagged and the flag, into the backward's workspace
+// (layouts as in WsParams).
+hipError_t chunked_ws_save_launch(const void *q, const void *k, const void *v, const void *g,
+                                  const void *beta, int gate, const float *S0,
+                                  const int32_t *cu_seqlens, int nseq, int T, int H, int dk, int dv,
+                                  int slice_width, bf16_t *wS, bf16_t *wX, bf16_t *wU, bf16_t *wTt,
+                                  bf16_t *wPt, float *wT, float *wM, float *wP, int32_t *wF,
+                                  hipStream_t stream)
+{
+    WsParams p = {};
+    p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta;
+    p.S0 = S0;
+    p.cu_seqlens = cu_seqlens;
+    p.T = T; p.H = H; p.DV = dv;
+    p.units = nseq * H;
+    p.nslices = dv / slice_width;
+    p.wS = wS; p.wX = wX; p.wU = wU; p.wTt = wTt; p.wPt = wPt;
+    p.wT = wT; p.wM = wM; p.wP = wP; p.wF = wF;
+    const int nstrip = slice_width / 64;
+    if (dk == 128)
+        return nstrip == 2 ? launch_ws_save<128, 2>(p, gate, stream) : launch_ws_save<128, 1>(p, gate, stream);
+    return nstrip == 2 ? launch_ws_save<64, 2>(p, gate, stream) : launch_ws_save<64, 1>(p, gate, stream);
 }
 
 }  // namespace kda
