@@ -127,6 +127,31 @@ def test_bwd_strong_decay(dt):
     _compare(_gpu(x, "channel"), _ref(x, "channel"), TOL[dt], "strong decay")
 
 
+@pytest.mark.parametrize("gate", ["channel", "head"])
+def test_bwd_decay_band(gate):
+    """Chunks decaying by e^-64 (about 2^-92) on some channels: the forward
+    pass still factorises them (its limit is 2^-100), the gradient kernels
+    take them entry by entry (their limit is 2^-64)."""
+    _say(f"[bwd decay band] gate={gate} bf16")
+    x = _case(1, 200, 2, 64, 64, torch.bfloat16, seed=59)
+    la = x["log_alpha"].float()
+    for t0 in range(32, 200, 96):
+        la[:, t0:t0 + 32, :, : 32] = -2.0            # chunk 1, 4, ...: 32 x -2 = -64
+    x["log_alpha"] = la.to(torch.bfloat16)
+    if gate == "head":
+        x["log_alpha"] = x["log_alpha"][..., 0].contiguous()
+    _compare(_gpu(x, gate), _ref(x, gate), TOL[torch.bfloat16], "decay band")
+
+
+def test_bwd_whole_dv_slices():
+    """512 (sequence, head) units: the forward's chunk kernel takes whole
+    d_v = 128 per workgroup (two strips per consumer wave)."""
+    lengths = [40, 33, 1, 64, 35, 0, 70, 32, 41, 39, 38, 37, 36, 2, 65, 31]
+    _say(f"[bwd 512 units] H=32 lengths={lengths} bf16")
+    x = _case(1, 0, 32, 64, 128, torch.bfloat16, seed=61, lengths=lengths)
+    _compare(_gpu(x, "channel"), _ref(x, "channel"), TOL[torch.bfloat16], "512 units")
+
+
 def test_bwd_without_initial_state_or_final_gradient():
     _say("[bwd S0=None dS_T=None] bf16")
     x = _case(2, 90, 2, 128, 64, torch.bfloat16, seed=53, s0=False, dst=False)
