@@ -52,7 +52,7 @@ _CSRC = os.path.join(ROOT, "gated_delta_rule_81_amd", "csrc")
 KERNEL_SOURCES = {
     "chunked_ws_kernel": [os.path.join(_CSRC, f) for f in ("kda_chunked_ws.hip", "kda_device.h")],
     "decode_step_kernel": [os.path.join(_CSRC, f) for f in ("kda_decode.hip", "kda_device.h")],
-    "bwd_kernels": [os.path.join(_CSRC, f) for f in ("kda_bwd.hip", "kda_device.h")],
+    "bwd_kernels": [os.path.join(_CSRC, f) for f in ("kda_bwd.hip", "kda_chunked_ws.hip", "kda_device.h")],
 }
 
 
@@ -192,7 +192,7 @@ def bench_backward(torch, kda, synth, steps=10, warmup=2):
                         # HBM bytes of all the call's kernels, workspace traffic included
                         "traffic": read_traffic("bwd_kernels_B4_H32_T8192_d128.pmc.md", "bwd_kernels"),
                         "algorithmic_bytes_per_call": nbytes,
-                        "kernels": ["bwd_prep_kernel", "bwd_states_bf16_kernel",
+                        "kernels": ["chunked_ws_kernel (saving instantiation)",
                                     "bwd_dstates_bf16_kernel", "bwd_grads_bf16_kernel",
                                     "bwd_grads_kernel (exact chunks only)"],
                         "source_sha256_16": kernel_sources_hash("bwd_kernels")}}
