@@ -814,34 +814,29 @@ __global__ __launch_bounds__(512, 1) void chunked_ws_kernel(WsParams p)
                 }
             }
         }
-        // exclusive prefix / suffix products over the row groups (lanes 16
-        // apart), by three lane shifts each, so that
+        // exclusive prefix / suffix products over the 4 row groups (the 16-lane
+        // rows of the wave), so that
         //   E_r = pre * prod_{j <= r, j in group} alpha_j,
         //   R_r = post * prod_{j > r, j in group} alpha_j,
         //   gamma = pre * tot * post.
+        // A two-step butterfly on the VALU: v_permlane16_swap gives every row
+        // the value of row r ^ 1, v_permlane32_swap the pair product of rows
+        // r ^ 2 and r ^ 3 (all lanes take part in both).
         float pre[NCL], post[NCL], gam[NCL], preh = 1.0f, posth = 1.0f, gamh = 1.0f;
         if constexpr (GATE != GATE_NONE) {
-            const int up16 = (lane - 16) << 2, up32 = (lane - 32) << 2;
-            const int dn16 = (lane + 16) << 2, dn32 = (lane + 32) << 2;
-            auto shf = [](float x, int addr) {
-                return __int_as_float(__builtin_amdgcn_ds_bpermute(addr, __float_as_int(x)));
-            };
-            // every lane takes part in each shift (all lanes active), and
-            // lanes without a group on that side select 1 afterwards
             auto scan = [&](float tv, float &pr, float &po) {
-                float t;
-                t = shf(tv, up16);
-                const float a = rg >= 1 ? t : 1.0f;
-                t = shf(a, up16);
-                const float b = a * (rg >= 1 ? t : 1.0f);
-                t = shf(b, up32);
-                pr = b * (rg >= 2 ? t : 1.0f);
-                t = shf(tv, dn16);
-                const float a2 = rg <= 2 ? t : 1.0f;
-                t = shf(a2, dn16);
-                const float b2 = a2 * (rg <= 2 ? t : 1.0f);
-                t = shf(b2, dn32);
-                po = b2 * (rg <= 1 ? t : 1.0f);
+                const uint32_t u = __float_as_uint(tv);
+                // with both operands u: result[0] holds row r - 1 on odd rows,
+                // result[1] row r + 1 on even rows
+                const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+                const float p1 = __uint_as_float((rg & 1) ? a[0] : a[1]);
+                const uint32_t pu = __float_as_uint(tv * p1);     // v_{2m} v_{2m+1}
+                // result[0] holds the lower pair on rows 2, 3; result[1] the upper on rows 0, 1
+                const auto b = __builtin_amdgcn_permlane32_swap(pu, pu, false, false);
+                const float p2 = __uint_as_float(rg >= 2 ? b[0] : b[1]);
+                const float pre1 = (rg & 1) ? p1 : 1.0f, post1 = (rg & 1) ? 1.0f : p1;
+                pr = rg >= 2 ? pre1 * p2 : pre1;
+                po = rg >= 2 ? post1 : post1 * p2;
             };
             if constexpr (GATE == GATE_CHANNEL) {
 #pragma unroll
