@@ -382,6 +382,17 @@ def cpu_baseline(torch, x, target_s=10.0, max_units=128):
             break
         n = min(max_units, max(n + 1, int(n * target_s / max(el, 1e-3) * 1.1)))
     token_heads_per_s = n * T / el
+    # the same oracle on one thread, over as many units as take about 2 s
+    n1 = 1
+    while True:
+        pack1, S01, cu1 = units_inputs(n1)
+        t1 = time.perf_counter()
+        oracle.fwd(pack1["q"], pack1["k"], pack1["v"], pack1["log_alpha"], pack1["beta"], S01, cu1,
+                   nthreads=1)
+        el1 = time.perf_counter() - t1
+        if el1 >= 2.0 or n1 >= max_units:
+            break
+        n1 = min(max_units, max(n1 + 1, int(n1 * 2.0 / max(el1, 1e-3) * 1.1)))
     cpu_model = "unknown"
     try:
         with open("/proc/cpuinfo") as f:
@@ -396,9 +407,11 @@ def cpu_baseline(torch, x, target_s=10.0, max_units=128):
         "unit": "tokens/s",
         "cores": threads,
         "kind": "oracle",
+        "value_1core": n1 * T / el1 / H,
         "sample": (f"{n} of {B * H} (b,h) units x {T} tokens of the same workload "
                    f"(fp64 token loop, OpenMP over units), {el:.1f} s wall; tokens/s = "
-                   f"token-heads/s / H; host CPU: {cpu_model}"),
+                   f"token-heads/s / H; value_1core: {n1} units on one thread, {el1:.1f} s; "
+                   f"host CPU: {cpu_model}"),
     }
 
 
