@@ -54,7 +54,7 @@ typedef enum {
     KDA_OK = 0,
     KDA_ERR_INVALID_ARG = 1,   /* NULL required pointer, negative size, misaligned pointer,
                                   cu_seqlens with B != 1, workspace too small */
-    KDA_ERR_UNSUPPORTED = 2,   /* a size or dtype combination this build does not implement */
+    KDA_ERR_UNSUPPORTED = 2,   /* a size or dtype combination the library does not implement */
     KDA_ERR_HIP = 3            /* a HIP launch or query failed */
 } kda_status;
 
