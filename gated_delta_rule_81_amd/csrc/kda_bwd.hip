@@ -293,8 +293,8 @@ template <typename Tin, int DK, bool WITH_Q, int TPROW = 8> struct ChunkIn {
 };
 
 // Buffer descriptor over the memory from `base` on (scalar registers; any
-// offset from 2^31 on is out of bounds: its stores are dropped).  The chains
-// store through these with per-lane offsets fixed for the whole sequence and
+// offset from 2^31 on is out of bounds: its stores are dropped).  The bf16
+// gradient chain stores through these with per-lane offsets fixed for the whole sequence and
 // data kept in registers of their own until the next chunk: a store whose
 // address or data register is rewritten while it is pending makes the
 // compiler wait for the store to complete first.
@@ -741,7 +741,8 @@ __global__ void __launch_bounds__(NT) bwd_grads_kernel(Params p, long nslot) {
         int cl;
         if (!slot_chunk(p, slot, t0, cl)) return;
         const size_t wi = (size_t)slot * p.H + h;
-        // each chunk is done by the instantiation of its path (set by the prep kernel)
+        // each chunk is done by the instantiation of its path (the flag set by
+        // the prep kernel, or for bf16 inputs by the forward's chunk kernel)
         if ((p.wF[wi] != 0) != EXACT) return;
         // states and state gradients are stored in the input precision's kind:
         // fp32 for fp32 inputs, bf16 for bf16 inputs
@@ -1118,10 +1119,10 @@ __global__ void __launch_bounds__(NT) bwd_grads_kernel(Params p, long nslot) {
 
 
 // ---------------------------------------------------------------------------
-// bf16 inputs: the two state chains on bf16 MFMA.  The state (or its
-// gradient) stays fp32 in the accumulators; its bf16 copy is both the MFMA
-// operand and what the workspace keeps.  Every product contracts over 32
-// rows or over d_k, so each tile is one or four v_mfma_f32_16x16x32_bf16.
+// bf16 inputs: the state-gradient chain on bf16 MFMA.  The state gradient
+// stays fp32 in the accumulators; its bf16 copy is both the MFMA operand and
+// what the workspace keeps.  Every product contracts over 32 rows or over
+// d_k, so each tile is one or four v_mfma_f32_16x16x32_bf16.
 
 // acc tile (rows 16 tm + 4 lj + i, cols 16 tn + lr) written transposed as
 // bf16: dst[col][row..row+3], one 8-byte store.
@@ -1319,7 +1320,9 @@ __global__ void __launch_bounds__(NT2) bwd_dstates_bf16_kernel(Params p) {
     for (int x = 0; x < NTW; ++x) {
         const int tt = wave * NTW + x, tm = tt >> 2, tn = tt & 3;
         load_tile(D[x], p.dST, so + 16 * tm, p.DV, col0 + 16 * tn);
-        D[x] = pinned(D[x]);                        // landed before the loop (see the state chain)
+        // landed before the loop (otherwise the wait for it would sit inside
+        // the loop, draining the memory queue every chunk)
+        D[x] = pinned(D[x]);
     }
     // per-lane byte offsets of this lane's tile elements (fixed for the sequence)
     uint32_t oD[NTW][4], oX[4], oV[4];

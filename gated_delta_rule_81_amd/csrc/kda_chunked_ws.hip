@@ -32,6 +32,13 @@
 // LDS rows are made of 16-byte chunks stored at position chunk ^ key(row),
 // so that the 16 rows one fragment read touches fall in distinct banks
 // without row padding (padding would leave no room for four slots).
+//
+// The SAVE instantiation is the first step of the backward for bf16 inputs:
+// the same chain with no o and no final state, keeping instead, per chunk,
+// what the gradient kernels read (the entering state, X and U from the
+// consumers; T, M0, T^T, P^T, P where flagged and the flag from the
+// producers; layouts in WsParams).  The forward's instantiations compile to
+// the code they had before it existed.
 #include <type_traits>
 
 #include "kda_device.h"
