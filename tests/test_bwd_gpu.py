@@ -143,12 +143,13 @@ def test_bwd_decay_band(gate):
     _compare(_gpu(x, gate), _ref(x, gate), TOL[torch.bfloat16], "decay band")
 
 
-def test_bwd_whole_dv_slices():
+@pytest.mark.parametrize("dk", [64, 128])
+def test_bwd_whole_dv_slices(dk):
     """512 (sequence, head) units: the forward's chunk kernel takes whole
     d_v = 128 per workgroup (two strips per consumer wave)."""
     lengths = [40, 33, 1, 64, 35, 0, 70, 32, 41, 39, 38, 37, 36, 2, 65, 31]
-    _say(f"[bwd 512 units] H=32 lengths={lengths} bf16")
-    x = _case(1, 0, 32, 64, 128, torch.bfloat16, seed=61, lengths=lengths)
+    _say(f"[bwd 512 units] H=32 dk={dk} lengths={lengths} bf16")
+    x = _case(1, 0, 32, dk, 128, torch.bfloat16, seed=61, lengths=lengths)
     _compare(_gpu(x, "channel"), _ref(x, "channel"), TOL[torch.bfloat16], "512 units")
 
 
