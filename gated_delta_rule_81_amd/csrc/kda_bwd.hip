@@ -294,10 +294,8 @@ template <typename Tin, int DK, bool WITH_Q, int TPROW = 8> struct ChunkIn {
 
 // Buffer descriptor over the memory from `base` on (scalar registers; any
 // offset from 2^31 on is out of bounds: its stores are dropped).  The bf16
-// gradient chain stores through these with per-lane offsets fixed for the whole sequence and
-// data kept in registers of their own until the next chunk: a store whose
-// address or data register is rewritten while it is pending makes the
-// compiler wait for the store to complete first.
+// gradient chain stores its tiles through these, masking rows past the
+// sequence end with an out-of-bounds offset instead of a branch.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t brsrc(const void *base) {
     const uint64_t a = reinterpret_cast<uint64_t>(base);
     const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
@@ -1324,29 +1322,7 @@ __global__ void __launch_bounds__(NT2) bwd_dstates_bf16_kernel(Params p) {
         // the loop, draining the memory queue every chunk)
         D[x] = pinned(D[x]);
     }
-    // per-lane byte offsets of this lane's tile elements (fixed for the sequence)
-    uint32_t oD[NTW][4], oX[4], oV[4];
-#pragma unroll
-    for (int x = 0; x < NTW; ++x) {
-        const int tt = wave * NTW + x, tm = tt >> 2, tn = tt & 3;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            oD[x][i] = pinned((uint32_t)(((16 * tm + 4 * lj + i) * p.DV + 16 * tn + lr) * 2));
-    }
     const int xm = wave >> 2, xn = wave & 3;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        oX[i] = pinned((uint32_t)(((16 * xm + 4 * lj + i) * p.DV + 16 * xn + lr) * 2));
-        oV[i] = pinned((uint32_t)(((16 * xm + 4 * lj + i) * p.H * p.DV + 16 * xn + lr) * 2));
-    }
-    uint32_t dD[NTW][4], dUv[4], dXv[4];                      // stored values, kept until the next chunk
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        dUv[i] = 0u;
-        dXv[i] = 0u;
-#pragma unroll
-        for (int x = 0; x < NTW; ++x) dD[x][i] = 0u;
-    }
     // D, the gradient of the state leaving chunk n: to D^T in LDS and to the workspace
     auto put_grad = [&](int n) {
         const __amdgpu_buffer_rsrc_t r =
@@ -1356,11 +1332,8 @@ __global__ void __launch_bounds__(NT2) bwd_dstates_bf16_kernel(Params p) {
             const int tt = wave * NTW + x, tm = tt >> 2, tn = tt & 3;
             store_t(Dt, DKB, tm, tn, D[x]);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                asm volatile("" ::"v"(dD[x][i]));
-                dD[x][i] = to_bf16(D[x][i]).x;
-                bst16(dD[x][i], r, oD[x][i]);
-            }
+            for (int i = 0; i < 4; ++i)
+                bst16(to_bf16(D[x][i]).x, r, (uint32_t)(((16 * tm + 4 * lj + i) * p.DV + 16 * tn + lr) * 2));
         }
     };
     if (nch > 0) {
@@ -1383,11 +1356,8 @@ __global__ void __launch_bounds__(NT2) bwd_dstates_bf16_kernel(Params p) {
             store_t(dUt, CB, xm, xn, a);
             const __amdgpu_buffer_rsrc_t r = brsrc(p.wdU + wi * C * p.DV + col0);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                asm volatile("" ::"v"(dUv[i]));
-                dUv[i] = to_bf16(a[i]).x;
-                bst16(dUv[i], r, oX[i]);
-            }
+            for (int i = 0; i < 4; ++i)
+                bst16(to_bf16(a[i]).x, r, (uint32_t)(((16 * xm + 4 * lj + i) * p.DV + 16 * xn + lr) * 2));
         }
         __syncthreads();
         // (-dX)^T, dX = Diag(beta) T^T dU
@@ -1403,9 +1373,8 @@ __global__ void __launch_bounds__(NT2) bwd_dstates_bf16_kernel(Params p) {
             for (int i = 0; i < 4; ++i) {
                 const int row = 16 * xm + 4 * lj + i;
                 const float dx = sB[row] * a[i];
-                asm volatile("" ::"v"(dXv[i]));
-                dXv[i] = to_bf16(dx).x;
-                bst16(dXv[i], rv, row < cl ? oV[i] : kDrop);
+                bst16(to_bf16(dx).x, rv,
+                      row < cl ? (uint32_t)((row * p.H * p.DV + 16 * xn + lr) * 2) : kDrop);
                 a[i] = -dx;
             }
             store_t(mdXt, CB, xm, xn, a);
