@@ -29,6 +29,8 @@
  *     with 16-byte aligned base pointers.
  *   - The caller owns every buffer.  The library allocates nothing, keeps no
  *     state between calls, never synchronises the stream, and is reentrant.
+ *     A call enqueues kernel launches only (no memset or copy), so it can be
+ *     captured into a HIP graph and replayed.
  *   - `stream` is a hipStream_t passed as void*; NULL is the null stream.
  *     Work is only enqueued; errors of the asynchronous kernels themselves
  *     surface at the caller's next synchronisation.
