@@ -110,6 +110,23 @@ def read_traffic(summary: str, kernel: str):
     return float(m_bytes.group(1))
 
 
+def read_busy(summary: str, kernel: str):
+    """VALU / MFMA / LDS busy fractions from a committed SQ counter summary,
+    while its recorded source hash matches the current kernel source (else None)."""
+    path = os.path.join(PROFILES, summary)
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_hash = re.search(r"source_sha256_16:\s*([0-9a-f]+)", text)
+    if not m_hash or m_hash.group(1) != kernel_sources_hash(kernel):
+        return None
+    out = {}
+    for key in ("valu_busy_frac", "mfma_busy_frac", "lds_busy_frac"):
+        m = re.search(key + r":\s*([0-9.]+)", text)
+        out[key] = float(m.group(1)) if m else None
+    return out
+
+
 def time_loop(torch, fn, steps, warmup):
     for _ in range(warmup):
         fn()
@@ -451,6 +468,8 @@ def main():
         "avg_launch_us": round(fw["t_step"] * 1e6, 2),
         "mfma_useful_tflops": round(fw["flops"] / fw["t_step"] / 1e12, 1),
         "mfma_useful_frac": round(fw["flops"] / fw["t_step"] / 1e12 / BF16_DENSE_PEAK_TFLOPS, 4),
+        # rocprof SQ counters of the same kernel (committed summary; None once stale)
+        "sq_busy": read_busy("chunked_ws_kernel_B4_H32_T8192_d128.sq.md", "chunked_ws_kernel"),
         "source_sha256_16": kernel_sources_hash("chunked_ws_kernel"),
     }
     out = {
