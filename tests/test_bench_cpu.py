@@ -1,0 +1,63 @@
+"""Host logic of bench.py (no GPU): the algorithmic byte and flop counts the
+roofline fractions divide by, and the rule that a committed counter summary
+only applies to the kernel source it was taken on."""
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+
+def test_forward_bytes_and_flops():
+    # B=4 H=32 T=8192 d=128 bf16: q, k, log_alpha, v and o at 256 B and beta at 2 B
+    # per token-head, plus the fp32 S0 and S_T (64 KB each) per (sequence, head)
+    tok = 4 * 8192 * 32
+    assert bench.fwd_algorithmic_bytes(4, 8192, 32, 128, 128, 4) == tok * 1282 + 2 * 4 * 32 * 65536
+    assert bench.fwd_algorithmic_bytes(4, 8192, 32, 128, 128, 4) == 1_361_051_648
+    # useful flops at C = 32: 6 dk dv + C (3 dk + 2 dv) + C^2 / 3 per token-head
+    per = 6 * 128 * 128 + 32 * (3 * 128 + 2 * 128) + 32 * 32 / 3.0
+    assert abs(bench.fwd_useful_flops(4, 8192, 32, 128, 128) - tok * per) < 1.0
+    assert round(per) == 119125
+
+
+def test_decode_and_backward_bytes():
+    # decode: the 1 GiB fp32 cache read and written, plus ~1.3 KB per (n, h)
+    nb = bench.decode_algorithmic_bytes(512, 32, 128, 128)
+    assert nb == 512 * 32 * (2 * 65536 + (3 * 128 + 128 + 1) * 2 + 128 * 2)
+    assert abs(nb - 2.17e9) / 2.17e9 < 0.01
+    # backward: 2,308 B per token-head plus S0, dS_T and dS0 (64 KB each) per (sequence, head)
+    tokens = 4 * 8192                                  # B * T; the count multiplies by H itself
+    assert bench._bwd_bytes(tokens, 32, 128, 128, 4) == tokens * 32 * 2308 + 3 * 4 * 32 * 65536
+    assert bench._bwd_bytes(tokens, 32, 128, 128, 4) == 2_445_279_232
+
+
+def _summary(tmp_path, name, hash16, extra):
+    p = tmp_path / name
+    p.write_text(f"# test summary\n{extra}\nsource_sha256_16: {hash16}\n")
+    return p
+
+
+def test_counter_summaries_follow_the_source(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    cur = bench.kernel_sources_hash("chunked_ws_kernel")
+    _summary(tmp_path, "ok.pmc.md", cur, "traffic_bytes_per_launch: 1234.5")
+    _summary(tmp_path, "stale.pmc.md", "0" * 16, "traffic_bytes_per_launch: 1234.5")
+    assert bench.read_traffic("ok.pmc.md", "chunked_ws_kernel") == 1234.5
+    assert bench.read_traffic("stale.pmc.md", "chunked_ws_kernel") is None
+    assert bench.read_traffic("missing.pmc.md", "chunked_ws_kernel") is None
+    _summary(tmp_path, "ok.sq.md", cur, "valu_busy_frac: 0.52\nmfma_busy_frac: 0.13\nlds_busy_frac: 0.47")
+    _summary(tmp_path, "stale.sq.md", "f" * 16, "valu_busy_frac: 0.52")
+    assert bench.read_busy("ok.sq.md", "chunked_ws_kernel") == {
+        "valu_busy_frac": 0.52, "mfma_busy_frac": 0.13, "lds_busy_frac": 0.47}
+    assert bench.read_busy("stale.sq.md", "chunked_ws_kernel") is None
+
+
+def test_committed_summaries_are_current():
+    """The committed counter summaries were taken on the sources as they are."""
+    for summary, kernel in (("chunked_ws_kernel_B4_H32_T8192_d128.pmc.md", "chunked_ws_kernel"),
+                            ("decode_step_kernel_N512_H32_d128.pmc.md", "decode_step_kernel"),
+                            ("bwd_kernels_B4_H32_T8192_d128.pmc.md", "bwd_kernels")):
+        assert bench.read_traffic(summary, kernel) is not None, summary
+    assert bench.read_busy("chunked_ws_kernel_B4_H32_T8192_d128.sq.md", "chunked_ws_kernel") is not None
