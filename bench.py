@@ -22,7 +22,9 @@ Also reported on the same JSON line:
                 also the same step on states at scattered rows of a pool, and
                 four tokens per sequence per call from such a pool (decode
                 kernel and chunked forward)
-  copy_ceiling  a plain device copy of 1 GiB (practical HBM ceiling)
+  copy_ceiling  practical HBM ceiling: 1 GiB moved by the library's streaming
+                copy and in-place read-modify-write kernels (the decode step's
+                access pattern) and by torch's device copy
   cpu_baseline  the fp64 oracle on a bounded sample of the same workload,
                 timed on this host's cores
 
@@ -360,11 +362,26 @@ def bench_decode(torch, kda, synth, steps=None):
     return dict(w=w, t_step=t_step, bytes=nbytes, steps=n)
 
 
-def bench_copy(torch, nbytes=1 << 30, reps=20):
+def bench_copy(torch, kda, nbytes=1 << 30, reps=20):
+    """Practical HBM ceilings, GB/s (read + write bytes over time): torch's
+    device copy, and the library's streaming kernels with the decode step's
+    access pattern (16-byte non-temporal accesses, persistent grid): a copy
+    between two buffers and an in-place read-modify-write of one."""
     src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
     dst = torch.empty_like(src)
+    out = {}
     secs = time_loop(torch, lambda: dst.copy_(src), reps, 3)
-    return 2 * nbytes / (secs / reps) / 1e9
+    out["torch_copy"] = round(2 * nbytes / (secs / reps) / 1e9, 1)
+    secs = time_loop(torch, lambda: kda.measure_copy(src, dst), reps, 3)
+    out["stream_copy"] = round(2 * nbytes / (secs / reps) / 1e9, 1)
+    secs = time_loop(torch, lambda: kda.measure_rmw(src), reps, 3)
+    out["stream_rmw"] = round(2 * nbytes / (secs / reps) / 1e9, 1)
+    ok = bool(torch.equal(src, dst)) and bool((src == 1.0).all())
+    out["bytes"] = nbytes
+    out["checked"] = ok
+    del src, dst
+    torch.cuda.empty_cache()
+    return out
 
 
 def cpu_baseline(torch, x, target_s=10.0, max_units=128):
@@ -507,7 +524,9 @@ def main():
         }
         out["decode_pool"] = bench_pooled_decode(torch, kda, synth)
         out["multi_token_decode"] = bench_multi_token_decode(torch, kda, synth)
-    out["copy_ceiling_GBps"] = round(bench_copy(torch), 1)
+    ceil = bench_copy(torch, kda)
+    out["copy_ceiling_GBps"] = max(ceil["stream_copy"], ceil["stream_rmw"])
+    out["copy_ceiling"] = ceil
     if not args.no_cpu:
         log("[bench] oracle CPU baseline")
         out["cpu_baseline"] = cpu_baseline(torch, fw["x"])

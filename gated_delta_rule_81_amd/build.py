@@ -10,7 +10,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkda.so")
 SOURCES = ["kda_api.hip", "kda_decode.hip", "kda_chunked.hip", "kda_chunked_ws.hip",
-           "kda_bwd.hip"]
+           "kda_bwd.hip", "kda_measure.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -17,6 +17,8 @@ hipError_t chunked_fwd_launch(const void *q, const void *k, const void *v, const
                               const int32_t *cu_seqlens, int num_seqs, int B, int T, int H,
                               int dk, int dv, bool bf16, void *workspace, hipStream_t stream);
 size_t bwd_workspace_bytes(int B, int T, int H, int dk, int dv, int num_seqs);
+void ws_set_spin_limit(int polls);
+hipError_t ws_device_errors(unsigned *bits, bool clear);
 hipError_t bwd_launch(const void *q, const void *k, const void *v, const void *g, const void *beta,
                       int gate, const float *S0, const void *dO, const float *dST,
                       const int32_t *cu_seqlens, int num_seqs, int B, int T, int H, int dk, int dv,
@@ -206,6 +208,21 @@ kda_status kda_bwd_chunked(const void *q, const void *k, const void *v,
                                    T, H, dk, dv, dtype == KDA_BF16, dq, dk_out, dv_out, dg, dbeta,
                                    dS0, workspace, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status kda_device_errors(unsigned *bits, int clear, void *stream)
+{
+    if (!bits) return KDA_ERR_INVALID_ARG;
+    *bits = 0;
+    if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess) return KDA_ERR_HIP;
+    return kda::ws_device_errors(bits, clear != 0) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status kda_set_wait_limit(int polls)
+{
+    if (polls < 0) return KDA_ERR_INVALID_ARG;
+    kda::ws_set_spin_limit(polls);
+    return KDA_OK;
 }
 
 }  // extern "C"

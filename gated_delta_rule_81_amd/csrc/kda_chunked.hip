@@ -815,20 +815,84 @@ __global__ __launch_bounds__(256, 1) void chunked_fwd_kernel(ChunkParams p)
     }
 }
 
-// Longest-first processing order of packed sequences: order[rank] = seq.
-// One thread per sequence counts the sequences that sort before it
-// (longer, or equally long with a smaller index).
-__global__ void varlen_order_kernel(const int32_t *__restrict__ cu, int n, int32_t *__restrict__ order)
+// Longest-first processing order of packed sequences: order[rank] = seq
+// (a permutation of 0..n-1; the results do not depend on it, only the load
+// balance does).  One workgroup of ORDER_THREADS threads.
+//   n <= ORDER_SORT_MAX: exact order (longer first, equal lengths by index),
+//     a bitonic sort of (length, index) keys in LDS: O(n log^2 n) work over
+//     the threads, no global scratch.
+//   larger n: a counting sort by length class (octave of the length and its
+//     next three bits, 8 classes per octave, longest class first); inside a
+//     class the order is whatever the atomics give.  O(n) work.
+constexpr int ORDER_THREADS = 1024;
+constexpr int ORDER_SORT_MAX = 8192;
+constexpr int ORDER_CLASSES = 33 * 8;
+
+__device__ __forceinline__ int length_class(int len) {
+    // 0 for len <= 0; else 8 * (octave + 1) + next three bits, increasing with len
+    if (len <= 0) return 0;
+    const int oct = 31 - __builtin_clz((unsigned)len);
+    const int frac = oct >= 3 ? (len >> (oct - 3)) & 7 : (len << (3 - oct)) & 7;
+    return 8 * (oct + 1) + frac;
+}
+
+__global__ __launch_bounds__(ORDER_THREADS) void varlen_order_kernel(const int32_t *__restrict__ cu, int n,
+                                                                     int32_t *__restrict__ order)
 {
-    const int s = blockIdx.x * blockDim.x + threadIdx.x;
-    if (s >= n) return;
-    const int ls = cu[s + 1] - cu[s];
-    int rank = 0;
-    for (int o = 0; o < n; ++o) {
-        const int lo = cu[o + 1] - cu[o];
-        rank += (lo > ls) || (lo == ls && o < s);
+    __shared__ unsigned long long keys[ORDER_SORT_MAX];
+    __shared__ int cls_count[ORDER_CLASSES];
+    const int tid = threadIdx.x;
+    if (n <= ORDER_SORT_MAX) {
+        int m = 1;
+        while (m < n) m <<= 1;
+        // ascending order of (~length, index): longest first, ties by index;
+        // padding keys sort last
+        for (int i = tid; i < m; i += ORDER_THREADS) {
+            if (i < n) {
+                const unsigned len = (unsigned)(cu[i + 1] - cu[i]);
+                keys[i] = ((unsigned long long)(~len) << 32) | (unsigned)i;
+            } else {
+                keys[i] = ~0ull;
+            }
+        }
+        __syncthreads();
+        for (int k = 2; k <= m; k <<= 1) {
+            for (int j = k >> 1; j > 0; j >>= 1) {
+                for (int i = tid; i < m; i += ORDER_THREADS) {
+                    const int l = i ^ j;
+                    if (l > i) {
+                        const unsigned long long a = keys[i], b = keys[l];
+                        const bool up = (i & k) == 0;
+                        if ((a > b) == up) {
+                            keys[i] = b;
+                            keys[l] = a;
+                        }
+                    }
+                }
+                __syncthreads();
+            }
+        }
+        for (int i = tid; i < n; i += ORDER_THREADS) order[i] = (int32_t)(keys[i] & 0xffffffffu);
+        return;
     }
-    order[rank] = s;
+    for (int c = tid; c < ORDER_CLASSES; c += ORDER_THREADS) cls_count[c] = 0;
+    __syncthreads();
+    for (int i = tid; i < n; i += ORDER_THREADS) atomicAdd(&cls_count[length_class(cu[i + 1] - cu[i])], 1);
+    __syncthreads();
+    if (tid == 0) {
+        // exclusive prefix over classes, longest class first
+        int run = 0;
+        for (int c = ORDER_CLASSES - 1; c >= 0; --c) {
+            const int cnt = cls_count[c];
+            cls_count[c] = run;
+            run += cnt;
+        }
+    }
+    __syncthreads();
+    for (int i = tid; i < n; i += ORDER_THREADS) {
+        const int pos = atomicAdd(&cls_count[length_class(cu[i + 1] - cu[i])], 1);
+        order[pos] = i;
+    }
 }
 
 template <int DK, int NSTRIP, bool F32>
@@ -886,7 +950,7 @@ hipError_t chunked_fwd_launch(const void *q, const void *k, const void *v, const
     if (p.units == 0) return hipSuccess;
     if (cu_seqlens && nseq > 1 && workspace) {
         int32_t *order = static_cast<int32_t *>(workspace);
-        hipLaunchKernelGGL(varlen_order_kernel, dim3((nseq + 255) / 256), dim3(256), 0, stream,
+        hipLaunchKernelGGL(varlen_order_kernel, dim3(1), dim3(ORDER_THREADS), 0, stream,
                            cu_seqlens, nseq, order);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;

@@ -27,7 +27,12 @@
 // ring of 4 LDS slots, slot p belonging to producer p, with per-slot flags
 // (full: chunk id + 1 written by the producer; freed: consumer completions).
 // Every wait is bounded; a wait that runs out marks the workgroup dead and
-// all waves leave, so a protocol error gives wrong numbers, never a hang.
+// all waves leave, so a protocol error can never hang the device.  Its
+// consumers first write NaN into every output the workgroup has not produced
+// yet (o rows, its columns of S_T; the SAVE instantiation's remaining chunk
+// states, X and U) and set a bit in the device's error word (g_ws_error,
+// read and cleared through kda_device_errors), so a timed-out wait never
+// passes for a result.
 //
 // LDS rows are made of 16-byte chunks stored at position chunk ^ key(row),
 // so that the 16 rows one fragment read touches fall in distinct banks
@@ -54,6 +59,7 @@ struct WsParams {
     const int32_t *order;
     const int32_t *state_idx;   // slot map of S0 / S_T rows (NULL: row = sequence)
     int T, H, DV, units, nslices, pool;
+    int spin_limit;             // polls a bounded wait makes before giving up
     // What the backward keeps of the forward (SAVE instantiation), per
     // (chunk slot, head); a sequence's chunks take consecutive slots from
     // floor(cu_seqlens[s] / 32) + s (packed) or s * ceil(T / 32) (dense):
@@ -137,14 +143,19 @@ __device__ __forceinline__ int idxT(int ch, int j) {
     return (ch >> 2) * (4 * C) + (((((ch & 3) << 2) | j) ^ keyT(ch)) << 3);
 }
 
+// Sticky error bits of this device (kda_device_error_bits in kda.h): set by
+// a workgroup whose bounded wait ran out, read and cleared by the host.
+__device__ unsigned int g_ws_error;
+constexpr unsigned WS_ERR_WAIT_TIMEOUT = 1u;
+
 __device__ __forceinline__ int ld_acquire(const int *p) {
     return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
 // Wait until *p >= target (or, with eq, *p == target).  Returns false when
 // the workgroup is dead or the wait ran out (which kills the workgroup).
-__device__ __forceinline__ bool wait_flag(const int *p, int target, bool eq, int *dead) {
-    for (int it = 0; it < SPIN_LIMIT; ++it) {
+__device__ __forceinline__ bool wait_flag(const int *p, int target, bool eq, int *dead, int limit) {
+    for (int it = 0; it < limit; ++it) {
         const int v = ld_acquire(p);
         if (eq ? (v == target) : (v >= target)) return true;
         if (__hip_atomic_load(dead, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) return false;
@@ -460,13 +471,51 @@ __global__ __launch_bounds__(512, 1) void chunked_ws_kernel(WsParams p)
         // every iteration, so the loop head needs no wait on memory
         __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
 
+        // After a wait ran out (the workgroup is dead): NaN into this wave's
+        // columns of every output not yet produced, chunks n_from onwards, and
+        // the device's error bit.  Runs only on that failure.
+        auto give_up = [&](int n_from) {
+            if (lane == 0) atomicOr(&g_ws_error, WS_ERR_WAIT_TIMEOUT);
+            const float qnan = __builtin_nanf("");
+            for (int m = n_from; m < nchunks; ++m) {
+                const long cm = (long)m * C;
+                const int cl = (int)((len - cm) < C ? (len - cm) : C);
+#pragma unroll
+                for (int s = 0; s < NSTRIP; ++s) {
+                    const uint32_t co = 16 * (w + 4 * s) + mr;
+                    if constexpr (!SAVE) {
+                        bf16_t *ob = go + ((size_t)(t0 + cm) * H + head) * DV + col0;
+                        for (int r = jg; r < cl; r += 4) ob[(size_t)r * tokv + co] = to_bf16(qnan);
+                    } else {
+                        const size_t slotm = (size_t)(sbase + m) * H + head;
+                        for (int r = jg; r < DK; r += 4) p.wS[(slotm * DK + r) * DV + col0 + co] = to_bf16(qnan);
+                        for (int r = jg; r < C; r += 4) {
+                            p.wX[(slotm * C + r) * DV + col0 + co] = to_bf16(qnan);
+                            p.wU[(slotm * C + r) * DV + col0 + co] = to_bf16(qnan);
+                        }
+                    }
+                }
+            }
+            if (p.S_T && strow >= 0) {
+                float *st = p.S_T + ((size_t)strow * H + head) * DK * DV + col0;
+#pragma unroll
+                for (int s = 0; s < NSTRIP; ++s) {
+                    const uint32_t co = 16 * (w + 4 * s) + mr;
+                    for (int r = jg; r < DK; r += 4) st[(uint32_t)r * DV + co] = qnan;
+                }
+            }
+        };
+
         for (int n = 0; n < nchunks; ++n) {
             const int slot = n % NSLOT;
             const long cs = (long)n * C;
             const int cl = (int)((len - cs) < C ? (len - cs) : C);
-            // a dead workgroup (a bounded wait ran out) leaves at once; its
-            // outputs are not meaningful, and the state is not written back
-            if (!wait_flag(&s_full[slot], n + 1, true, s_dead)) return;
+            // a dead workgroup (a bounded wait ran out) marks what it has not
+            // produced as NaN and leaves
+            if (!wait_flag(&s_full[slot], n + 1, true, s_dead, p.spin_limit)) {
+                give_up(n);
+                return;
+            }
             const unsigned char *sb = smem + slot * L::SLOT;
             const bf16_t *sKU = reinterpret_cast<const bf16_t *>(sb + L::KU);
             const bf16_t *sQU = reinterpret_cast<const bf16_t *>(sb + L::QU);
@@ -872,7 +921,7 @@ __global__ __launch_bounds__(512, 1) void chunked_ws_kernel(WsParams p)
 
         // wait for the slot: the consumers are done with chunk n - NSLOT
         if (n >= NSLOT) {
-            if (!wait_flag(&s_freed[slot], 4 * (n / NSLOT), false, s_dead)) break;
+            if (!wait_flag(&s_freed[slot], 4 * (n / NSLOT), false, s_dead, p.spin_limit)) break;
         }
         if (lane < C) pBeta[lane] = lane < cl ? __uint_as_float(bx << 16) : 0.0f;
         unsigned char *sb = smem + slot * L::SLOT;
@@ -1246,9 +1295,27 @@ __global__ __launch_bounds__(512, 1) void chunked_ws_kernel(WsParams p)
     }
 }
 
-template <int DK, int NSTRIP, int GATE, int PREP, bool SAVE = false>
-static hipError_t launch_ws(const WsParams &p, hipStream_t stream)
+// Polls a bounded wait makes before giving up (process-wide; tests of the
+// timeout handling lower it).
+static int g_spin_limit = ws::SPIN_LIMIT;
+
+void ws_set_spin_limit(int polls) { g_spin_limit = polls; }
+
+// The device's sticky error bits (current device), cleared when asked.
+hipError_t ws_device_errors(unsigned *bits, bool clear)
 {
+    hipError_t e = hipMemcpyFromSymbol(bits, HIP_SYMBOL(ws::g_ws_error), sizeof(unsigned), 0,
+                                       hipMemcpyDeviceToHost);
+    if (e != hipSuccess || !clear || *bits == 0) return e;
+    const unsigned zero = 0;
+    return hipMemcpyToSymbol(HIP_SYMBOL(ws::g_ws_error), &zero, sizeof(unsigned), 0,
+                             hipMemcpyHostToDevice);
+}
+
+template <int DK, int NSTRIP, int GATE, int PREP, bool SAVE = false>
+static hipError_t launch_ws(WsParams p, hipStream_t stream)
+{
+    p.spin_limit = g_spin_limit;
     const int groups = (p.units + 7) / 8;
     const dim3 grid(groups * 8 * p.nslices);
     hipLaunchKernelGGL((chunked_ws_kernel<DK, NSTRIP, GATE, PREP, SAVE>), grid, dim3(512), 0, stream, p);

@@ -21,6 +21,8 @@ KDA_F32, KDA_BF16 = 0, 1
 KDA_GATE_CHANNEL, KDA_GATE_HEAD, KDA_GATE_NONE = 0, 1, 2
 _GATES = {"channel": KDA_GATE_CHANNEL, "head": KDA_GATE_HEAD, "none": KDA_GATE_NONE}
 KDA_FLAG_L2NORM_QK, KDA_FLAG_GATE_SOFTPLUS = 1, 2
+KDA_DEVERR_WAIT_TIMEOUT = 1
+WAIT_LIMIT_DEFAULT = 1 << 20
 
 _vp = ctypes.c_void_p
 _lib = None
@@ -69,6 +71,15 @@ def lib() -> ctypes.CDLL:
                                   ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                   ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp, _vp,
                                   _vp, _vp, _vp, ctypes.c_size_t, _vp]
+    L.kda_device_errors.restype = ctypes.c_int
+    L.kda_device_errors.argtypes = [ctypes.POINTER(ctypes.c_uint), ctypes.c_int, _vp]
+    L.kda_set_wait_limit.restype = ctypes.c_int
+    L.kda_set_wait_limit.argtypes = [ctypes.c_int]
+    # measurement kernels (include/kda_measure.h)
+    L.kda_measure_copy.restype = ctypes.c_int
+    L.kda_measure_copy.argtypes = [_vp, _vp, ctypes.c_size_t, _vp]
+    L.kda_measure_rmw.restype = ctypes.c_int
+    L.kda_measure_rmw.argtypes = [_vp, ctypes.c_size_t, _vp]
     _lib = L
     return L
 
@@ -329,3 +340,45 @@ def bwd_chunked(q, k, v, log_alpha, beta, dO, S0=None, dS_T=None, cu_seqlens=Non
     if st != KDA_OK:
         raise KdaError(st, "kda_bwd_chunked")
     return dq, dk_, dv_, dg, db, dS0
+
+
+def device_errors(clear: bool = False, device=None) -> int:
+    """The current device's sticky error bits (kda_device_errors), after
+    synchronising the current stream; KDA_DEVERR_WAIT_TIMEOUT when a bounded
+    wait inside a kernel ran out.  clear=True resets them."""
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    bits = ctypes.c_uint(0)
+    with torch.cuda.device(dev):
+        st = lib().kda_device_errors(ctypes.byref(bits), int(bool(clear)), _stream(dev))
+    if st != KDA_OK:
+        raise KdaError(st, "kda_device_errors")
+    return int(bits.value)
+
+
+def set_wait_limit(polls: int) -> None:
+    """Diagnostics (kda_set_wait_limit): polls a bounded wait makes before it
+    gives up, process-wide, for launches after the call."""
+    st = lib().kda_set_wait_limit(int(polls))
+    if st != KDA_OK:
+        raise KdaError(st, "kda_set_wait_limit")
+
+
+def measure_copy(src: torch.Tensor, dst: torch.Tensor) -> None:
+    """kda_measure_copy: dst = src byte for byte with the decode step's access
+    pattern (include/kda_measure.h); both contiguous GPU tensors of equal size."""
+    _check(src, "src", src.device)
+    _check(dst, "dst", src.device)
+    n = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != n:
+        raise ValueError("src and dst sizes differ")
+    st = lib().kda_measure_copy(_ptr(src), _ptr(dst), n, _stream(src.device))
+    if st != KDA_OK:
+        raise KdaError(st, "kda_measure_copy")
+
+
+def measure_rmw(buf: torch.Tensor) -> None:
+    """kda_measure_rmw: every 16 bytes of buf read and written back in place."""
+    _check(buf, "buf", buf.device)
+    st = lib().kda_measure_rmw(_ptr(buf), buf.numel() * buf.element_size(), _stream(buf.device))
+    if st != KDA_OK:
+        raise KdaError(st, "kda_measure_rmw")

@@ -165,3 +165,129 @@ def random_fwd(B, T, H, dk, dv, dtype=torch.float32, seed=0, gate_mu=0.0, s0_std
     w = FwdWorkload(f"adhoc_{B}x{T}x{H}x{dk}x{dv}", B, T, H, dk, dv, dtype, gate_mu,
                     s0_std, seed, varlen=list(lengths) if lengths is not None else None)
     return fwd_inputs(w, device=device)
+
+
+# ---- inputs at the edges of the operator's domain ---------------------------
+#
+# Each case changes one thing about the recipe above (seeded like it); the
+# tests run the GPU path and the oracle on the same tensors.
+#   beta_wide    beta ~ U[-0.5, 2): negative and greater-than-one write strengths
+#   beta_zero    beta = 0 exactly: nothing is written, only decay
+#   beta_one     beta = 1 exactly
+#   beta_01      beta drawn from {0, 1}
+#   raw_keys     keys not normalised: unit directions times norms ~ U[0.1, 4],
+#                beta = u * 1.9 / |k|^2 with u ~ U(0, 1) (so beta |k|^2 < 2 and
+#                the state stays bounded; beta itself spans about 0 .. 190)
+#   big_key      as the recipe, but one 32-token block (tokens 32..63) holds a
+#                key with one element just above 2^16 in magnitude (66048) and
+#                beta = 1 / |k|^2 on that token
+#   overwrite    associative recall: orthonormal keys (rows of a Hadamard
+#                matrix / 8 at d_k = 64, signed unit vectors otherwise; exact in
+#                bf16), no decay (log_alpha = 0), S0 = 0; tokens 0..47 write
+#                keys 0..47 with beta = 1, tokens 48..55 write new values for
+#                keys 1, 7, 13, .., 43 with beta = 1, tokens 56..103 query every
+#                key (q = k = key j, beta = 0)
+EDGE_KINDS = ("beta_wide", "beta_zero", "beta_one", "beta_01", "raw_keys", "big_key", "overwrite")
+
+OVERWRITE_WRITES = 48
+OVERWRITE_REWRITES = tuple(range(1, 48, 6))          # keys written a second time
+OVERWRITE_T = 48 + len(OVERWRITE_REWRITES) + 48      # writes, rewrites, queries
+
+
+def _hadamard(n: int) -> torch.Tensor:
+    h = torch.ones(1, 1)
+    while h.shape[0] < n:
+        h = torch.cat([torch.cat([h, h], 1), torch.cat([h, -h], 1)], 0)
+    return h
+
+
+def orthonormal_keys(dk: int, g: torch.Generator) -> torch.Tensor:
+    """dk orthonormal rows whose entries are exact in bf16: a row-permuted
+    Hadamard matrix scaled by 1/8 at dk = 64, signed permuted unit vectors
+    otherwise."""
+    perm = torch.randperm(dk, generator=g)
+    if dk == 64:
+        return _hadamard(64)[perm] / 8.0
+    sign = torch.where(torch.rand(dk, generator=g) < 0.5, -1.0, 1.0)
+    return torch.eye(dk)[perm] * sign[:, None]
+
+
+def edge_fwd(kind: str, B: int, T: int, H: int, dk: int, dv: int, dtype=torch.bfloat16,
+             seed: int = 0, gate_mu: float = -1.0, s0_std: float = 0.5) -> dict:
+    """Forward inputs for one of EDGE_KINDS (generated on the CPU).  For
+    "overwrite" T is fixed (OVERWRITE_T) and the result also holds
+    "expected": (B, OVERWRITE_T, H, dv) fp32 values the query tokens must
+    recall (the latest value written for their key; rows of write tokens are
+    NaN), as bookkeeping of which value was written last -- no arithmetic of
+    the operator."""
+    if kind not in EDGE_KINDS:
+        raise ValueError(f"unknown edge case {kind!r}")
+    if kind == "overwrite":
+        return _overwrite_inputs(B, H, dk, dv, dtype, seed)
+    x = random_fwd(B, T, H, dk, dv, dtype=torch.float32, seed=seed, gate_mu=gate_mu,
+                   s0_std=s0_std)
+    g = _gen("cpu", seed * 7 + 13)
+    beta = x["beta"]
+    if kind == "beta_wide":
+        beta = torch.rand(beta.shape, generator=g) * 2.5 - 0.5
+    elif kind == "beta_zero":
+        beta = torch.zeros_like(beta)
+    elif kind == "beta_one":
+        beta = torch.ones_like(beta)
+    elif kind == "beta_01":
+        beta = (torch.rand(beta.shape, generator=g) < 0.5).float()
+    elif kind == "raw_keys":
+        norms = 0.1 + 3.9 * torch.rand(x["k"].shape[:-1] + (1,), generator=g)
+        k = (x["k"] * norms).to(dtype).float()     # the stored keys decide beta below
+        sq = (k * k).sum(-1)
+        beta = torch.rand(beta.shape, generator=g).clamp_min(1e-3) * 1.9 / sq
+        x["k"] = k
+    elif kind == "big_key":
+        t = min(40, T - 1)
+        k = x["k"].clone()
+        k[:, t, :, 3] = 66048.0                     # bf16 0x4781: just above 2^16
+        sq = (k[:, t].to(dtype).float() ** 2).sum(-1)
+        beta = beta.clone()
+        beta[:, t] = 1.0 / sq
+        x["k"] = k
+    x["beta"] = beta
+    for key in ("q", "k", "v", "log_alpha", "beta"):
+        x[key] = x[key].to(dtype)
+    return x
+
+
+def _overwrite_inputs(B, H, dk, dv, dtype, seed):
+    g = _gen("cpu", seed)
+    T = OVERWRITE_T
+    q = torch.zeros(B, T, H, dk)
+    k = torch.zeros(B, T, H, dk)
+    v = torch.zeros(B, T, H, dv)
+    beta = torch.zeros(B, T, H)
+    expected = torch.full((B, T, H, dv), float("nan"))
+    nw, nr = OVERWRITE_WRITES, len(OVERWRITE_REWRITES)
+    for b in range(B):
+        for h in range(H):
+            keys = orthonormal_keys(dk, g)[:nw]
+            vals = torch.randn(nw, dv, generator=g).to(dtype).float()
+            latest = vals.clone()
+            k[b, :nw, h] = keys
+            v[b, :nw, h] = vals
+            beta[b, :nw, h] = 1.0
+            for i, j in enumerate(OVERWRITE_REWRITES):
+                new = torch.randn(dv, generator=g).to(dtype).float()
+                k[b, nw + i, h] = keys[j]
+                v[b, nw + i, h] = new
+                beta[b, nw + i, h] = 1.0
+                latest[j] = new
+            q[b, : nw + nr, h] = torch.randn(nw + nr, dk, generator=g) / dk ** 0.5
+            order = torch.randperm(nw, generator=g)
+            for i, j in enumerate(order.tolist()):
+                t = nw + nr + i
+                q[b, t, h] = keys[j]
+                k[b, t, h] = keys[j]
+                v[b, t, h] = torch.randn(dv, generator=g)
+                expected[b, t, h] = latest[j]
+    return dict(q=q.to(dtype), k=k.to(dtype), v=v.to(dtype),
+                log_alpha=torch.zeros(B, T, H, dk).to(dtype), beta=beta.to(dtype), S0=None,
+                cu_seqlens=None, B=B, T=T, H=H, dk=dk, dv=dv, N=B, lengths=None,
+                expected=expected)

@@ -261,6 +261,38 @@ kda_status kda_bwd_chunked(const void *q, const void *k, const void *v,
                            void *dq, void *dk_out, void *dv_out, void *dlog_alpha, void *dbeta,
                            float *dS0, void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * Faults the kernels detect while they run.
+ *
+ * The chunked forward (and the first kernel of the backward for bf16
+ * inputs) hands each chunk from the waves that prepare it to the waves that
+ * apply it through flags in on-chip memory.  Every wait on such a flag is
+ * bounded.  Should one run out (it does not in correct operation), the
+ * workgroup stops instead of hanging: it writes NaN into every output it has
+ * not produced yet (the remaining rows of o in its value columns and its
+ * columns of S_T; in the backward, the chunk states its later kernels read,
+ * so the gradients are not meaningful) and sets KDA_DEVERR_WAIT_TIMEOUT in a
+ * sticky per-device error word.  The call itself has already returned KDA_OK
+ * by then, since kernels run asynchronously.
+ */
+typedef enum {
+    KDA_DEVERR_WAIT_TIMEOUT = 1
+} kda_device_error_bits;
+
+/* Synchronise `stream`, then store the current device's error word (an OR of
+ * kda_device_error_bits, 0 when nothing went wrong) in *bits; clear != 0
+ * resets it to 0.  Returns KDA_ERR_INVALID_ARG for bits == NULL and
+ * KDA_ERR_HIP when the synchronisation or the read fails.  It copies memory
+ * and blocks, unlike the compute entry points. */
+kda_status kda_device_errors(unsigned *bits, int clear, void *stream);
+
+/* Diagnostics: the number of polls a bounded wait makes before it gives up
+ * (default 1048576, about 1e8 GPU cycles).  It applies process-wide to
+ * launches made after the call.  Tests of the timeout handling set it to 0,
+ * so that every such wait gives up at once.  polls < 0 is
+ * KDA_ERR_INVALID_ARG. */
+kda_status kda_set_wait_limit(int polls);
+
 #ifdef __cplusplus
 }
 #endif

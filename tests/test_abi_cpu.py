@@ -28,8 +28,9 @@ def L():
 
 def test_header_declares_expected_entry_points():
     assert declared_functions() == ["kda_bwd_chunked", "kda_bwd_workspace_bytes",
-                                    "kda_decode_step", "kda_decode_step_ex", "kda_fwd_chunked",
-                                    "kda_fwd_chunked_ex", "kda_fwd_workspace_bytes",
+                                    "kda_decode_step", "kda_decode_step_ex", "kda_device_errors",
+                                    "kda_fwd_chunked", "kda_fwd_chunked_ex",
+                                    "kda_fwd_workspace_bytes", "kda_set_wait_limit",
                                     "kda_status_string"]
 
 
@@ -253,3 +254,10 @@ def test_bwd_workspace_rules(L):
     # varlen needs B == 1
     assert bwd(L, cu=FAKE, N=2, B=2) == 1
     assert bwd(L, B=0) == 0                              # nothing to do
+
+
+def test_diagnostics_argument_checks(L):
+    # no GPU work: both return before touching the device
+    assert L.kda_set_wait_limit(-1) == 1
+    assert L.kda_device_errors(None, 0, None) == 1
+    assert L.kda_set_wait_limit(1 << 20) == 0

@@ -5,7 +5,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_util import TOL, f64, oracle_on_units, rel_err, sample_units
+from gpu_util import TOL, f64, rel_err
 
 pytestmark = pytest.mark.gpu
 
@@ -158,31 +158,74 @@ def test_final_state_options_and_continuation(dt, dk):
     assert rel_err(f64(S), f64(S_full)) <= tol
 
 
-def test_h32_t8k_workload_sampled():
-    from gated_delta_rule_81_amd import synth
-    _say("case: kda_fwd_bf16 B4 H32 T8192 d128 (sampled units)")
+def _nan_outputs(x, dev=DEV):
+    B, T, H, dk, dv, N = x["B"], x["T"], x["H"], x["dk"], x["dv"], x["N"]
+    o = torch.full((B, T, H, dv), float("nan"), dtype=x["q"].dtype, device=dev)
+    S_T = torch.full((N, H, dk, dv), float("nan"), dtype=torch.float32, device=dev)
+    return o, S_T
+
+
+def _oracle_seq(g, o, S_T, seq):
+    """The oracle on every head of one sequence (a batch row, or one packed
+    sequence), against the GPU's o and S_T there.  Returns (err o, err S_T,
+    max |o_ref|, max |S_ref|) with errors as max |x - ref| (absolute)."""
+    import oracle
+    cu = g["cu_seqlens"]
+    if cu is None:
+        b, ts = seq, slice(0, g["T"])
+    else:
+        c = cu.tolist()
+        b, ts = 0, slice(c[seq], c[seq + 1])
+    part = {k: f64(g[k][b:b + 1, ts]) for k in ("q", "k", "v", "log_alpha", "beta")}
+    S0 = f64(g["S0"][seq:seq + 1]) if g["S0"] is not None else None
+    o_ref, S_ref = oracle.fwd(part["q"], part["k"], part["v"], part["log_alpha"], part["beta"], S0)
+    o_got = f64(o[b:b + 1, ts])
+    S_got = f64(S_T[seq:seq + 1])
+    return (float(np.max(np.abs(o_got - o_ref))) if o_ref.size else 0.0,
+            float(np.max(np.abs(S_got - S_ref))),
+            float(np.max(np.abs(o_ref))) if o_ref.size else 0.0,
+            float(np.max(np.abs(S_ref))))
+
+
+def _check_all_sequences(g, o, S_T, nseq, label):
+    """Every (sequence, head) unit against the oracle, one sequence at a time
+    (all its heads together), with the tolerance metric over the whole tensors
+    (max |x - ref| over all units / max |ref| over all units)."""
+    eo = es = mo = ms = 0.0
+    for s in range(nseq):
+        a, b, c, d = _oracle_seq(g, o, S_T, s)
+        eo, es, mo, ms = max(eo, a), max(es, b), max(mo, c), max(ms, d)
+    ro, rs = eo / (mo if mo > 0 else 1.0), es / (ms if ms > 0 else 1.0)
+    _say(f"  {label}: all {nseq} sequences x {g['H']} heads: rel err o={ro:.3e} S_T={rs:.3e}")
+    assert ro <= TOL[torch.bfloat16] and rs <= TOL[torch.bfloat16], (ro, rs)
+
+
+def test_h32_t8k_workload_all_units():
+    """B=4 H=32 T=8192 d=128 bf16 in the launch configuration the benchmark
+    times; all 128 (sequence, head) units against the oracle.  o and S_T start
+    as NaN, so a unit the kernel never writes fails."""
+    from gated_delta_rule_81_amd import synth, kda
+    _say("case: kda_fwd_bf16 B4 H32 T8192 d128 (every unit)")
     x = synth.fwd_inputs(synth.FWD_H32_T8K, device=DEV)
-    g, o, S_T = _run_gpu(x)
-    assert torch.isfinite(o.float()).all() and torch.isfinite(S_T).all()
-    units = sample_units(4, 32, 8, seed=2)
-    eo, es = oracle_on_units(g, units, o, S_T)
-    _say(f"  units {units}: rel err o={eo:.3e} S_T={es:.3e}")
-    assert eo <= TOL[torch.bfloat16] and es <= TOL[torch.bfloat16]
+    o, S_T = _nan_outputs(x)
+    kda.fwd_chunked(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["S0"], None, o=o, S_T=S_T)
+    torch.cuda.synchronize()
+    assert not torch.isnan(o.float()).any() and not torch.isnan(S_T).any()
+    _check_all_sequences(x, o, S_T, x["N"], "headline")
 
 
-def test_varlen_workload_sampled():
-    from gated_delta_rule_81_amd import synth
-    _say("case: kda_fwd_varlen 64 seqs H32 d128 (sampled units)")
+def test_varlen_workload_all_units():
+    """64 packed sequences of 512..16384 tokens, H=32, d=128 bf16 (processed
+    longest first); all 2048 (sequence, head) units against the oracle."""
+    from gated_delta_rule_81_amd import synth, kda
+    _say("case: kda_fwd_varlen 64 seqs H32 d128 (every unit)")
     x = synth.fwd_inputs(synth.VARLEN_64, device=DEV)
-    g, o, S_T = _run_gpu(x)
-    assert torch.isfinite(o.float()).all() and torch.isfinite(S_T).all()
-    lens = x["lengths"]
-    longest = int(np.argmax(lens))
-    shortest = int(np.argmin(lens))
-    units = [(longest, 0), (shortest, 31)] + sample_units(64, 32, 4, seed=3)
-    eo, es = oracle_on_units(g, units, o, S_T)
-    _say(f"  units {units}: rel err o={eo:.3e} S_T={es:.3e}")
-    assert eo <= TOL[torch.bfloat16] and es <= TOL[torch.bfloat16]
+    o, S_T = _nan_outputs(x)
+    kda.fwd_chunked(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["S0"], x["cu_seqlens"],
+                    o=o, S_T=S_T)
+    torch.cuda.synchronize()
+    assert not torch.isnan(o.float()).any() and not torch.isnan(S_T).any()
+    _check_all_sequences(x, o, S_T, x["N"], "varlen")
 
 
 @pytest.mark.parametrize("dt,dk,dv", [(torch.bfloat16, 128, 128), (torch.float32, 64, 64)])
@@ -201,3 +244,32 @@ def test_decode_chain_matches_chunked(dt, dk, dv):
     o_dec = torch.stack(outs, dim=1)
     assert rel_err(f64(o_dec), f64(o)) <= TOL[dt]
     assert rel_err(f64(S), f64(S_T)) <= TOL[dt]
+
+
+@pytest.mark.parametrize("nseq", [4096, 10000])
+def test_varlen_many_short_sequences(nseq):
+    """Packed prefill of many short sequences (lengths 0..40, H=2, d=128 bf16):
+    every unit against the oracle.  The workspace holds the processing order,
+    which must be a permutation; up to 8192 sequences it is exactly longest
+    first (ties by index), beyond that longest length class first."""
+    from gated_delta_rule_81_amd import kda, synth
+    gen = torch.Generator().manual_seed(nseq)
+    lens = torch.randint(0, 41, (nseq,), generator=gen).tolist()
+    _say(f"case: varlen {nseq} short sequences, {sum(lens)} tokens, H2 d128 bf16")
+    x = synth.random_fwd(1, 0, 2, 128, 128, dtype=torch.bfloat16, seed=nseq + 1, gate_mu=-1.0,
+                         s0_std=0.3, lengths=lens)
+    g = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in x.items()}
+    o, S_T = _nan_outputs(x)
+    ws = torch.empty(kda.workspace_bytes(1, x["T"], 2, 128, 128, nseq), dtype=torch.uint8, device=DEV)
+    kda.fwd_chunked(g["q"], g["k"], g["v"], g["log_alpha"], g["beta"], g["S0"], g["cu_seqlens"],
+                    o=o, S_T=S_T, workspace=ws)
+    torch.cuda.synchronize()
+    order = ws[: 4 * nseq].view(torch.int32).cpu()
+    assert sorted(order.tolist()) == list(range(nseq))
+    L = torch.tensor(lens)[order.long()]
+    if nseq <= 8192:
+        key = [(-int(L[i]), int(order[i])) for i in range(nseq)]
+        assert key == sorted(key)
+    else:
+        assert (L[:-1] >= L[1:] // 2).all()        # never a whole octave out of order
+    _check_full(x, o, S_T, TOL[torch.bfloat16])
