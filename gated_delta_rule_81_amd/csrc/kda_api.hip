@@ -18,6 +18,8 @@ hipError_t chunked_fwd_launch(const void *q, const void *k, const void *v, const
                               int dk, int dv, bool bf16, void *workspace, hipStream_t stream);
 size_t bwd_workspace_bytes(int B, int T, int H, int dk, int dv, int num_seqs);
 void ws_set_spin_limit(int polls);
+int noalloc_max_seqs();
+hipError_t noalloc_scratch(int32_t **out);
 hipError_t ws_device_errors(unsigned *bits, bool clear);
 hipError_t bwd_launch(const void *q, const void *k, const void *v, const void *g, const void *beta,
                       int gate, const float *S0, const void *dO, const float *dST,
@@ -62,6 +64,7 @@ const char *kda_status_string(kda_status status)
     case KDA_ERR_INVALID_ARG: return "KDA_ERR_INVALID_ARG";
     case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED";
     case KDA_ERR_HIP: return "KDA_ERR_HIP";
+    case KDA_ERR_SCRATCH_LIMIT: return "KDA_ERR_SCRATCH_LIMIT";
     }
     return "KDA_ERR_UNKNOWN";
 }
@@ -114,6 +117,28 @@ kda_status kda_fwd_chunked_ex(const void *q, const void *k, const void *v,
                                            dtype == KDA_BF16, cu_seqlens ? workspace : nullptr,
                                            static_cast<hipStream_t>(stream));
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status kda_fwd_chunked_noalloc(const void *q, const void *k, const void *v,
+                                   const void *log_alpha, const void *beta, kda_gate gate,
+                                   unsigned flags,
+                                   const float *S0, float *S_T, const int32_t *state_idx,
+                                   int pool_size, const int32_t *cu_seqlens, int num_seqs,
+                                   int B, int T, int H, int dk, int dv, kda_dtype dtype,
+                                   void *o, void *stream)
+{
+    if (cu_seqlens && num_seqs > kda::noalloc_max_seqs()) return KDA_ERR_SCRATCH_LIMIT;
+    void *order = nullptr;
+    size_t order_bytes = 0;
+    if (cu_seqlens && num_seqs > 1 && B == 1) {
+        int32_t *p = nullptr;
+        if (kda::noalloc_scratch(&p) != hipSuccess) return KDA_ERR_HIP;
+        order = p;
+        order_bytes = (size_t)kda::noalloc_max_seqs() * sizeof(int32_t);
+    }
+    return kda_fwd_chunked_ex(q, k, v, log_alpha, beta, gate, flags, S0, S_T, state_idx, pool_size,
+                              cu_seqlens, num_seqs, B, T, H, dk, dv, dtype, o, order, order_bytes,
+                              stream);
 }
 
 kda_status kda_fwd_chunked(const void *q, const void *k, const void *v,

@@ -45,6 +45,8 @@
 // the chunk is <= 96 in log2 units (no factor leaves [2^-96, 2^96]).  A chunk
 // with stronger decay inside a 16-row block takes an exact slower path that
 // forms A and P entry by entry with e^{Gamma_r - Gamma_i} evaluated directly.
+#include <mutex>
+
 #include "kda_device.h"
 
 namespace kda {
@@ -928,6 +930,44 @@ hipError_t chunked_ws_launch(const void *q, const void *k, const void *v, const 
                              const int32_t *state_idx, int pool, void *o,
                              const int32_t *cu_seqlens, const int32_t *order, int nseq, int T,
                              int H, int dk, int dv, int slice_width, hipStream_t stream);
+
+// ---- allocation-free forward ------------------------------------------------
+// The forward's only scratch is the processing order of packed sequences.
+// kda_fwd_chunked_noalloc keeps it in this file-scope device array instead of
+// a caller's workspace: one copy per GPU, shared by every call on that GPU
+// (overlapping calls on one GPU race), holding up to NOALLOC_MAX_SEQS
+// entries.  Host code never passes the array's name to a kernel (in host
+// code it is only a stand-in for the symbol): the device address is looked
+// up once per device with hipGetSymbolAddress and kept.
+constexpr int NOALLOC_MAX_SEQS = 65536;
+static __device__ __align__(256) int32_t scratch[NOALLOC_MAX_SEQS];
+
+namespace {
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+int32_t *g_scratch_ptr[MAX_DEVICES] = {};
+}  // namespace
+
+int noalloc_max_seqs() { return NOALLOC_MAX_SEQS; }
+
+// Device address of this GPU's scratch array (current device), looked up on
+// the first call on each device.
+hipError_t noalloc_scratch(int32_t **out)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[dev] = static_cast<int32_t *>(ptr);
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
 
 hipError_t chunked_fwd_launch(const void *q, const void *k, const void *v, const void *g,
                               const void *beta, int gate, int prep, const float *S0, float *S_T,

@@ -17,6 +17,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkda.so")
 
 KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_HIP = 0, 1, 2, 3
+KDA_ERR_SCRATCH_LIMIT = 4
+NOALLOC_MAX_SEQS = 65536
 KDA_F32, KDA_BF16 = 0, 1
 KDA_GATE_CHANNEL, KDA_GATE_HEAD, KDA_GATE_NONE = 0, 1, 2
 _GATES = {"channel": KDA_GATE_CHANNEL, "head": KDA_GATE_HEAD, "none": KDA_GATE_NONE}
@@ -71,6 +73,11 @@ def lib() -> ctypes.CDLL:
                                   ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                   ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp, _vp,
                                   _vp, _vp, _vp, ctypes.c_size_t, _vp]
+    L.kda_fwd_chunked_noalloc.restype = ctypes.c_int
+    L.kda_fwd_chunked_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, ctypes.c_int, ctypes.c_uint, _vp,
+                                          _vp, _vp, ctypes.c_int, _vp, ctypes.c_int, ctypes.c_int,
+                                          ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                          ctypes.c_int, _vp, _vp]
     L.kda_device_errors.restype = ctypes.c_int
     L.kda_device_errors.argtypes = [ctypes.POINTER(ctypes.c_uint), ctypes.c_int, _vp]
     L.kda_set_wait_limit.restype = ctypes.c_int
@@ -382,3 +389,45 @@ def measure_rmw(buf: torch.Tensor) -> None:
     st = lib().kda_measure_rmw(_ptr(buf), buf.numel() * buf.element_size(), _stream(buf.device))
     if st != KDA_OK:
         raise KdaError(st, "kda_measure_rmw")
+
+
+def fwd_chunked_noalloc(q, k, v, log_alpha, beta, S0, cu_seqlens, o, S_T=None, *,
+                        gate: str = "channel", state_idx=None, pool_size: Optional[int] = None,
+                        flags: int = 0) -> None:
+    """kda_fwd_chunked_noalloc: the chunked forward into caller-given outputs
+    (o, and S_T or None) with no workspace; nothing is allocated here or in
+    the library.  Arguments as in fwd_chunked.  Calls that overlap on one GPU
+    must not be issued (they share that GPU's scratch)."""
+    dev = q.device
+    dt = q.dtype
+    for name, t in (("q", q), ("k", k), ("v", v), ("beta", beta), ("o", o)):
+        _check(t, name, dev, dt)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    gcode = _check_gate(log_alpha, gate, q.shape, dev, dt)
+    if k.shape != q.shape or v.shape != (B, T, H, dv) or beta.shape != (B, T, H) \
+            or o.shape != v.shape:
+        raise ValueError("inconsistent input shapes")
+    N = B
+    if cu_seqlens is not None:
+        _check(cu_seqlens, "cu_seqlens", dev, torch.int32)
+        N = cu_seqlens.shape[0] - 1
+    rows = N
+    if state_idx is not None:
+        _check(state_idx, "state_idx", dev, torch.int32)
+        if pool_size is None:
+            ref = S0 if S0 is not None else S_T
+            pool_size = ref.shape[0] if ref is not None else 0
+        rows = pool_size
+    for name, t in (("S0", S0), ("S_T", S_T)):
+        if t is not None:
+            _check(t, name, dev, torch.float32)
+            if t.shape != (rows, H, dk, dv):
+                raise ValueError(f"{name} must have shape {(rows, H, dk, dv)}")
+    ga = None if gcode == KDA_GATE_NONE else log_alpha
+    st = lib().kda_fwd_chunked_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(ga), _ptr(beta), gcode,
+                                       int(flags), _ptr(S0), _ptr(S_T), _ptr(state_idx), int(rows),
+                                       _ptr(cu_seqlens), N, B, T, H, dk, dv, _dtype_code(q), _ptr(o),
+                                       _stream(dev))
+    if st != KDA_OK:
+        raise KdaError(st, "kda_fwd_chunked_noalloc")

@@ -57,7 +57,9 @@ typedef enum {
     KDA_ERR_INVALID_ARG = 1,   /* NULL required pointer, negative size, misaligned pointer,
                                   cu_seqlens with B != 1, workspace too small */
     KDA_ERR_UNSUPPORTED = 2,   /* a size or dtype combination the library does not implement */
-    KDA_ERR_HIP = 3            /* a HIP launch or query failed */
+    KDA_ERR_HIP = 3,           /* a HIP launch or query failed */
+    KDA_ERR_SCRATCH_LIMIT = 4  /* more packed sequences than kda_fwd_chunked_noalloc's
+                                  fixed scratch holds (KDA_NOALLOC_MAX_SEQS) */
 } kda_status;
 
 typedef enum {
@@ -173,6 +175,34 @@ kda_status kda_fwd_chunked_ex(const void *q, const void *k, const void *v,
                               const int32_t *cu_seqlens, int num_seqs,
                               int B, int T, int H, int dk, int dv, kda_dtype dtype,
                               void *o, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * kda_fwd_chunked_noalloc -- kda_fwd_chunked_ex with no workspace argument.
+ *
+ * For callers that cannot allocate device memory: code being captured into
+ * a graph, tight serving loops, harnesses that forbid allocation.  The call
+ * allocates nothing (no hipMalloc, no library allocator); the only scratch
+ * the forward needs, the processing order of packed sequences, lives in a
+ * fixed array of KDA_NOALLOC_MAX_SEQS int32 entries (256 KiB) that the
+ * library holds on each GPU it runs on until the process ends.  Every call
+ * on one GPU uses that GPU's array, so calls that overlap on one GPU (on
+ * different streams, or from different host threads) race and must not be
+ * issued; calls on one stream are ordered and safe.  The array is fully
+ * rewritten by each packed call before it is read.
+ *
+ * Arguments, results, supported sizes and errors are those of
+ * kda_fwd_chunked_ex without workspace and workspace_bytes, plus
+ * KDA_ERR_SCRATCH_LIMIT when cu_seqlens is given with num_seqs >
+ * KDA_NOALLOC_MAX_SEQS (nothing is enqueued then).
+ */
+#define KDA_NOALLOC_MAX_SEQS 65536
+kda_status kda_fwd_chunked_noalloc(const void *q, const void *k, const void *v,
+                                   const void *log_alpha, const void *beta, kda_gate gate,
+                                   unsigned flags,
+                                   const float *S0, float *S_T, const int32_t *state_idx,
+                                   int pool_size, const int32_t *cu_seqlens, int num_seqs,
+                                   int B, int T, int H, int dk, int dv, kda_dtype dtype,
+                                   void *o, void *stream);
 
 /*
  * kda_decode_step -- one token for each of N independent sequences.

@@ -30,6 +30,7 @@ def test_header_declares_expected_entry_points():
     assert declared_functions() == ["kda_bwd_chunked", "kda_bwd_workspace_bytes",
                                     "kda_decode_step", "kda_decode_step_ex", "kda_device_errors",
                                     "kda_fwd_chunked", "kda_fwd_chunked_ex",
+                                    "kda_fwd_chunked_noalloc",
                                     "kda_fwd_workspace_bytes", "kda_set_wait_limit",
                                     "kda_status_string"]
 
@@ -46,6 +47,7 @@ def test_status_strings(L):
     assert kda.status_string(1) == "KDA_ERR_INVALID_ARG"
     assert kda.status_string(2) == "KDA_ERR_UNSUPPORTED"
     assert kda.status_string(3) == "KDA_ERR_HIP"
+    assert kda.status_string(4) == "KDA_ERR_SCRATCH_LIMIT"
     assert kda.status_string(99) == "KDA_ERR_UNKNOWN"
 
 
