@@ -16,7 +16,7 @@ int cu_count();
 namespace {
 
 constexpr int THREADS = 1024;
-constexpr int BATCH = 8;            // 16-byte accesses per thread in flight
+constexpr int BATCH = 8;            // 16-byte accesses per thread and block
 constexpr int kNonTemporal = 2;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, uint32_t bytes) {
@@ -30,23 +30,29 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, uint32_
 // dst[i] = src[i] (RMW: src == dst and each value is rewritten after an add
 // of zero), over n16 16-byte units.  Each block of THREADS * BATCH units is
 // one buffer window; accesses past the window's valid bytes read zero and
-// drop their stores, so the ragged last block needs no branch.
+// drop their stores, so the ragged last block needs no branch.  As in the
+// decode step, the loads of a workgroup's next block are issued before the
+// stores of its current one, so a block's worth of reads is always in flight.
 template <bool RMW>
 __global__ __launch_bounds__(THREADS) void stream_kernel(const uint4 *src, uint4 *dst, size_t n16)
 {
     constexpr size_t BLK = (size_t)THREADS * BATCH;
     const size_t nblk = (n16 + BLK - 1) / BLK;
-    for (size_t b = blockIdx.x; b < nblk; b += gridDim.x) {
-        const size_t first = b * BLK;
-        const size_t left = n16 - first;
-        const uint32_t bytes = (uint32_t)((left < BLK ? left : BLK) * 16);
-        const __amdgpu_buffer_rsrc_t rs = rsrc(src + first, bytes);
-        const __amdgpu_buffer_rsrc_t rd = rsrc(dst + first, bytes);
-        uint4 r[BATCH];
+    size_t b = blockIdx.x;
+    if (b >= nblk) return;
+    auto window = [&](size_t blk) {
+        const size_t left = n16 - blk * BLK;
+        return (uint32_t)((left < BLK ? left : BLK) * 16);
+    };
+    auto load = [&](size_t blk, uint4 (&r)[BATCH]) {
+        const __amdgpu_buffer_rsrc_t rs = rsrc(src + blk * BLK, window(blk));
 #pragma unroll
         for (int i = 0; i < BATCH; ++i)
             r[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
                 rs, (uint32_t)((i * THREADS + threadIdx.x) * 16), 0, kNonTemporal));
+    };
+    auto store = [&](size_t blk, const uint4 (&r)[BATCH]) {
+        const __amdgpu_buffer_rsrc_t rd = rsrc(dst + blk * BLK, window(blk));
 #pragma unroll
         for (int i = 0; i < BATCH; ++i) {
             uint4 v = r[i];
@@ -56,10 +62,23 @@ __global__ __launch_bounds__(THREADS) void stream_kernel(const uint4 *src, uint4
                 v.z = __float_as_uint(__uint_as_float(v.z) + 0.0f);
                 v.w = __float_as_uint(__uint_as_float(v.w) + 0.0f);
             }
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) uint32_t, v), rd,
-                                                   (uint32_t)((i * THREADS + threadIdx.x) * 16), 0,
-                                                   kNonTemporal);
+            __builtin_amdgcn_raw_buffer_store_b128(
+                __builtin_bit_cast(__attribute__((ext_vector_type(4))) uint32_t, v), rd,
+                (uint32_t)((i * THREADS + threadIdx.x) * 16), 0, kNonTemporal);
         }
+    };
+    uint4 ra[BATCH], rb[BATCH];
+    load(b, ra);
+    // two register sets alternate, so the prefetched block is never copied
+    for (;;) {
+        const size_t nb = b + gridDim.x;
+        if (nb < nblk) load(nb, rb);
+        store(b, ra);
+        if (nb >= nblk) return;
+        b = nb + gridDim.x;
+        if (b < nblk) load(b, ra);
+        store(nb, rb);
+        if (b >= nblk) return;
     }
 }
 
