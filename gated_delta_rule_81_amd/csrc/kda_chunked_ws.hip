@@ -209,6 +209,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *base) {
     return __builtin_amdgcn_make_buffer_rsrc(u, 0, 0x7ffffff0, 0x00020000);
 }
 constexpr uint32_t OOB_OFF = 0x80000000u;
+// The same over `bytes` bytes only: accesses past them read zero and drop
+// their stores (the rows of a chunk past its end, with a window of the
+// chunk's valid rows).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc_n(const void *base, uint32_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    void *u = reinterpret_cast<void *>(((uint64_t)hi << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(u, 0, bytes, 0x00020000);
+}
 __device__ __forceinline__ float bf_hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
 
 // Sum over the 16 lanes of a row (lanes 16j .. 16j + 15), in every lane of it:
@@ -451,18 +461,18 @@ __global__ __launch_bounds__(512, 1) void chunked_ws_kernel(WsParams p)
         auto load_v = [&](int n) {
             const long cs = (long)n * C;
             const int cl = (int)((len - cs) < C ? (len - cs) : C);
-            const __amdgpu_buffer_rsrc_t rv = buf_rsrc(gv + ((size_t)(t0 + cs) * H + head) * DV + col0);
+            // a window of the chunk's cl valid rows: rows past them read zero
+            const __amdgpu_buffer_rsrc_t rv =
+                buf_rsrc_n(gv + ((size_t)(t0 + cs) * H + head) * DV + col0, (uint32_t)cl * tokv * 2u);
 #pragma unroll
             for (int s = 0; s < NSTRIP; ++s)
 #pragma unroll
                 for (int h = 0; h < 2; ++h)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const int row = crow(h, 4 * jg + i);
                         // the aligned 4-byte word holding this column (and its
                         // neighbour): the register is the load's own result
-                        const uint32_t off = row < cl ? ((vlane + (uint32_t)(4 * h + i) * tokv * 2u + 128u * s) & ~3u)
-                                                      : OOB_OFF;
+                        const uint32_t off = (vlane + (uint32_t)(4 * h + i) * tokv * 2u + 128u * s) & ~3u;
                         rawv[s][4 * h + i] = __builtin_amdgcn_raw_buffer_load_b32(rv, off, 0, 0);
                     }
         };
@@ -506,16 +516,17 @@ __global__ __launch_bounds__(512, 1) void chunked_ws_kernel(WsParams p)
             }
         };
 
+        int dead_at = -1;
         for (int n = 0; n < nchunks; ++n) {
             const int slot = n % NSLOT;
             const long cs = (long)n * C;
             const int cl = (int)((len - cs) < C ? (len - cs) : C);
-            // a dead workgroup (a bounded wait ran out) marks what it has not
-            // produced as NaN and leaves
-            if (!wait_flag(&s_full[slot], n + 1, true, s_dead, p.spin_limit)) {
-                give_up(n);
-                return;
-            }
+            // In a dead workgroup (a bounded wait ran out) every later wait
+            // returns at once; the chunks are still walked, on whatever the
+            // slots hold, and what was not produced is overwritten with NaN
+            // after the loop.  (A loop with one exit keeps the state in place
+            // from one chunk to the next.)
+            if (!wait_flag(&s_full[slot], n + 1, true, s_dead, p.spin_limit) && dead_at < 0) dead_at = n;
             const unsigned char *sb = smem + slot * L::SLOT;
             const bf16_t *sKU = reinterpret_cast<const bf16_t *>(sb + L::KU);
             const bf16_t *sQU = reinterpret_cast<const bf16_t *>(sb + L::QU);
@@ -523,7 +534,9 @@ __global__ __launch_bounds__(512, 1) void chunked_ws_kernel(WsParams p)
             const bf16_t *sTp = reinterpret_cast<const bf16_t *>(sb + L::TP);
             const bf16_t *sP = reinterpret_cast<const bf16_t *>(sb + L::PM);
             const float *sG = reinterpret_cast<const float *>(sb + L::GM);
-            const __amdgpu_buffer_rsrc_t ro = buf_rsrc(go + ((size_t)(t0 + cs) * H + head) * DV + col0);
+            // a window of the chunk's cl valid rows: stores past them are dropped
+            const __amdgpu_buffer_rsrc_t ro =
+                buf_rsrc_n(go + ((size_t)(t0 + cs) * H + head) * DV + col0, (uint32_t)cl * tokv * 2u);
 
             // v of this chunk out of the prefetch registers, which then take
             // the next chunk's loads at once (a whole chunk of latency slack).
@@ -678,8 +691,7 @@ __global__ __launch_bounds__(512, 1) void chunked_ws_kernel(WsParams p)
                     for (int h = 0; h < 2; ++h)
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
-                            const int row = crow(h, 4 * jg + i);
-                            const uint32_t off = row < cl ? vlane + (uint32_t)(4 * h + i) * tokv * 2u + 128u * s : OOB_OFF;
+                            const uint32_t off = vlane + (uint32_t)(4 * h + i) * tokv * 2u + 128u * s;
                             __builtin_amdgcn_raw_buffer_store_b16(to_bf16(O[h][i]).x, ro, off, 0, 0);
                         }
                 }
@@ -690,6 +702,10 @@ __global__ __launch_bounds__(512, 1) void chunked_ws_kernel(WsParams p)
                 __hip_atomic_fetch_add(&s_freed[slot], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         }
 
+        if (dead_at >= 0) {
+            give_up(dead_at);
+            return;
+        }
         if (p.S_T && strow >= 0) {
             float *st = p.S_T + ((size_t)strow * H + head) * DK * DV + col0;
 #pragma unroll
@@ -733,25 +749,28 @@ __global__ __launch_bounds__(512, 1) void chunked_ws_kernel(WsParams p)
         const long cs = (long)n * C;
         const int cl = (int)((len - cs) < C ? (len - cs) : C);
         const size_t tb = (size_t)(t0 + cs) * H + head;
-        const char *bg = reinterpret_cast<const char *>(gg + tb * DK);
-        const char *bk = reinterpret_cast<const char *>(gk + tb * DK);
+        // windows of the chunk's cl valid rows: rows past them read zero
+        // (the decay step below still sets what such rows must hold)
+        const uint32_t wbytes = (uint32_t)cl * tokk * 2u;
+        const __amdgpu_buffer_rsrc_t rg_ = buf_rsrc_n(gg + (GATE == GATE_CHANNEL ? tb * DK : 0), wbytes);
+        const __amdgpu_buffer_rsrc_t rk_ = buf_rsrc_n(gk + tb * DK, wbytes);
         const uint32_t base_off = ((uint32_t)r0 * tokk + (uint32_t)c0) * 2u;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const uint32_t off = (r0 + i < cl) ? base_off + (uint32_t)i * tokk * 2u : (uint32_t)c0 * 2u;
+            const uint32_t off = base_off + (uint32_t)i * tokk * 2u;
             if constexpr (NCL == 8) {
                 if constexpr (GATE == GATE_CHANNEL) {
-                    const uint4 g4 = *reinterpret_cast<const uint4 *>(bg + off);
+                    const uint4 g4 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rg_, off, 0, 0));
                     gx[i][0] = g4.x; gx[i][1] = g4.y; gx[i][2] = g4.z; gx[i][3] = g4.w;
                 }
-                const uint4 k4 = *reinterpret_cast<const uint4 *>(bk + off);
+                const uint4 k4 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk_, off, 0, 0));
                 kx[i][0] = k4.x; kx[i][1] = k4.y; kx[i][2] = k4.z; kx[i][3] = k4.w;
             } else {
                 if constexpr (GATE == GATE_CHANNEL) {
-                    const uint2 g2 = *reinterpret_cast<const uint2 *>(bg + off);
+                    const uint2 g2 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rg_, off, 0, 0));
                     gx[i][0] = g2.x; gx[i][1] = g2.y;
                 }
-                const uint2 k2 = *reinterpret_cast<const uint2 *>(bk + off);
+                const uint2 k2 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rk_, off, 0, 0));
                 kx[i][0] = k2.x; kx[i][1] = k2.y;
             }
             if constexpr (GATE == GATE_HEAD)
@@ -783,15 +802,15 @@ __global__ __launch_bounds__(512, 1) void chunked_ws_kernel(WsParams p)
         uint32_t qx[8][NCL / 2];
         {
             const uint32_t base_off = ((uint32_t)r0 * tokk + (uint32_t)c0) * 2u;
+            const __amdgpu_buffer_rsrc_t rq_ = buf_rsrc_n(bq, (uint32_t)cl * tokk * 2u);
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                const uint32_t off = (r0 + i < cl) ? base_off + (uint32_t)i * tokk * 2u : (uint32_t)c0 * 2u;
-                const char *pq = reinterpret_cast<const char *>(bq) + off;
+                const uint32_t off = base_off + (uint32_t)i * tokk * 2u;
                 if constexpr (NCL == 8) {
-                    const uint4 q4 = *reinterpret_cast<const uint4 *>(pq);
+                    const uint4 q4 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rq_, off, 0, 0));
                     qx[i][0] = q4.x; qx[i][1] = q4.y; qx[i][2] = q4.z; qx[i][3] = q4.w;
                 } else {
-                    const uint2 q2 = *reinterpret_cast<const uint2 *>(pq);
+                    const uint2 q2 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rq_, off, 0, 0));
                     qx[i][0] = q2.x; qx[i][1] = q2.y;
                 }
             }
