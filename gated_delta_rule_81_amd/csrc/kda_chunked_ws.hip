@@ -1095,22 +1095,30 @@ __global__ __launch_bounds__(512, 1) void chunked_ws_kernel(WsParams p)
         // P bf16 into the slot
         if (fast) {
             f32x4 accA[3], accP[3];
+            // the operand fragments of both row blocks, each read once
+            // (the three tiles share them)
+            bf16x8 fk[2][NRUN], fq[2][NRUN], fd[2][NRUN];
+#pragma unroll
+            for (int R = 0; R < 2; ++R) {
+                const int ra = 16 * R + mr;
+#pragma unroll
+                for (int rr = 0; rr < NRUN; ++rr) {
+                    const int ka = ra * DK + (((4 * rr + jg) ^ keyK<DK>(ra)) << 3);
+                    fk[R][rr] = *reinterpret_cast<const bf16x8 *>(&sKU[ka]);
+                    fq[R][rr] = *reinterpret_cast<const bf16x8 *>(&sQU[ka]);
+                    fd[R][rr] = *reinterpret_cast<const bf16x8 *>(&pKD[ka]);
+                }
+            }
             // tiles (R, I) = (0,0), (1,0), (1,1)
 #pragma unroll
             for (int t = 0; t < 3; ++t) {
                 const int R = (t == 0) ? 0 : 1, I = (t == 2) ? 1 : 0;
-                const int ra = 16 * R + mr, rb = 16 * I + mr;
                 f32x4 a = {0.f, 0.f, 0.f, 0.f}, q = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int rr = 0; rr < NRUN; ++rr) {
-                    const int ka = ra * DK + (((4 * rr + jg) ^ keyK<DK>(ra)) << 3);
-                    const int kb = rb * DK + (((4 * rr + jg) ^ keyK<DK>(rb)) << 3);
-                    const bf16x8 fk = *reinterpret_cast<const bf16x8 *>(&sKU[ka]);
-                    const bf16x8 fq = *reinterpret_cast<const bf16x8 *>(&sQU[ka]);
-                    const bf16x8 fd = *reinterpret_cast<const bf16x8 *>(&pKD[kb]);
-                    a = mfma_bf16(fk, fd, a);
+                    a = mfma_bf16(fk[R][rr], fd[I][rr], a);
                     // P^T tile: lane ends up with P[16R + mr][16I + 4jg + i]
-                    q = mfma_bf16(fd, fq, q);
+                    q = mfma_bf16(fd[I][rr], fq[R][rr], q);
                 }
                 accA[t] = a;
                 accP[t] = q;
