@@ -91,7 +91,6 @@ kda_status kda_fwd_chunked_ex(const void *q, const void *k, const void *v,
     if (cu_seqlens && (B != 1 || num_seqs < 0)) return KDA_ERR_INVALID_ARG;
     const int nseq = cu_seqlens ? num_seqs : B;
     if (!dim_ok(dk) || !dim_ok(dv)) return KDA_ERR_UNSUPPORTED;
-    if (dtype == KDA_F32 && dk != 64) return KDA_ERR_UNSUPPORTED;
     if (!sizes_fit(B, T, H, dk > dv ? dk : dv) || !sizes_fit(nseq, H, dk, dv)) return KDA_ERR_INVALID_ARG;
     if ((long long)nseq * H * 2 >= ((long long)1 << 31)) return KDA_ERR_INVALID_ARG;
     if (state_idx) {

@@ -189,21 +189,35 @@ struct Lds {
     static constexpr int LDK = DK + PAD;          // row stride of [64][DK] operand arrays
     static constexpr int LCH = CH + PAD;          // row stride of [*][64] operand arrays
     static constexpr int LF = CH + 4;             // row stride of fp32 [64][64] arrays
+    // fp32 operands leave no room for separate K_right^T, T and T' arrays at
+    // d_k = 128 (217 KB), so the fp32 layout drops all three: K_right is read
+    // from the k b rows times a per-block channel factor, T is built inside A's
+    // array (diagonal blocks in place, block (R, I) at the mirror position
+    // (I, R), which A never uses), and T' then overwrites A's lower blocks.
     static constexpr int KU = 0;                                         // K_up  [64][LDK]
     static constexpr int QU = KU + CH * LDK * (int)sizeof(op_t);         // Q_up  [64][LDK]
-    static constexpr int KRT = QU + CH * LDK * (int)sizeof(op_t);        // K_right^T [DK][LCH]
-    static constexpr int KB = KRT + DK * LCH * (int)sizeof(op_t);        // k b   [64][LDK]
-    static constexpr int AM = KB + CH * LDK * (int)sizeof(op_t);         // A fp32 [64][LF]
-    static constexpr int TF = AM + CH * LF * 4;                          // T fp32 [64][LF]
-    static constexpr int TP = TF + CH * LF * 4;                          // T' op [64][LCH]
-    static constexpr int PM = TP + CH * LCH * (int)sizeof(op_t);         // P op  [64][LCH]
+    static constexpr int KB = QU + CH * LDK * (int)sizeof(op_t);         // k b   [64][LDK]
+    static constexpr int KRT = KB + CH * LDK * (int)sizeof(op_t);        // K_right^T [DK][LCH] (bf16)
+    static constexpr int AM = F32 ? KRT : KRT + DK * LCH * (int)sizeof(op_t);   // A fp32 [64][LF]
+    static constexpr int TF = F32 ? AM : AM + CH * LF * 4;               // T fp32 [64][LF]
+    static constexpr int TP = F32 ? AM : TF + CH * LF * 4;               // T' op [64][LCH]
+    static constexpr int PM = F32 ? AM + CH * LF * 4 : TP + CH * LCH * (int)sizeof(op_t);   // P op [64][LCH]
     static constexpr int FAC = PM + CH * LCH * (int)sizeof(op_t);        // factors fp32 [20][DK]
     static constexpr int TOT = FAC + 20 * DK * 4;                        // block sums [4][2][DK] + dummy
     static constexpr int BETA = TOT + (8 * DK + 256 + DK) * 4;          // beta [64]
     static constexpr int BYTES = BETA + CH * 4;
-    // slow path: Gamma fp32 [64][DK] over AM..TF (both fp32 [64][LF])
-    static_assert(CH * DK * 4 <= 2 * CH * LF * 4 + CH * LDK * (int)sizeof(op_t), "slow-path Gamma fits");
+    // slow path: Gamma fp32 [64][DK] over k b (fp32) or over A..T (bf16)
+    static constexpr int GAM = F32 ? KB : AM;
+    static_assert(!F32 || (LCH == LF && CH * DK * 4 <= CH * LDK * 4), "fp32 aliasing");
+    static_assert(F32 || CH * DK * 4 <= 2 * CH * LF * 4, "slow-path Gamma fits");
+    static_assert(BYTES <= 160 * 1024, "LDS");
 };
+// Position of element (r, c) of block (Rb, Ib), Ib <= Rb, of T in the fp32
+// layout: diagonal blocks in place, the others at the mirror block (Ib, Rb).
+template <int LF>
+__device__ __forceinline__ int t_at(int Rb, int Ib, int r, int c) {
+    return Rb == Ib ? (16 * Rb + r) * LF + 16 * Ib + c : (16 * Ib + r) * LF + 16 * Rb + c;
+}
 // factor rows in Lds::FAC
 constexpr int F_B = 0;      // e^{Gamma_mid(R)}, R = 0..3
 constexpr int F_W = 4;      // e^{Gamma_mid(R) - Gamma_mid(I)}, (1,0),(2,0),(2,1),(3,0),(3,1),(3,2)
@@ -239,7 +253,7 @@ __global__ __launch_bounds__(256, 1) void chunked_fwd_kernel(ChunkParams p)
     float *sFac = reinterpret_cast<float *>(smem + L::FAC);
     float *sTot = reinterpret_cast<float *>(smem + L::TOT);
     float *sBeta = reinterpret_cast<float *>(smem + L::BETA);
-    float *sGam = reinterpret_cast<float *>(smem + L::AM);   // slow path only
+    float *sGam = reinterpret_cast<float *>(smem + L::GAM);  // slow path only
 
     // ---- work unit: XCD-aware (sequence, head, slice) ------------------------
     // Blocks b and b + 8 run on the same XCD (round-robin dispatch), so the
@@ -508,10 +522,14 @@ __global__ __launch_bounds__(256, 1) void chunked_fwd_kernel(ChunkParams p)
                 store_run<F32>(&sKU[rloc * L::LDK + cbase], ku);
                 store_run<F32>(&sQU[rloc * L::LDK + cbase], qu);
                 store_run<F32>(&sKB[rloc * L::LDK + cbase], kb);
+                if constexpr (!F32) {
 #pragma unroll
-                for (int e = 0; e < RUN; ++e) store_elem(&sKRt[(cbase + e) * L::LCH + rloc], kr[e]);
+                    for (int e = 0; e < RUN; ++e) store_elem(&sKRt[(cbase + e) * L::LCH + rloc], kr[e]);
+                }
             }
-            if (has_next) load_prep(c0 + CH, clen_next);
+            // (at d_k = 128 the next chunk's rows are loaded after the A / P
+            // tiles, whose operand registers would otherwise spill)
+            if (DK <= 64 && has_next) load_prep(c0 + CH, clen_next);
             __syncthreads();
 
             // wave R: tiles (R, I), I = 0..R
@@ -552,6 +570,7 @@ __global__ __launch_bounds__(256, 1) void chunked_fwd_kernel(ChunkParams p)
                     store_elem(&sP[row * L::LCH + col], pv);
                 }
             }
+            if (DK > 64 && has_next) load_prep(c0 + CH, clen_next);
         } else {
             // ---- exact path: A and P entry by entry -----------------------------
             float Gabs[NCH];
@@ -631,8 +650,13 @@ __global__ __launch_bounds__(256, 1) void chunked_fwd_kernel(ChunkParams p)
                 }
                 store_run<F32>(&sKU[rloc * L::LDK + cbase], ku);
                 store_run<F32>(&sQU[rloc * L::LDK + cbase], qu);
+                if constexpr (F32) {
+                    // K_right itself, row-major (read with factor 1)
+                    store_run<F32>(&sKB[rloc * L::LDK + cbase], kr);
+                } else {
 #pragma unroll
-                for (int e = 0; e < RUN; ++e) store_elem(&sKRt[(cbase + e) * L::LCH + rloc], kr[e]);
+                    for (int e = 0; e < RUN; ++e) store_elem(&sKRt[(cbase + e) * L::LCH + rloc], kr[e]);
+                }
             }
             if (has_next) load_prep(c0 + CH, clen_next);
         }
@@ -666,7 +690,8 @@ __global__ __launch_bounds__(256, 1) void chunked_fwd_kernel(ChunkParams p)
 #pragma unroll
                     for (int s = 0; s < 4; ++s) {
                         const float av = sA[(16 * R + mr) * L::LF + 16 * J + 4 * jg + s];
-                        const float bv = sTf[(16 * J + 4 * jg + s) * L::LF + 16 * I + mr];
+                        const float bv = F32 ? sTf[t_at<L::LF>(J, I, 4 * jg + s, mr)]
+                                             : sTf[(16 * J + 4 * jg + s) * L::LF + 16 * I + mr];
                         Mx = mfma_f32(av, bv, Mx);
                     }
                 }
@@ -678,15 +703,22 @@ __global__ __launch_bounds__(256, 1) void chunked_fwd_kernel(ChunkParams p)
                     Tx = mfma_f32(av, Mx[s], Tx);
                 }
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    sTf[(16 * R + 4 * jg + i) * L::LF + 16 * I + mr] = -Tx[i];
+                for (int i = 0; i < 4; ++i) {
+                    if constexpr (F32) sTf[t_at<L::LF>(R, I, 4 * jg + i, mr)] = -Tx[i];
+                    else sTf[(16 * R + 4 * jg + i) * L::LF + 16 * I + mr] = -Tx[i];
+                }
             }
             __syncthreads();
         }
+        // (fp32: each thread reads a diagonal or upper position and writes the
+        // same diagonal position or a lower one, so no element is read by one
+        // thread after another has overwritten it)
         for (int idx = tid; idx < CH * CH; idx += 256) {
             const int r = idx / CH, c = idx % CH;
-            if ((c >> 4) <= (r >> 4))
-                store_elem(&sTp[r * L::LCH + c], sTf[r * L::LF + c] * sBeta[c]);
+            if ((c >> 4) <= (r >> 4)) {
+                const float t = F32 ? sTf[t_at<L::LF>(r >> 4, c >> 4, r & 15, c & 15)] : sTf[r * L::LF + c];
+                store_elem(&sTp[r * L::LCH + c], t * sBeta[c]);
+            }
         }
         __syncthreads();
 
@@ -772,7 +804,16 @@ __global__ __launch_bounds__(256, 1) void chunked_fwd_kernel(ChunkParams p)
                 const int chrow = rowmap<RUN>(rho, h, mr);
 #pragma unroll
                 for (int rr = 0; rr < CRUN; ++rr) {
-                    const frag_t fa = *reinterpret_cast<const frag_t *>(&sKRt[chrow * L::LCH + 4 * RUN * rr + RUN * jg]);
+                    frag_t fa;
+                    if constexpr (F32) {
+                        // K_right = k b e^{Gamma_last - Gamma_mid(rr)} on run rr's rows
+                        // (K_right itself on the exact path)
+                        const float fz = slow ? 1.0f : sFac[(F_Z + rr) * DK + chrow];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) fa[e] = sKB[(16 * rr + 4 * jg + e) * L::LDK + chrow] * fz;
+                    } else {
+                        fa = *reinterpret_cast<const frag_t *>(&sKRt[chrow * L::LCH + 4 * RUN * rr + RUN * jg]);
+                    }
                     S[s][tt] = mma_run<F32>(S[s][tt], fa, uf[rr]);
                 }
             }
@@ -1002,7 +1043,9 @@ hipError_t chunked_fwd_launch(const void *q, const void *k, const void *v, const
                                  p.order, nseq, T, H, dk, dv, dvs, stream);
     p.nslices = dv / dvs;
     const int nstrip = dvs / 64;
-    // fp32 inputs (d_k = 64): fp32 MFMA, 64-token chunks
+    // fp32 inputs: fp32 MFMA, 64-token chunks
+    if (dk == 128)
+        return nstrip == 2 ? launch_chunked<128, 2, true>(p, stream) : launch_chunked<128, 1, true>(p, stream);
     return nstrip == 2 ? launch_chunked<64, 2, true>(p, stream) : launch_chunked<64, 1, true>(p, stream);
 }
 

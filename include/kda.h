@@ -130,8 +130,8 @@ size_t kda_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int num_seqs
  *   workspace       : device scratch of at least kda_fwd_workspace_bytes(...) bytes
  *                                        (may be NULL when that size is 0)
  *
- * Supported: dk in {64, 128}, dv in {64, 128}; dtype KDA_BF16 for every such
- * size, KDA_F32 for dk = 64.  Zero-length sequences are allowed (S_T = S0).
+ * Supported: dk in {64, 128}, dv in {64, 128}; dtype KDA_BF16 or KDA_F32.
+ * Zero-length sequences are allowed (S_T = S0).
  * The chunk length is internal (32 tokens for bf16 inputs, 64 for fp32).
  */
 kda_status kda_fwd_chunked(const void *q, const void *k, const void *v,

@@ -75,8 +75,10 @@ def test_fwd_unsupported_sizes(L, dk, dv):
     assert fwd(L, dk=dk, dv=dv) == 2
 
 
-def test_fwd_fp32_needs_dk64(L):
-    assert fwd(L, dk=128, dv=64, dt=0) == 2
+@pytest.mark.parametrize("dt", [0, 1])
+@pytest.mark.parametrize("dk,dv", [(96, 64), (64, 32), (256, 128)])
+def test_fwd_unsupported_dims(L, dt, dk, dv):
+    assert fwd(L, dk=dk, dv=dv, dt=dt) == 2
 
 
 @pytest.mark.parametrize("kw", [dict(q=None), dict(k=None), dict(v=None), dict(g=None),

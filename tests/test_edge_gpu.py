@@ -68,7 +68,8 @@ def _check_recall(x, o, tol):
     assert err <= tol, err
 
 
-FWD_CASES = [(torch.bfloat16, 128, 128), (torch.bfloat16, 64, 64), (torch.float32, 64, 64)]
+FWD_CASES = [(torch.bfloat16, 128, 128), (torch.bfloat16, 64, 64), (torch.float32, 64, 64),
+             (torch.float32, 128, 128)]
 
 
 @pytest.mark.parametrize("kind", KINDS)

@@ -78,7 +78,7 @@ def test_gate_layouts_small(gate, B, T, H, dk, dv, dt):
 
 
 @pytest.mark.parametrize("gate", ["head", "none"])
-@pytest.mark.parametrize("dt,dk", [(torch.bfloat16, 128), (torch.float32, 64)])
+@pytest.mark.parametrize("dt,dk", [(torch.bfloat16, 128), (torch.float32, 64), (torch.float32, 128)])
 def test_gate_layouts_varlen(gate, dt, dk):
     lens = [0, 1, 63, 64, 65, 130, 0, 7]
     H = 64 if dt == torch.bfloat16 else 3     # bf16: whole d_v per workgroup
@@ -90,7 +90,8 @@ def test_gate_layouts_varlen(gate, dt, dk):
 
 
 @pytest.mark.parametrize("kind", ["all_strong", "mixed_chunks"])
-@pytest.mark.parametrize("dt,dk", [(torch.bfloat16, 128), (torch.bfloat16, 64), (torch.float32, 64)])
+@pytest.mark.parametrize("dt,dk", [(torch.bfloat16, 128), (torch.bfloat16, 64), (torch.float32, 64),
+                                   (torch.float32, 128)])
 def test_head_gate_strong_decay(kind, dt, dk):
     """Decay beyond 2^100 within a chunk: the exact per-entry path with a per-head gate."""
     _say(f"case: head gate strong decay {kind} dk{dk} {dt}")

@@ -67,6 +67,10 @@ SMALL = [
     (2, 63, 3, 64, 64, torch.float32, True),
     (1, 65, 2, 64, 128, torch.float32, True),
     (1, 200, 2, 64, 64, torch.float32, True),
+    (1, 1, 2, 128, 128, torch.float32, True),
+    (2, 100, 2, 128, 64, torch.float32, True),
+    (1, 130, 3, 128, 128, torch.float32, True),
+    (1, 70, 512, 128, 128, torch.float32, True),     # 512 units: whole d_v per workgroup
     (1, 1, 2, 128, 128, torch.bfloat16, True),
     (2, 64, 2, 128, 128, torch.bfloat16, False),
     (1, 129, 3, 128, 128, torch.bfloat16, True),
@@ -86,7 +90,8 @@ def test_small_shapes(B, T, H, dk, dv, dt, s0):
     _check_full(x, o, S_T, TOL[dt])
 
 
-@pytest.mark.parametrize("dt,dk", [(torch.bfloat16, 128), (torch.float32, 64), (torch.bfloat16, 64)])
+@pytest.mark.parametrize("dt,dk", [(torch.bfloat16, 128), (torch.float32, 64), (torch.bfloat16, 64),
+                                   (torch.float32, 128)])
 def test_varlen_small_with_empty_sequences(dt, dk):
     from gated_delta_rule_81_amd import synth
     lens = [0, 1, 63, 64, 65, 130, 0, 7]
@@ -121,10 +126,9 @@ def _strong_decay_inputs(kind, dt, dk=64, dv=64, T=192, H=2):
 
 
 @pytest.mark.parametrize("kind", ["all_strong", "resets", "mixed_chunks"])
-@pytest.mark.parametrize("dt", [torch.float32, torch.bfloat16])
-def test_strong_decay(kind, dt):
-    _say(f"case: strong decay {kind} {dt}")
-    dk = 64
+@pytest.mark.parametrize("dt,dk", [(torch.float32, 64), (torch.bfloat16, 64), (torch.float32, 128)])
+def test_strong_decay(kind, dt, dk):
+    _say(f"case: strong decay {kind} {dt} dk{dk}")
     x = _strong_decay_inputs(kind, dt, dk=dk, dv=64 if dt == torch.float32 else 128)
     _, o, S_T = _run_gpu(x)
     _check_full(x, o, S_T, TOL[dt])
