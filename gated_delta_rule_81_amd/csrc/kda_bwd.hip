@@ -34,7 +34,9 @@
 //   the forward's fused chunk kernel (kda_chunked_ws.hip) in its saving
 //   instantiation: M0, P, T and the forward state chain, storing the state
 //   entering each chunk with X and U;
-//   bwd_dstates_bf16_kernel  the state-gradient chain (64-column slices);
+//   bwd_dstates_bf16_kernel  the state-gradient chain (64-column slices; four
+//                            waves stage each chunk's operands while four
+//                            others carry 16-column strips of D);
 //   bwd_grads_bf16_kernel    the chunk gradients where every pairwise decay
 //                            factor stays below 2^64 (factorised), and
 //   bwd_grads_kernel         the exact instantiation for the other chunks.
@@ -75,6 +77,13 @@ struct Params {
     bf16_t *wTt, *wPt;                // bf16 inputs: T^T and P^T (C x C) for the gradient chain
     int32_t *wF;                     // per (chunk slot, head): 1 = exact path
 };
+
+// Layout of the bf16 state gradients (d_k x d_v) and dU (C x d_v) of a chunk
+// in the workspace: 16-column strips, each `rows` x 16 contiguous, so that
+// the gradient chain, whose waves own 16-column strips, stores whole lines.
+__device__ __forceinline__ size_t strip_off(int row, int col, int rows) {
+    return (size_t)(col >> 4) * rows * 16 + (size_t)row * 16 + (col & 15);
+}
 
 // A chunk takes the factorised path (K_dn = K e^{-Gamma} as an MFMA operand)
 // when every channel's total log2 decay is at least -64, so that e^{-Gamma}
@@ -752,7 +761,8 @@ __global__ void __launch_bounds__(NT) bwd_grads_kernel(Params p, long nslot) {
         Seg<Tin, 4> vin, oin;
         auto issue_slice = [&](int col0) {
             sin.load(gS, (size_t)sr * p.DV + col0 + sc, true);
-            din.load(gD, (size_t)sr * p.DV + col0 + sc, true);
+            din.load(gD, std::is_same<Tin, bf16_t>::value ? strip_off(sr, col0 + sc, DK)
+                                                          : (size_t)sr * p.DV + col0 + sc, true);
             const size_t e = ((size_t)(t0 + vr) * p.H + h) * p.DV + col0 + vc;
             vin.load(p.v, e, vr < cl);
             oin.load(p.dO, e, vr < cl);
@@ -1117,132 +1127,84 @@ __global__ void __launch_bounds__(NT) bwd_grads_kernel(Params p, long nslot) {
 
 
 // ---------------------------------------------------------------------------
-// bf16 inputs: the state-gradient chain on bf16 MFMA.  The state gradient
-// stays fp32 in the accumulators; its bf16 copy is both the MFMA operand and
-// what the workspace keeps.  Every product contracts over 32 rows or over
-// d_k, so each tile is one or four v_mfma_f32_16x16x32_bf16.
-
-// acc tile (rows 16 tm + 4 lj + i, cols 16 tn + lr) written transposed as
-// bf16: dst[col][row..row+3], one 8-byte store.
-__device__ __forceinline__ void store_t(__bf16 *dst, int pitch, int tm, int tn, f32x4 v) {
-    const int lane = threadIdx.x & 63, lr = lane & 15, lj = lane >> 4;
-    bf16x4 x;
-    x[0] = (__bf16)v[0];
-    x[1] = (__bf16)v[1];
-    x[2] = (__bf16)v[2];
-    x[3] = (__bf16)v[3];
-    *reinterpret_cast<bf16x4 *>(dst + (16 * tn + lr) * pitch + 16 * tm + 4 * lj) = x;
-}
-
-// The gradient chain for bf16 inputs: one workgroup of 8 waves per
-// (sequence, head, 64-column slice of d_v).  Raw k and q sit in LDS so that
-// the scaling step can run one thread per key channel: its row-major outputs
-// are then contiguous across lanes and its transposed ones are one vector
-// store per thread, with no bank conflicts.  Each chunk takes four barriers:
-// the next chunk's inputs go to LDS in the same step as the state-gradient
-// update, and its scaling (running gate sums included) in the same step as
-// the store of the state gradient.
+// bf16 inputs: the state-gradient chain, pipelined over two wave groups.
+//
+// The chain is separable over d_v columns: column j of
+//   dU = P^T dO + K_right D,   dX = Diag(beta) T^T dU,
+//   D  <- Diag(gamma) D + Q_up^T dO - K_up^T dX
+// reads column j of D, dO and dX and the chunk's matrices only.  So each of
+// the four consumer waves of a workgroup (one per sequence, head and
+// 64-column slice of d_v) owns a 16-column strip of the slice, keeps its
+// strip of D (d_k x 16, fp32) in MFMA accumulators for the whole sequence
+// and runs the three products with no synchronisation between waves.  The
+// four producer waves meanwhile build the next chunk's operands in the other
+// of two LDS slots: running log2 gate sums per key channel, K_right
+// (row-major), Q_up^T and -K_up^T, gamma, and T^T, P^T and dO^T as they come
+// from memory.  One barrier per chunk hands a slot over.
+//
+// Accumulator rows are ordered by crow(rho, h, m) = 32 rho + 8 (m >> 2) +
+// 4 h + (m & 3): a lane's four values of tiles (rho, 0) and (rho, 1) are then
+// exactly its eight k-slots of run rho of a v_mfma_f32_16x16x32_bf16 B
+// operand, so D, dU and dX feed the next product straight from registers
+// (the A operands are read at the matching permuted rows).
+// Arithmetic as before this split: bf16 operands, fp32 accumulation, D kept
+// fp32 and rounded to bf16 as an operand and for the workspace.
 constexpr int W2 = 64;                 // d_v columns per chain workgroup
-template <int DK> struct ChainLayout {
-    static constexpr int DKP = DK + 1, DKB = DK + 8, CB = C + 8;
-    static constexpr int G = 0;                            // fp32 [C][DKP]: log2 gates
-    static constexpr int KRAW = G + 4 * C * DKP;           // bf16 [C][DKB]
-    static constexpr int QRAW = KRAW + 2 * C * DKB;        // bf16 [C][DKB]
-    static constexpr int XT = QRAW + 2 * C * DKB;          // bf16 [W2][DKB]: D^T
-    static constexpr int KA = XT + 2 * W2 * DKB;           // bf16 [C][DKB]: K_right
-    static constexpr int KT1 = KA + 2 * C * DKB;           // bf16 [DK][CB]: Q_up^T
-    static constexpr int KT2 = KT1 + 2 * DK * CB;          // bf16 [DK][CB]: K_up^T
-    static constexpr int M1 = KT2 + 2 * DK * CB;           // bf16 [C][CB]: T^T
-    static constexpr int M2 = M1 + 2 * C * CB;             // bf16 [C][CB]: P^T
-    static constexpr int Y1 = M2 + 2 * C * CB;             // bf16 [W2][CB] x 2: dO^T
-    static constexpr int Y2 = Y1 + 4 * W2 * CB;            // bf16 [W2][CB]: dU^T
-    static constexpr int Y3 = Y2 + 2 * W2 * CB;            // bf16 [W2][CB]: (-dX)^T
-    static constexpr int GC = Y3 + 2 * W2 * CB;            // fp32 [DK]
-    static constexpr int GAM = GC + 4 * DK;
-    static constexpr int SB = GAM + 4 * DK;                // fp32 [C]
-    static constexpr int BYTES = SB + 4 * C;
+constexpr int CTP = C + 8;             // pitch of bf16 [*][C] operand rows
+template <int DK> struct ChainSlot {
+    static constexpr int KRP = DK + 8;
+    static constexpr int KR = 0;                         // bf16 [C][KRP]: K_right
+    static constexpr int QT = KR + 2 * C * KRP;          // bf16 [DK][CTP]: Q_up^T
+    static constexpr int KT = QT + 2 * DK * CTP;         // bf16 [DK][CTP]: -K_up^T
+    static constexpr int TT = KT + 2 * DK * CTP;         // bf16 [C][CTP]: T^T
+    static constexpr int PT = TT + 2 * C * CTP;          // bf16 [C][CTP]: P^T
+    static constexpr int OT = PT + 2 * C * CTP;          // bf16 [W2][CTP]: dO^T
+    static constexpr int GAM = OT + 2 * W2 * CTP;        // fp32 [DK]: gamma
+    static constexpr int BETA = GAM + 4 * DK;            // fp32 [C]
+    static constexpr int BYTES = BETA + 4 * C;
+    static_assert(BYTES % 16 == 0, "slot alignment");
 };
-
-// Running log2-gate sums G (inclusive), K_right = k 2^{G_c - G} row-major and
-// Q_up = q 2^G, K_up = k 2^G transposed; gc = G_c and gamma = 2^G_c.
-// Thread (channel c, block of RPT rows) reads its channel's 32 raw log2 gates
-// itself, so no separate pass over the gates is needed.
-template <int DK>
-__device__ __forceinline__ void chain_scale(const float *sG, const __bf16 *kraw, const __bf16 *qraw,
-                                            float *gc, float *gam, __bf16 *rowA, __bf16 *trA,
-                                            __bf16 *trB) {
-    constexpr int DKP = DK + 1, DKB = DK + 8, CB = C + 8, RPT = C * DK / NT2;
-    const int c = threadIdx.x % DK, r0 = (threadIdx.x / DK) * RPT;
-    float g[C];
+__device__ __forceinline__ int crow(int rho, int h, int m) {
+    return 32 * rho + 8 * (m >> 2) + 4 * h + (m & 3);
+}
+__device__ __forceinline__ bf16x8 frag2(f32x4 lo, f32x4 hi) {
+    bf16x8 f;
 #pragma unroll
-    for (int r = 0; r < C; ++r) g[r] = sG[r * DKP + c];
-    float tot = 0.0f;
-#pragma unroll
-    for (int r = 0; r < C; ++r) {
-        tot += g[r];
-        g[r] = tot;                              // inclusive running sum
+    for (int i = 0; i < 4; ++i) {
+        f[i] = (__bf16)lo[i];
+        f[4 + i] = (__bf16)hi[i];
     }
-    if (r0 == 0) {
-        gc[c] = tot;
-        gam[c] = __builtin_amdgcn_exp2f(tot);
-    }
-    bf16x8 ta[RPT / 8 > 0 ? RPT / 8 : 1], tb[RPT / 8 > 0 ? RPT / 8 : 1];
-    bf16x4 ua, ub;
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-        const int r = r0 + i;
-        // g[r0 + i] with r0 uniform per wave: select by the row block
-        float G = 0.0f;
-#pragma unroll
-        for (int b = 0; b < C / RPT; ++b)
-            if (r0 == b * RPT) G = g[b * RPT + i];
-        const float kv = (float)kraw[r * DKB + c];
-        const float E = __builtin_amdgcn_exp2f(G), R = __builtin_amdgcn_exp2f(tot - G);
-        rowA[r * DKB + c] = (__bf16)(kv * R);
-        const __bf16 a = (__bf16)((float)qraw[r * DKB + c] * E), bb = (__bf16)(kv * E);
-        if constexpr (RPT >= 8) {
-            ta[i >> 3][i & 7] = a;
-            tb[i >> 3][i & 7] = bb;
-        } else {
-            ua[i] = a;
-            ub[i] = bb;
-        }
-    }
-    if constexpr (RPT >= 8) {
-#pragma unroll
-        for (int v = 0; v < RPT / 8; ++v) {
-            *reinterpret_cast<bf16x8 *>(trA + c * CB + r0 + 8 * v) = ta[v];
-            *reinterpret_cast<bf16x8 *>(trB + c * CB + r0 + 8 * v) = tb[v];
-        }
-    } else {
-        *reinterpret_cast<bf16x4 *>(trA + c * CB + r0) = ua;
-        *reinterpret_cast<bf16x4 *>(trB + c * CB + r0) = ub;
-    }
+    return f;
 }
 
-// raw k and q rows of a chunk into LDS as bf16, log2 gates and beta as fp32
-template <int DK>
-__device__ __forceinline__ void chain_store_in(const Params &p, const ChunkIn<bf16_t, DK, true, 16> &in,
-                                               __bf16 *kraw, __bf16 *qraw, float *sG, float *sB) {
-    constexpr int DKB = DK + 8, NE = DK / 16;
-    const int tid = threadIdx.x, r = tid >> 4, c0 = (tid & 15) * NE;
-    if constexpr (NE == 8) {
-        *reinterpret_cast<uint4 *>(kraw + r * DKB + c0) =
-            in.k.ok ? make_uint4(in.k.w[0], in.k.w[1], in.k.w[2], in.k.w[3]) : make_uint4(0, 0, 0, 0);
-        *reinterpret_cast<uint4 *>(qraw + r * DKB + c0) =
-            in.q.ok ? make_uint4(in.q.w[0], in.q.w[1], in.q.w[2], in.q.w[3]) : make_uint4(0, 0, 0, 0);
-    } else {
-        *reinterpret_cast<uint2 *>(kraw + r * DKB + c0) = in.k.ok ? make_uint2(in.k.w[0], in.k.w[1]) : make_uint2(0, 0);
-        *reinterpret_cast<uint2 *>(qraw + r * DKB + c0) =
-            in.q.ok ? make_uint2(in.q.w[0], in.q.w[1]) : make_uint2(0, 0);
-    }
-    in.store_gb(p, sG, sB);
+// One 16 x 16 accumulator tile as bf16 row segments for 8-byte stores.  A
+// lane (column n, group j) holds tile rows 4 j .. 4 j + 3 of column n as two
+// bf16 pairs w0 (rows 0, 1) and w1 (rows 2, 3); after two exchanges inside
+// its quad of lanes it holds columns (n & ~3) .. + 3 of tile row
+// 4 j + quad_row(n), quad_row = 0, 2, 1, 3 for n & 3 = 0, 1, 2, 3.
+__device__ __forceinline__ int quad_row(int n) { return ((n & 1) << 1) | ((n >> 1) & 1); }
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ u32x2 quad_rows(uint32_t w0, uint32_t w1, int n) {
+    const bool odd = n & 1, up = n & 2;
+    // with lane n ^ 1: the even lane gets rows 0, 1 of columns n, n + 1, the
+    // odd lane rows 2, 3 of columns n - 1, n
+    const uint32_t r1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)(odd ? w0 : w1), 0xB1, 0xf, 0xf, false);
+    // (selects of plain values first: selects of whole expressions become branches)
+    const uint32_t a = odd ? r1 : w0, b = odd ? w1 : r1;    // columns n & ~1 and n | 1
+    const uint32_t d0 = __builtin_amdgcn_perm(b, a, 0x05040100u);   // low halves: a.lo, b.lo
+    const uint32_t d1 = __builtin_amdgcn_perm(b, a, 0x07060302u);   // high halves: a.hi, b.hi
+    // with lane n ^ 2: the other two columns of the kept row
+    const uint32_t r2 = (uint32_t)__builtin_amdgcn_mov_dpp((int)(up ? d0 : d1), 0x4E, 0xf, 0xf, false);
+    u32x2 v;
+    v.x = up ? r2 : d0;
+    v.y = up ? d1 : r2;
+    return v;
 }
 
 // (sequence-head unit, d_v slice) of a chain workgroup.  With two slices per
 // unit and a multiple of 8 units, the slices of a unit are numbered 8 apart:
 // workgroups b and b + 8 run on the same XCD, so the second read of the
-// chunk's shared inputs (k, q, gates, T, P) is served from that XCD's L2.
+// chunk's shared inputs (k, q, gates, T^T, P^T) is served from that XCD's L2.
 __device__ __forceinline__ void chain_unit(const Params &p, int b, int &unit, int &slice) {
     const int nsl = p.DV / W2;
     const long units = (long)p.num_seqs * p.H;
@@ -1255,161 +1217,341 @@ __device__ __forceinline__ void chain_unit(const Params &p, int b, int &unit, in
     }
 }
 
+// Buffer descriptor over `bytes` bytes from `base` (scalar registers): a load
+// past the end reads zeros, which masks rows past a chunk's end for free.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t brsrc_n(const void *base, uint32_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    void *u = reinterpret_cast<void *>(((uint64_t)hi << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(u, 0, bytes, 0x00020000);
+}
+
+// DPP helpers for the producer's scans: lane i of a row of 16 receives
+// x from lane i - s (0 below the row start), or lane n's x.
+template <int S> __device__ __forceinline__ float dpp_shr(float x) {
+    return __builtin_amdgcn_update_dpp(0.0f, x, 0x110 + S, 0xf, 0xf, false);
+}
+template <int N> __device__ __forceinline__ float dpp_bcast(float x) {
+    return __builtin_amdgcn_update_dpp(0.0f, x, 0x150 + N, 0xf, 0xf, false);
+}
+// x plus, where `take`, the x of the lane S below.  The shifted copy is
+// pinned so that it is formed in every lane: moved under the condition, the
+// DPP move would run with the source lanes switched off and read nothing.
+template <int S> __device__ __forceinline__ float add_from_below(float x, bool take) {
+    const float y = pinned(dpp_shr<S>(x));
+    return x + (take ? y : 0.0f);
+}
+
+// What one producer thread (pt = 0..255) reads of a chunk: four key
+// channels 4 cq .. 4 cq + 3 over RPB consecutive rows RPB rb .. (8-byte
+// loads of g, k and q), with rb = lane % NRB running over the NRB row blocks
+// within a group of NRB lanes and cq over the groups; four values of T^T and
+// of P^T; eight columns of one dO row; beta of row pt.  Buffer loads over
+// the chunk's valid rows only: rows past its end read 0.
+template <int DK> struct ChainIn {
+    static constexpr int RPB = C * DK / 1024;          // 4 (d_k = 128) or 2 (64)
+    static constexpr int NRB = C / RPB;                // 8 or 16 row blocks
+    uint2 g[RPB], k[RPB], q[RPB];
+    uint32_t b;
+    uint2 tt, pt;
+    uint4 o;
+    __device__ __forceinline__ void load(const Params &p, long t0, int cl, int h, size_t wi, int col0, int ptid) {
+        const int lane = ptid & 63, rb = lane % NRB, cq = (ptid >> 6) * (64 / NRB) + lane / NRB;
+        const uint32_t tokk = (uint32_t)p.H * DK * 2u, tokh = (uint32_t)p.H * 2u;   // bytes between rows
+        const size_t rowk = ((size_t)t0 * p.H + h) * DK, rowh = (size_t)t0 * p.H + h;
+        const bf16_t *gk = static_cast<const bf16_t *>(p.k), *gq = static_cast<const bf16_t *>(p.q);
+        const bf16_t *gg = static_cast<const bf16_t *>(p.g), *gb = static_cast<const bf16_t *>(p.beta);
+        const bool ch = p.gate == GATE_CHANNEL, hd = p.gate == GATE_HEAD;
+        const __amdgpu_buffer_rsrc_t rk = brsrc_n(gk + rowk, cl * tokk), rq = brsrc_n(gq + rowk, cl * tokk);
+        const __amdgpu_buffer_rsrc_t rg =
+            brsrc_n(ch ? gg + rowk : hd ? gg + rowh : gk, ch ? cl * tokk : hd ? cl * tokh : 0u);
+#pragma unroll
+        for (int i = 0; i < RPB; ++i) {
+            const uint32_t r = RPB * rb + i, off = r * tokk + 8u * cq;
+            k[i] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rk, off, 0, 0));
+            q[i] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rq, off, 0, 0));
+            // a per-head gate: its one value in the low half (spread over the
+            // channels when staged; no wait for the load here)
+            if (hd) g[i] = make_uint2(__builtin_amdgcn_raw_buffer_load_b16(rg, r * tokh, 0, 0), 0u);
+            else g[i] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rg, off, 0, 0));
+        }
+        tt = *reinterpret_cast<const uint2 *>(p.wTt + wi * C * C + 4 * ptid);
+        pt = *reinterpret_cast<const uint2 *>(p.wPt + wi * C * C + 4 * ptid);
+        const uint32_t tokv = (uint32_t)p.H * p.DV * 2u;
+        const __amdgpu_buffer_rsrc_t ro =
+            brsrc_n(static_cast<const bf16_t *>(p.dO) + ((size_t)t0 * p.H + h) * p.DV + col0, cl * tokv);
+        o = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                          ro, (ptid >> 3) * tokv + 16u * (ptid & 7), 0, 0));
+        const __amdgpu_buffer_rsrc_t rb_ = brsrc_n(gb + rowh, cl * tokh);
+        b = __builtin_amdgcn_raw_buffer_load_b16(rb_, ptid < C ? ptid * tokh : 0x7fffffffu, 0, 0);
+    }
+    // the chunk's operands into an LDS slot
+    __device__ __forceinline__ void stage(const Params &p, unsigned char *slot, int ptid) const {
+        using L = ChainSlot<DK>;
+        __bf16 *KR = reinterpret_cast<__bf16 *>(slot + L::KR);
+        __bf16 *QT = reinterpret_cast<__bf16 *>(slot + L::QT);
+        __bf16 *KT = reinterpret_cast<__bf16 *>(slot + L::KT);
+        const int lane = ptid & 63, rb = lane % NRB, cq = (ptid >> 6) * (64 / NRB) + lane / NRB;
+        const bool gated = p.gate != GATE_NONE;
+        auto lo = [](uint32_t w) { return __uint_as_float(w << 16); };
+        auto hi = [](uint32_t w) { return __uint_as_float(w & 0xffff0000u); };
+        // running log2-gate sums of this lane's rows (inclusive), per channel
+        float G[RPB][4];
+#pragma unroll
+        for (int i = 0; i < RPB; ++i) {
+            const bool hd = p.gate == GATE_HEAD;
+            const float x[4] = {lo(g[i].x), hd ? lo(g[i].x) : hi(g[i].x), hd ? lo(g[i].x) : lo(g[i].y),
+                                hd ? lo(g[i].x) : hi(g[i].y)};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float v = gated ? x[j] * kLog2e : 0.0f;
+                G[i][j] = i == 0 ? v : G[i - 1][j] + v;
+            }
+        }
+        // exclusive scan of the row-block totals over the NRB lanes of a
+        // group, and the chunk total gc (broadcast from the group's last lane)
+        float tot[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            float x = G[RPB - 1][j];
+            x = add_from_below<1>(x, rb >= 1);
+            x = add_from_below<2>(x, rb >= 2);
+            x = add_from_below<4>(x, rb >= 4);
+            if constexpr (NRB == 16) x = add_from_below<8>(x, rb >= 8);
+            const float below = pinned(dpp_shr<1>(x));
+            const float ex = rb >= 1 ? below : 0.0f;      // sum of the blocks before this one
+            if constexpr (NRB == 16) {
+                tot[j] = dpp_bcast<15>(x);
+            } else {
+                const float t7 = dpp_bcast<7>(x), t15 = dpp_bcast<15>(x);
+                tot[j] = (lane & 8) ? t15 : t7;
+            }
+#pragma unroll
+            for (int i = 0; i < RPB; ++i) G[i][j] += ex;
+        }
+        // K_right row-major; Q_up^T and -K_up^T transposed
+        bf16x4 qt[4], kt[4];
+#pragma unroll
+        for (int i = 0; i < RPB; ++i) {
+            const float kv[4] = {lo(k[i].x), hi(k[i].x), lo(k[i].y), hi(k[i].y)};
+            const float qv[4] = {lo(q[i].x), hi(q[i].x), lo(q[i].y), hi(q[i].y)};
+            bf16x4 kr;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float E = __builtin_amdgcn_exp2f(G[i][j]), R = __builtin_amdgcn_exp2f(tot[j] - G[i][j]);
+                kr[j] = (__bf16)(kv[j] * R);
+                qt[j][i] = (__bf16)(qv[j] * E);
+                kt[j][i] = (__bf16)(-kv[j] * E);
+            }
+            *reinterpret_cast<bf16x4 *>(KR + (RPB * rb + i) * L::KRP + 4 * cq) = kr;
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            __bf16 *dq = QT + (4 * cq + j) * CTP + RPB * rb, *dk = KT + (4 * cq + j) * CTP + RPB * rb;
+            if constexpr (RPB == 4) {
+                *reinterpret_cast<bf16x4 *>(dq) = qt[j];
+                *reinterpret_cast<bf16x4 *>(dk) = kt[j];
+            } else {
+                *reinterpret_cast<bf16x2 *>(dq) = bf16x2{qt[j][0], qt[j][1]};
+                *reinterpret_cast<bf16x2 *>(dk) = bf16x2{kt[j][0], kt[j][1]};
+            }
+        }
+        if (rb == NRB - 1) {
+            float4 gm;
+            gm.x = __builtin_amdgcn_exp2f(tot[0]);
+            gm.y = __builtin_amdgcn_exp2f(tot[1]);
+            gm.z = __builtin_amdgcn_exp2f(tot[2]);
+            gm.w = __builtin_amdgcn_exp2f(tot[3]);
+            *reinterpret_cast<float4 *>(reinterpret_cast<float *>(slot + L::GAM) + 4 * cq) = gm;
+        }
+        const int tr = ptid >> 3, tc = 4 * (ptid & 7);
+        *reinterpret_cast<uint2 *>(reinterpret_cast<__bf16 *>(slot + L::TT) + tr * CTP + tc) = tt;
+        *reinterpret_cast<uint2 *>(reinterpret_cast<__bf16 *>(slot + L::PT) + tr * CTP + tc) = pt;
+        // dO^T: this thread's row ro, columns 8 (pt & 7) ..
+        __bf16 *OT = reinterpret_cast<__bf16 *>(slot + L::OT);
+        const int ro = ptid >> 3, oc = 8 * (ptid & 7);
+        const uint32_t ow[4] = {o.x, o.y, o.z, o.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            OT[(oc + e) * CTP + ro] = __builtin_bit_cast(__bf16, (unsigned short)(ow[e >> 1] >> (16 * (e & 1))));
+        if (ptid < C) reinterpret_cast<float *>(slot + L::BETA)[ptid] = __uint_as_float(b << 16);
+    }
+};
+
 template <int DK>
 __global__ void __launch_bounds__(NT2) bwd_dstates_bf16_kernel(Params p) {
-    using L = ChainLayout<DK>;
-    constexpr int DKB = L::DKB, CB = L::CB, NTW = DK / 32;
-    __shared__ __attribute__((aligned(16))) unsigned char smem[L::BYTES];
-    float *sG = reinterpret_cast<float *>(smem + L::G);
-    __bf16 *kraw = reinterpret_cast<__bf16 *>(smem + L::KRAW);
-    __bf16 *qraw = reinterpret_cast<__bf16 *>(smem + L::QRAW);
-    __bf16 *Dt = reinterpret_cast<__bf16 *>(smem + L::XT);
-    __bf16 *Krb = reinterpret_cast<__bf16 *>(smem + L::KA);
-    __bf16 *Qt = reinterpret_cast<__bf16 *>(smem + L::KT1);
-    __bf16 *Kt = reinterpret_cast<__bf16 *>(smem + L::KT2);
-    __bf16 *TT = reinterpret_cast<__bf16 *>(smem + L::M1);
-    __bf16 *PT = reinterpret_cast<__bf16 *>(smem + L::M2);
-    __bf16 *dOt0 = reinterpret_cast<__bf16 *>(smem + L::Y1);   // dO^T of even / odd chunks
-    __bf16 *dUt = reinterpret_cast<__bf16 *>(smem + L::Y2);
-    __bf16 *mdXt = reinterpret_cast<__bf16 *>(smem + L::Y3);
-    float *gc = reinterpret_cast<float *>(smem + L::GC);
-    float *gam = reinterpret_cast<float *>(smem + L::GAM);
-    float *sB = reinterpret_cast<float *>(smem + L::SB);
+    using L = ChainSlot<DK>;
+    constexpr int NRUN = DK / 32;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * L::BYTES];
     int unit, slice;
     chain_unit(p, blockIdx.x, unit, slice);
     const int s = unit / p.H, h = unit % p.H, col0 = slice * W2;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, lj = lane >> 4;
-    // dO^T: thread (column oc, rows 4 ob .. 4 ob + 3); T^T, P^T: thread (row
-    // tr, columns tc, tc + 1)
-    const int oc = tid & 63, ob = tid >> 6, tr = tid >> 4, tc = 2 * (tid & 15);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool producer = wave >= 4;
+    const int ln = lane & 15, lj = lane >> 4;
+    const int cc = 16 * (wave & 3) + ln;                 // consumer: column within the slice
     long t0s, base;
     int len;
     seq_info(p, s, t0s, len, base);
     const int nch = (len + C - 1) / C;
     const size_t so = ((size_t)s * p.H + h) * DK;
-    ChunkIn<bf16_t, DK, true, 16> in;
-    One<bf16_t> oin[4];
-    uint32_t tin, pin;                                   // two bf16 each
-    auto issue = [&](int n) {
-        const long t0 = t0s + (long)n * C;
-        const int cl = len - n * C < C ? len - n * C : C;
-        const size_t wi = (size_t)(base + n) * p.H + h;
-        in.load(p, t0, cl, h);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = 4 * ob + i;
-            oin[i].load(p.dO, ((size_t)(t0 + r) * p.H + h) * p.DV + col0 + oc, r < cl);
+    auto chunk_len = [&](int n) { return len - n * C < C ? len - n * C : C; };
+    auto wslot = [&](int n) { return (size_t)(base + n) * p.H + h; };
+
+    // The two wave groups run separate loops with the same number of barriers
+    // (one before the first chunk and one per chunk), so that neither keeps
+    // the other's loop-invariant values in registers.
+    if (producer) {
+        // two register sets, so that a chunk's loads are issued two chunks
+        // before it is staged (one chunk of work does not cover the memory
+        // latency): ia holds chunks nch-1, nch-3, ..., ib the others
+        // Loads and stages are unconditional: a chunk index below 0 reads
+        // chunk 0 again (or nothing, for an empty sequence) and is staged
+        // into the slot no consumer reads, so that every path through the
+        // loop leaves the same loads in flight and the waits before a stage
+        // cover only the older of the two sets.
+        ChainIn<DK> ia, ib;
+        const int ptid = tid - 256;
+        auto load = [&](ChainIn<DK> &in, int n) {
+            n = n > 0 ? n : 0;
+            in.load(p, t0s + (long)n * C, chunk_len(n), h, wslot(n), col0, ptid);
+        };
+        load(ia, nch - 1);
+        load(ib, nch - 2);
+        ia.stage(p, smem + ((nch - 1) & 1) * L::BYTES, ptid);
+        load(ia, nch - 3);
+        __syncthreads();
+        // while the consumers work on chunk n: stage chunk n - 1, load n - 3
+        for (int n = nch - 1; n >= 0; n -= 2) {
+            ib.stage(p, smem + ((n - 1) & 1) * L::BYTES, ptid);
+            load(ib, n - 3);
+            __syncthreads();
+            if (n == 0) break;
+            ia.stage(p, smem + ((n - 2) & 1) * L::BYTES, ptid);
+            load(ia, n - 4);
+            __syncthreads();
         }
-        tin = *reinterpret_cast<const uint32_t *>(p.wTt + wi * C * C + 2 * tid);
-        pin = *reinterpret_cast<const uint32_t *>(p.wPt + wi * C * C + 2 * tid);
-    };
-    // chunk n's inputs into LDS (dO^T into the buffer of n's parity)
-    auto stage = [&](int n) {
-        chain_store_in<DK>(p, in, kraw, qraw, sG, sB);
-        bf16x4 ov;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) ov[i] = (__bf16)oin[i].get();
-        *reinterpret_cast<bf16x4 *>(dOt0 + (n & 1) * W2 * CB + oc * CB + 4 * ob) = ov;
-        *reinterpret_cast<uint32_t *>(TT + tr * CB + tc) = tin;
-        *reinterpret_cast<uint32_t *>(PT + tr * CB + tc) = pin;
-    };
-    f32x4 D[NTW];
-#pragma unroll
-    for (int x = 0; x < NTW; ++x) {
-        const int tt = wave * NTW + x, tm = tt >> 2, tn = tt & 3;
-        load_tile(D[x], p.dST, so + 16 * tm, p.DV, col0 + 16 * tn);
-        // landed before the loop (otherwise the wait for it would sit inside
-        // the loop, draining the memory queue every chunk)
-        D[x] = pinned(D[x]);
+        return;
     }
-    const int xm = wave >> 2, xn = wave & 3;
-    // D, the gradient of the state leaving chunk n: to D^T in LDS and to the workspace
-    auto put_grad = [&](int n) {
-        const __amdgpu_buffer_rsrc_t r =
-            brsrc(reinterpret_cast<bf16_t *>(p.wD) + ((size_t)(base + n) * p.H + h) * DK * p.DV + col0);
+    f32x4 D[NRUN][2];
 #pragma unroll
-        for (int x = 0; x < NTW; ++x) {
-            const int tt = wave * NTW + x, tm = tt >> 2, tn = tt & 3;
-            store_t(Dt, DKB, tm, tn, D[x]);
+    for (int rho = 0; rho < NRUN; ++rho)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                bst16(to_bf16(D[x][i]).x, r, (uint32_t)(((16 * tm + 4 * lj + i) * p.DV + 16 * tn + lr) * 2));
+                D[rho][hh][i] = p.dST ? p.dST[(so + crow(rho, hh, 4 * lj + i)) * p.DV + col0 + cc] : 0.0f;
+            // landed before the loop (otherwise the wait for it would sit
+            // inside the loop, draining the memory queue every chunk)
+            D[rho][hh] = pinned(D[rho][hh]);
         }
-    };
-    if (nch > 0) {
-        issue(nch - 1);
-        stage(nch - 1);
-        if (nch > 1) issue(nch - 2);
-        __syncthreads();
-        put_grad(nch - 1);
-        chain_scale<DK>(sG, kraw, qraw, gc, gam, Krb, Qt, Kt);
-        __syncthreads();
-    }
+    __syncthreads();
     for (int n = nch - 1; n >= 0; --n) {
-        const size_t wi = (size_t)(base + n) * p.H + h;
-        const __bf16 *dOt = dOt0 + (n & 1) * W2 * CB;
-        // dU^T, dU = P^T dO + K_right D
         {
-            f32x4 a = {0.f, 0.f, 0.f, 0.f};
-            a = mmb(a, PT + 16 * xm * CB, CB, dOt + 16 * xn * CB, CB, C);
-            a = mmb(a, Krb + 16 * xm * DKB, DKB, Dt + 16 * xn * DKB, DKB, DK);
-            store_t(dUt, CB, xm, xn, a);
-            const __amdgpu_buffer_rsrc_t r = brsrc(p.wdU + wi * C * p.DV + col0);
+            const unsigned char *slot = smem + (n & 1) * L::BYTES;
+            const __bf16 *KR = reinterpret_cast<const __bf16 *>(slot + L::KR);
+            const __bf16 *QT = reinterpret_cast<const __bf16 *>(slot + L::QT);
+            const __bf16 *KT = reinterpret_cast<const __bf16 *>(slot + L::KT);
+            const __bf16 *TT = reinterpret_cast<const __bf16 *>(slot + L::TT);
+            const __bf16 *PT = reinterpret_cast<const __bf16 *>(slot + L::PT);
+            const __bf16 *OT = reinterpret_cast<const __bf16 *>(slot + L::OT);
+            const float *gam = reinterpret_cast<const float *>(slot + L::GAM);
+            const float *bet = reinterpret_cast<const float *>(slot + L::BETA);
+            const size_t wi = wslot(n);
+            const int cl = chunk_len(n);
+            auto a8 = [&](const __bf16 *m, int pitch, int row, int k0) {
+                return *reinterpret_cast<const bf16x8 *>(m + row * pitch + k0 + 8 * lj);
+            };
+            // D, the gradient of the state leaving chunk n: bf16 B fragments,
+            // and to the workspace
+            bf16x8 dfr[NRUN];
+            {
+                const __amdgpu_buffer_rsrc_t r = brsrc(reinterpret_cast<bf16_t *>(p.wD) + wi * DK * p.DV +
+                                                       strip_off(0, col0 + 16 * (wave & 3), DK));
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                bst16(to_bf16(a[i]).x, r, (uint32_t)(((16 * xm + 4 * lj + i) * p.DV + 16 * xn + lr) * 2));
-        }
-        __syncthreads();
-        // (-dX)^T, dX = Diag(beta) T^T dU
-        {
-            f32x4 a = {0.f, 0.f, 0.f, 0.f};
-            a = mmb(a, TT + 16 * xm * CB, CB, dUt + 16 * xn * CB, CB, C);
-            // dX (= dV) to dv, where the gradient kernel reads it back
-            const long t0 = t0s + (long)n * C;
-            const int cl = len - n * C < C ? len - n * C : C;
-            const __amdgpu_buffer_rsrc_t rv =
-                brsrc(static_cast<bf16_t *>(p.dv) + ((size_t)t0 * p.H + h) * p.DV + col0);
+                for (int rho = 0; rho < NRUN; ++rho) {
+                    dfr[rho] = frag2(D[rho][0], D[rho][1]);
+                    const uint4 w = __builtin_bit_cast(uint4, dfr[rho]);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = 16 * xm + 4 * lj + i;
-                const float dx = sB[row] * a[i];
-                bst16(to_bf16(dx).x, rv,
-                      row < cl ? (uint32_t)((row * p.H * p.DV + 16 * xn + lr) * 2) : kDrop);
-                a[i] = -dx;
+                    for (int hh = 0; hh < 2; ++hh)
+                        __builtin_amdgcn_raw_buffer_store_b64(
+                            quad_rows(hh ? w.z : w.x, hh ? w.w : w.y, ln), r,
+                            (uint32_t)((crow(rho, hh, 4 * lj + quad_row(ln)) * 16 + (ln & ~3)) * 2), 0, 0);
+                }
             }
-            store_t(mdXt, CB, xm, xn, a);
-        }
-        __syncthreads();
-        // D = Diag(gamma) D + Q_up^T dO - K_up^T dX; the next chunk's inputs to LDS meanwhile
+            const bf16x8 ofr = *reinterpret_cast<const bf16x8 *>(OT + cc * CTP + 8 * lj);
+            // dU = P^T dO + K_right D (chunk rows in crow order)
+            f32x4 u[2];
 #pragma unroll
-        for (int x = 0; x < NTW; ++x) {
-            const int tt = wave * NTW + x, tm = tt >> 2, tn = tt & 3;
+            for (int hh = 0; hh < 2; ++hh) {
+                const int rm = crow(0, hh, ln);
+                f32x4 a = {0.f, 0.f, 0.f, 0.f};
+                a = mfma8(a8(PT, CTP, rm, 0), ofr, a);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) D[x][i] *= gam[16 * tm + 4 * lj + i];
-            D[x] = mmb(D[x], Qt + 16 * tm * CB, CB, dOt + 16 * tn * CB, CB, C);
-            D[x] = mmb(D[x], Kt + 16 * tm * CB, CB, mdXt + 16 * tn * CB, CB, C);
-        }
-        if (n > 0) {
-            stage(n - 1);
-            if (n > 1) issue(n - 2);
-        }
-        __syncthreads();
-        if (n > 0) {
-            put_grad(n - 1);
-            chain_scale<DK>(sG, kraw, qraw, gc, gam, Krb, Qt, Kt);
+                for (int rho = 0; rho < NRUN; ++rho) a = mfma8(a8(KR, L::KRP, rm, 32 * rho), dfr[rho], a);
+                u[hh] = a;
+            }
+            const bf16x8 ufr = frag2(u[0], u[1]);
+            // dX = Diag(beta) T^T dU; dX is dv
+            f32x4 x[2];
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const int rm = crow(0, hh, ln);
+                f32x4 a = {0.f, 0.f, 0.f, 0.f};
+                a = mfma8(a8(TT, CTP, rm, 0), ufr, a);
+                const float4 b4 = *reinterpret_cast<const float4 *>(bet + 8 * lj + 4 * hh);
+                x[hh][0] = b4.x * a[0];
+                x[hh][1] = b4.y * a[1];
+                x[hh][2] = b4.z * a[2];
+                x[hh][3] = b4.w * a[3];
+            }
+            const bf16x8 xfr = frag2(x[0], x[1]);
+            {
+                const long t0 = t0s + (long)n * C;
+                const int cw0 = col0 + 16 * (wave & 3);
+                const __amdgpu_buffer_rsrc_t ru = brsrc(p.wdU + wi * C * p.DV + strip_off(0, cw0, C));
+                const __amdgpu_buffer_rsrc_t rv =
+                    brsrc(static_cast<bf16_t *>(p.dv) + ((size_t)t0 * p.H + h) * p.DV + cw0);
+                const uint4 wu = __builtin_bit_cast(uint4, ufr), wx = __builtin_bit_cast(uint4, xfr);
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const int row = 8 * lj + 4 * hh + quad_row(ln);
+                    __builtin_amdgcn_raw_buffer_store_b64(quad_rows(hh ? wu.z : wu.x, hh ? wu.w : wu.y, ln), ru,
+                                                          (uint32_t)((row * 16 + (ln & ~3)) * 2), 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b64(
+                        quad_rows(hh ? wx.z : wx.x, hh ? wx.w : wx.y, ln), rv,
+                        row < cl ? (uint32_t)((row * p.H * p.DV + (ln & ~3)) * 2) : kDrop, 0, 0);
+                }
+            }
+            // D = Diag(gamma) D + Q_up^T dO - K_up^T dX
+#pragma unroll
+            for (int rho = 0; rho < NRUN; ++rho)
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const int rd = crow(rho, hh, ln);
+                    const float4 g4 = *reinterpret_cast<const float4 *>(gam + 32 * rho + 8 * lj + 4 * hh);
+                    f32x4 d = D[rho][hh];
+                    d[0] *= g4.x;
+                    d[1] *= g4.y;
+                    d[2] *= g4.z;
+                    d[3] *= g4.w;
+                    d = mfma8(a8(QT, CTP, rd, 0), ofr, d);
+                    d = mfma8(a8(KT, CTP, rd, 0), xfr, d);
+                    D[rho][hh] = d;
+                }
         }
         __syncthreads();
     }
     if (p.dS0) {
 #pragma unroll
-        for (int x = 0; x < NTW; ++x) {
-            const int tt = wave * NTW + x, tm = tt >> 2, tn = tt & 3;
+        for (int rho = 0; rho < NRUN; ++rho)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = 16 * tm + 4 * lj + i, col = col0 + 16 * tn + lr;
-                p.dS0[(so + row) * p.DV + col] = D[x][i];
-            }
-        }
+            for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    p.dS0[(so + crow(rho, hh, 4 * lj + i)) * p.DV + col0 + cc] = D[rho][hh][i];
     }
 }
 
@@ -1510,11 +1652,11 @@ __global__ void __launch_bounds__(NT2, 4) bwd_grads_bf16_kernel(Params p) {
     };
     auto issue_slice = [&](SliceIn &in, int col0) {
         in.s.load(gS, (size_t)sr * p.DV + col0 + sc, true);
-        in.d.load(gD, (size_t)sr * p.DV + col0 + sc, true);
+        in.d.load(gD, strip_off(sr, col0 + sc, DK), true);
         const size_t w = cx + (size_t)vr * p.DV + col0 + vc;
         in.x.load(p.wX, w, true);
         in.u.load(p.wU, w, true);
-        in.du.load(p.wdU, w, true);
+        in.du.load(p.wdU, cx + strip_off(vr, col0 + vc, C), true);
         const size_t e = ((size_t)(t0 + vr) * p.H + h) * p.DV + col0 + vc;
         in.dx.load(p.dv, e, vr < cl);
         in.o.load(p.dO, e, vr < cl);
