@@ -78,13 +78,6 @@ struct Params {
     int32_t *wF;                     // per (chunk slot, head): 1 = exact path
 };
 
-// Layout of the bf16 state gradients (d_k x d_v) and dU (C x d_v) of a chunk
-// in the workspace: 16-column strips, each `rows` x 16 contiguous, so that
-// the gradient chain, whose waves own 16-column strips, stores whole lines.
-__device__ __forceinline__ size_t strip_off(int row, int col, int rows) {
-    return (size_t)(col >> 4) * rows * 16 + (size_t)row * 16 + (col & 15);
-}
-
 // A chunk takes the factorised path (K_dn = K e^{-Gamma} as an MFMA operand)
 // when every channel's total log2 decay is at least -64, so that e^{-Gamma}
 // stays below 2^64; otherwise every pairwise decay factor is formed directly.
@@ -760,7 +753,8 @@ __global__ void __launch_bounds__(NT) bwd_grads_kernel(Params p, long nslot) {
         Seg<Tin, NES> sin, din;
         Seg<Tin, 4> vin, oin;
         auto issue_slice = [&](int col0) {
-            sin.load(gS, (size_t)sr * p.DV + col0 + sc, true);
+            sin.load(gS, std::is_same<Tin, bf16_t>::value ? strip_off(sr, col0 + sc, DK)
+                                                          : (size_t)sr * p.DV + col0 + sc, true);
             din.load(gD, std::is_same<Tin, bf16_t>::value ? strip_off(sr, col0 + sc, DK)
                                                           : (size_t)sr * p.DV + col0 + sc, true);
             const size_t e = ((size_t)(t0 + vr) * p.H + h) * p.DV + col0 + vc;
@@ -1175,30 +1169,6 @@ __device__ __forceinline__ bf16x8 frag2(f32x4 lo, f32x4 hi) {
         f[4 + i] = (__bf16)hi[i];
     }
     return f;
-}
-
-// One 16 x 16 accumulator tile as bf16 row segments for 8-byte stores.  A
-// lane (column n, group j) holds tile rows 4 j .. 4 j + 3 of column n as two
-// bf16 pairs w0 (rows 0, 1) and w1 (rows 2, 3); after two exchanges inside
-// its quad of lanes it holds columns (n & ~3) .. + 3 of tile row
-// 4 j + quad_row(n), quad_row = 0, 2, 1, 3 for n & 3 = 0, 1, 2, 3.
-__device__ __forceinline__ int quad_row(int n) { return ((n & 1) << 1) | ((n >> 1) & 1); }
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ u32x2 quad_rows(uint32_t w0, uint32_t w1, int n) {
-    const bool odd = n & 1, up = n & 2;
-    // with lane n ^ 1: the even lane gets rows 0, 1 of columns n, n + 1, the
-    // odd lane rows 2, 3 of columns n - 1, n
-    const uint32_t r1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)(odd ? w0 : w1), 0xB1, 0xf, 0xf, false);
-    // (selects of plain values first: selects of whole expressions become branches)
-    const uint32_t a = odd ? r1 : w0, b = odd ? w1 : r1;    // columns n & ~1 and n | 1
-    const uint32_t d0 = __builtin_amdgcn_perm(b, a, 0x05040100u);   // low halves: a.lo, b.lo
-    const uint32_t d1 = __builtin_amdgcn_perm(b, a, 0x07060302u);   // high halves: a.hi, b.hi
-    // with lane n ^ 2: the other two columns of the kept row
-    const uint32_t r2 = (uint32_t)__builtin_amdgcn_mov_dpp((int)(up ? d0 : d1), 0x4E, 0xf, 0xf, false);
-    u32x2 v;
-    v.x = up ? r2 : d0;
-    v.y = up ? d1 : r2;
-    return v;
 }
 
 // (sequence-head unit, d_v slice) of a chain workgroup.  With two slices per
@@ -1651,12 +1621,12 @@ __global__ void __launch_bounds__(NT2, 4) bwd_grads_bf16_kernel(Params p) {
         Seg<bf16_t, 4> x, u, du, dx, o;
     };
     auto issue_slice = [&](SliceIn &in, int col0) {
-        in.s.load(gS, (size_t)sr * p.DV + col0 + sc, true);
+        in.s.load(gS, strip_off(sr, col0 + sc, DK), true);
         in.d.load(gD, strip_off(sr, col0 + sc, DK), true);
-        const size_t w = cx + (size_t)vr * p.DV + col0 + vc;
+        const size_t w = cx + strip_off(vr, col0 + vc, C);
         in.x.load(p.wX, w, true);
         in.u.load(p.wU, w, true);
-        in.du.load(p.wdU, cx + strip_off(vr, col0 + vc, C), true);
+        in.du.load(p.wdU, w, true);
         const size_t e = ((size_t)(t0 + vr) * p.H + h) * p.DV + col0 + vc;
         in.dx.load(p.dv, e, vr < cl);
         in.o.load(p.dO, e, vr < cl);

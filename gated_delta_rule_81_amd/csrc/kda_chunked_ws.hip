@@ -498,10 +498,11 @@ __global__ __launch_bounds__(512, 1) void chunked_ws_kernel(WsParams p)
                         for (int r = jg; r < cl; r += 4) ob[(size_t)r * tokv + co] = to_bf16(qnan);
                     } else {
                         const size_t slotm = (size_t)(sbase + m) * H + head;
-                        for (int r = jg; r < DK; r += 4) p.wS[(slotm * DK + r) * DV + col0 + co] = to_bf16(qnan);
+                        for (int r = jg; r < DK; r += 4)
+                            p.wS[slotm * DK * DV + strip_off(r, col0 + co, DK)] = to_bf16(qnan);
                         for (int r = jg; r < C; r += 4) {
-                            p.wX[(slotm * C + r) * DV + col0 + co] = to_bf16(qnan);
-                            p.wU[(slotm * C + r) * DV + col0 + co] = to_bf16(qnan);
+                            p.wX[slotm * C * DV + strip_off(r, col0 + co, C)] = to_bf16(qnan);
+                            p.wU[slotm * C * DV + strip_off(r, col0 + co, C)] = to_bf16(qnan);
                         }
                     }
                 }
@@ -608,22 +609,23 @@ __global__ __launch_bounds__(512, 1) void chunked_ws_kernel(WsParams p)
                 bf16x8 sf[NRUN];
 #pragma unroll
                 for (int rr = 0; rr < NRUN; ++rr) sf[rr] = pack8(S[s][2 * rr], S[s][2 * rr + 1]);
-                // the lane's bf16 values of a [rows][d_v] array, element e of a
-                // fragment being row r0 + e of column co
+                // the lane's bf16 values of a [rows][d_v] array in the backward
+                // workspace's 16-column strips, element e of a fragment being
+                // row r0 + e of column 16 (w + 4 s) + mr: rows r0 .. r0 + 3 and
+                // r0 + 4 .. r0 + 7 regrouped within each quad of lanes, so that
+                // each of the two stores writes whole 128-byte lines
                 auto save_col = [&](bf16_t *base, uint32_t rows, const bf16x8 &f, uint32_t r0) {
-                    const __amdgpu_buffer_rsrc_t rs = buf_rsrc(base + ((size_t)(sbase + n) * H + head) * rows * DV + col0);
-                    const uint32_t co = 16 * (w + 4 * s) + mr;
+                    const __amdgpu_buffer_rsrc_t rs =
+                        buf_rsrc(base + ((size_t)(sbase + n) * H + head) * rows * DV +
+                                 strip_off(0, col0 + 16 * (w + 4 * s), rows));
                     // the fragment as four words, element e the half e & 1 of word e / 2
                     // (element-wise bit casts of the bf16 vector do not survive here)
                     const uint4 fw = __builtin_bit_cast(uint4, f);
-                    const uint32_t wd[4] = {fw.x, fw.y, fw.z, fw.w};
-                    // one address register per fragment; the row step is uniform
-                    const uint32_t voff = (r0 * (uint32_t)DV + co) * 2u;
 #pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        __builtin_amdgcn_raw_buffer_store_b16(
-                            (unsigned short)((e & 1) ? (wd[e >> 1] >> 16) : wd[e >> 1]), rs, voff,
-                            e * DV * 2, 0);
+                    for (int g = 0; g < 2; ++g)
+                        __builtin_amdgcn_raw_buffer_store_b64(
+                            quad_rows(g ? fw.z : fw.x, g ? fw.w : fw.y, mr), rs,
+                            ((r0 + 4u * g + (uint32_t)quad_row(mr)) * 16u + (uint32_t)(mr & ~3)) * 2u, 0, 0);
                 };
                 if constexpr (SAVE) {
                     // S entering the chunk: fragment rr holds rows 32 rr + 8 jg + e

@@ -68,4 +68,38 @@ __device__ __forceinline__ long state_row(const int32_t *state_idx, int pool, in
     return (r >= 0 && r < pool) ? (long)r : -1L;
 }
 
+// Layout of the backward's bf16 per-chunk matrices with d_v columns (the
+// states S and their gradients D, d_k x d_v; X, U and dU, 32 x d_v) in its
+// workspace: 16-column strips, each rows x 16 contiguous.  The kernels that
+// write them hold 16-column strips per wave, so every store covers whole
+// 128-byte lines.  Element (row, col) of a matrix with `rows` rows:
+__device__ __forceinline__ size_t strip_off(int row, int col, int rows) {
+    return (size_t)(col >> 4) * rows * 16 + (size_t)row * 16 + (col & 15);
+}
+
+// Four rows of a 16-column strip as bf16 row segments for 8-byte stores.  A
+// lane (column n of the strip) holds rows 0..3 of its column as two bf16
+// pairs w0 (rows 0, 1) and w1 (rows 2, 3); after two exchanges inside its
+// quad of lanes it holds columns (n & ~3) .. + 3 of row quad_row(n), where
+// quad_row = 0, 2, 1, 3 for n & 3 = 0, 1, 2, 3.  Every lane of the wave
+// must take part (the exchanges read the neighbours' registers).
+__device__ __forceinline__ int quad_row(int n) { return ((n & 1) << 1) | ((n >> 1) & 1); }
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ u32x2 quad_rows(uint32_t w0, uint32_t w1, int n) {
+    const bool odd = n & 1, up = n & 2;
+    // with lane n ^ 1: the even lane gets rows 0, 1 of columns n, n + 1, the
+    // odd lane rows 2, 3 of columns n - 1, n
+    const uint32_t r1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)(odd ? w0 : w1), 0xB1, 0xf, 0xf, false);
+    // (selects of plain values first: selects of whole expressions become branches)
+    const uint32_t a = odd ? r1 : w0, b = odd ? w1 : r1;    // columns n & ~1 and n | 1
+    const uint32_t d0 = __builtin_amdgcn_perm(b, a, 0x05040100u);   // low halves: a.lo, b.lo
+    const uint32_t d1 = __builtin_amdgcn_perm(b, a, 0x07060302u);   // high halves: a.hi, b.hi
+    // with lane n ^ 2: the other two columns of the kept row
+    const uint32_t r2 = (uint32_t)__builtin_amdgcn_mov_dpp((int)(up ? d0 : d1), 0x4E, 0xf, 0xf, false);
+    u32x2 v;
+    v.x = up ? r2 : d0;
+    v.y = up ? d1 : r2;
+    return v;
+}
+
 }  // namespace kda
