@@ -1448,7 +1448,7 @@ __global__ void __launch_bounds__(NT2) bwd_dstates_bf16_kernel(Params p) {
                     for (int hh = 0; hh < 2; ++hh)
                         __builtin_amdgcn_raw_buffer_store_b64(
                             quad_rows(hh ? w.z : w.x, hh ? w.w : w.y, ln), r,
-                            (uint32_t)((crow(rho, hh, 4 * lj + quad_row(ln)) * 16 + (ln & ~3)) * 2), 0, 0);
+                            (uint32_t)((crow(rho, hh, 4 * lj + quad_row(ln)) * 16 + (ln & ~3)) * 2), 0, kStreamStore);
                 }
             }
             const bf16x8 ofr = *reinterpret_cast<const bf16x8 *>(OT + cc * CTP + 8 * lj);
@@ -1489,7 +1489,7 @@ __global__ void __launch_bounds__(NT2) bwd_dstates_bf16_kernel(Params p) {
                 for (int hh = 0; hh < 2; ++hh) {
                     const int row = 8 * lj + 4 * hh + quad_row(ln);
                     __builtin_amdgcn_raw_buffer_store_b64(quad_rows(hh ? wu.z : wu.x, hh ? wu.w : wu.y, ln), ru,
-                                                          (uint32_t)((row * 16 + (ln & ~3)) * 2), 0, 0);
+                                                          (uint32_t)((row * 16 + (ln & ~3)) * 2), 0, kStreamStore);
                     __builtin_amdgcn_raw_buffer_store_b64(
                         quad_rows(hh ? wx.z : wx.x, hh ? wx.w : wx.y, ln), rv,
                         row < cl ? (uint32_t)((row * p.H * p.DV + (ln & ~3)) * 2) : kDrop, 0, 0);

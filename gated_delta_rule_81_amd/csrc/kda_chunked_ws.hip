@@ -625,7 +625,7 @@ __global__ __launch_bounds__(512, 1) void chunked_ws_kernel(WsParams p)
                     for (int g = 0; g < 2; ++g)
                         __builtin_amdgcn_raw_buffer_store_b64(
                             quad_rows(g ? fw.z : fw.x, g ? fw.w : fw.y, mr), rs,
-                            ((r0 + 4u * g + (uint32_t)quad_row(mr)) * 16u + (uint32_t)(mr & ~3)) * 2u, 0, 0);
+                            ((r0 + 4u * g + (uint32_t)quad_row(mr)) * 16u + (uint32_t)(mr & ~3)) * 2u, 0, kStreamStore);
                 };
                 if constexpr (SAVE) {
                     // S entering the chunk: fragment rr holds rows 32 rr + 8 jg + e

@@ -73,6 +73,10 @@ __device__ __forceinline__ long state_row(const int32_t *state_idx, int pool, in
 // workspace: 16-column strips, each rows x 16 contiguous.  The kernels that
 // write them hold 16-column strips per wave, so every store covers whole
 // 128-byte lines.  Element (row, col) of a matrix with `rows` rows:
+// Those stores are made non-temporal (the cache-policy operand of the buffer
+// store: nt): a later kernel reads the matrices, long after they would have
+// left the L2, so allocating them there only pushes out lines still in use.
+constexpr int kStreamStore = 2;
 __device__ __forceinline__ size_t strip_off(int row, int col, int rows) {
     return (size_t)(col >> 4) * rows * 16 + (size_t)row * 16 + (col & 15);
 }
