@@ -245,6 +245,42 @@ template <> struct One<bf16_t> {
     __device__ __forceinline__ float get() const { return ok ? __uint_as_float(w << 16) : 0.0f; }
 };
 
+// NE (4 or 8) consecutive fp32 of an LDS row as 16-byte accesses.  With
+// 8, lane groups 4-7 and 8-11 of each 16 take the upper half first, so that
+// the first (and the second) access of 8 or 16 neighbouring lanes covers
+// distinct banks instead of every other 16-byte column twice.
+__device__ __forceinline__ bool row4_swap() {
+    const int l = threadIdx.x & 15;
+    return (((l >> 2) ^ (l >> 3)) & 1) != 0;
+}
+// (the halves are chosen element by element and addressed by offset: a
+// select between whole vectors becomes a private array in scratch memory)
+template <int NE> __device__ __forceinline__ void row4_put(float *dst, const float *v) {
+    if constexpr (NE == 4) {
+        *reinterpret_cast<float4 *>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+    } else {
+        const bool sw = row4_swap();
+        const int o = sw ? 4 : 0;
+        *reinterpret_cast<float4 *>(dst + o) = make_float4(sw ? v[4] : v[0], sw ? v[5] : v[1],
+                                                           sw ? v[6] : v[2], sw ? v[7] : v[3]);
+        *reinterpret_cast<float4 *>(dst + (4 - o)) = make_float4(sw ? v[0] : v[4], sw ? v[1] : v[5],
+                                                                 sw ? v[2] : v[6], sw ? v[3] : v[7]);
+    }
+}
+template <int NE> __device__ __forceinline__ void row4_get(const float *src, float *v) {
+    if constexpr (NE == 4) {
+        const float4 a = *reinterpret_cast<const float4 *>(src);
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    } else {
+        const bool sw = row4_swap();
+        const int o = sw ? 4 : 0;
+        const float4 a = *reinterpret_cast<const float4 *>(src + o);
+        const float4 b = *reinterpret_cast<const float4 *>(src + (4 - o));
+        v[0] = sw ? b.x : a.x; v[1] = sw ? b.y : a.y; v[2] = sw ? b.z : a.z; v[3] = sw ? b.w : a.w;
+        v[4] = sw ? a.x : b.x; v[5] = sw ? a.y : b.y; v[6] = sw ? a.z : b.z; v[7] = sw ? a.w : b.w;
+    }
+}
+
 // The rows of one chunk that every kernel reads: k (and q) and the gate,
 // thread t holding row t / TPROW, channels (t % TPROW) * DK/TPROW onwards
 // (TPROW threads per row: 8 with 256 threads, 16 with 512); beta of row t.
@@ -280,16 +316,20 @@ template <typename Tin, int DK, bool WITH_Q, int TPROW = 8> struct ChunkIn {
         }
         if (tid < C) sB[tid] = b.get();
     }
-    // only the log2 gates and beta (k and q stay in the registers)
+    // only the log2 gates (row pitch PITCH, a multiple of 4) and beta (k and q
+    // stay in the registers), the row segment as 16-byte stores (row4_put)
+    template <int PITCH>
     __device__ __forceinline__ void store_gb(const Params &p, float *sG, float *sB) const {
+        static_assert(NE == 4 || NE == 8, "row segment of one or two 16-byte stores");
         const int tid = threadIdx.x, r = tid / TPROW, c0 = (tid % TPROW) * NE;
+        float gv[NE];
 #pragma unroll
         for (int j = 0; j < NE; ++j) {
-            float gv = 0.0f;
-            if (p.gate == GATE_CHANNEL) gv = g.get(j) * kLog2e;
-            else if (p.gate == GATE_HEAD) gv = gh.get() * kLog2e;
-            sG[r * DKP + c0 + j] = gv;
+            gv[j] = 0.0f;
+            if (p.gate == GATE_CHANNEL) gv[j] = g.get(j) * kLog2e;
+            else if (p.gate == GATE_HEAD) gv[j] = gh.get() * kLog2e;
         }
+        row4_put<NE>(sG + r * PITCH + c0, gv);
         if (tid < C) sB[tid] = b.get();
     }
 };
@@ -328,10 +368,10 @@ __device__ __forceinline__ void load_tile(f32x4 &t, const float *src, size_t row
 }
 
 // Running sums of the log2 gates down each channel (in place), their totals
-// gc and gamma = 2^gc.  Threads below DK take one channel each.
-template <int DK>
+// gc and gamma = 2^gc.  Threads below DK take one channel each.  DKP is the
+// row pitch of sG.
+template <int DK, int DKP = DK + 1>
 __device__ __forceinline__ void gate_sums(float *sG, float *gc, float *gam) {
-    constexpr int DKP = DK + 1;
     const int tid = threadIdx.x;
     if (tid < DK) {
         float x[C];
@@ -1538,8 +1578,12 @@ __global__ void __launch_bounds__(NT2) bwd_dstates_bf16_kernel(Params p) {
 constexpr int W3 = 64;                 // d_v columns per slice of the gradient kernel
 // LDS of the bf16 gradient kernel, at most 80 KB so that two 512-thread
 // workgroups share a CU (one loads while the other runs its C x C algebra).
+// The fp32 [C][d_k] arrays have a pitch of d_k + 4: rows stay 16-byte
+// aligned (row segments move as 16-byte accesses), and in the MFMA output
+// layout (rows 4j + i, columns r: r = lane & 15, j = lane >> 4) the 64 lanes
+// of an access fall in distinct banks.
 template <int DK> struct GbLayout {
-    static constexpr int DKP = DK + 1, WB = W3 + 8;
+    static constexpr int DKP = DK + 4, WB = W3 + 8;
     static constexpr int G = 0;                                   // fp32 [C][DKP]
     static constexpr int GC = G + 4 * C * DKP;                    // fp32 [DK] x 3
     static constexpr int GAM = GC + 4 * DK;
@@ -1557,16 +1601,16 @@ template <int DK> struct GbLayout {
     static constexpr int DXR = DUR + 2 * C * WB;
     static constexpr int DOR = DXR + 2 * C * WB;
     static constexpr int SLICE_END = DOR + 2 * C * WB;
-    // after the slices (in the area): M (then beta dA), dP and dA live to the
-    // end; T, dT' and Y only through the C x C algebra, then K_up, Q_up, K_dn
-    // take their place
+    // after the slices (in the area): M (then beta dA) and dP live to the
+    // end; dA, T, dT' and Y only through the C x C algebra, then K_up, Q_up,
+    // K_dn take their place
     static constexpr int MF = AREA;                               // fp32 [C][CP] x 6
     static constexpr int DPF = MF + 4 * C * CP;
     static constexpr int DAF = DPF + 4 * C * CP;
     static constexpr int TF = DAF + 4 * C * CP;
     static constexpr int DTF = TF + 4 * C * CP;
     static constexpr int YF = DTF + 4 * C * CP;
-    static constexpr int FK = TF;                                 // fp32 [C][DKP] x 3
+    static constexpr int FK = DAF;                                // fp32 [C][DKP] x 3
     static constexpr int FQ = FK + 4 * C * DKP;
     static constexpr int FKD = FQ + 4 * C * DKP;
     static constexpr int TAIL_END = FKD + 4 * C * DKP;
@@ -1645,10 +1689,10 @@ __global__ void __launch_bounds__(NT2, 4) bwd_grads_bf16_kernel(Params p) {
     min.load(p.wM, wi * C * C + t4, vt);
     issue_slice(s0, 0);
     issue_slice(s1, p.DV > W3 ? W3 : 0);
-    in.store_gb(p, sG, sB);
+    in.template store_gb<DKP>(p, sG, sB);
     if (tid < C) dB[tid] = 0.0f;
     __syncthreads();
-    gate_sums<DK>(sG, gc, gam);
+    gate_sums<DK, DKP>(sG, gc, gam);
 
     f32x4 aQ[NTW], aK[NTW], aR[NTW], aT = {0.f, 0.f, 0.f, 0.f}, aP = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -1770,19 +1814,27 @@ __global__ void __launch_bounds__(NT2, 4) bwd_grads_bf16_kernel(Params p) {
         }
         dB[r] += acc;
     }
+    // (K_up, Q_up and K_dn take the place of dA, read just above)
+    __syncthreads();
     // fp32 K_up, Q_up, K_dn for the decay-weighted sums
     float *fK = reinterpret_cast<float *>(smem + L::FK), *fQ = reinterpret_cast<float *>(smem + L::FQ);
     float *fKd = reinterpret_cast<float *>(smem + L::FKD);
     {
-        const int r = tid >> 4, c0 = (tid & 15) * NE;
+        const int r = tid >> 4, c0 = (tid & 15) * NE, o = r * DKP + c0;
+        float G[NE], v[NE];
+        row4_get<NE>(sG + o, G);
+        // one array at a time, so that few values are live at once
 #pragma unroll
-        for (int j = 0; j < NE; ++j) {
-            const int o = r * DKP + c0 + j;
-            const float G = sG[o], E = __builtin_amdgcn_exp2f(G), Ei = __builtin_amdgcn_exp2f(-G);
-            fK[o] = in.k.get(j) * E;
-            fQ[o] = in.q.get(j) * E;
-            fKd[o] = in.k.get(j) * Ei;
-        }
+        for (int j = 0; j < NE; ++j) v[j] = in.k.get(j) * __builtin_amdgcn_exp2f(-G[j]);
+        row4_put<NE>(fKd + o, v);
+#pragma unroll
+        for (int j = 0; j < NE; ++j) G[j] = __builtin_amdgcn_exp2f(G[j]);
+#pragma unroll
+        for (int j = 0; j < NE; ++j) v[j] = in.k.get(j) * G[j];
+        row4_put<NE>(fK + o, v);
+#pragma unroll
+        for (int j = 0; j < NE; ++j) v[j] = in.q.get(j) * G[j];
+        row4_put<NE>(fQ + o, v);
     }
     __syncthreads();
     // factorised decay sums and the direct terms, combined per element:
@@ -1850,13 +1902,17 @@ __global__ void __launch_bounds__(NT2, 4) bwd_grads_bf16_kernel(Params p) {
         const int r = tid >> 4, c0 = (tid & 15) * NE;
         if (r < cl) {
             const size_t e = ((size_t)(t0 + r) * p.H + h) * DK + c0;
+            float v[NE];
             vec a, b, g;
+            row4_get<NE>(fQ + r * DKP + c0, v);
 #pragma unroll
-            for (int j = 0; j < NE; ++j) {
-                a[j] = (__bf16)fQ[r * DKP + c0 + j];
-                b[j] = (__bf16)fK[r * DKP + c0 + j];
-                g[j] = (__bf16)fKd[r * DKP + c0 + j];
-            }
+            for (int j = 0; j < NE; ++j) a[j] = (__bf16)v[j];
+            row4_get<NE>(fK + r * DKP + c0, v);
+#pragma unroll
+            for (int j = 0; j < NE; ++j) b[j] = (__bf16)v[j];
+            row4_get<NE>(fKd + r * DKP + c0, v);
+#pragma unroll
+            for (int j = 0; j < NE; ++j) g[j] = (__bf16)v[j];
             *reinterpret_cast<vec *>(static_cast<bf16_t *>(p.dq) + e) = a;
             *reinterpret_cast<vec *>(static_cast<bf16_t *>(p.dk) + e) = b;
             if (p.gate == GATE_CHANNEL) *reinterpret_cast<vec *>(static_cast<bf16_t *>(p.dg) + e) = g;
@@ -1866,8 +1922,10 @@ __global__ void __launch_bounds__(NT2, 4) bwd_grads_bf16_kernel(Params p) {
         const size_t e = (size_t)(t0 + tid) * p.H + h;
         st<bf16_t>(p.dbeta, e, dB[tid]);
         if (p.gate == GATE_HEAD) {
+            // each lane starts at its own channel, so that the rows' reads
+            // spread over the banks
             float acc = 0.0f;
-            for (int c = 0; c < DK; ++c) acc += fKd[tid * DKP + c];
+            for (int i = 0; i < DK; ++i) acc += fKd[tid * DKP + ((i + tid) & (DK - 1))];
             st<bf16_t>(p.dg, e, acc);
         }
     }
