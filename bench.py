@@ -7,10 +7,12 @@ chunked_ws_kernel, 32-token chunks) over the B=4, H=32, T=8192, d_k=d_v=128
 bf16 workload with fp32 state, inputs already resident in HBM.  Reported
 value: tokens/s (B*T per step time).
 
-The headline is timed after every other GPU leg below, so that its W warmup
-and K timed calls see the clock the GPU holds in continuous use (a cold GPU
-runs the first ~60 back-to-back calls up to ~30% slower; `--only forward`
-times it cold); `timed_after` lists those legs.
+The headline is timed last: after every other GPU leg below, and right after
+`forward_steady` (300 untimed and 100 timed calls of the same kernel on the
+same inputs), so that its W warmup and K timed calls see the clock the GPU
+holds in continuous use.  A cold GPU runs the first ~60 back-to-back calls up
+to ~30% slower (power management; `--only forward` times it cold);
+`timed_after` lists the legs run before it.
 
 Also reported on the same JSON line:
   roofline      the chunked kernel's algorithmic HBM bytes per launch over its
@@ -27,9 +29,9 @@ Also reported on the same JSON line:
                 also the same step on states at scattered rows of a pool, and
                 four tokens per sequence per call from such a pool (decode
                 kernel and chunked forward)
-  forward_steady  the headline forward timed again after 300 untimed calls,
-                once the GPU clock has settled (a diagnostic; `value` keeps the
-                contract's W warmup + K timed steps)
+  forward_steady  the headline forward after 300 untimed calls, once the GPU
+                clock has settled: 100 timed calls, run just before the
+                headline's own W warmup + K timed steps (which give `value`)
   copy_ceiling  practical HBM ceiling: 1 GiB moved by the library's streaming
                 copy and in-place read-modify-write kernels (the decode step's
                 access pattern) and by torch's device copy
@@ -153,7 +155,9 @@ def time_loop(torch, fn, steps, warmup):
     return e0.elapsed_time(e1) / 1000.0   # seconds
 
 
-def bench_forward(torch, kda, synth, steps, warmup):
+def bench_forward(torch, kda, synth, steps, warmup, settle=0):
+    """The headline: W warmup + K timed calls of the chunked forward; with
+    `settle`, forward_steady runs on the same inputs just before them."""
     w = synth.FWD_H32_T8K
     log(f"[bench] generating {w.name} on the GPU")
     x = synth.fwd_inputs(w, device="cuda")
@@ -165,33 +169,23 @@ def bench_forward(torch, kda, synth, steps, warmup):
         kda.fwd_chunked(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["S0"], None,
                         o=o, S_T=S_T)
 
+    nbytes = fwd_algorithmic_bytes(B, T, H, dk, dv, N)
+    flops = fwd_useful_flops(B, T, H, dk, dv)
+    steady = forward_steady(torch, step, B, T, nbytes, settle) if settle else None
     log(f"[bench] chunked forward: {warmup} warmup + {steps} timed steps")
     secs = time_loop(torch, step, steps, warmup)
     t_step = secs / steps
-    nbytes = fwd_algorithmic_bytes(B, T, H, dk, dv, N)
-    flops = fwd_useful_flops(B, T, H, dk, dv)
     return dict(w=w, x=x, t_step=t_step, bytes=nbytes, flops=flops,
-                tokens_per_s=B * T / t_step)
+                tokens_per_s=B * T / t_step, steady=steady)
 
 
-def bench_forward_steady(torch, kda, fw, settle=300, steps=100):
-    """The headline forward again after `settle` back-to-back untimed calls
-    (about 0.15 s): the GPU's clock settles within the first ~60 calls of a
-    busy stretch, so the contract's short warmup times part of that ramp.
-    A diagnostic beside `value`, which stays the contract's measurement."""
-    x = fw["x"]
-    B, T, H, dv, N = x["B"], x["T"], x["H"], x["dv"], x["N"]
-    o = torch.empty((B, T, H, dv), dtype=fw["w"].dtype, device="cuda")
-    S_T = torch.empty((N, H, x["dk"], dv), dtype=torch.float32, device="cuda")
-
-    def step():
-        kda.fwd_chunked(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["S0"], None,
-                        o=o, S_T=S_T)
-
+def forward_steady(torch, step, B, T, nbytes, settle=300, steps=100):
+    """The headline forward after `settle` back-to-back untimed calls (about
+    0.15 s; the GPU's clock settles within the first ~60 calls of a busy
+    stretch), then `steps` timed calls."""
     log(f"[bench] chunked forward, settled clock: {settle} untimed + {steps} timed calls")
     secs = time_loop(torch, step, steps, settle) / steps
-    gbs = fw["bytes"] / secs / 1e9
-    del o, S_T
+    gbs = nbytes / secs / 1e9
     return {"settle_calls": settle, "steps": steps, "us_per_call": round(secs * 1e6, 2),
             "tokens_per_s": round(B * T / secs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
 
@@ -515,10 +509,11 @@ def main():
                                      "us_per_step": round(dc["t_step"] * 1e6, 2)}}), flush=True)
         return
 
-    # Every leg but the headline runs first, so that the headline's W warmup
-    # and K timed calls see the GPU at the clock it holds in continuous use
-    # (a cold GPU runs the first ~60 back-to-back calls up to ~30% slower;
-    # `--only forward` times it cold).
+    # Every leg but the headline runs first, and forward_steady just before it
+    # (inside bench_forward), so that the headline's W warmup and K timed calls
+    # see the GPU at the clock it holds in continuous use (a cold GPU runs the
+    # first ~60 back-to-back calls up to ~30% slower; `--only forward` times it
+    # cold).
     other = {}
     if args.only is None:
         other["workloads"] = bench_other_workloads(torch, kda, synth)
@@ -543,7 +538,8 @@ def main():
         other["copy_ceiling_GBps"] = max(ceil["stream_copy"], ceil["stream_rmw"])
         other["copy_ceiling"] = ceil
 
-    fw = bench_forward(torch, kda, synth, args.steps, args.warmup)
+    fw = bench_forward(torch, kda, synth, args.steps, args.warmup,
+                       settle=300 if args.only is None else 0)
     achieved = fw["bytes"] / fw["t_step"] / 1e9
     traffic = read_traffic("chunked_ws_kernel_B4_H32_T8192_d128.pmc.md", "chunked_ws_kernel")
     roofline = {
@@ -579,13 +575,14 @@ def main():
         "config": {"workload": fw["w"].name, "B": 4, "T": 8192, "H": 32, "dk": 128, "dv": 128,
                    "chunk": CHUNK, "state": "fp32", "parallelism": "single GPU"},
         "roofline": roofline,
-        "timed_after": [k for k in ("workloads", "backward", "decode", "copy_ceiling") if k in other],
+        "timed_after": [k for k in ("workloads", "backward", "decode", "copy_ceiling") if k in other]
+                       + (["forward_steady"] if fw["steady"] else []),
     }
     if args.only == "forward":
         print(json.dumps(out), flush=True)
         return
     out.update(other)
-    out["forward_steady"] = bench_forward_steady(torch, kda, fw)
+    out["forward_steady"] = fw["steady"]
     if not args.no_cpu:
         log("[bench] oracle CPU baseline")
         out["cpu_baseline"] = cpu_baseline(torch, fw["x"])
