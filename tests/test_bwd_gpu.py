@@ -102,9 +102,10 @@ def test_bwd_small(B, T, H, dk, dv, dt):
 
 @pytest.mark.parametrize("gate", ["head", "none"])
 @pytest.mark.parametrize("dt", [torch.float32, torch.bfloat16])
-def test_bwd_gate_layouts(gate, dt):
-    _say(f"[bwd gate={gate}] {dt}")
-    x = _case(1, 120, 2, 64, 64, dt, seed=41, gate=gate)
+@pytest.mark.parametrize("dk,dv", [(64, 64), (128, 128)])
+def test_bwd_gate_layouts(gate, dt, dk, dv):
+    _say(f"[bwd gate={gate}] dk={dk} dv={dv} {dt}")
+    x = _case(1, 120, 2, dk, dv, dt, seed=41, gate=gate)
     _compare(_gpu(x, gate), _ref(x, gate), TOL[dt], gate)
 
 
