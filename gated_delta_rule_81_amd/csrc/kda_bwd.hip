@@ -1591,7 +1591,8 @@ template <int DK> struct GbLayout {
     static constexpr int RKP = DGP + 4 * DK;                      // fp32 [2][DK]
     static constexpr int SB = RKP + 8 * DK;                       // fp32 [C] x 2
     static constexpr int DB = SB + 4 * C;
-    static constexpr int AREA = DB + 4 * C;
+    static constexpr int DBP = DB + 4 * C;                        // fp32 [2][C]
+    static constexpr int AREA = DBP + 8 * C;
     // slice phase (in the area): bf16, row-major
     static constexpr int SR = AREA;                               // [DK][WB]
     static constexpr int DR = SR + 2 * DK * WB;
@@ -1602,15 +1603,14 @@ template <int DK> struct GbLayout {
     static constexpr int DOR = DXR + 2 * C * WB;
     static constexpr int SLICE_END = DOR + 2 * C * WB;
     // after the slices (in the area): M (then beta dA) and dP live to the
-    // end; dA, T, dT' and Y only through the C x C algebra, then K_up, Q_up,
-    // K_dn take their place
-    static constexpr int MF = AREA;                               // fp32 [C][CP] x 6
+    // end; T, dT' and Y only through the C x C algebra, then K_up, Q_up, K_dn
+    // take their place (dA itself never leaves the registers)
+    static constexpr int MF = AREA;                               // fp32 [C][CP] x 5
     static constexpr int DPF = MF + 4 * C * CP;
-    static constexpr int DAF = DPF + 4 * C * CP;
-    static constexpr int TF = DAF + 4 * C * CP;
+    static constexpr int TF = DPF + 4 * C * CP;
     static constexpr int DTF = TF + 4 * C * CP;
     static constexpr int YF = DTF + 4 * C * CP;
-    static constexpr int FK = DAF;                                // fp32 [C][DKP] x 3
+    static constexpr int FK = TF;                                 // fp32 [C][DKP] x 3
     static constexpr int FQ = FK + 4 * C * DKP;
     static constexpr int FKD = FQ + 4 * C * DKP;
     static constexpr int TAIL_END = FKD + 4 * C * DKP;
@@ -1758,7 +1758,8 @@ __global__ void __launch_bounds__(NT2, 4) bwd_grads_bf16_kernel(Params p) {
 
     // C x C algebra (fp32)
     float *sdT = reinterpret_cast<float *>(smem + L::DTF), *sdP = reinterpret_cast<float *>(smem + L::DPF);
-    float *sY = reinterpret_cast<float *>(smem + L::YF), *sdA = reinterpret_cast<float *>(smem + L::DAF);
+    float *sY = reinterpret_cast<float *>(smem + L::YF);
+    float *dBp = reinterpret_cast<float *>(smem + L::DBP);
     if (vt) {
         const int tr = t4 / C, tc = t4 % C;
 #pragma unroll
@@ -1774,47 +1775,52 @@ __global__ void __launch_bounds__(NT2, 4) bwd_grads_bf16_kernel(Params p) {
         else sdP[row * CP + col] = col <= row ? aP[i] : 0.0f;
     }
     __syncthreads();
-    if (tid < C) {
-        float acc = 0.0f;
-#pragma unroll 8
-        for (int r = 0; r < C; ++r) acc += sT[r * CP + tid] * sdT[r * CP + tid];
-        dB[tid] = acc;
-    }
-    __syncthreads();
-    for (int idx = tid; idx < C * C; idx += NT2) {
-        const int r = idx / C, i = idx % C;
-        sdT[r * CP + i] *= sB[i];
-    }
-    __syncthreads();
     if (lo) {
+        // Y = T^T (dT' Diag(beta)) (waves 0-3, one 16 x 16 tile each), the
+        // column scale folded into the operand reads: every element this lane
+        // reads of dT' lies in its column 16 tn + lr
+        const float fb = sB[16 * tn + lr];
+        const float *pa = sT + 16 * tm + lr + lj * CP, *pb = sdT + lj * CP + 16 * tn + lr;
         f32x4 a = {0.f, 0.f, 0.f, 0.f};
-        a = mm(a, sT + 16 * tm, 1, CP, sdT + 16 * tn, CP, 1, C);
+#pragma unroll
+        for (int k0 = 0; k0 < C; k0 += 4) a = mfma4(pa[k0 * CP], pb[k0 * CP] * fb, a);
 #pragma unroll
         for (int i = 0; i < 4; ++i) sY[(16 * tm + 4 * lj + i) * CP + 16 * tn + lr] = a[i];
+    } else if (tid < 256 + C) {
+        // meanwhile, on waves with no share of the two products: dbeta's first
+        // term, the column sums of T o dT'
+        const int c = tid - 256;
+        float acc = 0.0f;
+#pragma unroll 8
+        for (int r = 0; r < C; ++r) acc += sT[r * CP + c] * sdT[r * CP + c];
+        dB[c] = acc;
     }
     __syncthreads();
     if (lo) {
+        // dA = -strict_lower(Y T^T), used where it lands: M <- Diag(beta) dA in
+        // place, and dbeta's second term, the row sums of dA o M (M before the
+        // update), per tile over its 16 columns (the lanes of a 16-lane group);
+        // the two column tiles' sums are added in a fixed order at the output
         f32x4 a = {0.f, 0.f, 0.f, 0.f};
         a = mm(a, sY + 16 * tm * CP, CP, 1, sT + 16 * tn * CP, 1, CP, C);
+        float part[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int row = 16 * tm + 4 * lj + i, col = 16 * tn + lr;
-            sdA[row * CP + col] = col < row ? -a[i] : 0.0f;
+            const float da = col < row ? -a[i] : 0.0f;
+            part[i] = da * sM[row * CP + col];
+            sM[row * CP + col] = sB[row] * da;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int off = 1; off < 16; off <<= 1) part[i] += __shfl_xor(part[i], off);
+        if (lr == 0) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dBp[tn * C + 16 * tm + 4 * lj + i] = part[i];
         }
     }
-    __syncthreads();
-    if (tid < C) {
-        const int r = tid;
-        float acc = 0.0f;
-#pragma unroll 8
-        for (int i = 0; i < C; ++i) {
-            const float a = sdA[r * CP + i];
-            acc += a * sM[r * CP + i];
-            sM[r * CP + i] = sB[r] * a;
-        }
-        dB[r] += acc;
-    }
-    // (K_up, Q_up and K_dn take the place of dA, read just above)
+    // (K_up, Q_up and K_dn take the place of T, dT' and Y, read just above)
     __syncthreads();
     // fp32 K_up, Q_up, K_dn for the decay-weighted sums
     float *fK = reinterpret_cast<float *>(smem + L::FK), *fQ = reinterpret_cast<float *>(smem + L::FQ);
@@ -1920,7 +1926,7 @@ __global__ void __launch_bounds__(NT2, 4) bwd_grads_bf16_kernel(Params p) {
     }
     if (tid < cl) {
         const size_t e = (size_t)(t0 + tid) * p.H + h;
-        st<bf16_t>(p.dbeta, e, dB[tid]);
+        st<bf16_t>(p.dbeta, e, dB[tid] + dBp[tid] + dBp[C + tid]);
         if (p.gate == GATE_HEAD) {
             // each lane starts at its own channel, so that the rows' reads
             // spread over the banks
